@@ -1,0 +1,81 @@
+"""Algorithmic byte counts for the verify/commit path (host-side bookkeeping only).
+
+"Algorithmic" bytes are what the method itself must move through HBM, each tensor
+once: the committed state read once per head by verify, every per-node input read once
+and every output written once, and the commit's read-modify-write of the accepted
+head's state plus the path rows it folds in.  Re-reads that a kernel happens to make
+through L2 are not counted.  These are the figures the roofline fraction divides by.
+
+Memory arithmetic of the TreeWY paper (arXiv 2608.20961, §2 "The memory problem" and
+§3 "Reconstruct on commit") is reproduced by ``gdn_state_bytes`` and friends and pinned
+by ``tests/golden/memory_arithmetic.json``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .inputs import tree_depths
+
+D = 128
+
+
+def gdn_state_bytes(layers: int, heads: int, dv: int = D, dk: int = D, elem: int = 2) -> int:
+    """Recurrent state held per sequence by the GDN layers: layers x heads x dv x dk."""
+    return layers * heads * dv * dk * elem
+
+
+def kv_bytes_per_token(softmax_layers: int, kv_heads: int, head_dim: int, elem: int = 2) -> int:
+    """Softmax KV cache per token: K and V for every softmax layer and KV head."""
+    return 2 * softmax_layers * kv_heads * head_dim * elem
+
+
+def storeall_blocks(n_nodes: int) -> int:
+    """Full-state snapshotting keeps the committed state plus one state per draft node."""
+    return n_nodes + 1
+
+
+def verify_bytes_per_head(N: int, elem: int, d: int = D) -> int:
+    """S0 read + per node (q, k, v rows, alpha, beta read; O, U rows and gamma written)."""
+    return 4 * d * d + N * (3 * d * elem + 8 + 2 * 4 * d + 4)
+
+
+def commit_bytes_per_head(depth_a: int, elem: int, d: int = D) -> int:
+    """Accepted head: S read + written, and depth(a) path rows of U (fp32), K and gamma."""
+    if depth_a <= 0:
+        return 0
+    return 2 * 4 * d * d + depth_a * (4 * d + elem * d + 4)
+
+
+def snapshot_verify_bytes_per_head(N: int, elem: int, d: int = D) -> int:
+    """S0 read + per node (q, k, v, alpha, beta read; O row and a full fp32 state written)."""
+    return 4 * d * d + N * (3 * d * elem + 8 + 4 * d + 4 * d * d)
+
+
+def snapshot_commit_bytes_per_head(accepted: int, d: int = D) -> int:
+    """Accepted head: copy its snapshot over S (read + write); nothing when a = -1."""
+    return 0 if accepted < 0 else 2 * 4 * d * d
+
+
+def step_bytes(parent: np.ndarray, accepted: np.ndarray, H: int, N: int, elem: int,
+               layers: int = 1) -> dict:
+    """Algorithmic bytes of one verify+commit pass over all layers, from the actual draws."""
+    B = parent.shape[0]
+    v = layers * (B * H * verify_bytes_per_head(N, elem) + B * 4 * N)
+    c = 0
+    for b in range(B):
+        a = int(accepted[b])
+        c += 4
+        if a >= 0:
+            da = int(tree_depths(parent[b])[a])
+            c += 4 * N + H * commit_bytes_per_head(da, elem)
+    c *= layers
+    return dict(verify=v, commit=c, total=v + c)
+
+
+def snapshot_step_bytes(parent: np.ndarray, accepted: np.ndarray, H: int, N: int, elem: int,
+                        layers: int = 1) -> dict:
+    B = parent.shape[0]
+    v = layers * (B * H * snapshot_verify_bytes_per_head(N, elem) + B * 4 * N)
+    c = layers * sum(4 + H * snapshot_commit_bytes_per_head(int(a)) for a in accepted)
+    return dict(verify=v, commit=c, total=v + c)

@@ -1,0 +1,135 @@
+"""Host logic: the seeded generator's laws and the byte accounting."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from linear_attention_speculative_head_amd import accounting, inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def is_dfs_preorder(parent):
+    """Every node's parent lies on the root-to-(t-1) path (or is S0)."""
+    path = []
+    for t, p in enumerate(parent):
+        if p >= 0:
+            if p not in path:
+                return False
+            path = path[: path.index(p) + 1]
+        else:
+            path = []
+        path.append(t)
+    return True
+
+
+def test_full_tree_node_counts_match_paper_tables():
+    """Tables 2 and 4 of the TreeWY paper: (w1,w2,w3) -> N nodes, store-all blk = N + 1."""
+    g = json.load(open(os.path.join(GOLDEN, "tree_shapes.json")))
+    for row in g["shapes"]:
+        par = inputs.full_tree(row["widths"])
+        assert len(par) == row["N"]
+        if row["blk"] is not None:
+            assert accounting.storeall_blocks(len(par)) == row["blk"]
+        assert is_dfs_preorder(par)
+        d = inputs.tree_depths(par)
+        assert d.max() == len(row["widths"])
+        # per-level branching
+        for lvl, w in enumerate(row["widths"]):
+            kids = [np.sum(par == p) for p in ([-1] if lvl == 0 else np.flatnonzero(d == lvl))]
+            assert all(k == w for k in kids)
+
+
+def test_memory_arithmetic_matches_paper():
+    """§2 of the paper: GDN state 30 / 90 MiB per sequence, KV 20 / 30 KiB per token,
+    store-all for a chain of k = 3 keeps 4 states (120 / 360 MiB); §3: a pseudo-value row is
+    128x smaller than a state."""
+    g = json.load(open(os.path.join(GOLDEN, "memory_arithmetic.json")))
+    for m in g["models"]:
+        st = accounting.gdn_state_bytes(m["gdn_layers"], m["value_heads"], g["dv"], g["dk"], g["elem_bytes"])
+        assert st == m["state_MiB_per_seq"] * 2 ** 20
+        kv = accounting.kv_bytes_per_token(m["softmax_layers"], g["kv_heads"], g["softmax_head_dim"], g["elem_bytes"])
+        assert kv == m["kv_KiB_per_token"] * 2 ** 10
+        assert accounting.storeall_blocks(3) * st == m["storeall_k3_MiB_per_seq"] * 2 ** 20
+    assert g["dk"] * g["dv"] // g["dv"] == g["pseudo_value_vs_state_ratio"]
+
+
+@pytest.mark.parametrize("N,md,mb", [(16, 5, 4), (64, 6, 8), (32, 6, 4), (5, 1, 5), (20, 3, 3)])
+def test_random_tree_laws(N, md, mb):
+    rng = np.random.default_rng(N * 100 + md)
+    for _ in range(30):
+        par = inputs.random_tree(rng, N, md, mb)
+        assert par.dtype == np.int32 and len(par) == N
+        assert all(-1 <= p < t for t, p in enumerate(par))
+        assert is_dfs_preorder(par)
+        assert inputs.tree_depths(par).max() <= md
+        counts = np.bincount(par + 1, minlength=N + 1)
+        assert counts.max() <= mb
+
+
+def test_random_tree_impossible_shape_raises():
+    with pytest.raises(ValueError):
+        inputs.random_tree(np.random.default_rng(0), 10, 2, 2)   # holds at most 6 nodes
+
+
+def test_seeds_reproduce_bit_exactly():
+    a = inputs.make_problem(2, B=8)
+    b = inputs.make_problem(2, B=8)
+    assert np.array_equal(a.parent, b.parent) and np.array_equal(a.accepted, b.accepted)
+    for x, y in zip(vars(a.layers[0]).values(), vars(b.layers[0]).values()):
+        assert np.array_equal(x, y)
+    c = inputs.make_problem(2, instance=1, B=8)
+    assert not np.array_equal(a.layers[0].S0, c.layers[0].S0)
+
+
+def test_layer_seeds_are_independent_of_layer_count():
+    a = inputs.make_problem(3, layers=1, B=2)
+    b = inputs.make_problem(3, layers=2, B=2)
+    assert np.array_equal(a.layers[0].k, b.layers[0].k)
+    assert not np.array_equal(b.layers[0].k, b.layers[1].k)
+
+
+def test_value_laws():
+    P = inputs.make_problem(2, B=16)
+    L = P.layers[0]
+    assert L.S0.shape == (16, 32, 128, 128) and L.q.shape == (16, 16, 32, 128)
+    assert abs(L.S0.std() - 0.05) < 1e-3
+    nk = np.linalg.norm(L.k.astype(np.float64), axis=-1)
+    assert np.all(np.abs(nk - 1) < 1e-2)                # unit to bf16 precision
+    for x in (L.q, L.k, L.v):                           # bf16-exact values
+        assert np.all((x.view(np.uint32) & 0xFFFF) == 0)
+    assert L.alpha.min() >= 0.9 and L.alpha.max() < 0.999
+    assert L.beta.min() > 0 and L.beta.max() < 1
+    P0 = inputs.make_problem(0)
+    assert P0.dtype == "f32" and np.any(P0.layers[0].k.view(np.uint32) & 0xFFFF)
+
+
+def test_round_bf16_ties_to_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -9], dtype=np.float32)
+    r = inputs.round_bf16(x)
+    assert list(r) == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 1.0]
+
+
+def test_accepted_laws():
+    P1 = inputs.make_problem(1, layers=0)
+    assert P1.accepted.min() >= -1 and P1.accepted.max() <= 3
+    assert np.array_equal(P1.parent[0], inputs.chain_tree(4))
+    frac_none = np.mean(np.concatenate([inputs.make_problem(1, instance=i, layers=0).accepted
+                                        for i in range(20)]) == -1)
+    assert 0.12 < frac_none < 0.28                       # prefix length 0 w.p. 1/5
+    P4 = inputs.make_problem(4, layers=0)
+    d = np.array([inputs.tree_depths(P4.parent[b])[P4.accepted[b]] for b in range(P4.B)])
+    assert np.mean((d == 3) | (d == 4)) > 0.7
+    P2 = inputs.make_problem(2, layers=0)
+    assert P2.accepted.min() >= 0
+
+
+def test_step_bytes_formulas():
+    par = np.stack([inputs.chain_tree(4)] * 2)
+    acc = np.array([-1, 2], dtype=np.int32)
+    sb = accounting.step_bytes(par, acc, H=3, N=4, elem=2)
+    assert sb["verify"] == 2 * 3 * (65536 + 4 * 1804) + 2 * 16
+    assert sb["commit"] == 4 + 4 + 16 + 3 * (131072 + 3 * 772)
+    assert accounting.verify_bytes_per_head(4, 4) == 65536 + 4 * 2572
