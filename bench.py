@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the TreeWY hot path on one MI355X: tree verify + commit.
+
+A step is one pass of the whole path over one batch: treewy_verify for every layer, then
+treewy_commit for every layer, on inputs already resident in HBM.  Steps cycle through a
+pool of independently drawn instances whose total footprint exceeds the 256 MB Infinity
+Cache, so the state stream is served from HBM rather than from the cache.
+
+Prints one JSON line: throughput in draft-nodes*heads per second, the roofline of the
+dominant kernel (algorithmic bytes per launch over its mean launch time, timed with HIP
+events on the launch stream inside the timed region), and the CPU oracle's rate on a
+bounded sample of the same workload as a reported baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1)")
+    ap.add_argument("--pool-gib", type=float, default=1.25,
+                    help="minimum device footprint of the rotating instance pool")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--snapshot", action="store_true",
+                    help="time the store-all comparison path instead of TreeWY")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "every (sequence, head) is independent, so N GPUs would each run this same "
+              "single-GPU pass on their share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_speculative_head_amd import accounting, binding, device, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.lib()
+    cfg = inputs.CONFIGS[args.config]
+    B, H, N, nl, dtype = cfg["B"], cfg["H"], cfg["N"], cfg["layers"], cfg["dtype"]
+    elem = 2 if dtype == "bf16" else 4
+
+    # ---- rotating pool of instances (each: all layers of the workload)
+    per_layer = (B * H * 128 * 128 * 4 + 3 * B * N * H * 128 * elem + 2 * B * N * H * 128 * 4
+                 + (B * H * N * 128 * 128 * 4 if args.snapshot else 0))
+    n_inst = max(1, math.ceil(args.pool_gib * 2 ** 30 / (per_layer * nl))) if args.config else 1
+    n_inst = min(n_inst, 32)
+    log(f"[bench] config {args.config}: {cfg['desc']}; {n_inst} instance(s) of {nl} layer(s), "
+        f"{per_layer * nl * n_inst / 2 ** 30:.2f} GiB on device")
+    t0 = time.time()
+    pool = []
+    for i in range(n_inst):
+        P = inputs.make_problem(args.config, instance=i)
+        parent, accepted = device.upload_tree(P)
+        layers = []
+        for L in P.layers:
+            dl = device.upload_layer(L, dtype)
+            out = device.alloc_outputs(B, H, N)
+            snap = (torch.empty((B, H, N, 128, 128), device="cuda") if args.snapshot else None)
+            layers.append((dl, out, snap))
+        pool.append(dict(P=P, parent=parent, accepted=accepted, layers=layers))
+        if i == 0:
+            first = P
+        else:
+            del P
+    torch.cuda.synchronize()
+    log(f"[bench] inputs drawn and uploaded in {time.time() - t0:.1f} s")
+
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bytes_fn = accounting.snapshot_step_bytes if args.snapshot else accounting.step_bytes
+    inst_bytes = [bytes_fn(x["P"].parent, x["P"].accepted, H, N, elem, layers=nl) for x in pool]
+    for x in pool:
+        x["P"] = None
+
+    def step(inst, ev=None):
+        x = pool[inst]
+        for j, (dl, out, snap) in enumerate(x["layers"]):
+            if ev is not None:
+                ev[0][j].record()
+            if args.snapshot:
+                binding.treewy_verify_snapshot(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta,
+                                               x["parent"], out.O, snap, status)
+            else:
+                binding.treewy_verify(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta, x["parent"],
+                                      out.O, out.U, out.gamma, status=status)
+            if ev is not None:
+                ev[1][j].record()
+        for j, (dl, out, snap) in enumerate(x["layers"]):
+            if ev is not None:
+                ev[2][j].record()
+            if args.snapshot:
+                binding.treewy_commit_snapshot(dl.S0, snap, x["accepted"], status)
+            else:
+                binding.treewy_commit(dl.S0, out.U, dl.K, out.gamma, x["parent"], x["accepted"],
+                                      status)
+            if ev is not None:
+                ev[3][j].record()
+
+    for s in range(args.warmup):
+        step(s % n_inst)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
+
+    K = args.steps
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(nl)] for _ in range(4)]
+              for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(K):
+        step((args.warmup + s) % n_inst, events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
+
+    ver_ms = np.array([[events[s][0][j].elapsed_time(events[s][1][j]) for j in range(nl)]
+                       for s in range(K)])
+    com_ms = np.array([[events[s][2][j].elapsed_time(events[s][3][j]) for j in range(nl)]
+                       for s in range(K)])
+    used = [(args.warmup + s) % n_inst for s in range(K)]
+    v_bytes = np.mean([inst_bytes[i]["verify"] for i in used]) / nl   # per launch
+    c_bytes = np.mean([inst_bytes[i]["commit"] for i in used]) / nl
+    step_bytes = np.mean([inst_bytes[i]["total"] for i in used])
+
+    ms_step = wall * 1e3 / K
+    nodes_heads = B * H * N * nl
+    value = nodes_heads * K / wall
+    kern = {"verify": (v_bytes, ver_ms.mean()), "commit": (c_bytes, com_ms.mean())}
+    dom = max(kern, key=lambda k: kern[k][1] * 1.0)
+    d_bytes, d_ms = kern[dom]
+    achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    name_v = "treewy_verify_snapshot" if args.snapshot else "treewy_verify"
+    name_c = "treewy_commit_snapshot" if args.snapshot else "treewy_commit"
+    log(f"[bench] {ms_step * 1e3:.1f} us/step; verify {ver_ms.mean() * 1e3:.1f} us "
+        f"({v_bytes / (ver_ms.mean() * 1e-3) / 1e9:.0f} GB/s), commit {com_ms.mean() * 1e3:.1f} us "
+        f"({c_bytes / max(com_ms.mean(), 1e-9) / 1e6:.0f} GB/s); "
+        f"step {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s algorithmic")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(first, args.cpu_seconds)
+
+    line = {
+        "metric": "tree verify+commit draft-nodes*heads/sec",
+        "value": value,
+        "unit": "nodes*heads/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; Qwen3.5-shaped GDN heads, dk=dv=128)",
+        "config": {"workload": f"config {args.config}: {cfg['desc']}"
+                   + ("; store-all snapshot path" if args.snapshot else ""),
+                   "B": B, "H": H, "N": N, "layers": nl, "qkv_dtype": dtype,
+                   "state_dtype": "f32", "instances_rotated": n_inst},
+        "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": name_v if dom == "verify" else name_c,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": d_bytes, "launch_us": d_ms * 1e3},
+        "kernels_us": {name_v: ver_ms.mean() * 1e3, name_c: com_ms.mean() * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(P, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload's heads."""
+    import oracle
+    threads = oracle.default_threads()
+    heads = [(b, h) for b in range(P.B) for h in range(P.H)]
+    L = P.layers[0]
+    done, elapsed, chunk = 0, 0.0, max(threads, 16)
+    while done < len(heads) and elapsed < seconds:
+        sel = heads[done: done + chunk]
+        t0 = time.perf_counter()
+        oracle.batch(L, P.parent, P.accepted, heads=sel, threads=threads)
+        dt = time.perf_counter() - t0
+        elapsed += dt
+        done += len(sel)
+        chunk = min(len(heads) - done, max(chunk, int(chunk * max(1.0, (seconds - elapsed) / max(dt, 1e-6) * 0.5))))
+        if chunk <= 0:
+            break
+    rate = done * P.N / elapsed
+    return {"value": rate, "unit": "nodes*heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads (layer 0, instance 0) of the same workload, "
+                      f"verify+commit replay in fp64, {elapsed:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,124 @@
+/*
+ * treewy.h -- C ABI of the TreeWY verify/commit path on MI355X (gfx950).
+ *
+ * Method: "TreeWY: Speculative Verification for Gated DeltaNet Hybrids"
+ * (arXiv 2608.20961).  A Gated DeltaNet head keeps a state S in R^{dv x dk} that
+ * follows the gated delta rule (Eq. 1, §1):
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,    o_t = S_t q_t.
+ * A draft tree of N nodes hangs off the committed state S0; node t's "previous
+ * state" is its parent's (§3 "Verifying a draft").
+ *
+ * Conventions shared by every call
+ *   d = dk = dv = 128 (fixed).  1 <= N <= 64.  B, H >= 1.
+ *   All pointers are DEVICE pointers owned by the caller; the library never
+ *   allocates, frees or retains them, and keeps no state between calls.
+ *   Layouts are dense and C-contiguous:
+ *     S0, S   [B, H, 128, 128] float32, row v contiguous over k (S[v][k])
+ *     Q, K    [B, N, H, 128]   element type given by in_dtype
+ *     V       [B, N, H, 128]   element type given by in_dtype
+ *     alpha, beta, gamma [B, N, H] float32
+ *     O, U    [B, N, H, 128]   float32
+ *     parent  [B, N] int32: parent[b][t] in [-1, t-1]; -1 = child of S0.  Several
+ *             children of S0 are allowed.  Any topological numbering works (DFS
+ *             pre-order, as in the paper, is one).
+ *     accepted [B] int32: accepted node in [-1, N-1]; -1 = nothing accepted.
+ *     Snap    [B, H, N, 128, 128] float32 (one full state per draft node).
+ *   in_dtype: TREEWY_F32 (float) or TREEWY_BF16 (bfloat16 bit patterns, uint16).
+ *   stream: a hipStream_t (NULL = the default stream).  Every call only enqueues
+ *   work on it and returns without synchronising; no call reads device data on the
+ *   host, so every call can be captured into a HIP graph.
+ *
+ * Errors
+ *   The return value reports what the host can check: TREEWY_EINVAL for a null
+ *   required pointer, N outside [1, 64], B or H < 1, an unknown in_dtype, or sizes
+ *   whose element counts overflow; TREEWY_EHIP when the launch fails.  Nothing is
+ *   enqueued when the return value is not TREEWY_OK.
+ *   What only the device can see is written to the optional device word `status`
+ *   (first error wins; the caller zeroes it beforehand): TREEWY_ETREE for a parent
+ *   outside [-1, t-1], TREEWY_EACCEPT for an accepted node outside [-1, N-1].  The
+ *   outputs of an offending sequence are then unspecified; other sequences are
+ *   computed normally, and no access leaves the documented buffers.
+ *
+ * Thread safety: calls are re-entrant; calls on different streams may overlap
+ * as long as their output buffers do not.
+ */
+#ifndef TREEWY_H
+#define TREEWY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TREEWY_VERSION 1
+
+enum {
+    TREEWY_OK = 0,
+    TREEWY_EINVAL = 1,
+    TREEWY_EHIP = 2,
+    TREEWY_ETREE = 3,
+    TREEWY_EACCEPT = 4
+};
+
+enum { TREEWY_F32 = 0, TREEWY_BF16 = 1 };
+
+/*
+ * Tree verification (paper §3, "Verifying a draft", Eq. 2, and its readout).
+ * For every (sequence b, head h) computes, for all N draft nodes t:
+ *   gamma[t] = g_t, the product of alpha over t and all its ancestors;
+ *   U[t]     = the pseudo-value vt~_t = b_t (v_t - a_t S_parent(t) k_t) (§3 "Key rewrite"),
+ *              obtained from the unit lower-triangular system
+ *              (I + diag(b) G) U = R,  G[t,i] = (g_t/g_i)(k_t . k_i) for strict ancestors i,
+ *              R[t] = b_t v_t - b_t g_t S0 k_t;
+ *   O[t]     = S_t q_t = g_t S0 q_t + sum over i ancestor-or-self of t of (g_t/g_i)(k_i . q_t) U[i].
+ * Optional outputs (NULL to skip): anc_out [B, N] uint64 with bit i set for every
+ * ancestor-or-self i of t; depth_out [B, N] int32 with depth 1 for children of S0.
+ * S0 is only read.
+ */
+int treewy_verify(const float* S0, const void* Q, const void* K, const void* V,
+                  const float* alpha, const float* beta, const int32_t* parent,
+                  int B, int H, int N, int in_dtype,
+                  float* O, float* U, float* gamma,
+                  uint64_t* anc_out, int32_t* depth_out, int32_t* status, void* stream);
+
+/*
+ * Commit (paper §3, "Reconstruct on commit", Eq. 3).  In place, for every sequence b
+ * with a = accepted[b] >= 0 and every head h:
+ *   S <- g_a S + sum over i ancestor-or-self of a of (g_a/g_i) U[i] k_i^T,
+ * i.e. the state after node a, which becomes the next committed state.  a = -1 leaves
+ * S untouched (not read, not written).  U and gamma are treewy_verify's outputs for the
+ * same S, K and tree; K's element type is in_dtype.
+ */
+int treewy_commit(float* S, const float* U, const void* K, const float* gamma,
+                  const int32_t* parent, const int32_t* accepted,
+                  int B, int H, int N, int in_dtype, int32_t* status, void* stream);
+
+/*
+ * Full-state snapshotting, the comparison scheme of the paper's §2 ("full-state
+ * snapshotting", store-all): every node's state S_t = Eq. (1) applied to its parent's
+ * state is materialised in Snap[b][h][t], and O[t] = S_t q_t.  S0 is only read.
+ */
+int treewy_verify_snapshot(const float* S0, const void* Q, const void* K, const void* V,
+                           const float* alpha, const float* beta, const int32_t* parent,
+                           int B, int H, int N, int in_dtype,
+                           float* O, float* Snap, int32_t* status, void* stream);
+
+/*
+ * Store-all rollback (paper §2): S[b][h] <- Snap[b][h][accepted[b]] for every sequence
+ * with accepted[b] >= 0; a = -1 leaves S untouched.
+ */
+int treewy_commit_snapshot(float* S, const float* Snap, const int32_t* accepted,
+                           int B, int H, int N, int32_t* status, void* stream);
+
+/* Static, NUL-terminated description of an error code (never NULL). */
+const char* treewy_strerror(int code);
+
+/* TREEWY_VERSION of the built library. */
+int treewy_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEWY_H */

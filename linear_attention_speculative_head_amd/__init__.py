@@ -1,0 +1,12 @@
+"""TreeWY speculative tree verification + commit for Gated DeltaNet layers, on MI355X.
+
+The compute path is ``libtreewy.so`` (HIP kernels for gfx950 behind the C ABI of
+``include/treewy.h``); ``binding`` marshals torch tensors into it.  ``inputs`` draws
+seeded synthetic workloads and ``accounting`` counts the algorithmic bytes.
+"""
+
+from .binding import (  # noqa: F401
+    TREEWY_BF16, TREEWY_EACCEPT, TREEWY_EHIP, TREEWY_EINVAL, TREEWY_ETREE, TREEWY_F32,
+    TREEWY_OK, TreeWYError, treewy_commit, treewy_commit_snapshot, treewy_strerror,
+    treewy_verify, treewy_verify_snapshot, treewy_version,
+)

@@ -1,0 +1,190 @@
+"""Thin Python binding of the TreeWY C ABI (include/treewy.h).
+
+Argument marshalling only: torch tensors on the GPU are checked for device, dtype,
+shape and contiguity, then their device pointers and torch's current HIP stream are
+passed to the library.  Every step of the computation runs in the HIP kernels of
+``libtreewy.so``; there is no fallback, and a missing library raises at once.
+
+The functions carry the C names and take caller-owned output tensors, like the ABI.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtreewy.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "treewy.h")
+
+TREEWY_OK, TREEWY_EINVAL, TREEWY_EHIP, TREEWY_ETREE, TREEWY_EACCEPT = 0, 1, 2, 3, 4
+TREEWY_F32, TREEWY_BF16 = 0, 1
+D = 128
+
+_lib = None
+
+
+class TreeWYError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = lib().treewy_strerror(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{where}: {msg} (code {code})")
+        self.code = code
+
+
+def lib():
+    """Load libtreewy.so (built in-tree by ``build.py``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        L.treewy_verify.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, P]
+        L.treewy_commit.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P]
+        L.treewy_verify_snapshot.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, P, P, P]
+        L.treewy_commit_snapshot.argtypes = [P, P, P, I, I, I, P, P]
+        L.treewy_strerror.argtypes = [I]
+        L.treewy_strerror.restype = ctypes.c_char_p
+        L.treewy_version.argtypes = []
+        for f in ("treewy_verify", "treewy_commit", "treewy_verify_snapshot",
+                  "treewy_commit_snapshot", "treewy_version"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_symbols():
+    """Function names declared in include/treewy.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(treewy_\w+)\s*\(", text, re.M)))
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(t, name, shape, dtypes, device):
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _qkv_dtype(Q):
+    import torch
+    if Q.dtype == torch.bfloat16:
+        return TREEWY_BF16, (torch.bfloat16,)
+    if Q.dtype == torch.float32:
+        return TREEWY_F32, (torch.float32,)
+    raise ValueError(f"Q/K/V dtype {Q.dtype} is not supported (float32 or bfloat16)")
+
+
+def _rc(code: int, where: str):
+    if code != TREEWY_OK:
+        raise TreeWYError(code, where)
+
+
+def treewy_verify(S0, Q, K, V, alpha, beta, parent, O, U, gamma,
+                  anc_out=None, depth_out=None, status=None, stream=None):
+    """Enqueue tree verification: fills O, U, gamma (and anc_out, depth_out if given)."""
+    import torch
+    B, N, H, _ = Q.shape
+    dev = S0.device
+    dt, qdt = _qkv_dtype(Q)
+    f32 = (torch.float32,)
+    _check(S0, "S0", (B, H, D, D), f32, dev)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check(t, n, (B, N, H, D), qdt, dev)
+    for n, t in (("alpha", alpha), ("beta", beta), ("gamma", gamma)):
+        _check(t, n, (B, N, H), f32, dev)
+    _check(parent, "parent", (B, N), (torch.int32,), dev)
+    _check(O, "O", (B, N, H, D), f32, dev)
+    _check(U, "U", (B, N, H, D), f32, dev)
+    _check(anc_out, "anc_out", (B, N), (torch.int64, torch.uint64), dev)
+    _check(depth_out, "depth_out", (B, N), (torch.int32,), dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    rc = lib().treewy_verify(_ptr(S0), _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha), _ptr(beta),
+                             _ptr(parent), B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma),
+                             _ptr(anc_out), _ptr(depth_out), _ptr(status), _stream(stream))
+    _rc(rc, "treewy_verify")
+
+
+def treewy_commit(S, U, K, gamma, parent, accepted, status=None, stream=None):
+    """Enqueue the in-place commit of the accepted node's state into S."""
+    import torch
+    B, N, H, _ = K.shape
+    dev = S.device
+    dt, kdt = _qkv_dtype(K)
+    f32 = (torch.float32,)
+    _check(S, "S", (B, H, D, D), f32, dev)
+    _check(U, "U", (B, N, H, D), f32, dev)
+    _check(K, "K", (B, N, H, D), kdt, dev)
+    _check(gamma, "gamma", (B, N, H), f32, dev)
+    _check(parent, "parent", (B, N), (torch.int32,), dev)
+    _check(accepted, "accepted", (B,), (torch.int32,), dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    rc = lib().treewy_commit(_ptr(S), _ptr(U), _ptr(K), _ptr(gamma), _ptr(parent),
+                             _ptr(accepted), B, H, N, dt, _ptr(status), _stream(stream))
+    _rc(rc, "treewy_commit")
+
+
+def treewy_verify_snapshot(S0, Q, K, V, alpha, beta, parent, O, Snap, status=None, stream=None):
+    """Enqueue store-all verification: every node's state into Snap, outputs into O."""
+    import torch
+    B, N, H, _ = Q.shape
+    dev = S0.device
+    dt, qdt = _qkv_dtype(Q)
+    f32 = (torch.float32,)
+    _check(S0, "S0", (B, H, D, D), f32, dev)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check(t, n, (B, N, H, D), qdt, dev)
+    for n, t in (("alpha", alpha), ("beta", beta)):
+        _check(t, n, (B, N, H), f32, dev)
+    _check(parent, "parent", (B, N), (torch.int32,), dev)
+    _check(O, "O", (B, N, H, D), f32, dev)
+    _check(Snap, "Snap", (B, H, N, D, D), f32, dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    rc = lib().treewy_verify_snapshot(_ptr(S0), _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha),
+                                      _ptr(beta), _ptr(parent), B, H, N, dt, _ptr(O),
+                                      _ptr(Snap), _ptr(status), _stream(stream))
+    _rc(rc, "treewy_verify_snapshot")
+
+
+def treewy_commit_snapshot(S, Snap, accepted, status=None, stream=None):
+    """Enqueue store-all rollback: S <- Snap[accepted] per sequence."""
+    import torch
+    B, H, N = Snap.shape[:3]
+    dev = S.device
+    f32 = (torch.float32,)
+    _check(S, "S", (B, H, D, D), f32, dev)
+    _check(Snap, "Snap", (B, H, N, D, D), f32, dev)
+    _check(accepted, "accepted", (B,), (torch.int32,), dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    rc = lib().treewy_commit_snapshot(_ptr(S), _ptr(Snap), _ptr(accepted), B, H, N,
+                                      _ptr(status), _stream(stream))
+    _rc(rc, "treewy_commit_snapshot")
+
+
+def treewy_strerror(code: int) -> str:
+    return lib().treewy_strerror(int(code)).decode()
+
+
+def treewy_version() -> int:
+    return lib().treewy_version()

@@ -1,0 +1,87 @@
+// C ABI of the TreeWY path (declared in include/treewy.h): host-side argument checks,
+// then one kernel launch on the caller's stream.  No allocation, no synchronisation, no
+// host read of device memory.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "treewy.h"
+
+namespace {
+
+// A launch covers B*H workgroups of 256 lanes; the dispatch grid is counted in lanes
+// and must fit 32 bits.
+bool sizes_ok(int B, int H, int N) {
+    if (B < 1 || H < 1 || N < 1 || N > 64) return false;
+    const uint64_t groups = static_cast<uint64_t>(B) * static_cast<uint64_t>(H);
+    return groups * 256u <= 0xffffffffull;
+}
+
+bool dtype_ok(int d) { return d == TREEWY_F32 || d == TREEWY_BF16; }
+
+int map_hip(hipError_t e) { return e == hipSuccess ? TREEWY_OK : TREEWY_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int treewy_verify(const float* S0, const void* Q, const void* K, const void* V,
+                  const float* alpha, const float* beta, const int32_t* parent, int B, int H,
+                  int N, int in_dtype, float* O, float* U, float* gamma, uint64_t* anc_out,
+                  int32_t* depth_out, int32_t* status, void* stream)
+{
+    if (!S0 || !Q || !K || !V || !alpha || !beta || !parent || !O || !U || !gamma)
+        return TREEWY_EINVAL;
+    if (!sizes_ok(B, H, N) || !dtype_ok(in_dtype)) return TREEWY_EINVAL;
+    treewy::VerifyArgs a{S0, Q, K, V, alpha, beta, parent, B, H, N, in_dtype,
+                         O, U, gamma, anc_out, depth_out, status};
+    return map_hip(treewy::launch_verify(a, static_cast<hipStream_t>(stream)));
+}
+
+int treewy_commit(float* S, const float* U, const void* K, const float* gamma,
+                  const int32_t* parent, const int32_t* accepted, int B, int H, int N,
+                  int in_dtype, int32_t* status, void* stream)
+{
+    if (!S || !U || !K || !gamma || !parent || !accepted) return TREEWY_EINVAL;
+    if (!sizes_ok(B, H, N) || !dtype_ok(in_dtype)) return TREEWY_EINVAL;
+    treewy::CommitArgs a{S, U, K, gamma, parent, accepted, B, H, N, in_dtype, status};
+    return map_hip(treewy::launch_commit(a, static_cast<hipStream_t>(stream)));
+}
+
+int treewy_verify_snapshot(const float* S0, const void* Q, const void* K, const void* V,
+                           const float* alpha, const float* beta, const int32_t* parent,
+                           int B, int H, int N, int in_dtype, float* O, float* Snap,
+                           int32_t* status, void* stream)
+{
+    if (!S0 || !Q || !K || !V || !alpha || !beta || !parent || !O || !Snap) return TREEWY_EINVAL;
+    if (!sizes_ok(B, H, N) || !dtype_ok(in_dtype)) return TREEWY_EINVAL;
+    treewy::SnapshotVerifyArgs a{S0, Q, K, V, alpha, beta, parent, B, H, N, in_dtype,
+                                 O, Snap, status};
+    return map_hip(treewy::launch_verify_snapshot(a, static_cast<hipStream_t>(stream)));
+}
+
+int treewy_commit_snapshot(float* S, const float* Snap, const int32_t* accepted, int B, int H,
+                           int N, int32_t* status, void* stream)
+{
+    if (!S || !Snap || !accepted) return TREEWY_EINVAL;
+    if (!sizes_ok(B, H, N)) return TREEWY_EINVAL;
+    treewy::SnapshotCommitArgs a{S, Snap, accepted, B, H, N, status};
+    return map_hip(treewy::launch_commit_snapshot(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* treewy_strerror(int code)
+{
+    switch (code) {
+        case TREEWY_OK: return "success";
+        case TREEWY_EINVAL: return "invalid argument (null pointer, size or dtype)";
+        case TREEWY_EHIP: return "HIP launch or runtime error";
+        case TREEWY_ETREE: return "malformed draft tree (parent outside [-1, t-1])";
+        case TREEWY_EACCEPT: return "accepted node outside [-1, N-1]";
+        default: return "unknown error code";
+    }
+}
+
+int treewy_version(void) { return TREEWY_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace treewy {
+
+struct VerifyArgs {
+    const float* S0;
+    const void* Q;
+    const void* K;
+    const void* V;
+    const float* alpha;
+    const float* beta;
+    const int32_t* parent;
+    int B, H, N, in_dtype;
+    float* O;
+    float* U;
+    float* gamma;
+    uint64_t* anc_out;
+    int32_t* depth_out;
+    int32_t* status;
+};
+
+struct CommitArgs {
+    float* S;
+    const float* U;
+    const void* K;
+    const float* gamma;
+    const int32_t* parent;
+    const int32_t* accepted;
+    int B, H, N, in_dtype;
+    int32_t* status;
+};
+
+struct SnapshotVerifyArgs {
+    const float* S0;
+    const void* Q;
+    const void* K;
+    const void* V;
+    const float* alpha;
+    const float* beta;
+    const int32_t* parent;
+    int B, H, N, in_dtype;
+    float* O;
+    float* Snap;
+    int32_t* status;
+};
+
+struct SnapshotCommitArgs {
+    float* S;
+    const float* Snap;
+    const int32_t* accepted;
+    int B, H, N;
+    int32_t* status;
+};
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
+hipError_t launch_verify_snapshot(const SnapshotVerifyArgs& a, hipStream_t stream);
+hipError_t launch_commit_snapshot(const SnapshotCommitArgs& a, hipStream_t stream);
+
+}  // namespace treewy

@@ -1,0 +1,67 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching the GPU (no compute calls here)."""
+
+import ctypes
+
+import pytest
+
+from linear_attention_speculative_head_amd import binding
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import os
+    if not os.path.exists(binding.LIB_PATH):
+        from linear_attention_speculative_head_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_exports_every_header_symbol(lib):
+    names = binding.header_symbols()
+    assert set(names) == {"treewy_verify", "treewy_commit", "treewy_verify_snapshot",
+                          "treewy_commit_snapshot", "treewy_strerror", "treewy_version"}
+    raw = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_strerror(lib):
+    assert lib.treewy_version() == 1
+    for code in range(5):
+        assert lib.treewy_strerror(code)
+    assert lib.treewy_strerror(99) == b"unknown error code"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+def verify_args(**kw):
+    a = dict(S0=FAKE, Q=FAKE, K=FAKE, V=FAKE, alpha=FAKE, beta=FAKE, parent=FAKE, B=1, H=1, N=4,
+             dt=binding.TREEWY_BF16, O=FAKE, U=FAKE, gamma=FAKE, anc=None, depth=None,
+             status=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(S0=None), dict(Q=None), dict(parent=None), dict(gamma=None),
+                                 dict(N=0), dict(N=65), dict(B=0), dict(H=-1), dict(dt=7),
+                                 dict(B=1 << 20, H=1 << 10)])
+def test_verify_rejects(lib, bad):
+    assert lib.treewy_verify(*verify_args(**bad)) == binding.TREEWY_EINVAL
+
+
+@pytest.mark.parametrize("bad", [dict(S=None), dict(U=None), dict(accepted=None), dict(N=100),
+                                 dict(dt=-1)])
+def test_commit_rejects(lib, bad):
+    a = dict(S=FAKE, U=FAKE, K=FAKE, gamma=FAKE, parent=FAKE, accepted=FAKE, B=2, H=2, N=8,
+             dt=binding.TREEWY_F32, status=None, stream=None)
+    a.update(bad)
+    assert lib.treewy_commit(*a.values()) == binding.TREEWY_EINVAL
+
+
+def test_snapshot_rejects(lib):
+    assert lib.treewy_verify_snapshot(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 4, 1,
+                                      FAKE, None, None, None) == binding.TREEWY_EINVAL
+    assert lib.treewy_commit_snapshot(FAKE, FAKE, None, 1, 1, 4, None, None) == binding.TREEWY_EINVAL
+    assert lib.treewy_commit_snapshot(FAKE, FAKE, FAKE, 1, 1, 0, None, None) == binding.TREEWY_EINVAL
