@@ -45,6 +45,8 @@ def parse():
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--snapshot", action="store_true",
                     help="time the store-all comparison path instead of TreeWY")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each instance's step as a captured HIP graph")
     return ap.parse_args()
 
 
@@ -121,22 +123,53 @@ def main():
             if ev is not None:
                 ev[3][j].record()
 
+    graphs = None
+    if args.graph:
+        # one graph per instance: verify for every layer, then commit for every layer
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(n_inst):           # warm the launch path outside capture
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(n_inst):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i, ev=None):
+        if graphs is not None and ev is None:
+            graphs[i].replay()
+        else:
+            step(i, ev)
+
     for s in range(args.warmup):
-        step(s % n_inst)
+        run(s % n_inst)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, f"device status {int(status.item())}"
 
+    # ---- timed region: exactly K steps, nothing else on the stream
     K = args.steps
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(nl)] for _ in range(4)]
-              for _ in range(K)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(K):
-        step((args.warmup + s) % n_inst, events[s])
+        run((args.warmup + s) % n_inst)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     assert int(status.item()) == 0, f"device status {int(status.item())}"
 
+    # ---- kernel timing: the same K steps again, each launch between two HIP events on
+    #      the stream it is launched on (the events add gaps, so this pass is not `value`)
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(nl)] for _ in range(4)]
+              for _ in range(K)]
+    torch.cuda.synchronize()
+    for s in range(K):
+        run((args.warmup + s) % n_inst, events[s])
+    torch.cuda.synchronize()
     ver_ms = np.array([[events[s][0][j].elapsed_time(events[s][1][j]) for j in range(nl)]
                        for s in range(K)])
     com_ms = np.array([[events[s][2][j].elapsed_time(events[s][3][j]) for j in range(nl)]
@@ -180,7 +213,8 @@ def main():
         "config": {"workload": f"config {args.config}: {cfg['desc']}"
                    + ("; store-all snapshot path" if args.snapshot else ""),
                    "B": B, "H": H, "N": N, "layers": nl, "qkv_dtype": dtype,
-                   "state_dtype": "f32", "instances_rotated": n_inst},
+                   "state_dtype": "f32", "instances_rotated": n_inst,
+                   "launch": "hip-graph" if args.graph else "stream"},
         "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": name_v if dom == "verify" else name_c,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -193,26 +227,32 @@ def main():
 
 
 def cpu_baseline(P, seconds):
-    """The oracle, as it stands, on a bounded sample of the same workload's heads."""
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    Heads of layer 0 of instance 0 are replayed (verify + commit, fp64) in batches,
+    cycling over the heads, until about ``seconds`` of wall time have been spent."""
     import oracle
     threads = oracle.default_threads()
     heads = [(b, h) for b in range(P.B) for h in range(P.H)]
     L = P.layers[0]
-    done, elapsed, chunk = 0, 0.0, max(threads, 16)
-    while done < len(heads) and elapsed < seconds:
-        sel = heads[done: done + chunk]
+    done, elapsed, pos, chunk = 0, 0.0, 0, max(threads, 16)
+    while elapsed < seconds:
+        sel = [heads[(pos + i) % len(heads)] for i in range(chunk)]
         t0 = time.perf_counter()
         oracle.batch(L, P.parent, P.accepted, heads=sel, threads=threads)
         dt = time.perf_counter() - t0
         elapsed += dt
         done += len(sel)
-        chunk = min(len(heads) - done, max(chunk, int(chunk * max(1.0, (seconds - elapsed) / max(dt, 1e-6) * 0.5))))
-        if chunk <= 0:
-            break
+        pos = (pos + len(sel)) % len(heads)
+        # grow the batch towards about a quarter of the remaining budget
+        per = dt / len(sel)
+        chunk = int(min(max(chunk, 0.25 * (seconds - elapsed) / max(per, 1e-9)), 2048))
+        chunk = max(chunk, threads)
     rate = done * P.N / elapsed
     return {"value": rate, "unit": "nodes*heads/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(heads)} heads (layer 0, instance 0) of the same workload, "
-                      f"verify+commit replay in fp64, {elapsed:.1f} s wall"}
+            "sample": f"{done} head replays (cycling over the {len(heads)} heads of layer 0, "
+                      f"instance 0) of the same workload, verify+commit in fp64, "
+                      f"{elapsed:.1f} s wall on {threads} threads"}
 
 
 if __name__ == "__main__":

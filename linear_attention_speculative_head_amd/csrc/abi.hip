@@ -10,12 +10,12 @@
 
 namespace {
 
-// A launch covers B*H workgroups of 256 lanes; the dispatch grid is counted in lanes
-// and must fit 32 bits.
+// A launch covers up to 2*B*H workgroups of 256 lanes; the dispatch grid is counted in
+// lanes and must fit 32 bits.
 bool sizes_ok(int B, int H, int N) {
     if (B < 1 || H < 1 || N < 1 || N > 64) return false;
     const uint64_t groups = static_cast<uint64_t>(B) * static_cast<uint64_t>(H);
-    return groups * 256u <= 0xffffffffull;
+    return groups * 2u * 256u <= 0xffffffffull;
 }
 
 bool dtype_ok(int d) { return d == TREEWY_F32 || d == TREEWY_BF16; }

@@ -5,10 +5,10 @@
 // of (g_a/g_i) vt~_i k_i^T.  Only the pseudo-values U (one 128-row per node), the keys and
 // the cumulative gates of a's path are needed; no per-node state exists.
 //
-// One workgroup of 256 lanes per (sequence, head).  The state is a pure HBM stream: every
-// lane issues its 16 float4 loads of S at once, the path (at most 64 nodes) is walked in LDS
-// while they are in flight, the rank-depth(a) update is applied in registers and S is
-// written back.  a = -1 exits before touching S.
+// One workgroup of 256 lanes per (sequence, head, half of the rows).  The state is a pure
+// HBM stream: every lane issues its 8 float4 loads of S at once, the path (at most 64
+// nodes) is walked in LDS while they are in flight, the rank-depth(a) update is applied in
+// registers and S is written back.  a = -1 exits before touching S.
 
 #include "device_common.h"
 #include "launch.h"
@@ -19,10 +19,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 8;                        // path rows staged per pass
-constexpr int kVec = D * D / 4 / kThreads;       // float4 of S per lane (16)
+constexpr int kParts = 2;                         // row slices per head
+constexpr int kVec = D * D / 4 / kThreads / kParts;  // float4 of S per lane (8)
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void commit_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
+void commit_kernel(
     float* __restrict__ S, const float* __restrict__ U, const T* __restrict__ K,
     const float* __restrict__ gamma, const int32_t* __restrict__ parent,
     const int32_t* __restrict__ accepted, int H, int N, int32_t* __restrict__ status)
@@ -34,20 +36,22 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
     __shared__ float s_k[kChunk][D];    // k_i
 
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / kParts;
+    const int part = blockIdx.x - bh * kParts;
     const int b = bh / H;
     const int h = bh - b * H;
     const size_t node0 = static_cast<size_t>(b) * N;
 
     const int a = accepted[b];
     if (a < -1 || a >= N) {
-        if (tid == 0 && h == 0) report(status, TREEWY_EACCEPT);
+        if (tid == 0 && h == 0 && part == 0) report(status, TREEWY_EACCEPT);
         return;
     }
     if (a < 0) return;
 
     // issue the state loads first; they do not depend on the path
-    float4* Sh = reinterpret_cast<float4*>(S + static_cast<size_t>(bh) * D * D);
+    constexpr int kRowsPart = D / kParts;
+    float4* Sh = reinterpret_cast<float4*>(S + (static_cast<size_t>(bh) * D + part * kRowsPart) * D);
     float4 s[kVec];
 #pragma unroll
     for (int j = 0; j < kVec; ++j) s[j] = Sh[j * kThreads + tid];
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
             i = p;
         }
         s_len = ok ? len : -1;
-        if (!ok && h == 0) report(status, TREEWY_ETREE);
+        if (!ok && h == 0 && part == 0) report(status, TREEWY_ETREE);
     }
     __syncthreads();
     const int len = s_len;
@@ -87,15 +91,16 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
             const int i = s_path[c0 + jj];
             const size_t row = ((node0 + i) * H + h) * D;
             const float coef = ga / gamma[(node0 + i) * H + h];
-            s_cu[jj][x] = coef * U[row + x];
+            s_cu[jj][x] = coef * U[row + x];   // only this part's rows are used
             s_k[jj][x] = Elem<T>::load1(K + row + x);
         }
         __syncthreads();
+#pragma unroll 1
         for (int jj = 0; jj < nj; ++jj) {
             const float4 kv = *reinterpret_cast<const float4*>(&s_k[jj][4 * c4]);
 #pragma unroll
             for (int j = 0; j < kVec; ++j) {
-                const int r = (j * kThreads + tid) >> 5;
+                const int r = part * kRowsPart + ((j * kThreads + tid) >> 5);
                 const float cu = s_cu[jj][r];
                 s[j].x += cu * kv.x; s[j].y += cu * kv.y; s[j].z += cu * kv.z; s[j].w += cu * kv.w;
             }
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
 
 template <typename T>
 static hipError_t launch_commit_t(const CommitArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(commit_kernel<T>, dim3(a.B * a.H), dim3(kThreads), 0, stream, a.S, a.U,
+    hipLaunchKernelGGL(commit_kernel<T>, dim3(a.B * a.H * kParts), dim3(kThreads), 0, stream, a.S, a.U,
                        static_cast<const T*>(a.K), a.gamma, a.parent, a.accepted, a.H, a.N,
                        a.status);
     return hipGetLastError();

@@ -43,6 +43,15 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Workgroup barrier that orders LDS only: every wave's LDS writes before it are visible to
+// every wave after it, while global loads and stores stay in flight (a plain __syncthreads
+// also waits for all outstanding global memory operations).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void report(int32_t* status, int code) {
     if (status) atomicCAS(reinterpret_cast<int*>(status), 0, code);
 }

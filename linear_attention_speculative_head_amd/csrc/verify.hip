@@ -179,6 +179,750 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// bf16 inputs: the S0 contractions on the matrix cores.
+//
+// P^T = S0 [K;Q]^T is a [128 x 128] x [128 x 2N] product per head.  S0 is fp32; it is split
+// as S0 = hi + lo, hi = S0 rounded to bf16 and lo = the (exact) remainder rounded to bf16,
+// so |S0 - hi - lo| <= 2^-18 |S0|.  q and k are exact in bf16, so two bf16 MFMAs with fp32
+// accumulation give an fp32-grade product.
+//
+// Work split: one workgroup per (sequence, head, half of the value rows); the two halves of
+// a head are paired on one XCD (blocks b and b+8 of every 16 run there) so its keys and
+// queries are fetched into that XCD's L2 once.  Each wave owns 16 rows of S0.
+//
+// S0 goes HBM -> LDS directly (global_load_lds_dwordx4: lane l of a wave instruction lands
+// at base + 16 l), fully coalesced: a wave instruction covers two whole rows.  Within a row
+// the 16-byte chunk c is stored at slot c ^ (row % 16), which makes the MFMA operand reads
+// below conflict-free.  Operands follow v_mfma_f32_16x16x32_bf16: lane L holds row L % 16
+// of a 16-row tile and 8 consecutive k's from 8 (L / 16); both operands use the same k
+// order, so the sums are those of the plain product.  Output columns: keys 0..N-1, then
+// queries N..2N-1, in NCT tiles of 16.  The same key fragments give the Gram matrix
+// K [K;Q]^T (k_m.k_n and k_m.q_n), whose ancestor entries become the solve coefficients.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kParts = 2;                  // workgroups per head (value-row halves)
+constexpr int kRowsPart = D / kParts;      // 64
+
+__device__ __forceinline__ void split_hi_lo(f32x4_t a, f32x4_t b, bf16x8_t& hi, bf16x8_t& lo) {
+    const f32x8_t f = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    hi = __builtin_convertvector(f, bf16x8_t);                       // round to nearest even
+    const u32x4_t hw = __builtin_bit_cast(u32x4_t, hi);
+    f32x8_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        r[2 * j] = f[2 * j] - __uint_as_float(hw[j] << 16);          // exact remainders
+        r[2 * j + 1] = f[2 * j + 1] - __uint_as_float(hw[j] & 0xffff0000u);
+    }
+    lo = __builtin_convertvector(r, bf16x8_t);
+}
+
+// Shared-memory plan (floats), one region reused:
+//   during the contractions: S0 rows of this half, [64][128], chunk-swizzled;
+//   afterwards: P [N][64] | Y [N][64] | anc (u64) [64] | g [64] | beta [64] | depth [64] |
+//               base [65] | pair_c [np] | pair_w [np] | pair_i (bytes) [np]
+struct VerifyLayout {
+    int N, np;
+    int P, Y, anc, g, beta, depth, base, pc, pw, pi, total;
+    __host__ __device__ explicit VerifyLayout(int n) : N(n), np(n * (n + 1) / 2) {
+        P = 0;
+        Y = P + N * kRowsPart;
+        anc = Y + N * kRowsPart;          // 64 uint64 = 128 floats (8-byte aligned: N*128 even)
+        g = anc + 2 * MAXN;
+        beta = g + MAXN;
+        depth = beta + MAXN;
+        base = depth + MAXN;
+        pc = base + MAXN + 1;
+        pw = pc + np;
+        pi = pw + np;
+        const int post = pi + (np + 3) / 4;
+        total = post > kRowsPart * D ? post : kRowsPart * D;
+    }
+};
+
+template <int NCT> struct MfmaOcc { static constexpr int waves = NCT <= 2 ? 4 : (NCT == 4 ? 3 : 2); };
+
+template <int NCT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MfmaOcc<NCT>::waves)))
+void verify_mfma_kernel(
+    const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N,
+    float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
+    uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
+    int32_t* __restrict__ status)
+{
+    extern __shared__ __align__(16) float lds[];
+    const VerifyLayout Lo(N);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    // pair the two halves of a head on one XCD: blocks b and b + 8 of a group of 16
+    const int blk = blockIdx.x;
+    const int g16 = static_cast<int>(gridDim.x) & ~15;
+    const int lid = blk < g16 ? ((blk & ~15) | ((blk & 7) << 1) | ((blk >> 3) & 1)) : blk;
+    const int bh = lid / kParts;
+    const int part = lid - bh * kParts;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * N;
+    const int row0 = part * kRowsPart;            // first value row of this workgroup
+    const int kq = 8 * (lane >> 4);
+
+    // ---- S0 rows of this half straight into LDS: wave w takes local rows 16w..16w+15
+    {
+        const float* src = S0 + (static_cast<size_t>(bh) * D + row0) * D;
+        const int half = lane >> 5;
+        const int slot = lane & 31;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 16 * wave + 2 * i + half;                    // local row
+            const int c = slot ^ (r & 15);                              // logical chunk
+            __builtin_amdgcn_global_load_lds(src + r * D + 4 * c,
+                                             lds + (16 * wave + 2 * i) * D, 16, 0, 0);
+        }
+    }
+
+    // ---- key/query operand fragments of output column tile c
+    auto load_bfrag = [&](int c, bf16x8_t (&bv)[4]) {
+        const int n = 16 * c + (lane & 15);
+        const uint16_t* src = nullptr;
+        if (n < N) src = K + ((node0 + n) * H + h) * D + kq;
+        else if (n < 2 * N) src = Q + ((node0 + n - N) * H + h) * D + kq;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4_t w = {0u, 0u, 0u, 0u};
+            if (src) w = *reinterpret_cast<const u32x4_t*>(src + 32 * ks);
+            bv[ks] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    };
+    constexpr bool kPre = NCT <= 2;
+    bf16x8_t bpre[kPre ? NCT : 1][4];
+    if constexpr (kPre) {
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) load_bfrag(c, bpre[c]);
+    }
+    const int gm = 16 * wave + (lane & 15);           // Gram row (key) of this lane
+    const bool has_gram = 16 * wave < N;
+    bf16x8_t ka[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (gm < N) w = *reinterpret_cast<const u32x4_t*>(K + ((node0 + gm) * H + h) * D + kq + 32 * ks);
+        ka[ks] = __builtin_bit_cast(bf16x8_t, w);
+    }
+
+    // ---- v for this lane's (t, local column) items
+    constexpr int kVpt = 2 * NCT;                 // >= N * 64 / 256
+    float vpre[kVpt];
+#pragma unroll
+    for (int j = 0; j < kVpt; ++j) {
+        const int p = tid + kThreads * j;
+        vpre[j] = p < N * kRowsPart
+                      ? bf16_to_f32(V[((node0 + (p >> 6)) * H + h) * D + row0 + (p & 63)])
+                      : 0.f;
+    }
+
+    // ---- tree walk (wave 0, kept in registers until the region is free)
+    NodeInfo ni{0ull, 1.0f, 0, false};
+    float beta_t = 0.f;
+    int start = 0, total_pairs = 0;
+    if (tid < 64) {
+        const int t = tid;
+        const size_t nh = (node0 + t) * H + h;
+        ni = tree_walk(parent + node0, N, t < N ? alpha[nh] : 1.0f);
+        if (ni.bad && part == 0) report(status, TREEWY_ETREE);
+        int incl = t < N ? ni.depth : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (t >= off) incl += y;
+        }
+        start = incl - (t < N ? ni.depth : 0);
+        total_pairs = __shfl(incl, N - 1);
+        if (t < N) {
+            beta_t = beta[nh];
+            if (part == 0) {
+                gamma[nh] = ni.g;
+                if (h == 0) {
+                    if (anc_out) anc_out[node0 + t] = ni.anc;
+                    if (depth_out) depth_out[node0 + t] = ni.depth;
+                }
+            }
+        }
+    }
+
+    // ---- contractions and Gram on the matrix cores
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x4_t acc[NCT], gacc[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        gacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    {
+        const int r = 16 * wave + (lane & 15);
+        const float* rowp = lds + r * D;
+        bf16x8_t ahi[4], alo[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int c0 = 2 * (lane >> 4) + 8 * ks;                   // logical chunk
+            const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15)));
+            const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15)));
+            split_hi_lo(x0, x1, ahi[ks], alo[ks]);
+        }
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+            bf16x8_t bv[4];
+            if constexpr (kPre) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) bv[ks] = bpre[c][ks];
+            } else {
+                load_bfrag(c, bv);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], bv[ks], acc[c], 0, 0, 0);
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bv[ks], acc[c], 0, 0, 0);
+                if (has_gram)
+                    gacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], bv[ks], gacc[c], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();                                  // the region is free from here on
+
+    float* P = lds + Lo.P;                            // [N][64]: S0 k_t, then R, then U
+    float* Y = lds + Lo.Y;                            // [N][64]: S0 q_t
+    uint64_t* s_anc = reinterpret_cast<uint64_t*>(lds + Lo.anc);
+    float* s_g = lds + Lo.g;
+    float* s_beta = lds + Lo.beta;
+    int* s_depth = reinterpret_cast<int*>(lds + Lo.depth);
+    int* s_base = reinterpret_cast<int*>(lds + Lo.base);
+    float* pair_c = lds + Lo.pc;
+    float* pair_w = lds + Lo.pw;
+    uint8_t* pair_i = reinterpret_cast<uint8_t*>(lds + Lo.pi);
+
+    // C tile layout: lane L holds rows 4 (L / 16) + i (i = 0..3) of column L % 16
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        const int n = 16 * c + (lane & 15);
+        const int v0 = 16 * wave + 4 * (lane >> 4);
+        if (n < N) *reinterpret_cast<f32x4_t*>(P + n * kRowsPart + v0) = acc[c];
+        else if (n < 2 * N) *reinterpret_cast<f32x4_t*>(Y + (n - N) * kRowsPart + v0) = acc[c];
+    }
+    if (tid < 64) {
+        const int t = tid;
+        if (t < N) {
+            s_anc[t] = ni.anc;
+            s_g[t] = ni.g;
+            s_beta[t] = beta_t;
+            s_depth[t] = ni.depth;
+            s_base[t] = start;
+            uint64_t m = ni.anc;                       // ancestors, root first
+            int idx = start;
+            while (m) {
+                pair_i[idx++] = static_cast<uint8_t>(__ffsll(static_cast<unsigned long long>(m)) - 1);
+                m &= m - 1;
+            }
+        }
+        if (t == 0) s_base[N] = total_pairs;
+    }
+    __syncthreads();
+
+    // ---- ancestor entries of the Gram matrix -> solve and readout coefficients.
+    // Pair (t, i) with i an ancestor-or-self of t sits at base[t] + depth[i] - 1.
+    if (has_gram) {
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+            const int n = 16 * c + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = 16 * wave + 4 * (lane >> 4) + e;
+                if (m >= N || n >= 2 * N) continue;
+                const float gv = gacc[c][e];
+                if (n < N) {                            // k_m . k_n, m strict ancestor of n
+                    if (m != n && ((s_anc[n] >> m) & 1ull))
+                        pair_c[s_base[n] + s_depth[m] - 1] = s_beta[n] * (s_g[n] / s_g[m]) * gv;
+                } else {                                // k_m . q_t, m ancestor-or-self of t
+                    const int t = n - N;
+                    if ((s_anc[t] >> m) & 1ull)
+                        pair_w[s_base[t] + s_depth[m] - 1] = (s_g[t] / s_g[m]) * gv;
+                }
+            }
+        }
+    }
+    // ---- right-hand side R[t] = b_t (v_t - g_t P[t]), in place
+#pragma unroll
+    for (int j = 0; j < kVpt; ++j) {
+        const int p = tid + kThreads * j;
+        if (p < N * kRowsPart) {
+            const int t = p >> 6;
+            P[p] = s_beta[t] * (vpre[j] - s_g[t] * P[p]);
+        }
+    }
+    __syncthreads();
+
+    // ---- forward substitution, parents before children; lane = value column
+    if (tid < kRowsPart) {
+        const int v = tid;
+        for (int t = 0; t < N; ++t) {
+            float r = P[t * kRowsPart + v];
+            const int p0 = s_base[t];
+            const int p1 = p0 + s_depth[t] - 1;
+            for (int p = p0; p < p1; ++p) r -= pair_c[p] * P[pair_i[p] * kRowsPart + v];
+            P[t * kRowsPart + v] = r;
+        }
+    }
+    __syncthreads();
+
+    // ---- readout O[t] = g_t Y[t] + sum_i W[t,i] U[i]; write O and U
+    for (int p = tid; p < N * kRowsPart; p += kThreads) {
+        const int t = p >> 6;
+        const int v = p & (kRowsPart - 1);
+        float o = s_g[t] * Y[p];
+        const int p0 = s_base[t];
+        const int p1 = p0 + s_depth[t];
+        for (int q = p0; q < p1; ++q) o += pair_w[q] * P[pair_i[q] * kRowsPart + v];
+        const size_t out = ((node0 + t) * H + h) * D + row0 + v;
+        O[out] = o;
+        U[out] = P[p];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Small trees (N <= 16): persistent workgroups of 256 lanes over (head, value-row half)
+// items, the solve in registers.
+//
+// Four workgroups stay resident per CU, each with one 32 KB LDS buffer.  A workgroup reads
+// its item's S0 rows from the buffer into MFMA operand registers, and at once the next
+// item's rows start streaming HBM -> LDS into that same buffer (global_load_lds_dwordx4),
+// together with the next item's keys, queries, values, gates and tree (into registers).
+// So 32 KB per workgroup are in flight while it finishes the current item, and the HBM
+// stream does not pause for the per-item arithmetic.  The two halves of a head go to
+// workgroups on the same XCD (slots s and s + 8 of every 16) in the same round, so the
+// head's keys and queries are fetched into that XCD's L2 once.
+//
+// The contractions are those of the kernel above, on this half's 64 rows: wave w owns rows
+// 16w..16w+15.  Keys occupy output columns 0..N-1 of tile 0 and queries columns N..2N-1
+// (tile 0 or 1), so after the contractions lane L of a wave holds P[t][v..v+3] for node
+// t = L % 16 and rows v = 16w + 4 (L / 16) .. +3.  The forward substitution and the readout
+// then run on those registers: every lane walks its node's ancestors root first (the set
+// bits of its ancestor mask, in increasing order = increasing depth), fetching the
+// ancestor's U from the lane that holds it (same 16-lane group) with a lane permute.  At
+// step d every node at depth > d subtracts the term of its depth-d ancestor, whose value
+// became final at step d - 1, so nodes of all depths advance together and the number of
+// steps is the tree depth.  Coefficients come from the Gram matrix staged in LDS.
+
+constexpr int kSmallThreads = 256;
+// s_waitcnt operand (gfx9 encoding): vmcnt = 2 (bits 3:0 and 15:14), expcnt and lgkmcnt
+// left at their maxima (no wait on them)
+constexpr int kWaitAllButTwoStores = 2 | (7 << 4) | (15 << 8);
+// dword 3 of a raw (unstrided, range-checked) buffer descriptor on gfx9-family parts
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kSmallRows = 64;              // value rows per item
+constexpr int kSmallParts = D / kSmallRows; // items per head
+
+template <int NCT>
+struct SmallPrefetch {
+    bf16x8_t bfr[NCT][4];     // key/query operand fragments
+    uint2 vraw;               // v_t, rows v0..v0+3 (bf16)
+    int par;                  // parent of node t = lane % 16
+    float alpha, beta;        // gates of node t
+};
+
+// Item number -> (head, half).  Slots s and s + 8 of every group of 16 run on one XCD and
+// take the two halves of one head; a grid that is not a multiple of 16 uses plain order.
+__device__ __forceinline__ void small_item(int round, int slot, int grid, int& bh, int& part) {
+    int item;
+    if ((grid & 15) == 0) {
+        const int pair = (grid >> 1) * round + ((slot >> 4) << 3) + (slot & 7);
+        item = 2 * pair + ((slot >> 3) & 1);
+    } else {
+        item = grid * round + slot;
+    }
+    bh = item >> 1;
+    part = item & 1;
+}
+
+// Eight HBM -> LDS row-pair loads (global_load_lds_dwordx4) of one wave: load i sends lane
+// l's 16 bytes from base + voff[i] to LDS byte lds0 + 1024 i + 16 l.  Written as one asm block
+// so the compiler does not treat every later LDS access as a possible alias of the transfer
+// (it would wait for it right away); the caller waits on vmcnt before reading the rows.
+// M0 holds the LDS destination and is restored afterwards; only vector memory is accessed.
+__device__ __forceinline__ void dma_rows_x8(const void* base, const uint32_t (&voff)[8],
+                                            uint32_t lds0) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %9, %17\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %10, %17\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %11, %17\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %12, %17\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %13, %17\n\t"
+        "s_mov_b32 m0, %6\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %14, %17\n\t"
+        "s_mov_b32 m0, %7\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %15, %17\n\t"
+        "s_mov_b32 m0, %8\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %16, %17\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds0), "s"(lds0 + 1024u), "s"(lds0 + 2048u), "s"(lds0 + 3072u),
+          "s"(lds0 + 4096u), "s"(lds0 + 5120u), "s"(lds0 + 6144u), "s"(lds0 + 7168u),
+          "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]),
+          "v"(voff[6]), "v"(voff[7]), "s"(base)
+        : "memory");
+}
+
+// S0 rows of an item -> LDS: wave w takes rows 16w..16w+15, two whole rows per wave load;
+// chunk c of row r lands at slot c ^ (r % 16).  `wave` is wave-uniform (an SGPR), so the
+// LDS destinations are scalar; the source is a scalar base plus a 32-bit lane offset.
+__device__ __forceinline__ void small_issue_s0(const float* S0, float* buf, int bh, int part,
+                                               int wave, int lane) {
+    const char* src = reinterpret_cast<const char*>(S0) +
+                      (static_cast<size_t>(bh) * D + part * kSmallRows) * D * sizeof(float);
+    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+    const uint32_t slot = static_cast<uint32_t>(lane) & 31u;
+    uint32_t voff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = 16u * wave + 2u * i + hl;
+        voff[i] = r * (D * 4u) + 16u * (slot ^ ((2u * i + hl) & 15u));
+    }
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf + 16 * wave * D));
+    dma_rows_x8(src, voff, lds0);
+}
+
+template <int NCT>
+__device__ __forceinline__ void small_prefetch(SmallPrefetch<NCT>& pf, const uint16_t* Q,
+                                               const uint16_t* K, const uint16_t* V,
+                                               const float* alpha, const float* beta,
+                                               const int32_t* parent, int H, int N, int bh,
+                                               int part, int wave, int lane) {
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * N;
+    const uint32_t col = static_cast<uint32_t>(lane) & 15u;
+    const uint32_t kq = 8u * (static_cast<uint32_t>(lane) >> 4);
+    const uint32_t node_stride = static_cast<uint32_t>(H) * D;       // elements between nodes
+    // scalar bases of this (sequence, head); lane offsets stay 32-bit
+    const uint16_t* Kh = K + (node0 * H + h) * D;
+    const uint16_t* Qh = Q + (node0 * H + h) * D;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        const uint32_t n = 16u * c + col;
+        const bool is_k = n < static_cast<uint32_t>(N);
+        const bool is_q = !is_k && n < 2u * N;
+        const uint16_t* src = is_k ? Kh + (n * node_stride + kq)
+                                   : Qh + ((n - N) * node_stride + kq);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4_t w = {0u, 0u, 0u, 0u};
+            if (is_k || is_q) w = *reinterpret_cast<const u32x4_t*>(src + 32 * ks);
+            pf.bfr[c][ks] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    }
+    pf.vraw = make_uint2(0u, 0u);
+    if (col < static_cast<uint32_t>(N)) {
+        const uint16_t* Vh = V + (node0 * H + h) * D + part * kSmallRows + 16 * wave;
+        pf.vraw = *reinterpret_cast<const uint2*>(Vh + (col * node_stride + 4u * (lane >> 4)));
+    }
+    pf.par = -1;
+    pf.alpha = 1.0f;
+    pf.beta = 0.0f;
+    if (col < static_cast<uint32_t>(N)) {               // node t = lane % 16 of every group
+        const size_t nh = (node0 + col) * H + h;
+        pf.par = parent[node0 + col];
+        pf.alpha = alpha[nh];
+        pf.beta = beta[nh];
+    }
+}
+
+// resident workgroups (= waves per SIMD) per CU: the 32 KB buffer and registers allow 4
+template <int NCT> struct SmallOcc { static constexpr int wgs = 4; };
+
+template <int NCT>
+__global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(SmallOcc<NCT>::wgs)))
+void verify_small_kernel(
+    const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
+    float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
+    uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
+    int32_t* __restrict__ status)
+{
+    extern __shared__ __align__(16) float lds[];    // S0 rows of the item [64][128]
+    __shared__ float G[16 * 32];                    // G[m][n] = k_m . (k|q)_n
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
+    const int col = lane & 15;                      // output column within a tile
+    const int grp = lane >> 4;                      // 16-lane group: rows 4 grp .. 4 grp + 3
+    const int base = lane & 48;                     // first lane of this 16-lane group
+    const int t = col;                              // this lane's node in the tail
+    const bool node_ok = t < N;
+    const int grid = gridDim.x;
+    const int slot = blockIdx.x;
+
+    int bh, part;
+    small_item(0, slot, grid, bh, part);
+    if (bh >= BH) return;
+    SmallPrefetch<NCT> pf;
+    small_issue_s0(S0, lds, bh, part, wave, lane);
+    small_prefetch<NCT>(pf, Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane);
+    // the first item has to arrive anyway; settling it here keeps the compiler's count at the
+    // loop head exact (it then waits only as far as the top-of-loop wait below)
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(pf.bfr[c][ks]));
+    asm volatile("" ::"v"(pf.vraw), "v"(pf.par), "v"(pf.alpha), "v"(pf.beta));
+
+    for (int round = 0;; ) {
+        const int b = bh / H;
+        const int h = bh - b * H;
+        const size_t node0 = static_cast<size_t>(b) * N;
+        const int v0 = part * kSmallRows + 16 * wave + 4 * grp;   // this lane's value rows
+
+        const uint2 vraw = pf.vraw;
+        const int my_par = pf.par;
+        const float my_alpha = pf.alpha, my_beta = pf.beta;
+
+        // This item's rows and inputs have landed once at most the two stores of the
+        // previous item (O and U, issued last) are still in flight: vector memory operations
+        // retire in issue order, so vmcnt <= 2 covers everything else.  The empty asm makes
+        // the compiler settle its own waits for the prefetched registers here as well, before
+        // the next transfer is issued (a later wait of its own would also wait for that).
+        __builtin_amdgcn_s_waitcnt(kWaitAllButTwoStores);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(pf.bfr[c][ks]));
+        asm volatile("" ::"v"(vraw), "v"(my_par), "v"(my_alpha), "v"(my_beta));
+        lds_barrier();                              // ... for every wave; last item fully done
+
+        // ---- tree walk, in every 16-lane group (lane = node t): pointer jumping as in
+        //      tree_walk, four rounds for the at most 16 nodes of a small tree
+        uint32_t anc;
+        float g_t, rg_t;
+        {
+            int p = my_par;
+            const bool bad = node_ok && (p < -1 || p >= t);
+            if (bad) p = -1;
+            uint32_t am = node_ok ? (1u << t) : 0u;
+            float g = node_ok ? my_alpha : 1.0f;
+            int j = p;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int src = base | (j < 0 ? t : j);
+                const uint32_t aj = __shfl(am, src);
+                const float gj = __shfl(g, src);
+                const int jj = __shfl(j, src);
+                if (j >= 0) { am |= aj; g *= gj; j = jj; }
+            }
+            anc = am;
+            g_t = g;
+            rg_t = 1.0f / g;
+            if (wave == 0 && grp == 0 && node_ok && part == 0) {
+                if (bad) report(status, TREEWY_ETREE);
+                gamma[(node0 + t) * H + h] = g;
+                if (h == 0) {
+                    if (anc_out) anc_out[node0 + t] = am;
+                    if (depth_out) depth_out[node0 + t] = __popc(am);
+                }
+            }
+        }
+
+        // ---- wave 0: Gram matrix G = K [K;Q]^T (keys of tile 0 are the A operand) -> LDS
+        if (wave == 0) {
+            f32x4_t gacc[NCT];
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) {
+                gacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    bf16x8_t ka = pf.bfr[0][ks];
+                    if (col >= N) ka = bf16x8_t{};
+                    gacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pf.bfr[c][ks], gacc[c], 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) G[(4 * grp + e) * 32 + 16 * c + col] = gacc[c][e];
+            }
+        }
+
+        // ---- MFMA operands of this wave's 16 rows, split into bf16 hi and lo
+        bf16x8_t ahi[4], alo[4];
+        {
+            const int r = 16 * wave + col;
+            const float* rowp = lds + r * D;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int c0 = 2 * grp + 8 * ks;
+                split_hi_lo(*reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15))),
+                            *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15))),
+                            ahi[ks], alo[ks]);
+            }
+        }
+        lds_barrier();                              // rows read and G visible: refill the buffer
+        ++round;
+        int bh_n, part_n;
+        small_item(round, slot, grid, bh_n, part_n);
+        const bool more = bh_n < BH;
+        if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+
+        // ---- contractions on the matrix cores
+        f32x4_t acc[NCT];
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+            acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], pf.bfr[c][ks], acc[c], 0, 0, 0);
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], pf.bfr[c][ks], acc[c], 0, 0, 0);
+            }
+        }
+        // the operands are consumed: the next item's small inputs go in flight too
+        if (more)
+            small_prefetch<NCT>(pf, Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
+
+        // ---- per lane: node t, rows v0..v0+3
+        float Yv[4];
+        {
+            // query t sits in column N + t: tile (N + t) / 16, lane (N + t) % 16.  Each source
+            // lane s serves exactly one node (t = s - N in tile 0, or t = s + 16 - N in tile
+            // 1), so it publishes that tile's value and one permute per row suffices.
+            const int src = base | ((N + t) & 15);
+            const int tile = (NCT > 1 && col < N) ? 1 : 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float pub = NCT > 1 ? (tile ? acc[NCT > 1 ? 1 : 0][e] : acc[0][e]) : acc[0][e];
+                Yv[e] = __shfl(pub, src);
+            }
+        }
+        const float b_t = node_ok ? my_beta : 0.f;
+        const float gg_t = node_ok ? g_t : 0.f;
+        const float bg_t = b_t * gg_t;
+        const float vv[4] = {__uint_as_float(vraw.x << 16), __uint_as_float(vraw.x & 0xffff0000u),
+                             __uint_as_float(vraw.y << 16), __uint_as_float(vraw.y & 0xffff0000u)};
+        float Uv[4], Ov[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Uv[e] = b_t * vv[e] - bg_t * acc[0][e];  // R[t] = b_t (v_t - g_t S0 k_t)
+            Ov[e] = gg_t * Yv[e];                    // g_t S0 q_t
+        }
+
+        // One walk down the ancestors serves both the forward substitution and the readout:
+        // at step d the depth-d ancestor a of t is final (its own terms ended at step d - 1),
+        // so its U enters both U[t] -= b_t (g_t/g_a)(k_t.k_a) U[a] and
+        // O[t] += (g_t/g_a)(k_a.q_t) U[a].  The wave goes on while any lane has ancestors left.
+        uint32_t m = anc & ~(1u << t);
+        while (__any(m != 0u)) {
+            const bool has = m != 0u;
+            const int a = has ? __builtin_ctz(m) : t;
+            m &= m - 1u;
+            const float rg_a = __shfl(rg_t, base | a);
+            const float cs = has ? bg_t * rg_a * G[t * 32 + a] : 0.f;
+            const float cw = has ? gg_t * rg_a * G[a * 32 + N + t] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = __shfl(Uv[e], base | a);
+                Uv[e] -= cs * x;
+                Ov[e] += cw * x;
+            }
+        }
+        {
+            const float cw = node_ok ? G[t * 32 + N + t] : 0.f;   // the node itself: g_t/g_t = 1
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ov[e] += cw * Uv[e];
+        }
+        // O and U rows of this head through buffer descriptors that span exactly its rows:
+        // lanes without a node get an offset past the end, which the hardware drops.  The
+        // stores are thus unconditional, so the compiler's wait at the next item's top can
+        // leave them in flight.
+        {
+            const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
+            const size_t row0 = (node0 * H + h) * D;
+            const uint32_t off = node_ok ? static_cast<uint32_t>((t * H * D + v0) * sizeof(float)) : span;
+            const f32x4_t ov = {Ov[0], Ov[1], Ov[2], Ov[3]};
+            const f32x4_t uv = {Uv[0], Uv[1], Uv[2], Uv[3]};
+            __builtin_amdgcn_raw_buffer_store_b128(
+                ov, __builtin_amdgcn_make_buffer_rsrc(O + row0, 0, span, kRawBufferFlags), off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                uv, __builtin_amdgcn_make_buffer_rsrc(U + row0, 0, span, kRawBufferFlags), off, 0, 0);
+        }
+        if (!more) break;
+        bh = bh_n;
+        part = part_n;
+    }
+}
+
+// Compute units of the current device, cached per device.
+int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev >= 0 && dev < 64) cache[dev] = cus;
+    return cus;
+}
+
+template <int NCT>
+static hipError_t launch_small(const VerifyArgs& a, hipStream_t stream) {
+    const size_t dyn = sizeof(float) * kSmallRows * D;
+    auto kern = verify_small_kernel<NCT>;
+    const int BH = a.B * a.H;
+    const int items = BH * kSmallParts;
+    const int slots = SmallOcc<NCT>::wgs * device_cu_count();   // resident workgroups
+    const int grid = items < slots ? items : slots;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), dyn, stream, a.S0,
+                       static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                       static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
+                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status);
+    return hipGetLastError();
+}
+
+template <int NCT>
+static hipError_t launch_mfma(const VerifyArgs& a, hipStream_t stream) {
+    const size_t dyn = sizeof(float) * static_cast<size_t>(VerifyLayout(a.N).total);
+    auto kern = verify_mfma_kernel<NCT>;
+    if (dyn > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(dyn));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(a.B * a.H * kParts), dim3(kThreads), dyn, stream, a.S0,
+                       static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                       static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
+                       a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 template <typename T>
@@ -199,8 +943,11 @@ static hipError_t launch_verify_t(const VerifyArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
-    return a.in_dtype == TREEWY_BF16 ? launch_verify_t<uint16_t>(a, stream)
-                                     : launch_verify_t<float>(a, stream);
+    if (a.in_dtype != TREEWY_BF16) return launch_verify_t<float>(a, stream);
+    if (a.N <= 8) return launch_small<1>(a, stream);
+    if (a.N <= 16) return launch_small<2>(a, stream);
+    if (a.N <= 32) return launch_mfma<4>(a, stream);
+    return launch_mfma<8>(a, stream);
 }
 
 }  // namespace treewy
