@@ -188,26 +188,18 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
 // so |S0 - hi - lo| <= 2^-18 |S0|.  q and k are exact in bf16, so two bf16 MFMAs with fp32
 // accumulation give an fp32-grade product.
 //
-// Work split: one workgroup per (sequence, head, half of the value rows); the two halves of
-// a head are paired on one XCD (blocks b and b+8 of every 16 run there) so its keys and
-// queries are fetched into that XCD's L2 once.  Each wave owns 16 rows of S0.
-//
 // S0 goes HBM -> LDS directly (global_load_lds_dwordx4: lane l of a wave instruction lands
 // at base + 16 l), fully coalesced: a wave instruction covers two whole rows.  Within a row
 // the 16-byte chunk c is stored at slot c ^ (row % 16), which makes the MFMA operand reads
 // below conflict-free.  Operands follow v_mfma_f32_16x16x32_bf16: lane L holds row L % 16
 // of a 16-row tile and 8 consecutive k's from 8 (L / 16); both operands use the same k
-// order, so the sums are those of the plain product.  Output columns: keys 0..N-1, then
-// queries N..2N-1, in NCT tiles of 16.  The same key fragments give the Gram matrix
-// K [K;Q]^T (k_m.k_n and k_m.q_n), whose ancestor entries become the solve coefficients.
+// order, so the sums are those of the plain product.  The same key fragments give the Gram
+// matrix K [K;Q]^T (k_m.k_n and k_m.q_n), whose ancestor entries are the solve coefficients.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kParts = 2;                  // workgroups per head (value-row halves)
-constexpr int kRowsPart = D / kParts;      // 64
 
 __device__ __forceinline__ void split_hi_lo(f32x4_t a, f32x4_t b, bf16x8_t& hi, bf16x8_t& lo) {
     const f32x8_t f = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -220,280 +212,6 @@ __device__ __forceinline__ void split_hi_lo(f32x4_t a, f32x4_t b, bf16x8_t& hi, 
         r[2 * j + 1] = f[2 * j + 1] - __uint_as_float(hw[j] & 0xffff0000u);
     }
     lo = __builtin_convertvector(r, bf16x8_t);
-}
-
-// Shared-memory plan (floats), one region reused:
-//   during the contractions: S0 rows of this half, [64][128], chunk-swizzled;
-//   afterwards: P [N][64] | Y [N][64] | anc (u64) [64] | g [64] | beta [64] | depth [64] |
-//               base [65] | pair_c [np] | pair_w [np] | pair_i (bytes) [np]
-struct VerifyLayout {
-    int N, np;
-    int P, Y, anc, g, beta, depth, base, pc, pw, pi, total;
-    __host__ __device__ explicit VerifyLayout(int n) : N(n), np(n * (n + 1) / 2) {
-        P = 0;
-        Y = P + N * kRowsPart;
-        anc = Y + N * kRowsPart;          // 64 uint64 = 128 floats (8-byte aligned: N*128 even)
-        g = anc + 2 * MAXN;
-        beta = g + MAXN;
-        depth = beta + MAXN;
-        base = depth + MAXN;
-        pc = base + MAXN + 1;
-        pw = pc + np;
-        pi = pw + np;
-        const int post = pi + (np + 3) / 4;
-        total = post > kRowsPart * D ? post : kRowsPart * D;
-    }
-};
-
-template <int NCT> struct MfmaOcc { static constexpr int waves = NCT <= 2 ? 4 : (NCT == 4 ? 3 : 2); };
-
-template <int NCT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MfmaOcc<NCT>::waves)))
-void verify_mfma_kernel(
-    const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const float* __restrict__ alpha,
-    const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N,
-    float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
-    uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
-    int32_t* __restrict__ status)
-{
-    extern __shared__ __align__(16) float lds[];
-    const VerifyLayout Lo(N);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    // pair the two halves of a head on one XCD: blocks b and b + 8 of a group of 16
-    const int blk = blockIdx.x;
-    const int g16 = static_cast<int>(gridDim.x) & ~15;
-    const int lid = blk < g16 ? ((blk & ~15) | ((blk & 7) << 1) | ((blk >> 3) & 1)) : blk;
-    const int bh = lid / kParts;
-    const int part = lid - bh * kParts;
-    const int b = bh / H;
-    const int h = bh - b * H;
-    const size_t node0 = static_cast<size_t>(b) * N;
-    const int row0 = part * kRowsPart;            // first value row of this workgroup
-    const int kq = 8 * (lane >> 4);
-
-    // ---- S0 rows of this half straight into LDS: wave w takes local rows 16w..16w+15
-    {
-        const float* src = S0 + (static_cast<size_t>(bh) * D + row0) * D;
-        const int half = lane >> 5;
-        const int slot = lane & 31;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 16 * wave + 2 * i + half;                    // local row
-            const int c = slot ^ (r & 15);                              // logical chunk
-            __builtin_amdgcn_global_load_lds(src + r * D + 4 * c,
-                                             lds + (16 * wave + 2 * i) * D, 16, 0, 0);
-        }
-    }
-
-    // ---- key/query operand fragments of output column tile c
-    auto load_bfrag = [&](int c, bf16x8_t (&bv)[4]) {
-        const int n = 16 * c + (lane & 15);
-        const uint16_t* src = nullptr;
-        if (n < N) src = K + ((node0 + n) * H + h) * D + kq;
-        else if (n < 2 * N) src = Q + ((node0 + n - N) * H + h) * D + kq;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            u32x4_t w = {0u, 0u, 0u, 0u};
-            if (src) w = *reinterpret_cast<const u32x4_t*>(src + 32 * ks);
-            bv[ks] = __builtin_bit_cast(bf16x8_t, w);
-        }
-    };
-    constexpr bool kPre = NCT <= 2;
-    bf16x8_t bpre[kPre ? NCT : 1][4];
-    if constexpr (kPre) {
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) load_bfrag(c, bpre[c]);
-    }
-    const int gm = 16 * wave + (lane & 15);           // Gram row (key) of this lane
-    const bool has_gram = 16 * wave < N;
-    bf16x8_t ka[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (gm < N) w = *reinterpret_cast<const u32x4_t*>(K + ((node0 + gm) * H + h) * D + kq + 32 * ks);
-        ka[ks] = __builtin_bit_cast(bf16x8_t, w);
-    }
-
-    // ---- v for this lane's (t, local column) items
-    constexpr int kVpt = 2 * NCT;                 // >= N * 64 / 256
-    float vpre[kVpt];
-#pragma unroll
-    for (int j = 0; j < kVpt; ++j) {
-        const int p = tid + kThreads * j;
-        vpre[j] = p < N * kRowsPart
-                      ? bf16_to_f32(V[((node0 + (p >> 6)) * H + h) * D + row0 + (p & 63)])
-                      : 0.f;
-    }
-
-    // ---- tree walk (wave 0, kept in registers until the region is free)
-    NodeInfo ni{0ull, 1.0f, 0, false};
-    float beta_t = 0.f;
-    int start = 0, total_pairs = 0;
-    if (tid < 64) {
-        const int t = tid;
-        const size_t nh = (node0 + t) * H + h;
-        ni = tree_walk(parent + node0, N, t < N ? alpha[nh] : 1.0f);
-        if (ni.bad && part == 0) report(status, TREEWY_ETREE);
-        int incl = t < N ? ni.depth : 0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off);
-            if (t >= off) incl += y;
-        }
-        start = incl - (t < N ? ni.depth : 0);
-        total_pairs = __shfl(incl, N - 1);
-        if (t < N) {
-            beta_t = beta[nh];
-            if (part == 0) {
-                gamma[nh] = ni.g;
-                if (h == 0) {
-                    if (anc_out) anc_out[node0 + t] = ni.anc;
-                    if (depth_out) depth_out[node0 + t] = ni.depth;
-                }
-            }
-        }
-    }
-
-    // ---- contractions and Gram on the matrix cores
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    f32x4_t acc[NCT], gacc[NCT];
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-        acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        gacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    {
-        const int r = 16 * wave + (lane & 15);
-        const float* rowp = lds + r * D;
-        bf16x8_t ahi[4], alo[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int c0 = 2 * (lane >> 4) + 8 * ks;                   // logical chunk
-            const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15)));
-            const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15)));
-            split_hi_lo(x0, x1, ahi[ks], alo[ks]);
-        }
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-            bf16x8_t bv[4];
-            if constexpr (kPre) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) bv[ks] = bpre[c][ks];
-            } else {
-                load_bfrag(c, bv);
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], bv[ks], acc[c], 0, 0, 0);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bv[ks], acc[c], 0, 0, 0);
-                if (has_gram)
-                    gacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], bv[ks], gacc[c], 0, 0, 0);
-            }
-        }
-    }
-    __syncthreads();                                  // the region is free from here on
-
-    float* P = lds + Lo.P;                            // [N][64]: S0 k_t, then R, then U
-    float* Y = lds + Lo.Y;                            // [N][64]: S0 q_t
-    uint64_t* s_anc = reinterpret_cast<uint64_t*>(lds + Lo.anc);
-    float* s_g = lds + Lo.g;
-    float* s_beta = lds + Lo.beta;
-    int* s_depth = reinterpret_cast<int*>(lds + Lo.depth);
-    int* s_base = reinterpret_cast<int*>(lds + Lo.base);
-    float* pair_c = lds + Lo.pc;
-    float* pair_w = lds + Lo.pw;
-    uint8_t* pair_i = reinterpret_cast<uint8_t*>(lds + Lo.pi);
-
-    // C tile layout: lane L holds rows 4 (L / 16) + i (i = 0..3) of column L % 16
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-        const int n = 16 * c + (lane & 15);
-        const int v0 = 16 * wave + 4 * (lane >> 4);
-        if (n < N) *reinterpret_cast<f32x4_t*>(P + n * kRowsPart + v0) = acc[c];
-        else if (n < 2 * N) *reinterpret_cast<f32x4_t*>(Y + (n - N) * kRowsPart + v0) = acc[c];
-    }
-    if (tid < 64) {
-        const int t = tid;
-        if (t < N) {
-            s_anc[t] = ni.anc;
-            s_g[t] = ni.g;
-            s_beta[t] = beta_t;
-            s_depth[t] = ni.depth;
-            s_base[t] = start;
-            uint64_t m = ni.anc;                       // ancestors, root first
-            int idx = start;
-            while (m) {
-                pair_i[idx++] = static_cast<uint8_t>(__ffsll(static_cast<unsigned long long>(m)) - 1);
-                m &= m - 1;
-            }
-        }
-        if (t == 0) s_base[N] = total_pairs;
-    }
-    __syncthreads();
-
-    // ---- ancestor entries of the Gram matrix -> solve and readout coefficients.
-    // Pair (t, i) with i an ancestor-or-self of t sits at base[t] + depth[i] - 1.
-    if (has_gram) {
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-            const int n = 16 * c + (lane & 15);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = 16 * wave + 4 * (lane >> 4) + e;
-                if (m >= N || n >= 2 * N) continue;
-                const float gv = gacc[c][e];
-                if (n < N) {                            // k_m . k_n, m strict ancestor of n
-                    if (m != n && ((s_anc[n] >> m) & 1ull))
-                        pair_c[s_base[n] + s_depth[m] - 1] = s_beta[n] * (s_g[n] / s_g[m]) * gv;
-                } else {                                // k_m . q_t, m ancestor-or-self of t
-                    const int t = n - N;
-                    if ((s_anc[t] >> m) & 1ull)
-                        pair_w[s_base[t] + s_depth[m] - 1] = (s_g[t] / s_g[m]) * gv;
-                }
-            }
-        }
-    }
-    // ---- right-hand side R[t] = b_t (v_t - g_t P[t]), in place
-#pragma unroll
-    for (int j = 0; j < kVpt; ++j) {
-        const int p = tid + kThreads * j;
-        if (p < N * kRowsPart) {
-            const int t = p >> 6;
-            P[p] = s_beta[t] * (vpre[j] - s_g[t] * P[p]);
-        }
-    }
-    __syncthreads();
-
-    // ---- forward substitution, parents before children; lane = value column
-    if (tid < kRowsPart) {
-        const int v = tid;
-        for (int t = 0; t < N; ++t) {
-            float r = P[t * kRowsPart + v];
-            const int p0 = s_base[t];
-            const int p1 = p0 + s_depth[t] - 1;
-            for (int p = p0; p < p1; ++p) r -= pair_c[p] * P[pair_i[p] * kRowsPart + v];
-            P[t * kRowsPart + v] = r;
-        }
-    }
-    __syncthreads();
-
-    // ---- readout O[t] = g_t Y[t] + sum_i W[t,i] U[i]; write O and U
-    for (int p = tid; p < N * kRowsPart; p += kThreads) {
-        const int t = p >> 6;
-        const int v = p & (kRowsPart - 1);
-        float o = s_g[t] * Y[p];
-        const int p0 = s_base[t];
-        const int p1 = p0 + s_depth[t];
-        for (int q = p0; q < p1; ++q) o += pair_w[q] * P[pair_i[q] * kRowsPart + v];
-        const size_t out = ((node0 + t) * H + h) * D + row0 + v;
-        O[out] = o;
-        U[out] = P[p];
-    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -878,6 +596,313 @@ void verify_small_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Larger trees (16 < N <= 64): the persistent streaming design of the small-tree kernel,
+// with NKT = ceil(N / 16) node tiles per lane.
+//
+// Output columns: keys at 0..N-1 (tiles 0..NKT-1), queries at 16 NKT + t (tiles NKT..2NKT-1),
+// so lane L holds P[t] and Y[t] for the nodes t = 16 kt + L % 16 of every node tile kt, rows
+// 16w + 4 (L / 16) .. +3.  Each wave walks the tree with lane = node (six pointer-jump rounds)
+// and hands every lane its nodes' masks and gates by lane permutes.  The forward substitution
+// and readout are the same ancestor walk as above; U of the ancestors is exchanged through a
+// per-wave LDS scratch [64 nodes][16 rows] instead of lane permutes, because an ancestor may sit
+// in another node tile.  A wave's LDS operations complete in issue order, so a value written
+// at the end of step d - 1 is what other lanes of the wave read at step d.  The Gram matrix
+// G = K [K;Q]^T (same column layout) is formed by waves 0..NKT-1 and staged in LDS.
+
+template <int NKT>
+struct LargeLayout {
+    static constexpr int kCols = 32 * NKT;                // G row pitch (keys | queries)
+    static constexpr int kS0 = kSmallRows * D;            // floats
+    static constexpr int kG = 16 * NKT * kCols;           // G [16 NKT][kCols]
+    static constexpr int kU = 4 * 16 * NKT * 16;          // per wave [16 NKT nodes][16 rows]
+    static constexpr int kTotal = kS0 + kG + kU;
+    // s_waitcnt operand: vmcnt <= 2 NKT (the previous item's O and U stores), no other wait
+    static constexpr int kWait = (2 * NKT) | (7 << 4) | (15 << 8);
+};
+
+template <int NKT>
+struct LargePrefetch {
+    uint2 vraw[NKT];          // v of node 16 kt + lane % 16, rows v0..v0+3 (bf16)
+    int par;                  // parent of node `lane` (tree walk layout)
+    float alpha, beta;        // gates of node `lane`
+};
+
+template <int NKT>
+__device__ __forceinline__ void large_prefetch(LargePrefetch<NKT>& pf, const uint16_t* V,
+                                               const float* alpha, const float* beta,
+                                               const int32_t* parent, int H, int N, int bh,
+                                               int part, int wave, int lane) {
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * N;
+    const uint32_t col = static_cast<uint32_t>(lane) & 15u;
+    const uint32_t node_stride = static_cast<uint32_t>(H) * D;
+    const uint16_t* Vh = V + (node0 * H + h) * D + part * kSmallRows + 16 * wave;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+        const uint32_t t = 16u * kt + col;
+        pf.vraw[kt] = make_uint2(0u, 0u);
+        if (t < static_cast<uint32_t>(N))
+            pf.vraw[kt] = *reinterpret_cast<const uint2*>(Vh + (t * node_stride + 4u * (lane >> 4)));
+    }
+    pf.par = -1;
+    pf.alpha = 1.0f;
+    pf.beta = 0.0f;
+    if (lane < N) {
+        const size_t nh = (node0 + lane) * H + h;
+        pf.par = parent[node0 + lane];
+        pf.alpha = alpha[nh];
+        pf.beta = beta[nh];
+    }
+}
+
+template <int NKT>
+__global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(NKT == 2 ? 3 : 2)))
+void verify_large_kernel(
+    const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
+    float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
+    uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
+    int32_t* __restrict__ status)
+{
+    using Lo = LargeLayout<NKT>;
+    constexpr int NCT = 2 * NKT;
+    constexpr int kCols = Lo::kCols;
+    extern __shared__ __align__(16) float lds[];
+    float* G = lds + Lo::kS0;                       // G[m][n], n: keys 0..N-1, queries 16NKT+t
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int kq = 8 * grp;
+    float* Us = lds + Lo::kS0 + Lo::kG + wave * (16 * NKT * 16);   // this wave's U scratch
+    const int grid = gridDim.x;
+    const int slot = blockIdx.x;
+
+    int bh, part;
+    small_item(0, slot, grid, bh, part);
+    if (bh >= BH) return;
+    LargePrefetch<NKT> pf;
+    small_issue_s0(S0, lds, bh, part, wave, lane);
+    large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh, part, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(pf.vraw[kt]));
+    asm volatile("" ::"v"(pf.par), "v"(pf.alpha), "v"(pf.beta));
+
+    for (int round = 0;; ) {
+        const int b = bh / H;
+        const int h = bh - b * H;
+        const size_t node0 = static_cast<size_t>(b) * N;
+        const int v0 = part * kSmallRows + 16 * wave + 4 * grp;
+        const uint32_t node_stride = static_cast<uint32_t>(H) * D;
+        const uint16_t* Kh = K + (node0 * H + h) * D;
+        const uint16_t* Qh = Q + (node0 * H + h) * D;
+
+        uint2 vraw[NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) vraw[kt] = pf.vraw[kt];
+        const int my_par = pf.par;
+        const float my_alpha = pf.alpha, my_beta = pf.beta;
+
+        // this item's rows and inputs have landed once only the previous item's stores (2 NKT,
+        // issued last) may still be in flight
+        __builtin_amdgcn_s_waitcnt(Lo::kWait);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(vraw[kt]));
+        asm volatile("" ::"v"(my_par), "v"(my_alpha), "v"(my_beta));
+        lds_barrier();
+
+        // ---- tree walk, lane = node (every wave)
+        uint64_t anc_l;
+        float g_l, rg_l;
+        {
+            NodeInfo ni;
+            {
+                int p = my_par;
+                const bool bad = lane < N && (p < -1 || p >= lane);
+                if (bad) p = -1;
+                uint64_t am = lane < N ? (1ull << lane) : 0ull;
+                float g = lane < N ? my_alpha : 1.0f;
+                int j = p;
+#pragma unroll
+                for (int r = 0; r < 6; ++r) {
+                    const int src = j < 0 ? lane : j;
+                    const uint64_t aj = shfl_u64(am, src);
+                    const float gj = __shfl(g, src);
+                    const int jj = __shfl(j, src);
+                    if (j >= 0) { am |= aj; g *= gj; j = jj; }
+                }
+                ni.anc = am; ni.g = g; ni.depth = __popcll(am); ni.bad = bad;
+            }
+            anc_l = ni.anc;
+            g_l = ni.g;
+            rg_l = 1.0f / ni.g;
+            if (wave == 0 && lane < N && part == 0) {
+                if (ni.bad) report(status, TREEWY_ETREE);
+                gamma[(node0 + lane) * H + h] = ni.g;
+                if (h == 0) {
+                    if (anc_out) anc_out[node0 + lane] = ni.anc;
+                    if (depth_out) depth_out[node0 + lane] = ni.depth;
+                }
+            }
+        }
+
+        // ---- MFMA operands of this wave's 16 rows
+        bf16x8_t ahi[4], alo[4];
+        {
+            const int r = 16 * wave + col;
+            const float* rowp = lds + r * D;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int c0 = 2 * grp + 8 * ks;
+                split_hi_lo(*reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15))),
+                            *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15))),
+                            ahi[ks], alo[ks]);
+            }
+        }
+        lds_barrier();                              // rows read: refill the buffer
+        ++round;
+        int bh_n, part_n;
+        small_item(round, slot, grid, bh_n, part_n);
+        const bool more = bh_n < BH;
+        if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+
+        // ---- contractions and Gram rows 16w..16w+15 (waves with keys there)
+        const bool has_gram = wave < NKT && 16 * wave < N;
+        bf16x8_t ka[4];
+        {
+            const uint32_t m = 16u * wave + col;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                u32x4_t w = {0u, 0u, 0u, 0u};
+                if (has_gram && m < static_cast<uint32_t>(N))
+                    w = *reinterpret_cast<const u32x4_t*>(Kh + (m * node_stride + kq + 32 * ks));
+                ka[ks] = __builtin_bit_cast(bf16x8_t, w);
+            }
+        }
+        f32x4_t acc[NCT];
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+            const uint32_t n = 16u * (c % NKT) + col;          // node of this column
+            const bool is_q = c >= NKT;
+            const bool live = n < static_cast<uint32_t>(N);
+            const uint16_t* src = (is_q ? Qh : Kh) + (n * node_stride + kq);
+            bf16x8_t bv[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                u32x4_t w = {0u, 0u, 0u, 0u};
+                if (live) w = *reinterpret_cast<const u32x4_t*>(src + 32 * ks);
+                bv[ks] = __builtin_bit_cast(bf16x8_t, w);
+            }
+            acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            f32x4_t gacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], bv[ks], acc[c], 0, 0, 0);
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bv[ks], acc[c], 0, 0, 0);
+                if (has_gram)
+                    gacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], bv[ks], gacc, 0, 0, 0);
+            }
+            if (has_gram) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    G[(16 * wave + 4 * grp + e) * kCols + 16 * c + col] = gacc[e];
+            }
+        }
+        if (more)
+            large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
+        lds_barrier();                              // G visible to every wave
+
+        // ---- per lane: nodes t = 16 kt + col, rows v0..v0+3
+        float Uv[NKT][4], Ov[NKT][4];
+        uint64_t mrem[NKT];
+        float gt[NKT], bgt[NKT];
+        int tn[NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            const int t = 16 * kt + col;
+            tn[kt] = t;
+            const bool ok = t < N;
+            const uint64_t a_t = shfl_u64(anc_l, t);
+            const float g_t = ok ? __shfl(g_l, t) : 0.f;
+            const float b_t = ok ? __shfl(my_beta, t) : 0.f;
+            gt[kt] = g_t;
+            bgt[kt] = b_t * g_t;
+            mrem[kt] = ok ? (a_t & ~(1ull << t)) : 0ull;
+            const float vv[4] = {__uint_as_float(vraw[kt].x << 16), __uint_as_float(vraw[kt].x & 0xffff0000u),
+                                 __uint_as_float(vraw[kt].y << 16), __uint_as_float(vraw[kt].y & 0xffff0000u)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Uv[kt][e] = b_t * vv[e] - bgt[kt] * acc[kt][e];
+                Ov[kt][e] = g_t * acc[NKT + kt][e];
+            }
+            *reinterpret_cast<f32x4_t*>(Us + t * 16 + 4 * grp) =
+                f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
+        }
+        // ancestor walk: step d folds in every node's depth-d ancestor (final since step d - 1)
+        for (;;) {
+            bool any = false;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) any |= mrem[kt] != 0ull;
+            if (!__any(any)) break;
+            float rgsrc[NKT];
+            int asel[NKT];
+            bool hasa[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                hasa[kt] = mrem[kt] != 0ull;
+                asel[kt] = hasa[kt] ? __ffsll(static_cast<unsigned long long>(mrem[kt])) - 1 : tn[kt] & 63;
+                mrem[kt] &= mrem[kt] - 1;
+                rgsrc[kt] = __shfl(rg_l, asel[kt]);
+            }
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const int a = asel[kt];
+                const int t = tn[kt];
+                const float cs = hasa[kt] ? bgt[kt] * rgsrc[kt] * G[t * kCols + a] : 0.f;
+                const float cw = hasa[kt] ? gt[kt] * rgsrc[kt] * G[a * kCols + 16 * NKT + t] : 0.f;
+                const f32x4_t x = *reinterpret_cast<const f32x4_t*>(Us + a * 16 + 4 * grp);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Uv[kt][e] -= cs * x[e];
+                    Ov[kt][e] += cw * x[e];
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+                *reinterpret_cast<f32x4_t*>(Us + tn[kt] * 16 + 4 * grp) =
+                    f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
+        }
+        const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
+        const size_t row0 = (node0 * H + h) * D;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            const int t = tn[kt];
+            const bool ok = t < N;
+            const float cw = ok ? G[t * kCols + 16 * NKT + t] : 0.f;   // the node itself
+            f32x4_t ov, uv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ov[e] = Ov[kt][e] + cw * Uv[kt][e];
+                uv[e] = Uv[kt][e];
+            }
+            const uint32_t off = ok ? static_cast<uint32_t>((t * H * D + v0) * sizeof(float)) : span;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                ov, __builtin_amdgcn_make_buffer_rsrc(O + row0, 0, span, kRawBufferFlags), off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                uv, __builtin_amdgcn_make_buffer_rsrc(U + row0, 0, span, kRawBufferFlags), off, 0, 0);
+        }
+        if (!more) break;
+        bh = bh_n;
+        part = part_n;
+    }
+}
+
 // Compute units of the current device, cached per device.
 int device_cu_count() {
     static int cache[64] = {0};
@@ -906,22 +931,6 @@ static hipError_t launch_small(const VerifyArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int NCT>
-static hipError_t launch_mfma(const VerifyArgs& a, hipStream_t stream) {
-    const size_t dyn = sizeof(float) * static_cast<size_t>(VerifyLayout(a.N).total);
-    auto kern = verify_mfma_kernel<NCT>;
-    if (dyn > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(dyn));
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(kern, dim3(a.B * a.H * kParts), dim3(kThreads), dyn, stream, a.S0,
-                       static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
-                       static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
-                       a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status);
-    return hipGetLastError();
-}
 
 }  // namespace
 
@@ -942,12 +951,34 @@ static hipError_t launch_verify_t(const VerifyArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int NKT>
+static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream) {
+    const size_t dyn = sizeof(float) * LargeLayout<NKT>::kTotal;
+    auto kern = verify_large_kernel<NKT>;
+    if (dyn > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(dyn));
+        if (e != hipSuccess) return e;
+    }
+    const int BH = a.B * a.H;
+    const int items = BH * kSmallParts;
+    const int per_cu = NKT == 2 ? 3 : 2;            // resident workgroups (LDS and registers)
+    const int slots = per_cu * device_cu_count();
+    const int grid = items < slots ? items : slots;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), dyn, stream, a.S0,
+                       static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                       static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
+                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status);
+    return hipGetLastError();
+}
+
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     if (a.in_dtype != TREEWY_BF16) return launch_verify_t<float>(a, stream);
     if (a.N <= 8) return launch_small<1>(a, stream);
     if (a.N <= 16) return launch_small<2>(a, stream);
-    if (a.N <= 32) return launch_mfma<4>(a, stream);
-    return launch_mfma<8>(a, stream);
+    if (a.N <= 32) return launch_large<2>(a, stream);
+    return launch_large<4>(a, stream);
 }
 
 }  // namespace treewy
