@@ -28,6 +28,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 
+# HBM byte counts per launch taken with rocprofv3 (FETCH_SIZE, WRITE_SIZE, scaled by the same
+# counters on a plain copy of known size), per workload; used while the kernel source is the
+# one they were taken on
+TRAFFIC_FILES = {1: "profiles/traffic_chain4_b32h32.json"}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -47,6 +52,9 @@ def parse():
                     help="time the store-all comparison path instead of TreeWY")
     ap.add_argument("--graph", action="store_true",
                     help="replay each instance's step as a captured HIP graph")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a kernel of "
+                         "known traffic, used to scale HBM byte counters taken with rocprofv3)")
     return ap.parse_args()
 
 
@@ -193,6 +201,15 @@ def main():
         f"({c_bytes / max(com_ms.mean(), 1e-9) / 1e6:.0f} GB/s); "
         f"step {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s algorithmic")
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * 2 ** 20 // 4
+        src_t = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        torch.cuda.synchronize()
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(first, args.cpu_seconds)
@@ -218,12 +235,31 @@ def main():
         "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": name_v if dom == "verify" else name_c,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": (None if args.snapshot else
+                                 measured_traffic(args.config, name_v if dom == "verify" else name_c)),
                      "bytes_per_launch": d_bytes, "launch_us": d_ms * 1e3},
         "kernels_us": {name_v: ver_ms.mean() * 1e3, name_c: com_ms.mean() * 1e3},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(cfg: int, entry: str):
+    """Counted HBM bytes per launch of `entry` on workload `cfg`, or None when no count was
+    taken or the kernel source changed since."""
+    import hashlib
+    rel = TRAFFIC_FILES.get(cfg)
+    if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
+        return None
+    d = json.load(open(os.path.join(ROOT, rel)))
+    k = d.get("kernels", {}).get(entry)
+    if not k:
+        return None
+    src = os.path.join(ROOT, k["source"])
+    if not os.path.exists(src) or hashlib.sha1(open(src, "rb").read()).hexdigest() != k["source_sha1"]:
+        return None
+    return float(k["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(P, seconds):
