@@ -218,16 +218,17 @@ __device__ __forceinline__ void split_hi_lo(f32x4_t a, f32x4_t b, bf16x8_t& hi, 
 // Small trees (N <= 16): persistent workgroups of 256 lanes over (head, value-row half)
 // items, the solve in registers.
 //
-// Four workgroups stay resident per CU, each with one 32 KB LDS buffer.  A workgroup reads
-// its item's S0 rows from the buffer into MFMA operand registers, and at once the next
-// item's rows start streaming HBM -> LDS into that same buffer (global_load_lds_dwordx4),
-// together with the next item's keys, queries, values, gates and tree (into registers).
-// So 32 KB per workgroup are in flight while it finishes the current item, and the HBM
-// stream does not pause for the per-item arithmetic.  The two halves of a head go to
-// workgroups on the same XCD (slots s and s + 8 of every 16) in the same round, so the
-// head's keys and queries are fetched into that XCD's L2 once.
+// Every input of an item reaches LDS by direct HBM -> LDS transfers (global_load_lds), with
+// no trip through registers: the item's 64 S0 rows (32 KB), its keys and queries (2N rows of
+// 256 B), the item's half of its values (N rows of 128 B) and the parents and gates (one
+// 4-byte gather).  A workgroup reads its item's operands out of LDS into registers, and at
+// once the next item's transfers are issued into the same buffers, so the next item streams
+// in while the current one is solved and written.  The four waves fetch the keys and queries
+// once per workgroup instead of once per wave.  The two halves of a head go to workgroups on
+// the same XCD (slots s and s + 8 of every 16) in the same round, so the head's keys and
+// queries are fetched into that XCD's L2 once.
 //
-// The contractions are those of the kernel above, on this half's 64 rows: wave w owns rows
+// The contractions run on the matrix cores, on this half's 64 rows: wave w owns rows
 // 16w..16w+15.  Keys occupy output columns 0..N-1 of tile 0 and queries columns N..2N-1
 // (tile 0 or 1), so after the contractions lane L of a wave holds P[t][v..v+3] for node
 // t = L % 16 and rows v = 16w + 4 (L / 16) .. +3.  The forward substitution and the readout
@@ -247,12 +248,20 @@ constexpr int kRawBufferFlags = 0x00020000;
 constexpr int kSmallRows = 64;              // value rows per item
 constexpr int kSmallParts = D / kSmallRows; // items per head
 
+// LDS of one small-tree workgroup, in bytes.  Keys sit in rows 0 .. 4 ceil(N/4) - 1 of the
+// key/query area and queries right after them; 16-byte chunk c of row r is stored at chunk
+// c ^ (r % 16) (S0 rows: 32 chunks, key/query rows: 16), which keeps the operand reads free
+// of bank conflicts.
 template <int NCT>
-struct SmallPrefetch {
-    bf16x8_t bfr[NCT][4];     // key/query operand fragments
-    uint2 vraw;               // v_t, rows v0..v0+3 (bf16)
-    int par;                  // parent of node t = lane % 16
-    float alpha, beta;        // gates of node t
+struct SmallLayout {
+    static constexpr int kS0 = 0;                                // [64][128] fp32
+    static constexpr int kKQ = kS0 + kSmallRows * D * 4;         // [16 NCT][128] bf16
+    static constexpr int kV = kKQ + 16 * NCT * D * 2;            // [8 NCT][64] bf16
+    static constexpr int kSm = kV + 8 * NCT * kSmallRows * 2;    // parent, alpha, beta [16] each
+    static constexpr int kG = kSm + 64 * 4;                      // G [16][16 NCT] fp32
+    static constexpr int kBytes = kG + 16 * 16 * NCT * 4;
+    // resident workgroups per CU within the 160 KB of LDS
+    static constexpr int kWgs = (160 * 1024) / kBytes > 4 ? 4 : (160 * 1024) / kBytes;
 };
 
 // Item number -> (head, half).  Slots s and s + 8 of every group of 16 run on one XCD and
@@ -312,6 +321,48 @@ __device__ __forceinline__ void dma_rows_x8(const void* base, const uint32_t (&v
         : "memory");
 }
 
+// A pointer that is the same in every lane, kept in scalar registers (the compiler cannot
+// always prove it uniform).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t x = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+    return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// One HBM -> LDS load of 16 bytes per lane: lane l's bytes from base + voff land at LDS byte
+// lds + 16 l.
+__device__ __forceinline__ void dma_x4(const void* base, uint32_t voff, uint32_t lds) {
+    lds = __builtin_amdgcn_readfirstlane(lds);      // wave-uniform by construction
+    base = uniform_ptr(base);
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(base)
+        : "memory");
+}
+
+// One HBM -> LDS gather of 4 bytes per lane: lane l's word at its own address lands at LDS
+// byte lds + 4 l.
+__device__ __forceinline__ void dma_gather_x1(const void* addr, uint32_t lds) {
+    lds = __builtin_amdgcn_readfirstlane(lds);      // wave-uniform by construction
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(addr)
+        : "memory");
+}
+
 // S0 rows of an item -> LDS: wave w takes rows 16w..16w+15, two whole rows per wave load;
 // chunk c of row r lands at slot c ^ (r % 16).  `wave` is wave-uniform (an SGPR), so the
 // LDS destinations are scalar; the source is a scalar base plus a 32-bit lane offset.
@@ -331,56 +382,56 @@ __device__ __forceinline__ void small_issue_s0(const float* S0, float* buf, int 
     dma_rows_x8(src, voff, lds0);
 }
 
+// The rest of an item's inputs -> LDS, as a list of whole-wave transfers dealt round-robin
+// to the four waves: ceil(N/4) loads of four key rows, as many of four query rows,
+// ceil(N/8) loads of eight value half-rows, and one gather of parent, alpha and beta (lanes
+// 0-15, 16-31, 32-47).  Lanes past the last node load node 0 again, into rows nobody reads.
 template <int NCT>
-__device__ __forceinline__ void small_prefetch(SmallPrefetch<NCT>& pf, const uint16_t* Q,
-                                               const uint16_t* K, const uint16_t* V,
-                                               const float* alpha, const float* beta,
-                                               const int32_t* parent, int H, int N, int bh,
-                                               int part, int wave, int lane) {
+__device__ __forceinline__ void small_issue_inputs(const uint16_t* Q, const uint16_t* K,
+                                                   const uint16_t* V, const float* alpha,
+                                                   const float* beta, const int32_t* parent,
+                                                   int H, int N, int bh, int part, int wave,
+                                                   int lane, uint32_t lds) {
+    using Lo = SmallLayout<NCT>;
     const int b = bh / H;
     const int h = bh - b * H;
     const size_t node0 = static_cast<size_t>(b) * N;
-    const uint32_t col = static_cast<uint32_t>(lane) & 15u;
-    const uint32_t kq = 8u * (static_cast<uint32_t>(lane) >> 4);
-    const uint32_t node_stride = static_cast<uint32_t>(H) * D;       // elements between nodes
-    // scalar bases of this (sequence, head); lane offsets stay 32-bit
+    const uint32_t row_bytes = static_cast<uint32_t>(H) * D * 2;   // between nodes of a head
     const uint16_t* Kh = K + (node0 * H + h) * D;
     const uint16_t* Qh = Q + (node0 * H + h) * D;
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-        const uint32_t n = 16u * c + col;
-        const bool is_k = n < static_cast<uint32_t>(N);
-        const bool is_q = !is_k && n < 2u * N;
-        const uint16_t* src = is_k ? Kh + (n * node_stride + kq)
-                                   : Qh + ((n - N) * node_stride + kq);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            u32x4_t w = {0u, 0u, 0u, 0u};
-            if (is_k || is_q) w = *reinterpret_cast<const u32x4_t*>(src + 32 * ks);
-            pf.bfr[c][ks] = __builtin_bit_cast(bf16x8_t, w);
+    const uint16_t* Vh = V + (node0 * H + h) * D + part * kSmallRows;
+    const uint32_t un = static_cast<uint32_t>(N);
+    const int nq4 = (N + 3) >> 2;
+    const int nv8 = (N + 7) >> 3;
+    const int jobs = 2 * nq4 + nv8 + 1;
+    for (int j = wave; j < jobs; j += 4) {
+        if (j < 2 * nq4) {
+            const bool is_q = j >= nq4;
+            const uint32_t lr = static_cast<uint32_t>(lane) >> 4;
+            const uint32_t r = 4u * j + lr;                           // LDS row
+            const uint32_t n = 4u * (is_q ? j - nq4 : j) + lr;        // node
+            const uint32_t c = (static_cast<uint32_t>(lane) & 15u) ^ (r & 15u);
+            dma_x4(is_q ? Qh : Kh, (n < un ? n : 0u) * row_bytes + 16u * c,
+                   lds + Lo::kKQ + 1024u * j);
+        } else if (j < 2 * nq4 + nv8) {
+            const int jv = j - 2 * nq4;
+            const uint32_t n = 8u * jv + (static_cast<uint32_t>(lane) >> 3);
+            const uint32_t c = static_cast<uint32_t>(lane) & 7u;
+            dma_x4(Vh, (n < un ? n : 0u) * row_bytes + 16u * c, lds + Lo::kV + 1024u * jv);
+        } else {
+            const uint32_t t = static_cast<uint32_t>(lane) & 15u;
+            const uint32_t kind = static_cast<uint32_t>(lane) >> 4;
+            const size_t n = node0 + (t < un ? t : 0u);
+            const void* src = kind == 1 ? static_cast<const void*>(alpha + n * H + h)
+                            : kind == 2 ? static_cast<const void*>(beta + n * H + h)
+                                        : static_cast<const void*>(parent + n);
+            dma_gather_x1(src, lds + Lo::kSm);
         }
-    }
-    pf.vraw = make_uint2(0u, 0u);
-    if (col < static_cast<uint32_t>(N)) {
-        const uint16_t* Vh = V + (node0 * H + h) * D + part * kSmallRows + 16 * wave;
-        pf.vraw = *reinterpret_cast<const uint2*>(Vh + (col * node_stride + 4u * (lane >> 4)));
-    }
-    pf.par = -1;
-    pf.alpha = 1.0f;
-    pf.beta = 0.0f;
-    if (col < static_cast<uint32_t>(N)) {               // node t = lane % 16 of every group
-        const size_t nh = (node0 + col) * H + h;
-        pf.par = parent[node0 + col];
-        pf.alpha = alpha[nh];
-        pf.beta = beta[nh];
     }
 }
 
-// resident workgroups (= waves per SIMD) per CU: the 32 KB buffer and registers allow 4
-template <int NCT> struct SmallOcc { static constexpr int wgs = 4; };
-
 template <int NCT>
-__global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(SmallOcc<NCT>::wgs)))
+__global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(SmallLayout<NCT>::kWgs)))
 void verify_small_kernel(
     const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ alpha,
@@ -389,8 +440,12 @@ void verify_small_kernel(
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
     int32_t* __restrict__ status)
 {
-    extern __shared__ __align__(16) float lds[];    // S0 rows of the item [64][128]
-    __shared__ float G[16 * 32];                    // G[m][n] = k_m . (k|q)_n
+    using Lo = SmallLayout<NCT>;
+    constexpr int kGP = 16 * NCT;                   // G row pitch
+    extern __shared__ __align__(16) float lds[];
+    const char* ldsb = reinterpret_cast<const char*>(lds);
+    float* G = lds + Lo::kG / 4;                    // G[m][n] = k_m . (k|q)_n
+    const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -400,23 +455,16 @@ void verify_small_kernel(
     const int base = lane & 48;                     // first lane of this 16-lane group
     const int t = col;                              // this lane's node in the tail
     const bool node_ok = t < N;
+    const int nq4 = (N + 3) >> 2;
     const int grid = gridDim.x;
     const int slot = blockIdx.x;
 
     int bh, part;
     small_item(0, slot, grid, bh, part);
     if (bh >= BH) return;
-    SmallPrefetch<NCT> pf;
     small_issue_s0(S0, lds, bh, part, wave, lane);
-    small_prefetch<NCT>(pf, Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane);
-    // the first item has to arrive anyway; settling it here keeps the compiler's count at the
-    // loop head exact (it then waits only as far as the top-of-loop wait below)
-    __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-    for (int c = 0; c < NCT; ++c)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(pf.bfr[c][ks]));
-    asm volatile("" ::"v"(pf.vraw), "v"(pf.par), "v"(pf.alpha), "v"(pf.beta));
+    small_issue_inputs<NCT>(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr);
+    __builtin_amdgcn_s_waitcnt(0);                  // the first item: nothing else in flight
 
     for (int round = 0;; ) {
         const int b = bh / H;
@@ -424,22 +472,31 @@ void verify_small_kernel(
         const size_t node0 = static_cast<size_t>(b) * N;
         const int v0 = part * kSmallRows + 16 * wave + 4 * grp;   // this lane's value rows
 
-        const uint2 vraw = pf.vraw;
-        const int my_par = pf.par;
-        const float my_alpha = pf.alpha, my_beta = pf.beta;
-
-        // This item's rows and inputs have landed once at most the two stores of the
-        // previous item (O and U, issued last) are still in flight: vector memory operations
-        // retire in issue order, so vmcnt <= 2 covers everything else.  The empty asm makes
-        // the compiler settle its own waits for the prefetched registers here as well, before
-        // the next transfer is issued (a later wait of its own would also wait for that).
+        // This item's transfers have landed once at most the two stores of the previous item
+        // (O and U, issued last) are still in flight: vector memory operations retire in issue
+        // order, so vmcnt <= 2 covers everything else.
         __builtin_amdgcn_s_waitcnt(kWaitAllButTwoStores);
-#pragma unroll
-        for (int c = 0; c < NCT; ++c)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(pf.bfr[c][ks]));
-        asm volatile("" ::"v"(vraw), "v"(my_par), "v"(my_alpha), "v"(my_beta));
         lds_barrier();                              // ... for every wave; last item fully done
+
+        // ---- this item's operands out of LDS
+        const int my_par = node_ok ? reinterpret_cast<const int*>(ldsb + Lo::kSm)[t] : -1;
+        const float my_alpha = node_ok ? reinterpret_cast<const float*>(ldsb + Lo::kSm)[16 + t] : 1.0f;
+        const float my_beta = node_ok ? reinterpret_cast<const float*>(ldsb + Lo::kSm)[32 + t] : 0.0f;
+        uint2 vraw = make_uint2(0u, 0u);
+        if (node_ok) vraw = *reinterpret_cast<const uint2*>(ldsb + Lo::kV + t * 128 + 32 * wave + 8 * grp);
+        bf16x8_t bfr[NCT][4];
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+            const int n = 16 * c + col;
+            const int r = n < N ? n : (n < 2 * N ? 4 * nq4 + n - N : -1);
+            const char* rowp = ldsb + Lo::kKQ + 256 * (r < 0 ? 0 : r);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                u32x4_t w = {0u, 0u, 0u, 0u};
+                if (r >= 0) w = *reinterpret_cast<const u32x4_t*>(rowp + 16 * ((4 * ks + grp) ^ (r & 15)));
+                bfr[c][ks] = __builtin_bit_cast(bf16x8_t, w);
+            }
+        }
 
         // ---- tree walk, in every 16-lane group (lane = node t): pointer jumping as in
         //      tree_walk, four rounds for the at most 16 nodes of a small tree
@@ -481,12 +538,12 @@ void verify_small_kernel(
                 gacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    bf16x8_t ka = pf.bfr[0][ks];
+                    bf16x8_t ka = bfr[0][ks];
                     if (col >= N) ka = bf16x8_t{};
-                    gacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pf.bfr[c][ks], gacc[c], 0, 0, 0);
+                    gacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bfr[c][ks], gacc[c], 0, 0, 0);
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) G[(4 * grp + e) * 32 + 16 * c + col] = gacc[c][e];
+                for (int e = 0; e < 4; ++e) G[(4 * grp + e) * kGP + 16 * c + col] = gacc[c][e];
             }
         }
 
@@ -503,12 +560,16 @@ void verify_small_kernel(
                             ahi[ks], alo[ks]);
             }
         }
-        lds_barrier();                              // rows read and G visible: refill the buffer
+        lds_barrier();                              // operands read and G visible: refill
         ++round;
         int bh_n, part_n;
         small_item(round, slot, grid, bh_n, part_n);
         const bool more = bh_n < BH;
-        if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+        if (more) {
+            small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+            small_issue_inputs<NCT>(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
+                                    lds_addr);
+        }
 
         // ---- contractions on the matrix cores
         f32x4_t acc[NCT];
@@ -517,13 +578,10 @@ void verify_small_kernel(
             acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], pf.bfr[c][ks], acc[c], 0, 0, 0);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], pf.bfr[c][ks], acc[c], 0, 0, 0);
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], bfr[c][ks], acc[c], 0, 0, 0);
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bfr[c][ks], acc[c], 0, 0, 0);
             }
         }
-        // the operands are consumed: the next item's small inputs go in flight too
-        if (more)
-            small_prefetch<NCT>(pf, Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
 
         // ---- per lane: node t, rows v0..v0+3
         float Yv[4];
@@ -561,8 +619,9 @@ void verify_small_kernel(
             const int a = has ? __builtin_ctz(m) : t;
             m &= m - 1u;
             const float rg_a = __shfl(rg_t, base | a);
-            const float cs = has ? bg_t * rg_a * G[t * 32 + a] : 0.f;
-            const float cw = has ? gg_t * rg_a * G[a * 32 + N + t] : 0.f;
+            // lanes without an ancestor left read entry 0 (their coefficient is zero)
+            const float cs = has ? bg_t * rg_a * G[has ? t * kGP + a : 0] : 0.f;
+            const float cw = has ? gg_t * rg_a * G[has ? a * kGP + N + t : 0] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float x = __shfl(Uv[e], base | a);
@@ -571,7 +630,7 @@ void verify_small_kernel(
             }
         }
         {
-            const float cw = node_ok ? G[t * 32 + N + t] : 0.f;   // the node itself: g_t/g_t = 1
+            const float cw = node_ok ? G[node_ok ? t * kGP + N + t : 0] : 0.f;   // g_t/g_t = 1
 #pragma unroll
             for (int e = 0; e < 4; ++e) Ov[e] += cw * Uv[e];
         }
@@ -918,13 +977,13 @@ int device_cu_count() {
 
 template <int NCT>
 static hipError_t launch_small(const VerifyArgs& a, hipStream_t stream) {
-    const size_t dyn = sizeof(float) * kSmallRows * D;
+    using Lo = SmallLayout<NCT>;
     auto kern = verify_small_kernel<NCT>;
     const int BH = a.B * a.H;
     const int items = BH * kSmallParts;
-    const int slots = SmallOcc<NCT>::wgs * device_cu_count();   // resident workgroups
+    const int slots = Lo::kWgs * device_cu_count();   // resident workgroups
     const int grid = items < slots ? items : slots;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), dyn, stream, a.S0,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), Lo::kBytes, stream, a.S0,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
                        BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status);
