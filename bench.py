@@ -50,6 +50,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--snapshot", action="store_true",
                     help="time the store-all comparison path instead of TreeWY")
+    ap.add_argument("--fused", action="store_true",
+                    help="steady-state steps of treewy_commit_verify: each launch commits the "
+                         "previous step's accepted node and verifies this step's drafts")
     ap.add_argument("--graph", action="store_true",
                     help="replay each instance's step as a captured HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -78,6 +81,7 @@ def main():
     # ---- rotating pool of instances (each: all layers of the workload)
     per_layer = (B * H * 128 * 128 * 4 + 3 * B * N * H * 128 * elem + 2 * B * N * H * 128 * 4
                  + (B * H * N * 128 * 128 * 4 if args.snapshot else 0))
+    assert not (args.fused and args.snapshot), "--fused and --snapshot are exclusive"
     n_inst = max(1, math.ceil(args.pool_gib * 2 ** 30 / (per_layer * nl))) if args.config else 1
     n_inst = min(n_inst, 32)
     log(f"[bench] config {args.config}: {cfg['desc']}; {n_inst} instance(s) of {nl} layer(s), "
@@ -92,8 +96,10 @@ def main():
             dl = device.upload_layer(L, dtype)
             out = device.alloc_outputs(B, H, N)
             snap = (torch.empty((B, H, N, 128, 128), device="cuda") if args.snapshot else None)
+            if args.fused:                      # second set of per-step outputs, alternated
+                snap = device.alloc_outputs(B, H, N)
             layers.append((dl, out, snap))
-        pool.append(dict(P=P, parent=parent, accepted=accepted, layers=layers))
+        pool.append(dict(P=P, parent=parent, accepted=accepted, layers=layers, flip=0))
         if i == 0:
             first = P
         else:
@@ -102,13 +108,40 @@ def main():
     log(f"[bench] inputs drawn and uploaded in {time.time() - t0:.1f} s")
 
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    bytes_fn = accounting.snapshot_step_bytes if args.snapshot else accounting.step_bytes
-    inst_bytes = [bytes_fn(x["P"].parent, x["P"].accepted, H, N, elem, layers=nl) for x in pool]
+    if args.fused:
+        inst_bytes = [accounting.fused_step_bytes(x["P"].parent, x["P"].accepted, x["P"].parent,
+                                                  H, elem, layers=nl) for x in pool]
+        # the previous step of every instance: a plain verify, so that its U and gamma exist
+        for x in pool:
+            for dl, out, _ in x["layers"]:
+                binding.treewy_verify(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta, x["parent"],
+                                      out.O, out.U, out.gamma, status=status)
+        torch.cuda.synchronize()
+    else:
+        bytes_fn = accounting.snapshot_step_bytes if args.snapshot else accounting.step_bytes
+        inst_bytes = [bytes_fn(x["P"].parent, x["P"].accepted, H, N, elem, layers=nl)
+                      for x in pool]
     for x in pool:
         x["P"] = None
 
+    def fused_step(x, ev=None):
+        # this instance's previous step is its own last one (same tree and accepted node)
+        for j, (dl, o0, o1) in enumerate(x["layers"]):
+            prev, cur = (o0, o1) if x["flip"] == 0 else (o1, o0)
+            if ev is not None:
+                ev[0][j].record()
+            binding.treewy_commit_verify(dl.S0, prev.U, dl.K, prev.gamma, x["parent"],
+                                         x["accepted"], dl.Q, dl.K, dl.V, dl.alpha, dl.beta,
+                                         x["parent"], cur.O, cur.U, cur.gamma, status=status)
+            if ev is not None:
+                ev[1][j].record()
+        x["flip"] ^= 1
+
     def step(inst, ev=None):
         x = pool[inst]
+        if args.fused:
+            fused_step(x, ev)
+            return
         for j, (dl, out, snap) in enumerate(x["layers"]):
             if ev is not None:
                 ev[0][j].record()
@@ -132,6 +165,7 @@ def main():
                 ev[3][j].record()
 
     graphs = None
+    assert not (args.graph and args.fused), "--graph replays fixed buffers; --fused alternates them"
     if args.graph:
         # one graph per instance: verify for every layer, then commit for every layer
         graphs = []
@@ -180,12 +214,16 @@ def main():
     torch.cuda.synchronize()
     ver_ms = np.array([[events[s][0][j].elapsed_time(events[s][1][j]) for j in range(nl)]
                        for s in range(K)])
-    com_ms = np.array([[events[s][2][j].elapsed_time(events[s][3][j]) for j in range(nl)]
-                       for s in range(K)])
+    com_ms = (np.zeros_like(ver_ms) if args.fused else
+              np.array([[events[s][2][j].elapsed_time(events[s][3][j]) for j in range(nl)]
+                        for s in range(K)]))
     used = [(args.warmup + s) % n_inst for s in range(K)]
-    v_bytes = np.mean([inst_bytes[i]["verify"] for i in used]) / nl   # per launch
-    c_bytes = np.mean([inst_bytes[i]["commit"] for i in used]) / nl
     step_bytes = np.mean([inst_bytes[i]["total"] for i in used])
+    if args.fused:
+        v_bytes, c_bytes = step_bytes / nl, 0.0
+    else:
+        v_bytes = np.mean([inst_bytes[i]["verify"] for i in used]) / nl   # per launch
+        c_bytes = np.mean([inst_bytes[i]["commit"] for i in used]) / nl
 
     ms_step = wall * 1e3 / K
     nodes_heads = B * H * N * nl
@@ -194,7 +232,8 @@ def main():
     dom = max(kern, key=lambda k: kern[k][1] * 1.0)
     d_bytes, d_ms = kern[dom]
     achieved = d_bytes / (d_ms * 1e-3) / 1e9
-    name_v = "treewy_verify_snapshot" if args.snapshot else "treewy_verify"
+    name_v = ("treewy_verify_snapshot" if args.snapshot else
+              "treewy_commit_verify" if args.fused else "treewy_verify")
     name_c = "treewy_commit_snapshot" if args.snapshot else "treewy_commit"
     log(f"[bench] {ms_step * 1e3:.1f} us/step; verify {ver_ms.mean() * 1e3:.1f} us "
         f"({v_bytes / (ver_ms.mean() * 1e-3) / 1e9:.0f} GB/s), commit {com_ms.mean() * 1e3:.1f} us "
@@ -228,7 +267,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; Qwen3.5-shaped GDN heads, dk=dv=128)",
         "config": {"workload": f"config {args.config}: {cfg['desc']}"
-                   + ("; store-all snapshot path" if args.snapshot else ""),
+                   + ("; store-all snapshot path" if args.snapshot else "")
+                   + ("; previous commit fused into verify" if args.fused else ""),
                    "B": B, "H": H, "N": N, "layers": nl, "qkv_dtype": dtype,
                    "state_dtype": "f32", "instances_rotated": n_inst,
                    "launch": "hip-graph" if args.graph else "stream"},
@@ -236,10 +276,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": name_v if dom == "verify" else name_c,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (None if args.snapshot else
+                     "traffic": (None if args.snapshot or args.fused else
                                  measured_traffic(args.config, name_v if dom == "verify" else name_c)),
                      "bytes_per_launch": d_bytes, "launch_us": d_ms * 1e3},
-        "kernels_us": {name_v: ver_ms.mean() * 1e3, name_c: com_ms.mean() * 1e3},
+        "kernels_us": ({name_v: ver_ms.mean() * 1e3} if args.fused else
+                       {name_v: ver_ms.mean() * 1e3, name_c: com_ms.mean() * 1e3}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TREEWY_VERSION 1
+#define TREEWY_VERSION 2
 
 enum {
     TREEWY_OK = 0,
@@ -93,6 +93,39 @@ int treewy_verify(const float* S0, const void* Q, const void* K, const void* V,
 int treewy_commit(float* S, const float* U, const void* K, const float* gamma,
                   const int32_t* parent, const int32_t* accepted,
                   int B, int H, int N, int in_dtype, int32_t* status, void* stream);
+
+/*
+ * The previous step's commit fused into this step's verify (paper §4 "Implementation":
+ * on chains verify and commit run as one fused kernel; its Conclusion names fusion for
+ * trees as the next step).  Equivalent to
+ *     treewy_commit(S, U_prev, K_prev, gamma_prev, parent_prev, accepted_prev,
+ *                   B, H, N_prev, in_dtype, status, stream);
+ *     treewy_verify(S, Q, K, V, alpha, beta, parent, B, H, N, in_dtype,
+ *                   O, U, gamma, anc_out, depth_out, status, stream);
+ * but for bf16 inputs with N <= 16 it runs as one kernel that reads and writes each state
+ * once: the committed rows are formed on the way into the contractions.  Other shapes run
+ * the two kernels above in that order.
+ *   S                     [B, H, 128, 128] float32, in place: in, the state before the
+ *                         previous step's commit; out, the committed state (the state this
+ *                         step verified against).  Rows of sequences with
+ *                         accepted_prev[b] = -1 are not written.
+ *   U_prev, K_prev, gamma_prev, parent_prev, accepted_prev
+ *                         the previous step's U, keys, gamma, tree and accepted node, laid
+ *                         out with N_prev nodes (1 <= N_prev <= 64); K_prev has in_dtype.
+ *   Q, K, V, alpha, beta, parent, O, U, gamma, anc_out, depth_out
+ *                         this step's, as in treewy_verify, with N nodes.
+ * O, U and gamma must not overlap U_prev, K_prev or gamma_prev (TREEWY_EINVAL when they do):
+ * keep two sets of per-step buffers and alternate.  Device-side errors of either step go to
+ * `status`; a sequence whose previous accepted node or path is invalid keeps its S.
+ */
+int treewy_commit_verify(float* S, const float* U_prev, const void* K_prev,
+                         const float* gamma_prev, const int32_t* parent_prev,
+                         const int32_t* accepted_prev, int N_prev,
+                         const void* Q, const void* K, const void* V,
+                         const float* alpha, const float* beta, const int32_t* parent,
+                         int B, int H, int N, int in_dtype,
+                         float* O, float* U, float* gamma,
+                         uint64_t* anc_out, int32_t* depth_out, int32_t* status, void* stream);
 
 /*
  * Full-state snapshotting, the comparison scheme of the paper's §2 ("full-state

@@ -73,6 +73,23 @@ def step_bytes(parent: np.ndarray, accepted: np.ndarray, H: int, N: int, elem: i
     return dict(verify=v, commit=c, total=v + c)
 
 
+def fused_step_bytes(parent_prev: np.ndarray, accepted_prev: np.ndarray, parent: np.ndarray,
+                     H: int, elem: int, layers: int = 1) -> dict:
+    """One fused pass (the previous step's commit folded into this step's verify), over all
+    layers: per head the state read once, written back when the previous step accepted a
+    node, the path rows of that node, and this step's per-node I/O; per sequence both trees
+    and the accepted node."""
+    B, Np = parent_prev.shape
+    N = parent.shape[1]
+    t = B * H * verify_bytes_per_head(N, elem) + B * 4 * (N + Np + 1)
+    for b in range(B):
+        a = int(accepted_prev[b])
+        if a >= 0:
+            da = int(tree_depths(parent_prev[b])[a])
+            t += H * (4 * D * D + da * (4 * D + elem * D + 4))
+    return dict(fused=layers * t, total=layers * t)
+
+
 def snapshot_step_bytes(parent: np.ndarray, accepted: np.ndarray, H: int, N: int, elem: int,
                         layers: int = 1) -> dict:
     B = parent.shape[0]

@@ -46,11 +46,13 @@ def lib():
         L.treewy_commit.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P]
         L.treewy_verify_snapshot.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, P, P, P]
         L.treewy_commit_snapshot.argtypes = [P, P, P, I, I, I, P, P]
+        L.treewy_commit_verify.argtypes = ([P, P, P, P, P, P, I] + [P] * 6 + [I] * 4 +
+                                           [P] * 7)
         L.treewy_strerror.argtypes = [I]
         L.treewy_strerror.restype = ctypes.c_char_p
         L.treewy_version.argtypes = []
         for f in ("treewy_verify", "treewy_commit", "treewy_verify_snapshot",
-                  "treewy_commit_snapshot", "treewy_version"):
+                  "treewy_commit_snapshot", "treewy_commit_verify", "treewy_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -143,6 +145,41 @@ def treewy_commit(S, U, K, gamma, parent, accepted, status=None, stream=None):
     rc = lib().treewy_commit(_ptr(S), _ptr(U), _ptr(K), _ptr(gamma), _ptr(parent),
                              _ptr(accepted), B, H, N, dt, _ptr(status), _stream(stream))
     _rc(rc, "treewy_commit")
+
+
+def treewy_commit_verify(S, U_prev, K_prev, gamma_prev, parent_prev, accepted_prev,
+                         Q, K, V, alpha, beta, parent, O, U, gamma,
+                         anc_out=None, depth_out=None, status=None, stream=None):
+    """Enqueue the previous step's commit into S followed by this step's verify against the
+    committed S (one kernel where the library fuses them)."""
+    import torch
+    B, N, H, _ = Q.shape
+    Np = K_prev.shape[1]
+    dev = S.device
+    dt, qdt = _qkv_dtype(Q)
+    f32 = (torch.float32,)
+    _check(S, "S", (B, H, D, D), f32, dev)
+    _check(U_prev, "U_prev", (B, Np, H, D), f32, dev)
+    _check(K_prev, "K_prev", (B, Np, H, D), qdt, dev)
+    _check(gamma_prev, "gamma_prev", (B, Np, H), f32, dev)
+    _check(parent_prev, "parent_prev", (B, Np), (torch.int32,), dev)
+    _check(accepted_prev, "accepted_prev", (B,), (torch.int32,), dev)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check(t, n, (B, N, H, D), qdt, dev)
+    for n, t in (("alpha", alpha), ("beta", beta), ("gamma", gamma)):
+        _check(t, n, (B, N, H), f32, dev)
+    _check(parent, "parent", (B, N), (torch.int32,), dev)
+    _check(O, "O", (B, N, H, D), f32, dev)
+    _check(U, "U", (B, N, H, D), f32, dev)
+    _check(anc_out, "anc_out", (B, N), (torch.int64, torch.uint64), dev)
+    _check(depth_out, "depth_out", (B, N), (torch.int32,), dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    rc = lib().treewy_commit_verify(
+        _ptr(S), _ptr(U_prev), _ptr(K_prev), _ptr(gamma_prev), _ptr(parent_prev),
+        _ptr(accepted_prev), Np, _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha), _ptr(beta),
+        _ptr(parent), B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma), _ptr(anc_out),
+        _ptr(depth_out), _ptr(status), _stream(stream))
+    _rc(rc, "treewy_commit_verify")
 
 
 def treewy_verify_snapshot(S0, Q, K, V, alpha, beta, parent, O, Snap, status=None, stream=None):

@@ -22,6 +22,18 @@ bool dtype_ok(int d) { return d == TREEWY_F32 || d == TREEWY_BF16; }
 
 int map_hip(hipError_t e) { return e == hipSuccess ? TREEWY_OK : TREEWY_EHIP; }
 
+constexpr size_t D_ROW = 128;   // elements per node row
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(const Span& x, const Span& y) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(x.p), b0 = reinterpret_cast<uintptr_t>(y.p);
+    return a0 < b0 + y.bytes && b0 < a0 + x.bytes;
+}
+
 }  // namespace
 
 extern "C" {
@@ -47,6 +59,35 @@ int treewy_commit(float* S, const float* U, const void* K, const float* gamma,
     if (!sizes_ok(B, H, N) || !dtype_ok(in_dtype)) return TREEWY_EINVAL;
     treewy::CommitArgs a{S, U, K, gamma, parent, accepted, B, H, N, in_dtype, status};
     return map_hip(treewy::launch_commit(a, static_cast<hipStream_t>(stream)));
+}
+
+int treewy_commit_verify(float* S, const float* U_prev, const void* K_prev,
+                         const float* gamma_prev, const int32_t* parent_prev,
+                         const int32_t* accepted_prev, int N_prev, const void* Q, const void* K,
+                         const void* V, const float* alpha, const float* beta,
+                         const int32_t* parent, int B, int H, int N, int in_dtype, float* O,
+                         float* U, float* gamma, uint64_t* anc_out, int32_t* depth_out,
+                         int32_t* status, void* stream)
+{
+    if (!S || !U_prev || !K_prev || !gamma_prev || !parent_prev || !accepted_prev || !Q || !K ||
+        !V || !alpha || !beta || !parent || !O || !U || !gamma)
+        return TREEWY_EINVAL;
+    if (!sizes_ok(B, H, N) || !sizes_ok(B, H, N_prev) || !dtype_ok(in_dtype)) return TREEWY_EINVAL;
+    // this step's outputs must not overwrite the previous step's factors while they are read
+    const size_t esz = in_dtype == TREEWY_BF16 ? 2 : 4;
+    const size_t rows = static_cast<size_t>(B) * H * D_ROW;
+    const Span outs[3] = {{O, rows * N * 4}, {U, rows * N * 4},
+                          {gamma, static_cast<size_t>(B) * N * H * 4}};
+    const Span ins[3] = {{U_prev, rows * N_prev * 4}, {K_prev, rows * N_prev * esz},
+                         {gamma_prev, static_cast<size_t>(B) * N_prev * H * 4}};
+    for (const Span& o : outs)
+        for (const Span& i : ins)
+            if (overlap(o, i)) return TREEWY_EINVAL;
+    treewy::CommitArgs c{S, U_prev, K_prev, gamma_prev, parent_prev, accepted_prev, B, H, N_prev,
+                         in_dtype, status};
+    treewy::VerifyArgs a{S, Q, K, V, alpha, beta, parent, B, H, N, in_dtype,
+                         O, U, gamma, anc_out, depth_out, status};
+    return map_hip(treewy::launch_commit_verify(c, a, static_cast<hipStream_t>(stream)));
 }
 
 int treewy_verify_snapshot(const float* S0, const void* Q, const void* K, const void* V,

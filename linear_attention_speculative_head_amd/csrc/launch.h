@@ -60,5 +60,8 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
 hipError_t launch_verify_snapshot(const SnapshotVerifyArgs& a, hipStream_t stream);
 hipError_t launch_commit_snapshot(const SnapshotCommitArgs& a, hipStream_t stream);
+// the commit described by `c` (its S, U, K, gamma, parent, accepted and node count N of the
+// previous step), then the verify described by `a` on the committed state (a.S0 == c.S)
+hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStream_t stream);
 
 }  // namespace treewy

@@ -430,17 +430,164 @@ __device__ __forceinline__ void small_issue_inputs(const uint16_t* Q, const uint
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// The previous step's commit fused into this step's verify (paper §3 "Reconstruct on
+// commit", Eq. 3, applied to S0 on its way into the contractions).
+//
+// S holds the state before the previous step's commit.  For each item the S rows arrive in
+// LDS as above; each lane takes its 32 values of row r into registers, replaces them by
+//   S_a[r][k] = g_a S[r][k] + sum over i on the path of a of (g_a / g_i) U_prev[i][r] k_i[k]
+// (a = the previous step's accepted node; nothing when a = -1), writes them back to S and
+// splits them into the bf16 operands of this step's contractions.  So the state is read once
+// and written once per step, and the commit costs no launch of its own.
+//
+// The path's rows (U_prev half-rows, K_prev rows, gammas) must be in flight with the item's
+// other transfers, so the path has to be known one item early; it comes from the previous
+// tree and accepted node of the item's sequence, which are fetched two items early into one
+// of two LDS index slots.  At the top of item i the workgroup derives the path of item i + 1
+// (pointer jumping over the previous tree, lane = node); at the refill point of item i the
+// first kPath rows of that path go out together with item i + 1's S rows, and the index of
+// item i + 2 is fetched.  A path longer than kPath (depth > 8; no shape here reaches it
+// except deep chains) is finished in further chunks with a blocking wait.
+
+constexpr int kPath = 8;                    // path rows staged with an item
+
+struct CommitIn {
+    float* S;                               // state, updated in place
+    const float* U;                         // U of the previous step [B][Np][H][128]
+    const uint16_t* K;                      // its keys, bf16 [B][Np][H][128]
+    const float* gamma;                     // its cumulative gates [B][Np][H]
+    const int32_t* parent;                  // its tree [B][Np]
+    const int32_t* accepted;                // its accepted node [B], -1 = none
+    int Np;                                 // its node count
+};
+
+// LDS of one fused workgroup: the small-tree layout, then the path rows and index slots.
 template <int NCT>
-__global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(SmallLayout<NCT>::kWgs)))
+struct FusedLayout {
+    using Base = SmallLayout<NCT>;
+    static constexpr int kPU = Base::kBytes;                     // [kPath][64] fp32
+    static constexpr int kPK = kPU + kPath * kSmallRows * 4;     // [kPath][128] bf16
+    static constexpr int kPG = kPK + kPath * D * 2;              // [64] fp32 path gammas
+    static constexpr int kIdx = kPG + 64 * 4;                    // 2 x {parents[64], accepted[64]}
+    static constexpr int kBytes = kIdx + 2 * 512;
+    static constexpr int kWgs = (160 * 1024) / kBytes > 4 ? 4 : (160 * 1024) / kBytes;
+};
+
+// One item's commit: the path of the accepted node as a mask, its length, and in lane q the
+// q-th path node in increasing order (root first).
+struct PathInfo {
+    uint64_t mask;
+    int depth;                              // 0: nothing to commit
+    int pn;
+};
+
+// Sequence b's previous tree and accepted node -> an LDS index slot (parents in words 0-63,
+// lanes past Np repeating node 0; accepted[b] in every word of 64-127).
+__device__ __forceinline__ void fused_issue_index(const CommitIn& c, int b, int lane,
+                                                  uint32_t slot) {
+    const int n = lane < c.Np ? lane : 0;
+    dma_gather_x1(c.parent + static_cast<size_t>(b) * c.Np + n, slot);
+    dma_gather_x1(c.accepted + b, slot + 256u);
+}
+
+// The path of the accepted node from an index slot, by every wave (lane = node of the previous
+// tree): pointer jumping gives each node its inclusive ancestor mask and whether a malformed
+// parent lies on its way up.  An accepted node outside [-1, Np - 1] or a malformed path leaves
+// nothing to commit and is reported when `reporter` is set.
+__device__ __forceinline__ PathInfo fused_path(const char* slot, int Np, int lane, bool reporter,
+                                               int32_t* status) {
+    const int a = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(slot + 256)[0]);
+    const int p_raw = lane < Np ? reinterpret_cast<const int*>(slot)[lane] : -1;
+    const bool bad = lane < Np && (p_raw < -1 || p_raw >= lane);
+    int j = bad ? -1 : p_raw;
+    uint64_t am = lane < Np ? (1ull << lane) : 0ull;
+    int badp = bad ? 1 : 0;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+        const int src = j < 0 ? lane : j;
+        const uint64_t aj = shfl_u64(am, src);
+        const int bj = __shfl(badp, src);
+        const int jj = __shfl(j, src);
+        if (j >= 0) { am |= aj; badp |= bj; j = jj; }
+    }
+    PathInfo pi;
+    pi.mask = 0ull;
+    pi.depth = 0;
+    pi.pn = 0;
+    if (a < -1 || a >= Np) {
+        if (reporter && lane == 0) report(status, TREEWY_EACCEPT);
+        return pi;
+    }
+    if (a < 0) return pi;
+    const uint64_t m = shfl_u64(am, a);
+    const int mbad = __shfl(badp, a);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(m));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(m >> 32));
+    if (__builtin_amdgcn_readfirstlane(mbad)) {
+        if (reporter && lane == 0) report(status, TREEWY_ETREE);
+        return pi;
+    }
+    uint64_t mm = (static_cast<uint64_t>(hi) << 32) | lo;
+    pi.mask = mm;
+    pi.depth = __popcll(mm);
+    for (int q = 0; mm != 0ull; ++q) {
+        const int n = __builtin_ctzll(mm);
+        mm &= mm - 1ull;
+        if (lane == q) pi.pn = n;
+    }
+    return pi;
+}
+
+// Rows kPath c .. kPath c + kPath - 1 of an item's path -> LDS: U_prev half-rows (this item's
+// 64 value rows) and K_prev rows, four per transfer, and with the first chunk the gammas of
+// the whole path (one gather).  Slots past the path repeat its first node.
+__device__ __forceinline__ void fused_issue_path(const CommitIn& c, const PathInfo& pi, int chunk,
+                                                 int bh, int part, int H, int wave, int lane,
+                                                 uint32_t pu, uint32_t pk, uint32_t pg) {
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * c.Np;
+    const int cnt = pi.depth - kPath * chunk < kPath ? pi.depth - kPath * chunk : kPath;
+    const int nj = (cnt + 3) >> 2;
+    const int jobs = 2 * nj + (chunk == 0 ? 1 : 0);
+    const float* Uh = c.U + (node0 * H + h) * D + part * kSmallRows;
+    const uint16_t* Kh = c.K + (node0 * H + h) * D;
+    const uint32_t col16 = 16u * (static_cast<uint32_t>(lane) & 15u);
+    for (int j = wave; j < jobs; j += 4) {
+        if (j < 2 * nj) {
+            const bool is_k = j >= nj;
+            const int jj = is_k ? j - nj : j;
+            const int q = 4 * jj + (lane >> 4);
+            const uint32_t n = static_cast<uint32_t>(__shfl(pi.pn, kPath * chunk + (q < cnt ? q : 0)));
+            if (is_k)
+                dma_x4(Kh, n * static_cast<uint32_t>(H) * (D * 2u) + col16, pk + 1024u * jj);
+            else
+                dma_x4(Uh, n * static_cast<uint32_t>(H) * (D * 4u) + col16, pu + 1024u * jj);
+        } else {
+            const int n = __shfl(pi.pn, lane < pi.depth ? lane : 0);
+            dma_gather_x1(c.gamma + (node0 + n) * H + h, pg);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// The small-tree verify kernel; with FUSED the previous step's commit is applied to S on the
+// way in (see above), otherwise S0 is read as it is.
+
+template <int NCT, bool FUSED>
+__global__ __launch_bounds__(kSmallThreads)
+__attribute__((amdgpu_waves_per_eu(FUSED ? FusedLayout<NCT>::kWgs : SmallLayout<NCT>::kWgs)))
 void verify_small_kernel(
-    const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const float* S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ alpha,
     const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
     float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
-    int32_t* __restrict__ status)
+    int32_t* __restrict__ status, CommitIn cin)
 {
     using Lo = SmallLayout<NCT>;
+    using Fl = FusedLayout<NCT>;
     constexpr int kGP = 16 * NCT;                   // G row pitch
     extern __shared__ __align__(16) float lds[];
     const char* ldsb = reinterpret_cast<const char*>(lds);
@@ -462,6 +609,22 @@ void verify_small_kernel(
     int bh, part;
     small_item(0, slot, grid, bh, part);
     if (bh >= BH) return;
+
+    PathInfo cur{0ull, 0, 0};                       // this item's commit (FUSED)
+    if constexpr (FUSED) {
+        // index of items 0 and 1, then the path of item 0 before its transfers go out
+        int bh1, part1;
+        small_item(1, slot, grid, bh1, part1);
+        fused_issue_index(cin, bh / H, lane, lds_addr + Fl::kIdx);
+        if (bh1 < BH) fused_issue_index(cin, bh1 / H, lane, lds_addr + Fl::kIdx + 512);
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        cur = fused_path(ldsb + Fl::kIdx, cin.Np, lane, wave == 0 && bh % H == 0 && part == 0,
+                         status);
+        if (cur.depth > 0)
+            fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr + Fl::kPU,
+                             lds_addr + Fl::kPK, lds_addr + Fl::kPG);
+    }
     small_issue_s0(S0, lds, bh, part, wave, lane);
     small_issue_inputs<NCT>(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr);
     __builtin_amdgcn_s_waitcnt(0);                  // the first item: nothing else in flight
@@ -477,6 +640,16 @@ void verify_small_kernel(
         // order, so vmcnt <= 2 covers everything else.
         __builtin_amdgcn_s_waitcnt(kWaitAllButTwoStores);
         lds_barrier();                              // ... for every wave; last item fully done
+
+        int bh_n, part_n;
+        small_item(round + 1, slot, grid, bh_n, part_n);
+        const bool more = bh_n < BH;
+        PathInfo nxt{0ull, 0, 0};
+        if constexpr (FUSED) {
+            if (more)
+                nxt = fused_path(ldsb + Fl::kIdx + 512 * ((round + 1) & 1), cin.Np, lane,
+                                 wave == 0 && bh_n % H == 0 && part_n == 0, status);
+        }
 
         // ---- this item's operands out of LDS
         const int my_par = node_ok ? reinterpret_cast<const int*>(ldsb + Lo::kSm)[t] : -1;
@@ -547,28 +720,84 @@ void verify_small_kernel(
             }
         }
 
-        // ---- MFMA operands of this wave's 16 rows, split into bf16 hi and lo
-        bf16x8_t ahi[4], alo[4];
+        // ---- this wave's 16 rows of S0: lane L holds row 16w + L % 16, values
+        //      32 ks + 8 (L / 16) .. +7 for ks = 0..3 (the MFMA A-operand layout)
+        f32x4_t sv[4][2];
         {
             const int r = 16 * wave + col;
             const float* rowp = lds + r * D;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int c0 = 2 * grp + 8 * ks;
-                split_hi_lo(*reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15))),
-                            *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15))),
-                            ahi[ks], alo[ks]);
+                sv[ks][0] = *reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15)));
+                sv[ks][1] = *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15)));
             }
         }
+        if constexpr (FUSED) {
+            if (cur.depth > 0) {
+                // S_a = g_a S + sum over the path of (g_a / g_i) U_prev[i] k_i^T, on this
+                // lane's 32 values; the path's gammas are in LDS in path order (a is last)
+                const float* PG = reinterpret_cast<const float*>(ldsb + Fl::kPG);
+                const float* PU = reinterpret_cast<const float*>(ldsb + Fl::kPU);
+                const char* PK = ldsb + Fl::kPK;
+                const int r = 16 * wave + col;
+                const float ga = PG[cur.depth - 1];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) { sv[ks][0] *= ga; sv[ks][1] *= ga; }
+                for (int q0 = 0; q0 < cur.depth; q0 += kPath) {
+                    if (q0 > 0) {
+                        // a path deeper than kPath: the next chunk, with a blocking wait
+                        lds_barrier();
+                        fused_issue_path(cin, cur, q0 / kPath, bh, part, H, wave, lane,
+                                         lds_addr + Fl::kPU, lds_addr + Fl::kPK,
+                                         lds_addr + Fl::kPG);
+                        __builtin_amdgcn_s_waitcnt(0);
+                        lds_barrier();
+                    }
+                    const int cnt = cur.depth - q0 < kPath ? cur.depth - q0 : kPath;
+                    for (int q = 0; q < cnt; ++q) {
+                        const float cu = (ga / PG[q0 + q]) * PU[q * kSmallRows + r];
+#pragma unroll
+                        for (int ks = 0; ks < 4; ++ks) {
+                            const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(PK + q * 256 + 64 * ks + 16 * grp);
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) {
+                                sv[ks][0][2 * e] += cu * __uint_as_float(kw[e] << 16);
+                                sv[ks][0][2 * e + 1] += cu * __uint_as_float(kw[e] & 0xffff0000u);
+                                sv[ks][1][2 * e] += cu * __uint_as_float(kw[2 + e] << 16);
+                                sv[ks][1][2 * e + 1] += cu * __uint_as_float(kw[2 + e] & 0xffff0000u);
+                            }
+                        }
+                    }
+                }
+                // the committed rows back to HBM: per ks a wave writes 16 rows x 128 bytes
+                float* Srow = cin.S + (static_cast<size_t>(bh) * D + part * kSmallRows + r) * D + 8 * grp;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    *reinterpret_cast<f32x4_t*>(Srow + 32 * ks) = sv[ks][0];
+                    *reinterpret_cast<f32x4_t*>(Srow + 32 * ks + 4) = sv[ks][1];
+                }
+            }
+        }
+        // ---- MFMA operands of this wave's 16 rows, split into bf16 hi and lo
+        bf16x8_t ahi[4], alo[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) split_hi_lo(sv[ks][0], sv[ks][1], ahi[ks], alo[ks]);
         lds_barrier();                              // operands read and G visible: refill
         ++round;
-        int bh_n, part_n;
-        small_item(round, slot, grid, bh_n, part_n);
-        const bool more = bh_n < BH;
         if (more) {
             small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
             small_issue_inputs<NCT>(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
                                     lds_addr);
+            if constexpr (FUSED) {
+                if (nxt.depth > 0)
+                    fused_issue_path(cin, nxt, 0, bh_n, part_n, H, wave, lane, lds_addr + Fl::kPU,
+                                     lds_addr + Fl::kPK, lds_addr + Fl::kPG);
+                int bh_2, part_2;
+                small_item(round + 1, slot, grid, bh_2, part_2);
+                if (bh_2 < BH)
+                    fused_issue_index(cin, bh_2 / H, lane, lds_addr + Fl::kIdx + 512 * ((round + 1) & 1));
+            }
         }
 
         // ---- contractions on the matrix cores
@@ -652,6 +881,7 @@ void verify_small_kernel(
         if (!more) break;
         bh = bh_n;
         part = part_n;
+        if constexpr (FUSED) cur = nxt;
     }
 }
 
@@ -975,18 +1205,19 @@ int device_cu_count() {
     return cus;
 }
 
-template <int NCT>
-static hipError_t launch_small(const VerifyArgs& a, hipStream_t stream) {
-    using Lo = SmallLayout<NCT>;
-    auto kern = verify_small_kernel<NCT>;
+template <int NCT, bool FUSED>
+static hipError_t launch_small(const VerifyArgs& a, const CommitIn& cin, hipStream_t stream) {
+    const int bytes = FUSED ? FusedLayout<NCT>::kBytes : SmallLayout<NCT>::kBytes;
+    const int wgs = FUSED ? FusedLayout<NCT>::kWgs : SmallLayout<NCT>::kWgs;
+    auto kern = verify_small_kernel<NCT, FUSED>;
     const int BH = a.B * a.H;
     const int items = BH * kSmallParts;
-    const int slots = Lo::kWgs * device_cu_count();   // resident workgroups
+    const int slots = wgs * device_cu_count();   // resident workgroups
     const int grid = items < slots ? items : slots;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), Lo::kBytes, stream, a.S0,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), bytes, stream, a.S0,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
-                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status);
+                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status, cin);
     return hipGetLastError();
 }
 
@@ -1034,10 +1265,26 @@ static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream) {
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     if (a.in_dtype != TREEWY_BF16) return launch_verify_t<float>(a, stream);
-    if (a.N <= 8) return launch_small<1>(a, stream);
-    if (a.N <= 16) return launch_small<2>(a, stream);
+    const CommitIn none{};
+    if (a.N <= 8) return launch_small<1, false>(a, none, stream);
+    if (a.N <= 16) return launch_small<2, false>(a, none, stream);
     if (a.N <= 32) return launch_large<2>(a, stream);
     return launch_large<4>(a, stream);
+}
+
+// The previous step's commit fused into this step's verify where the small-tree kernel runs
+// (bf16 inputs, N <= 16); elsewhere the commit kernel and then the verify kernel, in order on
+// the stream, which computes the same.
+hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStream_t stream) {
+    if (a.in_dtype == TREEWY_BF16 && a.N <= 16) {
+        const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
+                           c.accepted, c.N};
+        return a.N <= 8 ? launch_small<1, true>(a, cin, stream)
+                        : launch_small<2, true>(a, cin, stream);
+    }
+    hipError_t e = launch_commit(c, stream);
+    if (e != hipSuccess) return e;
+    return launch_verify(a, stream);
 }
 
 }  // namespace treewy

@@ -20,14 +20,15 @@ def lib():
 def test_exports_every_header_symbol(lib):
     names = binding.header_symbols()
     assert set(names) == {"treewy_verify", "treewy_commit", "treewy_verify_snapshot",
-                          "treewy_commit_snapshot", "treewy_strerror", "treewy_version"}
+                          "treewy_commit_snapshot", "treewy_commit_verify", "treewy_strerror",
+                          "treewy_version"}
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_strerror(lib):
-    assert lib.treewy_version() == 1
+    assert lib.treewy_version() == 2
     for code in range(5):
         assert lib.treewy_strerror(code)
     assert lib.treewy_strerror(99) == b"unknown error code"
@@ -65,3 +66,39 @@ def test_snapshot_rejects(lib):
                                       FAKE, None, None, None) == binding.TREEWY_EINVAL
     assert lib.treewy_commit_snapshot(FAKE, FAKE, None, 1, 1, 4, None, None) == binding.TREEWY_EINVAL
     assert lib.treewy_commit_snapshot(FAKE, FAKE, FAKE, 1, 1, 0, None, None) == binding.TREEWY_EINVAL
+
+
+def fused_args(**kw):
+    """Arguments of treewy_commit_verify; distinct fake addresses far apart by default."""
+    f = lambda x: ctypes.c_void_p(x)
+    a = dict(S=f(0x10000000), U_prev=f(0x20000000), K_prev=f(0x30000000),
+             gamma_prev=f(0x40000000), parent_prev=f(0x50000000), accepted_prev=f(0x60000000),
+             Np=4, Q=f(0x70000000), K=f(0x80000000), V=f(0x90000000), alpha=f(0xa0000000),
+             beta=f(0xb0000000), parent=f(0xc0000000), B=2, H=2, N=4, dt=binding.TREEWY_BF16,
+             O=f(0xd0000000), U=f(0xe0000000), gamma=f(0xf0000000), anc=None, depth=None,
+             status=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(S=None), dict(U_prev=None), dict(K_prev=None),
+                                 dict(gamma_prev=None), dict(parent_prev=None),
+                                 dict(accepted_prev=None), dict(Q=None), dict(parent=None),
+                                 dict(O=None), dict(U=None), dict(gamma=None),
+                                 dict(Np=0), dict(Np=65), dict(N=0), dict(N=65), dict(B=0),
+                                 dict(dt=3)])
+def test_commit_verify_rejects(lib, bad):
+    assert lib.treewy_commit_verify(*fused_args(**bad)) == binding.TREEWY_EINVAL
+
+
+@pytest.mark.parametrize("which", ["U", "O", "gamma"])
+def test_commit_verify_rejects_outputs_over_previous_factors(lib, which):
+    """This step's outputs may not overlap the previous step's U, K or gamma."""
+    # U_prev spans B*Np*H*128*4 = 8 KiB from 0x20000000; an output starting inside it overlaps
+    inside = ctypes.c_void_p(0x20000000 + 4096)
+    assert lib.treewy_commit_verify(*fused_args(**{which: inside})) == binding.TREEWY_EINVAL
+    # K_prev (bf16, 4 KiB) and gamma_prev (64 B)
+    assert lib.treewy_commit_verify(*fused_args(**{which: ctypes.c_void_p(0x30000000 + 100)})) \
+        == binding.TREEWY_EINVAL
+    assert lib.treewy_commit_verify(*fused_args(**{which: ctypes.c_void_p(0x40000000)})) \
+        == binding.TREEWY_EINVAL

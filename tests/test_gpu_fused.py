@@ -1,0 +1,208 @@
+"""GPU parity of treewy_commit_verify: the previous step's commit followed by this step's
+verify against the committed state, through the C ABI, against the oracle composed the same
+way (replay of step 1 up to its accepted node, then a fresh verify of step 2 from there).
+
+Gate as for the separate calls: per (sequence, head), max|x - oracle| / max|oracle| <= 1e-3
+for this step's O, U, gamma and for the committed state; sequences with nothing accepted in
+the previous step keep their state bit for bit; ancestor masks and depths are bit-exact.
+"""
+
+import numpy as np
+import pytest
+
+from linear_attention_speculative_head_amd import inputs
+from parity import TOL, gather_heads, headwise_rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_attention_speculative_head_amd import binding
+    binding.lib()
+
+
+def run_fused(P1, P2, status_check=True):
+    """Step 1: treewy_verify on P1 (its U and gamma are the previous step's factors).
+    Step 2: treewy_commit_verify with P1's tree and accepted node and P2's drafts."""
+    import torch
+    from linear_attention_speculative_head_amd import binding, device
+    assert (P1.B, P1.H) == (P2.B, P2.H) and P1.dtype == P2.dtype
+    d1 = device.upload_layer(P1.layers[0], P1.dtype)
+    par1, acc1 = device.upload_tree(P1)
+    o1 = device.alloc_outputs(P1.B, P1.H, P1.N, fill=float("nan"))
+    binding.treewy_verify(d1.S0, d1.Q, d1.K, d1.V, d1.alpha, d1.beta, par1, o1.O, o1.U, o1.gamma)
+    d2 = device.upload_layer(P2.layers[0], P2.dtype)
+    par2, _ = device.upload_tree(P2)
+    o2 = device.alloc_outputs(P2.B, P2.H, P2.N, fill=float("nan"))
+    anc = torch.zeros((P2.B, P2.N), dtype=torch.int64, device="cuda")
+    dep = torch.zeros((P2.B, P2.N), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S = d1.S0.clone()
+    binding.treewy_commit_verify(S, o1.U, d1.K, o1.gamma, par1, acc1, d2.Q, d2.K, d2.V,
+                                 d2.alpha, d2.beta, par2, o2.O, o2.U, o2.gamma, anc, dep, status)
+    torch.cuda.synchronize()
+    res = dict(O=o2.O.cpu().numpy(), U=o2.U.cpu().numpy(), gamma=o2.gamma.cpu().numpy(),
+               S=S.cpu().numpy(), anc=anc.cpu().numpy().view(np.uint64),
+               depth=dep.cpu().numpy(), status=int(status.item()))
+    if status_check:
+        assert res["status"] == 0, f"device status {res['status']}"
+    return res
+
+
+def oracle_fused(P1, P2, heads):
+    """Committed state after step 1 and step 2's outputs from it, on the given heads."""
+    import oracle
+    r1 = oracle.batch(P1.layers[0], P1.parent, P1.accepted, heads=heads, commit=True)
+    S1 = P1.layers[0].S0.copy()
+    for i, (b, h) in enumerate(heads):
+        S1[b, h] = r1["S_new"][i].astype(np.float32)
+    L2 = P2.layers[0]
+    layer2 = inputs.Layer(S0=S1, q=L2.q, k=L2.k, v=L2.v, alpha=L2.alpha, beta=L2.beta)
+    r2 = oracle.batch(layer2, P2.parent, None, heads=heads, commit=False)
+    return r1["S_new"], r2
+
+
+def check_fused(P1, P2, gpu, heads=None, label=""):
+    import oracle
+    if heads is None:
+        heads = [(b, h) for b in range(P1.B) for h in range(P1.H)]
+    S_ref, r2 = oracle_fused(P1, P2, heads)
+    worst = {}
+    for key, kind, ref in (("O", "node", r2["O"]), ("U", "node", r2["U"]),
+                           ("gamma", "node", r2["gamma"]), ("S", "state", S_ref)):
+        g = gather_heads(gpu[key], heads, kind).astype(np.float64)
+        assert np.all(np.isfinite(g)), f"{label} {key}: non-finite GPU values"
+        e = headwise_rel(g, ref)
+        worst[key] = float(e.max())
+        bad = np.flatnonzero(e > TOL)
+        assert len(bad) == 0, (f"{label} {key}: {len(bad)} heads above {TOL}; worst "
+                               f"{e.max():.3e} at head {heads[int(np.argmax(e))]}")
+    for b in sorted({x[0] for x in heads}):
+        if P1.accepted[b] == -1:
+            assert np.array_equal(gpu["S"][b], P1.layers[0].S0[b]), f"{label}: b={b} not kept"
+        d, a = oracle.index_tree(P2.parent[b])
+        assert np.array_equal(gpu["depth"][b], d), f"{label} depth mismatch at b={b}"
+        assert np.array_equal(gpu["anc"][b], a), f"{label} anc mismatch at b={b}"
+    say(f"  {label} worst head-wise rel err: " + ", ".join(f"{k}={v:.2e}" for k, v in worst.items()))
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_fused_config_full(cfg):
+    """Two consecutive draws of a configuration: the fused kernel at full size, every head."""
+    say(f"[fused] config {cfg}: {inputs.CONFIGS[cfg]['desc']}")
+    P1 = inputs.make_problem(cfg, instance=0)
+    P2 = inputs.make_problem(cfg, instance=1)
+    gpu = run_fused(P1, P2)
+    check_fused(P1, P2, gpu, label=f"cfg{cfg}")
+
+
+@pytest.mark.parametrize("N1,tree1,N2,tree2,seed", [
+    (4, "chain", 4, "chain", 21),
+    (12, (5, 3), 5, (3, 2), 22),      # previous tree larger than this step's
+    (3, (2, 2), 16, (5, 4), 23),      # previous tree smaller
+    (20, "chain", 8, (4, 3), 24),     # previous paths up to depth 20: chunks of 8 rows
+    (64, "chain", 16, "chain", 25),   # depth up to 64: eight chunks
+    (40, (6, 4), 1, "chain", 26),
+    (7, (3, 3), 9, (4, 3), 27),
+])
+def test_fused_shapes(N1, tree1, N2, tree2, seed):
+    """Ragged node counts on both steps, deep previous paths, every head compared."""
+    say(f"[fused] N_prev={N1} {tree1} -> N={N2} {tree2}")
+    B, H = 5, 6
+    P1 = inputs.make_custom(seed, B=B, H=H, N=N1, tree=tree1)
+    # accepted nodes: the deepest node of some sequences, none in one, random elsewhere
+    d = np.array([inputs.tree_depths(P1.parent[b]) for b in range(B)])
+    acc = P1.accepted.copy()
+    acc[0] = int(np.argmax(d[0]))
+    acc[1] = -1
+    acc[2] = N1 - 1
+    P1 = inputs.Problem(cfg=-1, B=B, H=H, N=N1, dtype=P1.dtype, parent=P1.parent,
+                        accepted=acc.astype(np.int32), layers=P1.layers)
+    P2 = inputs.make_custom(seed + 1000, B=B, H=H, N=N2, tree=tree2)
+    gpu = run_fused(P1, P2)
+    check_fused(P1, P2, gpu, label=f"N_prev={N1} N={N2}")
+
+
+@pytest.mark.parametrize("N2,dtype", [(32, "bf16"), (64, "bf16"), (6, "f32")])
+def test_unfused_shapes_match(N2, dtype):
+    """Shapes the library runs as commit then verify give the same contract."""
+    say(f"[fused] two-kernel shape N={N2} {dtype}")
+    P1 = inputs.make_custom(31, B=3, H=4, N=10, dtype=dtype, tree=(4, 3))
+    P2 = inputs.make_custom(32, B=3, H=4, N=N2, dtype=dtype, tree=(6, 4))
+    gpu = run_fused(P1, P2)
+    check_fused(P1, P2, gpu, label=f"N={N2} {dtype}")
+
+
+def test_fused_steps_chain_like_decoding():
+    """Three steps in a row with alternating per-step buffers, against the oracle stepping
+    the same way (commit of step s, then verify of step s + 1)."""
+    import torch
+    import oracle
+    from linear_attention_speculative_head_amd import binding, device
+    B, H, N = 4, 3, 6
+    steps = [inputs.make_custom(40 + s, B=B, H=H, N=N, tree=(4, 2)) for s in range(4)]
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    # GPU: verify step 0, then commit_verify steps 1..3
+    dls = [device.upload_layer(P.layers[0], P.dtype) for P in steps]
+    trees = [device.upload_tree(P) for P in steps]
+    outs = [device.alloc_outputs(B, H, N, fill=float("nan")) for _ in range(2)]
+    S = dls[0].S0.clone()
+    d0 = dls[0]
+    binding.treewy_verify(S, d0.Q, d0.K, d0.V, d0.alpha, d0.beta, trees[0][0],
+                          outs[0].O, outs[0].U, outs[0].gamma)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for s in range(1, 4):
+        prev, cur = outs[(s - 1) % 2], outs[s % 2]
+        dp, dc = dls[s - 1], dls[s]
+        binding.treewy_commit_verify(S, prev.U, dp.K, prev.gamma, trees[s - 1][0], trees[s - 1][1],
+                                     dc.Q, dc.K, dc.V, dc.alpha, dc.beta, trees[s][0],
+                                     cur.O, cur.U, cur.gamma, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    # oracle: the same sequence of commits and verifies, state carried in float32
+    S_ref = steps[0].layers[0].S0.copy()
+    for s in range(0, 4):
+        L = steps[s].layers[0]
+        layer = inputs.Layer(S0=S_ref, q=L.q, k=L.k, v=L.v, alpha=L.alpha, beta=L.beta)
+        r = oracle.batch(layer, steps[s].parent, steps[s].accepted, heads=heads, commit=True)
+        if s == 3:
+            break
+        S_ref = r["S_new"].reshape(B, H, 128, 128).astype(np.float32)
+    last = outs[3 % 2]
+    for key, ref in (("O", r["O"]), ("U", r["U"])):
+        g = gather_heads(getattr(last, key).cpu().numpy(), heads, "node").astype(np.float64)
+        e = headwise_rel(g, ref)
+        assert e.max() <= TOL, f"{key}: worst {e.max():.3e}"
+    e = headwise_rel(S.cpu().numpy().reshape(B * H, -1).astype(np.float64),
+                     S_ref.reshape(B * H, -1).astype(np.float64))
+    assert e.max() <= TOL, f"S: worst {e.max():.3e}"
+    say(f"  three fused steps: worst O/U/S rel err within {TOL}")
+
+
+def test_fused_reports_bad_previous_step():
+    """An accepted node outside the previous tree, or a malformed parent on its path, is
+    reported; that sequence keeps its state, the others commit and verify normally."""
+    from linear_attention_speculative_head_amd import binding
+    B, H = 4, 2
+    P1 = inputs.make_custom(51, B=B, H=H, N=6, tree="chain",
+                            accepted=np.array([5, 9, 3, 4], dtype=np.int32))
+    P2 = inputs.make_custom(52, B=B, H=H, N=5, tree=(3, 2))
+    gpu = run_fused(P1, P2, status_check=False)
+    assert gpu["status"] == binding.TREEWY_EACCEPT
+    assert np.array_equal(gpu["S"][1], P1.layers[0].S0[1])
+    ok = [(b, h) for b in (0, 2, 3) for h in range(H)]
+    P1ok = inputs.Problem(cfg=-1, B=B, H=H, N=6, dtype=P1.dtype, parent=P1.parent,
+                          accepted=np.array([5, -1, 3, 4], dtype=np.int32), layers=P1.layers)
+    check_fused(P1ok, P2, gpu, heads=ok, label="beside a bad accepted node")
+
+    bad = P1.parent.copy()
+    bad[2, 3] = 5                      # node 3's parent after it: on the path of accepted 3
+    P1b = inputs.Problem(cfg=-1, B=B, H=H, N=6, dtype=P1.dtype, parent=bad,
+                         accepted=np.array([5, -1, 3, 4], dtype=np.int32), layers=P1.layers)
+    gpu = run_fused(P1b, P2, status_check=False)
+    assert gpu["status"] == binding.TREEWY_ETREE
+    assert np.array_equal(gpu["S"][2], P1.layers[0].S0[2])
