@@ -243,26 +243,53 @@ constexpr int kSmallThreads = 256;
 // s_waitcnt operand (gfx9 encoding): vmcnt = 2 (bits 3:0 and 15:14), expcnt and lgkmcnt
 // left at their maxima (no wait on them)
 constexpr int kWaitAllButTwoStores = 2 | (7 << 4) | (15 << 8);
+constexpr int kWaitAllButEight = 8 | (7 << 4) | (15 << 8);
 // dword 3 of a raw (unstrided, range-checked) buffer descriptor on gfx9-family parts
 constexpr int kRawBufferFlags = 0x00020000;
 constexpr int kSmallRows = 64;              // value rows per item
 constexpr int kSmallParts = D / kSmallRows; // items per head
 
-// LDS of one small-tree workgroup, in bytes.  Keys sit in rows 0 .. 4 ceil(N/4) - 1 of the
-// key/query area and queries right after them; 16-byte chunk c of row r is stored at chunk
-// c ^ (r % 16) (S0 rows: 32 chunks, key/query rows: 16), which keeps the operand reads free
-// of bank conflicts.
-template <int NCT>
-struct SmallLayout {
-    static constexpr int kS0 = 0;                                // [64][128] fp32
-    static constexpr int kKQ = kS0 + kSmallRows * D * 4;         // [16 NCT][128] bf16
-    static constexpr int kV = kKQ + 16 * NCT * D * 2;            // [8 NCT][64] bf16
-    static constexpr int kSm = kV + 8 * NCT * kSmallRows * 2;    // parent, alpha, beta [16] each
-    static constexpr int kG = kSm + 64 * 4;                      // G [16][16 NCT] fp32
-    static constexpr int kBytes = kG + 16 * 16 * NCT * 4;
-    // resident workgroups per CU within the 160 KB of LDS
-    static constexpr int kWgs = (160 * 1024) / kBytes > 4 ? 4 : (160 * 1024) / kBytes;
+// LDS of one small-tree workgroup, as byte offsets sized for the tree at hand (N nodes,
+// NCT column tiles), so that small trees leave room for more resident workgroups.  After the
+// S0 rows [64][128] fp32: keys in rows 0 .. 4 ceil(N/4) - 1 of the key/query area and queries
+// right after them (bf16 rows of 256 B); the item's half of the values (rows of 128 B);
+// parents, alphas, betas (words 0-15, 16-31, 32-47) and one more word (48); the Gram matrix
+// [16][16 NCT] fp32.  With the fused commit: `path` U_prev half-rows (256 B) and K_prev rows
+// (256 B), the path's gammas [64] and the previous tree's parents [64].  16-byte chunk c of a
+// row r of S0 or of the key/query area is stored at chunk c ^ (r % 16), which keeps the MFMA
+// operand reads free of bank conflicts.
+struct SmallLds {
+    uint32_t kq, v, sm, g, pu, pk, pg, idx, bytes;
+    int path;                                   // path rows staged per chunk (fused)
 };
+
+__host__ __device__ inline SmallLds small_lds(int N, int nct, bool fused) {
+    SmallLds L;
+    L.kq = kSmallRows * D * 4;
+    L.v = L.kq + 2048u * static_cast<uint32_t>((N + 3) / 4);
+    L.sm = L.v + 1024u * static_cast<uint32_t>((N + 7) / 8);
+    L.g = L.sm + 256u;
+    const uint32_t end = L.g + 1024u * static_cast<uint32_t>(nct);
+    L.path = N <= 4 ? 4 : 8;
+    L.pu = end;
+    L.pk = L.pu + 256u * L.path;
+    L.pg = L.pk + 256u * L.path;
+    L.idx = L.pg + 256u;
+    L.bytes = fused ? L.idx + 256u : end;
+    return L;
+}
+
+// Waves per SIMD the registers are budgeted for (= resident workgroups per CU): four for the
+// plain kernel on trees of up to 8 nodes; three where LDS allows no more (16 nodes) or the
+// fused commit needs the registers.
+template <int NCT, bool FUSED>
+constexpr int kSmallWavesPerSimd = (NCT == 2 || FUSED) ? 3 : 4;
+
+// resident workgroups per CU: the register budget, within the 160 KB of LDS
+inline int small_wgs(uint32_t bytes, int regs_wgs) {
+    const uint32_t w = (160u * 1024u) / bytes;
+    return w > static_cast<uint32_t>(regs_wgs) ? regs_wgs : static_cast<int>(w);
+}
 
 // Item number -> (head, half).  Slots s and s + 8 of every group of 16 run on one XCD and
 // take the two halves of one head; a grid that is not a multiple of 16 uses plain order.
@@ -385,14 +412,14 @@ __device__ __forceinline__ void small_issue_s0(const float* S0, float* buf, int 
 // The rest of an item's inputs -> LDS, as a list of whole-wave transfers dealt round-robin
 // to the four waves: ceil(N/4) loads of four key rows, as many of four query rows,
 // ceil(N/8) loads of eight value half-rows, and one gather of parent, alpha and beta (lanes
-// 0-15, 16-31, 32-47).  Lanes past the last node load node 0 again, into rows nobody reads.
-template <int NCT>
+// 0-15, 16-31, 32-47) plus the word at `extra` (lanes 48-63; their own parent again when it
+// is null).  Lanes past the last node load node 0 again, into rows nobody reads.
 __device__ __forceinline__ void small_issue_inputs(const uint16_t* Q, const uint16_t* K,
                                                    const uint16_t* V, const float* alpha,
                                                    const float* beta, const int32_t* parent,
                                                    int H, int N, int bh, int part, int wave,
-                                                   int lane, uint32_t lds) {
-    using Lo = SmallLayout<NCT>;
+                                                   int lane, uint32_t lds, const SmallLds& L,
+                                                   const int32_t* extra) {
     const int b = bh / H;
     const int h = bh - b * H;
     const size_t node0 = static_cast<size_t>(b) * N;
@@ -412,20 +439,21 @@ __device__ __forceinline__ void small_issue_inputs(const uint16_t* Q, const uint
             const uint32_t n = 4u * (is_q ? j - nq4 : j) + lr;        // node
             const uint32_t c = (static_cast<uint32_t>(lane) & 15u) ^ (r & 15u);
             dma_x4(is_q ? Qh : Kh, (n < un ? n : 0u) * row_bytes + 16u * c,
-                   lds + Lo::kKQ + 1024u * j);
+                   lds + L.kq + 1024u * j);
         } else if (j < 2 * nq4 + nv8) {
             const int jv = j - 2 * nq4;
             const uint32_t n = 8u * jv + (static_cast<uint32_t>(lane) >> 3);
             const uint32_t c = static_cast<uint32_t>(lane) & 7u;
-            dma_x4(Vh, (n < un ? n : 0u) * row_bytes + 16u * c, lds + Lo::kV + 1024u * jv);
+            dma_x4(Vh, (n < un ? n : 0u) * row_bytes + 16u * c, lds + L.v + 1024u * jv);
         } else {
             const uint32_t t = static_cast<uint32_t>(lane) & 15u;
             const uint32_t kind = static_cast<uint32_t>(lane) >> 4;
             const size_t n = node0 + (t < un ? t : 0u);
             const void* src = kind == 1 ? static_cast<const void*>(alpha + n * H + h)
                             : kind == 2 ? static_cast<const void*>(beta + n * H + h)
-                                        : static_cast<const void*>(parent + n);
-            dma_gather_x1(src, lds + Lo::kSm);
+                            : kind == 3 && extra ? static_cast<const void*>(extra)
+                                                 : static_cast<const void*>(parent + n);
+            dma_gather_x1(src, lds + L.sm);
         }
     }
 }
@@ -443,14 +471,13 @@ __device__ __forceinline__ void small_issue_inputs(const uint16_t* Q, const uint
 //
 // The path's rows (U_prev half-rows, K_prev rows, gammas) must be in flight with the item's
 // other transfers, so the path has to be known one item early; it comes from the previous
-// tree and accepted node of the item's sequence, which are fetched two items early into one
-// of two LDS index slots.  At the top of item i the workgroup derives the path of item i + 1
-// (pointer jumping over the previous tree, lane = node); at the refill point of item i the
-// first kPath rows of that path go out together with item i + 1's S rows, and the index of
-// item i + 2 is fetched.  A path longer than kPath (depth > 8; no shape here reaches it
-// except deep chains) is finished in further chunks with a blocking wait.
-
-constexpr int kPath = 8;                    // path rows staged with an item
+// tree and accepted node of the item's sequence, which are fetched two items early (the
+// parents into an LDS index slot, the accepted node as the spare word of the input gather).
+// At the top of item i the workgroup derives the path of item i + 1 (pointer jumping over
+// the previous tree, lane = node); at the refill point of item i the first rows of that path
+// (4 for trees of up to 4 nodes, else 8) go out together with item i + 1's S rows, and the
+// index of item i + 2 is fetched.  A longer path is finished in further chunks with a
+// blocking wait.
 
 struct CommitIn {
     float* S;                               // state, updated in place
@@ -462,18 +489,6 @@ struct CommitIn {
     int Np;                                 // its node count
 };
 
-// LDS of one fused workgroup: the small-tree layout, then the path rows and index slots.
-template <int NCT>
-struct FusedLayout {
-    using Base = SmallLayout<NCT>;
-    static constexpr int kPU = Base::kBytes;                     // [kPath][64] fp32
-    static constexpr int kPK = kPU + kPath * kSmallRows * 4;     // [kPath][128] bf16
-    static constexpr int kPG = kPK + kPath * D * 2;              // [64] fp32 path gammas
-    static constexpr int kIdx = kPG + 64 * 4;                    // 2 x {parents[64], accepted[64]}
-    static constexpr int kBytes = kIdx + 2 * 512;
-    static constexpr int kWgs = (160 * 1024) / kBytes > 4 ? 4 : (160 * 1024) / kBytes;
-};
-
 // One item's commit: the path of the accepted node as a mask, its length, and in lane q the
 // q-th path node in increasing order (root first).
 struct PathInfo {
@@ -482,23 +497,21 @@ struct PathInfo {
     int pn;
 };
 
-// Sequence b's previous tree and accepted node -> an LDS index slot (parents in words 0-63,
-// lanes past Np repeating node 0; accepted[b] in every word of 64-127).
+// Sequence b's previous tree -> the LDS index slot (lane n: parent of node n; lanes past Np
+// repeat node 0).
 __device__ __forceinline__ void fused_issue_index(const CommitIn& c, int b, int lane,
                                                   uint32_t slot) {
     const int n = lane < c.Np ? lane : 0;
     dma_gather_x1(c.parent + static_cast<size_t>(b) * c.Np + n, slot);
-    dma_gather_x1(c.accepted + b, slot + 256u);
 }
 
-// The path of the accepted node from an index slot, by every wave (lane = node of the previous
-// tree): pointer jumping gives each node its inclusive ancestor mask and whether a malformed
-// parent lies on its way up.  An accepted node outside [-1, Np - 1] or a malformed path leaves
-// nothing to commit and is reported when `reporter` is set.
-__device__ __forceinline__ PathInfo fused_path(const char* slot, int Np, int lane, bool reporter,
-                                               int32_t* status) {
-    const int a = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(slot + 256)[0]);
-    const int p_raw = lane < Np ? reinterpret_cast<const int*>(slot)[lane] : -1;
+// The path of accepted node `a`, by every wave (lane = node of the previous tree, p_raw = its
+// parent, -1 past Np): pointer jumping gives each node its inclusive ancestor mask and whether
+// a malformed parent lies on its way up.  An accepted node outside [-1, Np - 1] or a malformed
+// path leaves nothing to commit and is reported when `reporter` is set.
+__device__ __forceinline__ PathInfo fused_path(int p_raw, int a, int Np, int lane,
+                                               bool reporter, int32_t* status) {
+    a = __builtin_amdgcn_readfirstlane(a);
     const bool bad = lane < Np && (p_raw < -1 || p_raw >= lane);
     int j = bad ? -1 : p_raw;
     uint64_t am = lane < Np ? (1ull << lane) : 0ull;
@@ -539,16 +552,17 @@ __device__ __forceinline__ PathInfo fused_path(const char* slot, int Np, int lan
     return pi;
 }
 
-// Rows kPath c .. kPath c + kPath - 1 of an item's path -> LDS: U_prev half-rows (this item's
+// Path rows P c .. P c + P - 1 (P = L.path) of an item -> LDS: U_prev half-rows (this item's
 // 64 value rows) and K_prev rows, four per transfer, and with the first chunk the gammas of
 // the whole path (one gather).  Slots past the path repeat its first node.
 __device__ __forceinline__ void fused_issue_path(const CommitIn& c, const PathInfo& pi, int chunk,
                                                  int bh, int part, int H, int wave, int lane,
-                                                 uint32_t pu, uint32_t pk, uint32_t pg) {
+                                                 uint32_t lds, const SmallLds& L) {
     const int b = bh / H;
     const int h = bh - b * H;
     const size_t node0 = static_cast<size_t>(b) * c.Np;
-    const int cnt = pi.depth - kPath * chunk < kPath ? pi.depth - kPath * chunk : kPath;
+    const int P = L.path;
+    const int cnt = pi.depth - P * chunk < P ? pi.depth - P * chunk : P;
     const int nj = (cnt + 3) >> 2;
     const int jobs = 2 * nj + (chunk == 0 ? 1 : 0);
     const float* Uh = c.U + (node0 * H + h) * D + part * kSmallRows;
@@ -559,14 +573,14 @@ __device__ __forceinline__ void fused_issue_path(const CommitIn& c, const PathIn
             const bool is_k = j >= nj;
             const int jj = is_k ? j - nj : j;
             const int q = 4 * jj + (lane >> 4);
-            const uint32_t n = static_cast<uint32_t>(__shfl(pi.pn, kPath * chunk + (q < cnt ? q : 0)));
+            const uint32_t n = static_cast<uint32_t>(__shfl(pi.pn, P * chunk + (q < cnt ? q : 0)));
             if (is_k)
-                dma_x4(Kh, n * static_cast<uint32_t>(H) * (D * 2u) + col16, pk + 1024u * jj);
+                dma_x4(Kh, n * static_cast<uint32_t>(H) * (D * 2u) + col16, lds + L.pk + 1024u * jj);
             else
-                dma_x4(Uh, n * static_cast<uint32_t>(H) * (D * 4u) + col16, pu + 1024u * jj);
+                dma_x4(Uh, n * static_cast<uint32_t>(H) * (D * 4u) + col16, lds + L.pu + 1024u * jj);
         } else {
             const int n = __shfl(pi.pn, lane < pi.depth ? lane : 0);
-            dma_gather_x1(c.gamma + (node0 + n) * H + h, pg);
+            dma_gather_x1(c.gamma + (node0 + n) * H + h, lds + L.pg);
         }
     }
 }
@@ -577,7 +591,7 @@ __device__ __forceinline__ void fused_issue_path(const CommitIn& c, const PathIn
 
 template <int NCT, bool FUSED>
 __global__ __launch_bounds__(kSmallThreads)
-__attribute__((amdgpu_waves_per_eu(FUSED ? FusedLayout<NCT>::kWgs : SmallLayout<NCT>::kWgs)))
+__attribute__((amdgpu_waves_per_eu(kSmallWavesPerSimd<NCT, FUSED>)))
 void verify_small_kernel(
     const float* S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ alpha,
@@ -586,12 +600,11 @@ void verify_small_kernel(
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
     int32_t* __restrict__ status, CommitIn cin)
 {
-    using Lo = SmallLayout<NCT>;
-    using Fl = FusedLayout<NCT>;
     constexpr int kGP = 16 * NCT;                   // G row pitch
     extern __shared__ __align__(16) float lds[];
+    const SmallLds L = small_lds(N, NCT, FUSED);
     const char* ldsb = reinterpret_cast<const char*>(lds);
-    float* G = lds + Lo::kG / 4;                    // G[m][n] = k_m . (k|q)_n
+    float* G = lds + L.g / 4;                       // G[m][n] = k_m . (k|q)_n
     const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
     const int tid = threadIdx.x;
@@ -612,21 +625,31 @@ void verify_small_kernel(
 
     PathInfo cur{0ull, 0, 0};                       // this item's commit (FUSED)
     if constexpr (FUSED) {
-        // index of items 0 and 1, then the path of item 0 before its transfers go out
+        // item 0's previous tree and accepted node go out first, then its S rows; the path
+        // is derived while the rows stream in, then its own rows and item 0's other inputs
+        // (with item 1's accepted node and tree) follow
         int bh1, part1;
         small_item(1, slot, grid, bh1, part1);
-        fused_issue_index(cin, bh / H, lane, lds_addr + Fl::kIdx);
-        if (bh1 < BH) fused_issue_index(cin, bh1 / H, lane, lds_addr + Fl::kIdx + 512);
-        __builtin_amdgcn_s_waitcnt(0);
+        if (wave == 0) {
+            fused_issue_index(cin, bh / H, lane, lds_addr + L.idx);
+            dma_gather_x1(cin.accepted + bh / H, lds_addr + L.sm);
+        }
+        small_issue_s0(S0, lds, bh, part, wave, lane);
+        __builtin_amdgcn_s_waitcnt(kWaitAllButEight);   // the two gathers (the eight row loads go on)
         lds_barrier();
-        cur = fused_path(ldsb + Fl::kIdx, cin.Np, lane, wave == 0 && bh % H == 0 && part == 0,
-                         status);
-        if (cur.depth > 0)
-            fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr + Fl::kPU,
-                             lds_addr + Fl::kPK, lds_addr + Fl::kPG);
+        cur = fused_path(lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L.idx)[lane] : -1,
+                         reinterpret_cast<const int*>(ldsb + L.sm)[48], cin.Np, lane,
+                         wave == 0 && bh % H == 0 && part == 0, status);
+        lds_barrier();                              // index read by every wave: refill
+        if (cur.depth > 0) fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr, L);
+        small_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, L,
+                           bh1 < BH ? cin.accepted + bh1 / H : nullptr);
+        if (bh1 < BH && wave == 3) fused_issue_index(cin, bh1 / H, lane, lds_addr + L.idx);
+    } else {
+        small_issue_s0(S0, lds, bh, part, wave, lane);
+        small_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, L,
+                           nullptr);
     }
-    small_issue_s0(S0, lds, bh, part, wave, lane);
-    small_issue_inputs<NCT>(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr);
     __builtin_amdgcn_s_waitcnt(0);                  // the first item: nothing else in flight
 
     for (int round = 0;; ) {
@@ -644,31 +667,85 @@ void verify_small_kernel(
         int bh_n, part_n;
         small_item(round + 1, slot, grid, bh_n, part_n);
         const bool more = bh_n < BH;
-        PathInfo nxt{0ull, 0, 0};
+
         if constexpr (FUSED) {
-            if (more)
-                nxt = fused_path(ldsb + Fl::kIdx + 512 * ((round + 1) & 1), cin.Np, lane,
-                                 wave == 0 && bh_n % H == 0 && part_n == 0, status);
+            if (cur.depth > 0) {
+                // S_a = g_a S + sum over the path of (g_a / g_i) U_prev[i] k_i^T, applied to this
+                // wave's 16 rows where they sit in LDS, in the layout they arrived in (lane l:
+                // row 16w + 2i + l / 32, 16-byte chunk l % 32, for i = 0..7), and written back
+                // to HBM from there: every store is two whole 512-byte rows.  The path's gammas
+                // are in LDS in path order (a is last).
+                const float* PG = reinterpret_cast<const float*>(ldsb + L.pg);
+                const float* PU = reinterpret_cast<const float*>(ldsb + L.pu);
+                const char* PK = ldsb + L.pk;
+                const float ga = PG[cur.depth - 1];
+                const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+                const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
+                for (int q0 = 0; q0 < cur.depth; q0 += L.path) {
+                    if (q0 > 0) {
+                        // a path longer than one chunk: the next chunk, with a blocking wait
+                        lds_barrier();
+                        fused_issue_path(cin, cur, q0 / L.path, bh, part, H, wave, lane, lds_addr, L);
+                        __builtin_amdgcn_s_waitcnt(0);
+                        lds_barrier();
+                    }
+                    const int cnt = cur.depth - q0 < L.path ? cur.depth - q0 : L.path;
+                    f32x4_t x[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t r = 16u * wave + 2u * i + hl;
+                        x[i] = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
+                        if (q0 == 0) x[i] *= ga;
+                    }
+                    for (int q = 0; q < cnt; ++q) {
+                        const float cq = ga / PG[q0 + q];
+                        const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
+                        const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
+                                            __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const float cu = cq * PU[q * kSmallRows + 16 * wave + 2 * i + hl];
+                            x[i] += cu * kv;
+                        }
+                    }
+                    const bool last = q0 + L.path >= cur.depth;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t r = 16u * wave + 2u * i + hl;
+                        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
+                        if (last)
+                            *reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D +
+                                                                 part * kSmallRows + r) * D + 4 * ch) = x[i];
+                    }
+                }
+            }
         }
 
         // ---- this item's operands out of LDS
-        const int my_par = node_ok ? reinterpret_cast<const int*>(ldsb + Lo::kSm)[t] : -1;
-        const float my_alpha = node_ok ? reinterpret_cast<const float*>(ldsb + Lo::kSm)[16 + t] : 1.0f;
-        const float my_beta = node_ok ? reinterpret_cast<const float*>(ldsb + Lo::kSm)[32 + t] : 0.0f;
+        const int my_par = node_ok ? reinterpret_cast<const int*>(ldsb + L.sm)[t] : -1;
+        const float my_alpha = node_ok ? reinterpret_cast<const float*>(ldsb + L.sm)[16 + t] : 1.0f;
+        const float my_beta = node_ok ? reinterpret_cast<const float*>(ldsb + L.sm)[32 + t] : 0.0f;
         uint2 vraw = make_uint2(0u, 0u);
-        if (node_ok) vraw = *reinterpret_cast<const uint2*>(ldsb + Lo::kV + t * 128 + 32 * wave + 8 * grp);
+        if (node_ok) vraw = *reinterpret_cast<const uint2*>(ldsb + L.v + t * 128 + 32 * wave + 8 * grp);
         bf16x8_t bfr[NCT][4];
 #pragma unroll
         for (int c = 0; c < NCT; ++c) {
             const int n = 16 * c + col;
             const int r = n < N ? n : (n < 2 * N ? 4 * nq4 + n - N : -1);
-            const char* rowp = ldsb + Lo::kKQ + 256 * (r < 0 ? 0 : r);
+            const char* rowp = ldsb + L.kq + 256 * (r < 0 ? 0 : r);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 u32x4_t w = {0u, 0u, 0u, 0u};
                 if (r >= 0) w = *reinterpret_cast<const u32x4_t*>(rowp + 16 * ((4 * ks + grp) ^ (r & 15)));
                 bfr[c][ks] = __builtin_bit_cast(bf16x8_t, w);
             }
+        }
+        PathInfo nxt{0ull, 0, 0};
+        if constexpr (FUSED) {
+            if (more)
+                nxt = fused_path(lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L.idx)[lane] : -1,
+                                 reinterpret_cast<const int*>(ldsb + L.sm)[48], cin.Np, lane,
+                                 wave == 0 && bh_n % H == 0 && part_n == 0, status);
         }
 
         // ---- tree walk, in every 16-lane group (lane = node t): pointer jumping as in
@@ -720,83 +797,36 @@ void verify_small_kernel(
             }
         }
 
-        // ---- this wave's 16 rows of S0: lane L holds row 16w + L % 16, values
-        //      32 ks + 8 (L / 16) .. +7 for ks = 0..3 (the MFMA A-operand layout)
-        f32x4_t sv[4][2];
+        // ---- MFMA operands of this wave's 16 rows (committed, with FUSED), split into bf16
+        //      hi and lo: lane L takes row 16w + L % 16, values 32 ks + 8 (L / 16) .. +7
+        bf16x8_t ahi[4], alo[4];
         {
             const int r = 16 * wave + col;
             const float* rowp = lds + r * D;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int c0 = 2 * grp + 8 * ks;
-                sv[ks][0] = *reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15)));
-                sv[ks][1] = *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15)));
+                split_hi_lo(*reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15))),
+                            *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15))),
+                            ahi[ks], alo[ks]);
             }
         }
-        if constexpr (FUSED) {
-            if (cur.depth > 0) {
-                // S_a = g_a S + sum over the path of (g_a / g_i) U_prev[i] k_i^T, on this
-                // lane's 32 values; the path's gammas are in LDS in path order (a is last)
-                const float* PG = reinterpret_cast<const float*>(ldsb + Fl::kPG);
-                const float* PU = reinterpret_cast<const float*>(ldsb + Fl::kPU);
-                const char* PK = ldsb + Fl::kPK;
-                const int r = 16 * wave + col;
-                const float ga = PG[cur.depth - 1];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) { sv[ks][0] *= ga; sv[ks][1] *= ga; }
-                for (int q0 = 0; q0 < cur.depth; q0 += kPath) {
-                    if (q0 > 0) {
-                        // a path deeper than kPath: the next chunk, with a blocking wait
-                        lds_barrier();
-                        fused_issue_path(cin, cur, q0 / kPath, bh, part, H, wave, lane,
-                                         lds_addr + Fl::kPU, lds_addr + Fl::kPK,
-                                         lds_addr + Fl::kPG);
-                        __builtin_amdgcn_s_waitcnt(0);
-                        lds_barrier();
-                    }
-                    const int cnt = cur.depth - q0 < kPath ? cur.depth - q0 : kPath;
-                    for (int q = 0; q < cnt; ++q) {
-                        const float cu = (ga / PG[q0 + q]) * PU[q * kSmallRows + r];
-#pragma unroll
-                        for (int ks = 0; ks < 4; ++ks) {
-                            const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(PK + q * 256 + 64 * ks + 16 * grp);
-#pragma unroll
-                            for (int e = 0; e < 2; ++e) {
-                                sv[ks][0][2 * e] += cu * __uint_as_float(kw[e] << 16);
-                                sv[ks][0][2 * e + 1] += cu * __uint_as_float(kw[e] & 0xffff0000u);
-                                sv[ks][1][2 * e] += cu * __uint_as_float(kw[2 + e] << 16);
-                                sv[ks][1][2 * e + 1] += cu * __uint_as_float(kw[2 + e] & 0xffff0000u);
-                            }
-                        }
-                    }
-                }
-                // the committed rows back to HBM: per ks a wave writes 16 rows x 128 bytes
-                float* Srow = cin.S + (static_cast<size_t>(bh) * D + part * kSmallRows + r) * D + 8 * grp;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    *reinterpret_cast<f32x4_t*>(Srow + 32 * ks) = sv[ks][0];
-                    *reinterpret_cast<f32x4_t*>(Srow + 32 * ks + 4) = sv[ks][1];
-                }
-            }
-        }
-        // ---- MFMA operands of this wave's 16 rows, split into bf16 hi and lo
-        bf16x8_t ahi[4], alo[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) split_hi_lo(sv[ks][0], sv[ks][1], ahi[ks], alo[ks]);
         lds_barrier();                              // operands read and G visible: refill
         ++round;
         if (more) {
             small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
-            small_issue_inputs<NCT>(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
-                                    lds_addr);
             if constexpr (FUSED) {
-                if (nxt.depth > 0)
-                    fused_issue_path(cin, nxt, 0, bh_n, part_n, H, wave, lane, lds_addr + Fl::kPU,
-                                     lds_addr + Fl::kPK, lds_addr + Fl::kPG);
+                // item i + 1's inputs and path rows; item i + 2's accepted node and tree
                 int bh_2, part_2;
                 small_item(round + 1, slot, grid, bh_2, part_2);
-                if (bh_2 < BH)
-                    fused_issue_index(cin, bh_2 / H, lane, lds_addr + Fl::kIdx + 512 * ((round + 1) & 1));
+                small_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
+                                   lds_addr, L, bh_2 < BH ? cin.accepted + bh_2 / H : nullptr);
+                if (nxt.depth > 0)
+                    fused_issue_path(cin, nxt, 0, bh_n, part_n, H, wave, lane, lds_addr, L);
+                if (bh_2 < BH && wave == 3) fused_issue_index(cin, bh_2 / H, lane, lds_addr + L.idx);
+            } else {
+                small_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
+                                   lds_addr, L, nullptr);
             }
         }
 
@@ -1207,8 +1237,9 @@ int device_cu_count() {
 
 template <int NCT, bool FUSED>
 static hipError_t launch_small(const VerifyArgs& a, const CommitIn& cin, hipStream_t stream) {
-    const int bytes = FUSED ? FusedLayout<NCT>::kBytes : SmallLayout<NCT>::kBytes;
-    const int wgs = FUSED ? FusedLayout<NCT>::kWgs : SmallLayout<NCT>::kWgs;
+    const SmallLds L = small_lds(a.N, NCT, FUSED);
+    const int bytes = static_cast<int>(L.bytes);
+    const int wgs = small_wgs(L.bytes, kSmallWavesPerSimd<NCT, FUSED>);
     auto kern = verify_small_kernel<NCT, FUSED>;
     const int BH = a.B * a.H;
     const int items = BH * kSmallParts;
