@@ -1,15 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the TreeWY hot path on one MI355X: tree verify + commit.
 
-A step is one pass of the whole path over one batch: treewy_verify for every layer, then
-treewy_commit for every layer, on inputs already resident in HBM.  Steps cycle through a
-pool of independently drawn instances whose total footprint exceeds the 256 MB Infinity
-Cache, so the state stream is served from HBM rather than from the cache.
+A step is one pass of the whole path over one batch, on inputs already resident in HBM.
+By default it is the steady state of decoding: one treewy_commit_verify launch per layer,
+which commits the previous step's accepted node into the state and verifies this step's
+draft tree against it (the state is read and written once).  ``--separate`` times the same
+work as treewy_verify for every layer then treewy_commit for every layer; the default run
+also times that beside the fused step and reports it under ``separate_calls``.
+``--snapshot`` times the store-all comparison scheme instead.
+
+Steps cycle through a pool of independently drawn instances whose total footprint exceeds
+the 256 MB Infinity Cache, so the state stream is served from HBM rather than from the
+cache.  Every instance's "previous step" is its own last one (same tree and accepted node).
 
 Prints one JSON line: throughput in draft-nodes*heads per second, the roofline of the
 dominant kernel (algorithmic bytes per launch over its mean launch time, timed with HIP
-events on the launch stream inside the timed region), and the CPU oracle's rate on a
-bounded sample of the same workload as a reported baseline.
+events on the launch stream in a second pass of the same steps), and the CPU oracle's rate
+on a bounded sample of the same workload as a reported baseline.
 """
 
 from __future__ import annotations
@@ -48,13 +55,13 @@ def parse():
                     help="minimum device footprint of the rotating instance pool")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--separate", action="store_true",
+                    help="time treewy_verify then treewy_commit (two launches per layer)")
     ap.add_argument("--snapshot", action="store_true",
                     help="time the store-all comparison path instead of TreeWY")
-    ap.add_argument("--fused", action="store_true",
-                    help="steady-state steps of treewy_commit_verify: each launch commits the "
-                         "previous step's accepted node and verifies this step's drafts")
     ap.add_argument("--graph", action="store_true",
-                    help="replay each instance's step as a captured HIP graph")
+                    help="replay each instance's step as a captured HIP graph (--separate or "
+                         "--snapshot; the fused step alternates its per-step buffers)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a kernel of "
                          "known traffic, used to scale HBM byte counters taken with rocprofv3)")
@@ -68,6 +75,9 @@ def main():
               "every (sequence, head) is independent, so N GPUs would each run this same "
               "single-GPU pass on their share.", file=sys.stderr)
         sys.exit(2)
+    assert not (args.separate and args.snapshot), "--separate and --snapshot are exclusive"
+    mode = "snapshot" if args.snapshot else "separate" if args.separate else "fused"
+    assert not (args.graph and mode == "fused"), "--graph needs --separate or --snapshot"
 
     import torch
     from linear_attention_speculative_head_amd import accounting, binding, device, inputs
@@ -80,14 +90,15 @@ def main():
 
     # ---- rotating pool of instances (each: all layers of the workload)
     per_layer = (B * H * 128 * 128 * 4 + 3 * B * N * H * 128 * elem + 2 * B * N * H * 128 * 4
-                 + (B * H * N * 128 * 128 * 4 if args.snapshot else 0))
-    assert not (args.fused and args.snapshot), "--fused and --snapshot are exclusive"
+                 + (B * H * N * 128 * 128 * 4 if mode == "snapshot" else 0)
+                 + (2 * B * N * H * 128 * 4 if mode == "fused" else 0))
     n_inst = max(1, math.ceil(args.pool_gib * 2 ** 30 / (per_layer * nl))) if args.config else 1
     n_inst = min(n_inst, 32)
-    log(f"[bench] config {args.config}: {cfg['desc']}; {n_inst} instance(s) of {nl} layer(s), "
-        f"{per_layer * nl * n_inst / 2 ** 30:.2f} GiB on device")
+    log(f"[bench] config {args.config}: {cfg['desc']}; {mode} path; {n_inst} instance(s) of "
+        f"{nl} layer(s), {per_layer * nl * n_inst / 2 ** 30:.2f} GiB on device")
     t0 = time.time()
     pool = []
+    first = None
     for i in range(n_inst):
         P = inputs.make_problem(args.config, instance=i)
         parent, accepted = device.upload_tree(P)
@@ -95,37 +106,35 @@ def main():
         for L in P.layers:
             dl = device.upload_layer(L, dtype)
             out = device.alloc_outputs(B, H, N)
-            snap = (torch.empty((B, H, N, 128, 128), device="cuda") if args.snapshot else None)
-            if args.fused:                      # second set of per-step outputs, alternated
-                snap = device.alloc_outputs(B, H, N)
-            layers.append((dl, out, snap))
-        pool.append(dict(P=P, parent=parent, accepted=accepted, layers=layers, flip=0))
+            extra = None
+            if mode == "snapshot":
+                extra = torch.empty((B, H, N, 128, 128), device="cuda")
+            elif mode == "fused":                # second set of per-step outputs, alternated
+                extra = device.alloc_outputs(B, H, N)
+            layers.append((dl, out, extra))
+        nbytes = {
+            "fused": accounting.fused_step_bytes(P.parent, P.accepted, P.parent, H, elem,
+                                                 layers=nl),
+            "separate": accounting.step_bytes(P.parent, P.accepted, H, N, elem, layers=nl),
+            "snapshot": accounting.snapshot_step_bytes(P.parent, P.accepted, H, N, elem,
+                                                       layers=nl),
+        }
+        pool.append(dict(parent=parent, accepted=accepted, layers=layers, flip=0, bytes=nbytes))
         if i == 0:
             first = P
-        else:
-            del P
     torch.cuda.synchronize()
     log(f"[bench] inputs drawn and uploaded in {time.time() - t0:.1f} s")
 
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    if args.fused:
-        inst_bytes = [accounting.fused_step_bytes(x["P"].parent, x["P"].accepted, x["P"].parent,
-                                                  H, elem, layers=nl) for x in pool]
+    if mode == "fused":
         # the previous step of every instance: a plain verify, so that its U and gamma exist
         for x in pool:
             for dl, out, _ in x["layers"]:
                 binding.treewy_verify(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta, x["parent"],
                                       out.O, out.U, out.gamma, status=status)
         torch.cuda.synchronize()
-    else:
-        bytes_fn = accounting.snapshot_step_bytes if args.snapshot else accounting.step_bytes
-        inst_bytes = [bytes_fn(x["P"].parent, x["P"].accepted, H, N, elem, layers=nl)
-                      for x in pool]
-    for x in pool:
-        x["P"] = None
 
     def fused_step(x, ev=None):
-        # this instance's previous step is its own last one (same tree and accepted node)
         for j, (dl, o0, o1) in enumerate(x["layers"]):
             prev, cur = (o0, o1) if x["flip"] == 0 else (o1, o0)
             if ev is not None:
@@ -137,108 +146,119 @@ def main():
                 ev[1][j].record()
         x["flip"] ^= 1
 
-    def step(inst, ev=None):
-        x = pool[inst]
-        if args.fused:
-            fused_step(x, ev)
-            return
-        for j, (dl, out, snap) in enumerate(x["layers"]):
+    def two_call_step(x, ev=None, snapshot=False):
+        # verify for every layer, then commit for every layer
+        for j, (dl, out, extra) in enumerate(x["layers"]):
             if ev is not None:
                 ev[0][j].record()
-            if args.snapshot:
+            if snapshot:
                 binding.treewy_verify_snapshot(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta,
-                                               x["parent"], out.O, snap, status)
+                                               x["parent"], out.O, extra, status)
             else:
                 binding.treewy_verify(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta, x["parent"],
                                       out.O, out.U, out.gamma, status=status)
             if ev is not None:
                 ev[1][j].record()
-        for j, (dl, out, snap) in enumerate(x["layers"]):
+        for j, (dl, out, extra) in enumerate(x["layers"]):
             if ev is not None:
                 ev[2][j].record()
-            if args.snapshot:
-                binding.treewy_commit_snapshot(dl.S0, snap, x["accepted"], status)
+            if snapshot:
+                binding.treewy_commit_snapshot(dl.S0, extra, x["accepted"], status)
             else:
                 binding.treewy_commit(dl.S0, out.U, dl.K, out.gamma, x["parent"], x["accepted"],
                                       status)
             if ev is not None:
                 ev[3][j].record()
 
+    def step_fn(m):
+        if m == "fused":
+            return fused_step
+        return lambda x, ev=None: two_call_step(x, ev, snapshot=(m == "snapshot"))
+
+    K = args.steps
+
+    def measure(m, graphs=None):
+        """Warm-up, then exactly K timed steps with nothing else on the stream, then the same
+        K steps again with HIP events around every launch (kernel durations)."""
+        fn = step_fn(m)
+
+        def run(i, ev=None):
+            if graphs is not None and ev is None:
+                graphs[i].replay()
+            else:
+                fn(pool[i], ev)
+
+        for s in range(args.warmup):
+            run(s % n_inst)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, f"device status {int(status.item())}"
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for s in range(K):
+            run((args.warmup + s) % n_inst)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        assert int(status.item()) == 0, f"device status {int(status.item())}"
+        nev = 2 if m == "fused" else 4
+        events = [[[torch.cuda.Event(enable_timing=True) for _ in range(nl)] for _ in range(nev)]
+                  for _ in range(K)]
+        torch.cuda.synchronize()
+        for s in range(K):
+            run((args.warmup + s) % n_inst, events[s])
+        torch.cuda.synchronize()
+        names = (["treewy_commit_verify"] if m == "fused" else
+                 ["treewy_verify_snapshot", "treewy_commit_snapshot"] if m == "snapshot" else
+                 ["treewy_verify", "treewy_commit"])
+        keys = ["fused"] if m == "fused" else ["verify", "commit"]
+        used = [(args.warmup + s) % n_inst for s in range(K)]
+        kern = {}
+        for k, (name, key) in enumerate(zip(names, keys)):
+            ms = np.array([[events[s][2 * k][j].elapsed_time(events[s][2 * k + 1][j])
+                            for j in range(nl)] for s in range(K)])
+            nbytes = np.mean([pool[i]["bytes"][m][key] for i in used]) / nl   # per launch
+            kern[name] = (nbytes, ms.mean())
+        step_bytes = np.mean([pool[i]["bytes"][m]["total"] for i in used])
+        return wall, kern, step_bytes
+
     graphs = None
-    assert not (args.graph and args.fused), "--graph replays fixed buffers; --fused alternates them"
     if args.graph:
         # one graph per instance: verify for every layer, then commit for every layer
         graphs = []
+        fn = step_fn(mode)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for i in range(n_inst):           # warm the launch path outside capture
-                step(i)
+                fn(pool[i])
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         for i in range(n_inst):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(i)
+                fn(pool[i])
             graphs.append(g)
         torch.cuda.synchronize()
 
-    def run(i, ev=None):
-        if graphs is not None and ev is None:
-            graphs[i].replay()
-        else:
-            step(i, ev)
-
-    for s in range(args.warmup):
-        run(s % n_inst)
-    torch.cuda.synchronize()
-    assert int(status.item()) == 0, f"device status {int(status.item())}"
-
-    # ---- timed region: exactly K steps, nothing else on the stream
-    K = args.steps
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(K):
-        run((args.warmup + s) % n_inst)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    assert int(status.item()) == 0, f"device status {int(status.item())}"
-
-    # ---- kernel timing: the same K steps again, each launch between two HIP events on
-    #      the stream it is launched on (the events add gaps, so this pass is not `value`)
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(nl)] for _ in range(4)]
-              for _ in range(K)]
-    torch.cuda.synchronize()
-    for s in range(K):
-        run((args.warmup + s) % n_inst, events[s])
-    torch.cuda.synchronize()
-    ver_ms = np.array([[events[s][0][j].elapsed_time(events[s][1][j]) for j in range(nl)]
-                       for s in range(K)])
-    com_ms = (np.zeros_like(ver_ms) if args.fused else
-              np.array([[events[s][2][j].elapsed_time(events[s][3][j]) for j in range(nl)]
-                        for s in range(K)]))
-    used = [(args.warmup + s) % n_inst for s in range(K)]
-    step_bytes = np.mean([inst_bytes[i]["total"] for i in used])
-    if args.fused:
-        v_bytes, c_bytes = step_bytes / nl, 0.0
-    else:
-        v_bytes = np.mean([inst_bytes[i]["verify"] for i in used]) / nl   # per launch
-        c_bytes = np.mean([inst_bytes[i]["commit"] for i in used]) / nl
-
+    wall, kern, step_bytes = measure(mode, graphs)
     ms_step = wall * 1e3 / K
     nodes_heads = B * H * N * nl
     value = nodes_heads * K / wall
-    kern = {"verify": (v_bytes, ver_ms.mean()), "commit": (c_bytes, com_ms.mean())}
-    dom = max(kern, key=lambda k: kern[k][1] * 1.0)
+    dom = max(kern, key=lambda k: kern[k][1])
     d_bytes, d_ms = kern[dom]
     achieved = d_bytes / (d_ms * 1e-3) / 1e9
-    name_v = ("treewy_verify_snapshot" if args.snapshot else
-              "treewy_commit_verify" if args.fused else "treewy_verify")
-    name_c = "treewy_commit_snapshot" if args.snapshot else "treewy_commit"
-    log(f"[bench] {ms_step * 1e3:.1f} us/step; verify {ver_ms.mean() * 1e3:.1f} us "
-        f"({v_bytes / (ver_ms.mean() * 1e-3) / 1e9:.0f} GB/s), commit {com_ms.mean() * 1e3:.1f} us "
-        f"({c_bytes / max(com_ms.mean(), 1e-9) / 1e6:.0f} GB/s); "
-        f"step {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s algorithmic")
+    log(f"[bench] {mode}: {ms_step * 1e3:.1f} us/step; " + ", ".join(
+        f"{n} {t * 1e3:.1f} us ({b / (t * 1e-3) / 1e9:.0f} GB/s)" for n, (b, t) in kern.items())
+        + f"; step {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s algorithmic")
+
+    separate = None
+    if mode == "fused":
+        # the same work as two launches per layer, for comparison
+        w2, k2, b2 = measure("separate")
+        separate = {"ms_per_step": w2 * 1e3 / K, "value": nodes_heads * K / w2,
+                    "hbm_frac_step": b2 / (w2 / K) / 1e9 / HBM_PEAK_GBS,
+                    "kernels_us": {n: t * 1e3 for n, (b, t) in k2.items()}}
+        log(f"[bench] separate calls: {w2 * 1e6 / K:.1f} us/step; " + ", ".join(
+            f"{n} {t * 1e3:.1f} us" for n, (b, t) in k2.items()))
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * 2 ** 20 // 4
@@ -253,6 +273,9 @@ def main():
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(first, args.cpu_seconds)
 
+    desc = {"fused": "; steady state: previous step's commit fused into this step's verify",
+            "separate": "; verify then commit, two launches per layer",
+            "snapshot": "; store-all snapshot path"}[mode]
     line = {
         "metric": "tree verify+commit draft-nodes*heads/sec",
         "value": value,
@@ -266,21 +289,19 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; Qwen3.5-shaped GDN heads, dk=dv=128)",
-        "config": {"workload": f"config {args.config}: {cfg['desc']}"
-                   + ("; store-all snapshot path" if args.snapshot else "")
-                   + ("; previous commit fused into verify" if args.fused else ""),
+        "config": {"workload": f"config {args.config}: {cfg['desc']}" + desc,
                    "B": B, "H": H, "N": N, "layers": nl, "qkv_dtype": dtype,
                    "state_dtype": "f32", "instances_rotated": n_inst,
                    "launch": "hip-graph" if args.graph else "stream"},
         "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "kernel": name_v if dom == "verify" else name_c,
+        "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (None if args.snapshot or args.fused else
-                                 measured_traffic(args.config, name_v if dom == "verify" else name_c)),
+                     "traffic": (None if mode == "snapshot" else
+                                 measured_traffic(args.config, dom)),
                      "bytes_per_launch": d_bytes, "launch_us": d_ms * 1e3},
-        "kernels_us": ({name_v: ver_ms.mean() * 1e3} if args.fused else
-                       {name_v: ver_ms.mean() * 1e3, name_c: com_ms.mean() * 1e3}),
+        "kernels_us": {n: t * 1e3 for n, (b, t) in kern.items()},
+        "separate_calls": separate,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
