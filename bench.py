@@ -51,6 +51,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1)")
+    ap.add_argument("--tree", type=str, default=None,
+                    help="instead of a config: every sequence drafts the full tree W1,W2,W3 "
+                         "(B x H of config 1, accepted node uniform)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="every full-tree shape of the paper's Tables 2 and 4 (N = 3..39) in "
+                         "turn; one JSON line per shape")
     ap.add_argument("--pool-gib", type=float, default=1.25,
                     help="minimum device footprint of the rotating instance pool")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -68,6 +74,32 @@ def parse():
     return ap.parse_args()
 
 
+class Workload:
+    """What a run measures: sizes, a description and a seeded draw per instance."""
+
+    def __init__(self, args):
+        from linear_attention_speculative_head_amd import inputs
+        if args.tree is not None:
+            widths = tuple(int(w) for w in args.tree.split(","))
+            c1 = inputs.CONFIGS[1]
+            self.B, self.H, self.nl, self.dtype = c1["B"], c1["H"], 1, "bf16"
+            self.N = len(inputs.full_tree(widths))
+            self.name = f"tree {','.join(map(str, widths))}"
+            self.desc = (f"B{self.B} x H{self.H}, full tree {widths} (N={self.N}), bf16 q/k/v, "
+                         f"accepted uniform")
+            self.draw = lambda i: inputs.make_tree_shape(widths, instance=i, B=self.B, H=self.H)
+            self.rotate = True
+            self.traffic_key = None
+        else:
+            c = inputs.CONFIGS[args.config]
+            self.B, self.H, self.N, self.nl, self.dtype = c["B"], c["H"], c["N"], c["layers"], c["dtype"]
+            self.name = f"config {args.config}"
+            self.desc = c["desc"]
+            self.draw = lambda i: inputs.make_problem(args.config, instance=i)
+            self.rotate = args.config != 0
+            self.traffic_key = args.config
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -80,27 +112,51 @@ def main():
     assert not (args.graph and mode == "fused"), "--graph needs --separate or --snapshot"
 
     import torch
-    from linear_attention_speculative_head_amd import accounting, binding, device, inputs
+    from linear_attention_speculative_head_amd import binding, inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.lib()
-    cfg = inputs.CONFIGS[args.config]
-    B, H, N, nl, dtype = cfg["B"], cfg["H"], cfg["N"], cfg["layers"], cfg["dtype"]
+    if args.sweep:
+        rows = []
+        for w in inputs.PAPER_TREE_SHAPES:
+            args.tree = ",".join(map(str, w))
+            line = run(args, mode, Workload(args))
+            print(json.dumps(line), flush=True)
+            rows.append((w, line))
+        log("[bench] sweep: shape, N, fused us/step, separate us/step (verify + commit us), "
+            "fused GB/s")
+        for w, l in rows:
+            sep = l["separate_calls"] or {}
+            k = sep.get("kernels_us", {})
+            log(f"[bench]   {w} N={l['config']['N']:2d}: {l['ms_per_step'] * 1e3:7.1f} "
+                f"{sep.get('ms_per_step', float('nan')) * 1e3:7.1f} "
+                f"({k.get('treewy_verify', float('nan')):.1f} + {k.get('treewy_commit', float('nan')):.1f}) "
+                f"{l['roofline']['achieved']:.0f}")
+        return
+    print(json.dumps(run(args, mode, Workload(args))), flush=True)
+
+
+def run(args, mode, wl):
+    """Measure one workload; returns the JSON line as a dict."""
+    import torch
+    from linear_attention_speculative_head_amd import accounting, binding, device
+
+    B, H, N, nl, dtype = wl.B, wl.H, wl.N, wl.nl, wl.dtype
     elem = 2 if dtype == "bf16" else 4
 
     # ---- rotating pool of instances (each: all layers of the workload)
     per_layer = (B * H * 128 * 128 * 4 + 3 * B * N * H * 128 * elem + 2 * B * N * H * 128 * 4
                  + (B * H * N * 128 * 128 * 4 if mode == "snapshot" else 0)
                  + (2 * B * N * H * 128 * 4 if mode == "fused" else 0))
-    n_inst = max(1, math.ceil(args.pool_gib * 2 ** 30 / (per_layer * nl))) if args.config else 1
+    n_inst = max(1, math.ceil(args.pool_gib * 2 ** 30 / (per_layer * nl))) if wl.rotate else 1
     n_inst = min(n_inst, 32)
-    log(f"[bench] config {args.config}: {cfg['desc']}; {mode} path; {n_inst} instance(s) of "
+    log(f"[bench] {wl.name}: {wl.desc}; {mode} path; {n_inst} instance(s) of "
         f"{nl} layer(s), {per_layer * nl * n_inst / 2 ** 30:.2f} GiB on device")
     t0 = time.time()
     pool = []
     first = None
     for i in range(n_inst):
-        P = inputs.make_problem(args.config, instance=i)
+        P = wl.draw(i)
         parent, accepted = device.upload_tree(P)
         layers = []
         for L in P.layers:
@@ -270,7 +326,7 @@ def main():
         del src_t, dst_t
 
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.sweep:
         cpu = cpu_baseline(first, args.cpu_seconds)
 
     desc = {"fused": "; steady state: previous step's commit fused into this step's verify",
@@ -289,7 +345,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; Qwen3.5-shaped GDN heads, dk=dv=128)",
-        "config": {"workload": f"config {args.config}: {cfg['desc']}" + desc,
+        "config": {"workload": f"{wl.name}: {wl.desc}" + desc,
                    "B": B, "H": H, "N": N, "layers": nl, "qkv_dtype": dtype,
                    "state_dtype": "f32", "instances_rotated": n_inst,
                    "launch": "hip-graph" if args.graph else "stream"},
@@ -297,14 +353,16 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (None if mode == "snapshot" else
-                                 measured_traffic(args.config, dom)),
+                     "traffic": (None if mode == "snapshot" or wl.traffic_key is None else
+                                 measured_traffic(wl.traffic_key, dom)),
                      "bytes_per_launch": d_bytes, "launch_us": d_ms * 1e3},
         "kernels_us": {n: t * 1e3 for n, (b, t) in kern.items()},
         "separate_calls": separate,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    del pool
+    torch.cuda.empty_cache()
+    return line
 
 
 def measured_traffic(cfg: int, entry: str):

@@ -226,6 +226,27 @@ def make_problem(cfg: int, instance: int = 0, layers: Optional[int] = None,
     return P
 
 
+# the full-tree shapes of the paper's Table 2 and of Table 4 in Appendix B (w1, w2, w3 per
+# level, from a chain up to width 3 on every level)
+PAPER_TREE_SHAPES = [(1, 1, 1), (2, 1, 1), (2, 2, 1), (2, 2, 2), (3, 2, 2), (3, 3, 2), (3, 3, 3)]
+
+
+def make_tree_shape(widths: Sequence[int], instance: int = 0, B: int = 32, H: int = 32,
+                    dtype: str = "bf16") -> Problem:
+    """Every sequence drafts the same full tree (w1, w2, ...); the accepted node is uniform
+    over its nodes.  One layer, the configuration-1 batch (B x H) by default."""
+    par = full_tree(widths)
+    N = len(par)
+    key = [2000, instance] + [int(w) for w in widths]
+    seeds = np.random.SeedSequence(key).spawn(2)
+    tr = np.random.default_rng(seeds[0])
+    parent = np.stack([par] * B).astype(np.int32)
+    accepted = tr.integers(0, N, size=B).astype(np.int32)
+    P = Problem(cfg=-1, B=B, H=H, N=N, dtype=dtype, parent=parent, accepted=accepted)
+    P.layers.append(draw_layer(np.random.default_rng(seeds[1]), B, H, N, dtype))
+    return P
+
+
 def make_custom(seed: int, B: int, H: int, N: int, dtype: str = "bf16",
                 parent: Optional[np.ndarray] = None, tree=(6, 4),
                 accepted: Optional[np.ndarray] = None, dk: int = D, dv: int = D) -> Problem:

@@ -21,6 +21,11 @@ def say(*a):
     sys.stdout.flush()
 
 
+def _inputs():
+    from linear_attention_speculative_head_amd import inputs
+    return inputs
+
+
 def headwise_rel(x: np.ndarray, ref: np.ndarray) -> np.ndarray:
     """x, ref: [n_heads, ...] -> per-head max-abs error over max-abs reference."""
     n = x.shape[0]
@@ -90,3 +95,70 @@ def check_against_oracle(problem, gpu, heads=None, layer_idx=0, tol=TOL, label="
             assert np.array_equal(gpu["anc"][b], a), f"{label} anc mismatch at b={b}"
     say(f"  {label} worst head-wise rel err: " + ", ".join(f"{k}={v:.2e}" for k, v in worst.items()))
     return worst
+
+
+# ---- the fused entry point: the previous step's commit, then this step's verify
+
+def run_fused(P1, P2, status_check=True):
+    """Step 1: treewy_verify on P1 (its U and gamma are the previous step's factors).
+    Step 2: treewy_commit_verify with P1's tree and accepted node and P2's drafts."""
+    import torch
+    from linear_attention_speculative_head_amd import binding, device
+    assert (P1.B, P1.H) == (P2.B, P2.H) and P1.dtype == P2.dtype
+    d1 = device.upload_layer(P1.layers[0], P1.dtype)
+    par1, acc1 = device.upload_tree(P1)
+    o1 = device.alloc_outputs(P1.B, P1.H, P1.N, fill=float("nan"))
+    binding.treewy_verify(d1.S0, d1.Q, d1.K, d1.V, d1.alpha, d1.beta, par1, o1.O, o1.U, o1.gamma)
+    d2 = device.upload_layer(P2.layers[0], P2.dtype)
+    par2, _ = device.upload_tree(P2)
+    o2 = device.alloc_outputs(P2.B, P2.H, P2.N, fill=float("nan"))
+    anc = torch.zeros((P2.B, P2.N), dtype=torch.int64, device="cuda")
+    dep = torch.zeros((P2.B, P2.N), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S = d1.S0.clone()
+    binding.treewy_commit_verify(S, o1.U, d1.K, o1.gamma, par1, acc1, d2.Q, d2.K, d2.V,
+                                 d2.alpha, d2.beta, par2, o2.O, o2.U, o2.gamma, anc, dep, status)
+    torch.cuda.synchronize()
+    res = dict(O=o2.O.cpu().numpy(), U=o2.U.cpu().numpy(), gamma=o2.gamma.cpu().numpy(),
+               S=S.cpu().numpy(), anc=anc.cpu().numpy().view(np.uint64),
+               depth=dep.cpu().numpy(), status=int(status.item()))
+    if status_check:
+        assert res["status"] == 0, f"device status {res['status']}"
+    return res
+
+
+def oracle_fused(P1, P2, heads):
+    """Committed state after step 1 and step 2's outputs from it, on the given heads."""
+    import oracle
+    r1 = oracle.batch(P1.layers[0], P1.parent, P1.accepted, heads=heads, commit=True)
+    S1 = P1.layers[0].S0.copy()
+    for i, (b, h) in enumerate(heads):
+        S1[b, h] = r1["S_new"][i].astype(np.float32)
+    L2 = P2.layers[0]
+    layer2 = _inputs().Layer(S0=S1, q=L2.q, k=L2.k, v=L2.v, alpha=L2.alpha, beta=L2.beta)
+    r2 = oracle.batch(layer2, P2.parent, None, heads=heads, commit=False)
+    return r1["S_new"], r2
+
+
+def check_fused(P1, P2, gpu, heads=None, label=""):
+    import oracle
+    if heads is None:
+        heads = [(b, h) for b in range(P1.B) for h in range(P1.H)]
+    S_ref, r2 = oracle_fused(P1, P2, heads)
+    worst = {}
+    for key, kind, ref in (("O", "node", r2["O"]), ("U", "node", r2["U"]),
+                           ("gamma", "node", r2["gamma"]), ("S", "state", S_ref)):
+        g = gather_heads(gpu[key], heads, kind).astype(np.float64)
+        assert np.all(np.isfinite(g)), f"{label} {key}: non-finite GPU values"
+        e = headwise_rel(g, ref)
+        worst[key] = float(e.max())
+        bad = np.flatnonzero(e > TOL)
+        assert len(bad) == 0, (f"{label} {key}: {len(bad)} heads above {TOL}; worst "
+                               f"{e.max():.3e} at head {heads[int(np.argmax(e))]}")
+    for b in sorted({x[0] for x in heads}):
+        if P1.accepted[b] == -1:
+            assert np.array_equal(gpu["S"][b], P1.layers[0].S0[b]), f"{label}: b={b} not kept"
+        d, a = oracle.index_tree(P2.parent[b])
+        assert np.array_equal(gpu["depth"][b], d), f"{label} depth mismatch at b={b}"
+        assert np.array_equal(gpu["anc"][b], a), f"{label} anc mismatch at b={b}"
+    say(f"  {label} worst head-wise rel err: " + ", ".join(f"{k}={v:.2e}" for k, v in worst.items()))

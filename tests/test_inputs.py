@@ -133,3 +133,17 @@ def test_step_bytes_formulas():
     assert sb["verify"] == 2 * 3 * (65536 + 4 * 1804) + 2 * 16
     assert sb["commit"] == 4 + 4 + 16 + 3 * (131072 + 3 * 772)
     assert accounting.verify_bytes_per_head(4, 4) == 65536 + 4 * 2572
+
+
+def test_tree_shape_workloads():
+    """The sweep's workloads: every sequence drafts the paper's full tree, accepted nodes are
+    uniform over it, and a draw is reproducible."""
+    for w in inputs.PAPER_TREE_SHAPES:
+        P = inputs.make_tree_shape(w, B=8, H=2)
+        assert P.N == len(inputs.full_tree(w))
+        assert np.array_equal(P.parent, np.stack([inputs.full_tree(w)] * 8))
+        assert ((P.accepted >= 0) & (P.accepted < P.N)).all()
+        Q = inputs.make_tree_shape(w, B=8, H=2)
+        assert np.array_equal(P.layers[0].q, Q.layers[0].q)
+        assert np.array_equal(P.accepted, Q.accepted)
+    assert [len(inputs.full_tree(w)) for w in inputs.PAPER_TREE_SHAPES] == [3, 6, 10, 14, 21, 30, 39]
