@@ -390,6 +390,23 @@ __device__ __forceinline__ void dma_gather_x1(const void* addr, uint32_t lds) {
         : "memory");
 }
 
+// One HBM -> LDS load of 4 bytes per lane: lane l's word at base + voff lands at LDS byte
+// lds + 4 l.
+__device__ __forceinline__ void dma_x1(const void* base, uint32_t voff, uint32_t lds) {
+    lds = __builtin_amdgcn_readfirstlane(lds);      // wave-uniform by construction
+    base = uniform_ptr(base);
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(base)
+        : "memory");
+}
+
 // S0 rows of an item -> LDS: wave w takes rows 16w..16w+15, two whole rows per wave load;
 // chunk c of row r lands at slot c ^ (r % 16).  `wave` is wave-uniform (an SGPR), so the
 // LDS destinations are scalar; the source is a scalar base plus a 32-bit lane offset.
@@ -928,6 +945,13 @@ void verify_small_kernel(
 // in another node tile.  A wave's LDS operations complete in issue order, so a value written
 // at the end of step d - 1 is what other lanes of the wave read at step d.  The Gram matrix
 // G = K [K;Q]^T (same column layout) is formed by waves 0..NKT-1 and staged in LDS.
+//
+// The next item's S0 rows are requested once this item's contractions are done.  With
+// STAGE, its keys, queries, values, gates and tree then follow by direct transfers into LDS,
+// and the contractions read their fragments from there.  Without it they are plain loads
+// into registers (fragments from L2 inside the contraction loop, the rest prefetched).  A
+// wait for a plain load also covers every transfer issued before it, so in that form nothing
+// may go out ahead of the fragment loads.
 
 template <int NKT>
 struct LargeLayout {
@@ -939,6 +963,70 @@ struct LargeLayout {
     // s_waitcnt operand: vmcnt <= 2 NKT (the previous item's O and U stores), no other wait
     static constexpr int kWait = (2 * NKT) | (7 << 4) | (15 << 8);
 };
+
+// With STAGE, keys, queries, values and the tree/gate words reach LDS by direct transfers as in
+// the small-tree kernel, after the fixed part above (byte offsets): keys in rows
+// 0 .. 4 ceil(N/4) - 1 of a key/query area and queries right after them (256 B rows, chunk c of
+// row r at chunk c ^ (r % 16)); the item's half of the values (128 B rows); parents, alphas
+// and betas, 64 words each.
+struct LargeLds {
+    uint32_t kq, v, sm, bytes;
+};
+
+template <int NKT, bool STAGE>
+__host__ __device__ inline LargeLds large_lds(int N) {
+    LargeLds L;
+    const uint32_t fixed = sizeof(float) * LargeLayout<NKT>::kTotal;
+    L.kq = fixed;
+    L.v = L.kq + 2048u * static_cast<uint32_t>((N + 3) / 4);
+    L.sm = L.v + 1024u * static_cast<uint32_t>((N + 7) / 8);
+    L.bytes = STAGE ? L.sm + 768u : fixed;
+    return L;
+}
+
+// The staged inputs of an item -> LDS: ceil(N/4) loads of four key rows, as many of four
+// query rows, ceil(N/8) loads of eight value half-rows, and three gathers (parents, alphas,
+// betas: lane = node), dealt round-robin to the four waves.  Lanes past the last node load
+// node 0 again, into slots nobody reads.
+__device__ __forceinline__ void large_issue_inputs(const uint16_t* Q, const uint16_t* K,
+                                                   const uint16_t* V, const float* alpha,
+                                                   const float* beta, const int32_t* parent,
+                                                   int H, int N, int bh, int part, int wave,
+                                                   int lane, uint32_t lds, const LargeLds& L) {
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * N;
+    const uint32_t row_bytes = static_cast<uint32_t>(H) * D * 2;
+    const uint16_t* Kh = K + (node0 * H + h) * D;
+    const uint16_t* Qh = Q + (node0 * H + h) * D;
+    const uint16_t* Vh = V + (node0 * H + h) * D + part * kSmallRows;
+    const uint32_t un = static_cast<uint32_t>(N);
+    const uint32_t ln = static_cast<uint32_t>(lane) < un ? static_cast<uint32_t>(lane) : 0u;
+    const int nq4 = (N + 3) >> 2;
+    const int nv8 = (N + 7) >> 3;
+    const int jobs = 2 * nq4 + nv8 + 3;
+    for (int j = wave; j < jobs; j += 4) {
+        if (j < 2 * nq4) {
+            const bool is_q = j >= nq4;
+            const uint32_t lr = static_cast<uint32_t>(lane) >> 4;
+            const uint32_t r = 4u * j + lr;
+            const uint32_t n = 4u * (is_q ? j - nq4 : j) + lr;
+            const uint32_t c = (static_cast<uint32_t>(lane) & 15u) ^ (r & 15u);
+            dma_x4(is_q ? Qh : Kh, (n < un ? n : 0u) * row_bytes + 16u * c, lds + L.kq + 1024u * j);
+        } else if (j < 2 * nq4 + nv8) {
+            const int jv = j - 2 * nq4;
+            const uint32_t n = 8u * jv + (static_cast<uint32_t>(lane) >> 3);
+            const uint32_t c = static_cast<uint32_t>(lane) & 7u;
+            dma_x4(Vh, (n < un ? n : 0u) * row_bytes + 16u * c, lds + L.v + 1024u * jv);
+        } else if (j == 2 * nq4 + nv8) {
+            dma_x1(parent + node0, 4u * ln, lds + L.sm);
+        } else if (j == 2 * nq4 + nv8 + 1) {
+            dma_x1(alpha + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds + L.sm + 256u);
+        } else {
+            dma_x1(beta + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds + L.sm + 512u);
+        }
+    }
+}
 
 template <int NKT>
 struct LargePrefetch {
@@ -976,8 +1064,9 @@ __device__ __forceinline__ void large_prefetch(LargePrefetch<NKT>& pf, const uin
     }
 }
 
-template <int NKT>
-__global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(NKT == 2 ? 3 : 2)))
+template <int NKT, bool STAGE>
+__global__ __launch_bounds__(kSmallThreads)
+__attribute__((amdgpu_waves_per_eu(STAGE ? (NKT == 2 ? 2 : 1) : (NKT == 2 ? 3 : 2))))
 void verify_large_kernel(
     const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ alpha,
@@ -991,6 +1080,10 @@ void verify_large_kernel(
     constexpr int kCols = Lo::kCols;
     extern __shared__ __align__(16) float lds[];
     float* G = lds + Lo::kS0;                       // G[m][n], n: keys 0..N-1, queries 16NKT+t
+    const LargeLds Ls = large_lds<NKT, STAGE>(N);
+    const char* ldsb = reinterpret_cast<const char*>(lds);
+    const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+    const int nq4 = (N + 3) >> 2;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1007,7 +1100,10 @@ void verify_large_kernel(
     if (bh >= BH) return;
     LargePrefetch<NKT> pf;
     small_issue_s0(S0, lds, bh, part, wave, lane);
-    large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh, part, wave, lane);
+    if constexpr (STAGE)
+        large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, Ls);
+    else
+        large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh, part, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(pf.vraw[kt]));
@@ -1023,18 +1119,39 @@ void verify_large_kernel(
         const uint16_t* Qh = Q + (node0 * H + h) * D;
 
         uint2 vraw[NKT];
+        int my_par;
+        float my_alpha, my_beta;
+        if constexpr (STAGE) {
+            // this item's transfers have landed once only the previous item's stores (2 NKT,
+            // issued last) may still be in flight
+            __builtin_amdgcn_s_waitcnt(Lo::kWait);
+            lds_barrier();
+            const bool ok = lane < N;
+            my_par = ok ? reinterpret_cast<const int*>(ldsb + Ls.sm)[lane] : -1;
+            my_alpha = ok ? reinterpret_cast<const float*>(ldsb + Ls.sm + 256)[lane] : 1.0f;
+            my_beta = ok ? reinterpret_cast<const float*>(ldsb + Ls.sm + 512)[lane] : 0.0f;
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) vraw[kt] = pf.vraw[kt];
-        const int my_par = pf.par;
-        const float my_alpha = pf.alpha, my_beta = pf.beta;
+            for (int kt = 0; kt < NKT; ++kt) {
+                const int t = 16 * kt + col;
+                vraw[kt] = make_uint2(0u, 0u);
+                if (t < N)
+                    vraw[kt] = *reinterpret_cast<const uint2*>(ldsb + Ls.v + t * 128 + 32 * wave + 8 * grp);
+            }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) vraw[kt] = pf.vraw[kt];
+            my_par = pf.par;
+            my_alpha = pf.alpha;
+            my_beta = pf.beta;
 
-        // this item's rows and inputs have landed once only the previous item's stores (2 NKT,
-        // issued last) may still be in flight
-        __builtin_amdgcn_s_waitcnt(Lo::kWait);
+            // this item's rows and inputs have landed once only the previous item's stores
+            // (2 NKT, issued last) may still be in flight
+            __builtin_amdgcn_s_waitcnt(Lo::kWait);
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(vraw[kt]));
-        asm volatile("" ::"v"(my_par), "v"(my_alpha), "v"(my_beta));
-        lds_barrier();
+            for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(vraw[kt]));
+            asm volatile("" ::"v"(my_par), "v"(my_alpha), "v"(my_beta));
+            lds_barrier();
+        }
 
         // ---- tree walk, lane = node (every wave)
         uint64_t anc_l;
@@ -1084,12 +1201,11 @@ void verify_large_kernel(
                             ahi[ks], alo[ks]);
             }
         }
-        lds_barrier();                              // rows read: refill the buffer
+        lds_barrier();                              // rows read: the buffer may be refilled
         ++round;
         int bh_n, part_n;
         small_item(round, slot, grid, bh_n, part_n);
         const bool more = bh_n < BH;
-        if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
 
         // ---- contractions and Gram rows 16w..16w+15 (waves with keys there)
         const bool has_gram = wave < NKT && 16 * wave < N;
@@ -1099,8 +1215,13 @@ void verify_large_kernel(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 u32x4_t w = {0u, 0u, 0u, 0u};
-                if (has_gram && m < static_cast<uint32_t>(N))
-                    w = *reinterpret_cast<const u32x4_t*>(Kh + (m * node_stride + kq + 32 * ks));
+                if (has_gram && m < static_cast<uint32_t>(N)) {
+                    if constexpr (STAGE)
+                        w = *reinterpret_cast<const u32x4_t*>(
+                            ldsb + Ls.kq + 256 * m + 16 * ((4 * ks + grp) ^ (m & 15)));
+                    else
+                        w = *reinterpret_cast<const u32x4_t*>(Kh + (m * node_stride + kq + 32 * ks));
+                }
                 ka[ks] = __builtin_bit_cast(bf16x8_t, w);
             }
         }
@@ -1111,11 +1232,18 @@ void verify_large_kernel(
             const bool is_q = c >= NKT;
             const bool live = n < static_cast<uint32_t>(N);
             const uint16_t* src = (is_q ? Qh : Kh) + (n * node_stride + kq);
+            const uint32_t r = is_q ? 4u * nq4 + n : n;            // staged row
             bf16x8_t bv[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 u32x4_t w = {0u, 0u, 0u, 0u};
-                if (live) w = *reinterpret_cast<const u32x4_t*>(src + 32 * ks);
+                if (live) {
+                    if constexpr (STAGE)
+                        w = *reinterpret_cast<const u32x4_t*>(
+                            ldsb + Ls.kq + 256 * r + 16 * ((4u * ks + grp) ^ (r & 15u)));
+                    else
+                        w = *reinterpret_cast<const u32x4_t*>(src + 32 * ks);
+                }
                 bv[ks] = __builtin_bit_cast(bf16x8_t, w);
             }
             acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1133,9 +1261,19 @@ void verify_large_kernel(
                     G[(16 * wave + 4 * grp + e) * kCols + 16 * c + col] = gacc[e];
             }
         }
-        if (more)
-            large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
-        lds_barrier();                              // G visible to every wave
+        // the next item's rows only now: unstaged, the key and query fragments above are
+        // plain loads, and a wait for them would also wait for every transfer issued before
+        if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+        if constexpr (!STAGE) {
+            if (more)
+                large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
+        }
+        lds_barrier();                              // G visible to every wave; inputs read
+        if constexpr (STAGE) {
+            if (more)
+                large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
+                                   lds_addr, Ls);
+        }
 
         // ---- per lane: nodes t = 16 kt + col, rows v0..v0+3
         float Uv[NKT][4], Ov[NKT][4];
@@ -1272,10 +1410,11 @@ static hipError_t launch_verify_t(const VerifyArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int NKT>
+template <int NKT, bool STAGE>
 static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream) {
-    const size_t dyn = sizeof(float) * LargeLayout<NKT>::kTotal;
-    auto kern = verify_large_kernel<NKT>;
+    const LargeLds L = large_lds<NKT, STAGE>(a.N);
+    const size_t dyn = L.bytes;
+    auto kern = verify_large_kernel<NKT, STAGE>;
     if (dyn > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1284,8 +1423,9 @@ static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream) {
     }
     const int BH = a.B * a.H;
     const int items = BH * kSmallParts;
-    const int per_cu = NKT == 2 ? 3 : 2;            // resident workgroups (LDS and registers)
-    const int slots = per_cu * device_cu_count();
+    // resident workgroups per CU: the register budget, within the 160 KB of LDS
+    const int regs_wgs = STAGE ? (NKT == 2 ? 2 : 1) : (NKT == 2 ? 3 : 2);
+    const int slots = small_wgs(L.bytes, regs_wgs) * device_cu_count();
     const int grid = items < slots ? items : slots;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), dyn, stream, a.S0,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
@@ -1299,8 +1439,11 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     const CommitIn none{};
     if (a.N <= 8) return launch_small<1, false>(a, none, stream);
     if (a.N <= 16) return launch_small<2, false>(a, none, stream);
-    if (a.N <= 32) return launch_large<2>(a, stream);
-    return launch_large<4>(a, stream);
+    // trees of up to 32 nodes stage their inputs through LDS (two workgroups per CU); at 64
+    // nodes the staged inputs would leave room for one workgroup per CU, which measured
+    // slower than two that read key and query fragments from L2
+    if (a.N <= 32) return launch_large<2, true>(a, stream);
+    return launch_large<4, false>(a, stream);
 }
 
 // The previous step's commit fused into this step's verify where the small-tree kernel runs
