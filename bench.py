@@ -61,6 +61,9 @@ def parse():
                     help="minimum device footprint of the rotating instance pool")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--deferred", type=int, default=0, metavar="LMAX",
+                    help="steady state of the deferred commit with a log of LMAX terms "
+                         "(treewy_commit_verify_deferred); 0 = off")
     ap.add_argument("--separate", action="store_true",
                     help="time treewy_verify then treewy_commit (two launches per layer)")
     ap.add_argument("--snapshot", action="store_true",
@@ -107,9 +110,11 @@ def main():
               "every (sequence, head) is independent, so N GPUs would each run this same "
               "single-GPU pass on their share.", file=sys.stderr)
         sys.exit(2)
-    assert not (args.separate and args.snapshot), "--separate and --snapshot are exclusive"
-    mode = "snapshot" if args.snapshot else "separate" if args.separate else "fused"
-    assert not (args.graph and mode == "fused"), "--graph needs --separate or --snapshot"
+    assert sum([bool(args.separate), bool(args.snapshot), bool(args.deferred)]) <= 1, \
+        "--separate, --snapshot and --deferred are exclusive"
+    mode = ("snapshot" if args.snapshot else "separate" if args.separate else
+            "deferred" if args.deferred else "fused")
+    assert not (args.graph and mode in ("fused", "deferred")), "--graph needs --separate or --snapshot"
 
     import torch
     from linear_attention_speculative_head_amd import binding, inputs
@@ -147,7 +152,8 @@ def run(args, mode, wl):
     # ---- rotating pool of instances (each: all layers of the workload)
     per_layer = (B * H * 128 * 128 * 4 + 3 * B * N * H * 128 * elem + 2 * B * N * H * 128 * 4
                  + (B * H * N * 128 * 128 * 4 if mode == "snapshot" else 0)
-                 + (2 * B * N * H * 128 * 4 if mode == "fused" else 0))
+                 + (2 * B * N * H * 128 * 4 if mode in ("fused", "deferred") else 0)
+                 + (B * H * args.deferred * 128 * 6 if mode == "deferred" else 0))
     n_inst = max(1, math.ceil(args.pool_gib * 2 ** 30 / (per_layer * nl))) if wl.rotate else 1
     n_inst = min(n_inst, 32)
     log(f"[bench] {wl.name}: {wl.desc}; {mode} path; {n_inst} instance(s) of "
@@ -165,9 +171,10 @@ def run(args, mode, wl):
             extra = None
             if mode == "snapshot":
                 extra = torch.empty((B, H, N, 128, 128), device="cuda")
-            elif mode == "fused":                # second set of per-step outputs, alternated
+            elif mode in ("fused", "deferred"):  # second set of per-step outputs, alternated
                 extra = device.alloc_outputs(B, H, N)
-            layers.append((dl, out, extra))
+            dlog = device.alloc_log(B, H, args.deferred) if mode == "deferred" else None
+            layers.append((dl, out, extra, dlog))
         nbytes = {
             "fused": accounting.fused_step_bytes(P.parent, P.accepted, P.parent, H, elem,
                                                  layers=nl),
@@ -175,23 +182,34 @@ def run(args, mode, wl):
             "snapshot": accounting.snapshot_step_bytes(P.parent, P.accepted, H, N, elem,
                                                        layers=nl),
         }
-        pool.append(dict(parent=parent, accepted=accepted, layers=layers, flip=0, bytes=nbytes))
+        seq = []
+        if mode == "deferred":
+            # the log evolves the same way on every call of this instance: its bytes per call,
+            # worked out here so that no host work sits between the timed launches
+            lens = np.zeros(B, dtype=np.int64)
+            calls = math.ceil((args.warmup + 2 * args.steps) / n_inst) + 1
+            for _ in range(calls):
+                nb, lens = accounting.deferred_step_bytes(P.parent, P.accepted, P.parent, H,
+                                                          elem, lens, args.deferred)
+                seq.append(nb * nl)
+        pool.append(dict(parent=parent, accepted=accepted, layers=layers, flip=0, bytes=nbytes,
+                         dseq=seq, calls=0))
         if i == 0:
             first = P
     torch.cuda.synchronize()
     log(f"[bench] inputs drawn and uploaded in {time.time() - t0:.1f} s")
 
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    if mode == "fused":
+    if mode in ("fused", "deferred"):
         # the previous step of every instance: a plain verify, so that its U and gamma exist
         for x in pool:
-            for dl, out, _ in x["layers"]:
+            for dl, out, _, _ in x["layers"]:
                 binding.treewy_verify(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta, x["parent"],
                                       out.O, out.U, out.gamma, status=status)
         torch.cuda.synchronize()
 
     def fused_step(x, ev=None):
-        for j, (dl, o0, o1) in enumerate(x["layers"]):
+        for j, (dl, o0, o1, _) in enumerate(x["layers"]):
             prev, cur = (o0, o1) if x["flip"] == 0 else (o1, o0)
             if ev is not None:
                 ev[0][j].record()
@@ -201,10 +219,29 @@ def run(args, mode, wl):
             if ev is not None:
                 ev[1][j].record()
         x["flip"] ^= 1
+        return x["bytes"]["fused"]["total"]
+
+    def deferred_step(x, ev=None):
+        nb = x["dseq"][x["calls"]]
+        x["calls"] += 1
+        for j, (dl, o0, o1, dlog) in enumerate(x["layers"]):
+            prev, cur = (o0, o1) if x["flip"] == 0 else (o1, o0)
+            si, so, li, lo = dlog.headers()
+            if ev is not None:
+                ev[0][j].record()
+            binding.treewy_commit_verify_deferred(
+                dl.S0, dlog.U, dlog.K, si, so, li, lo, prev.U, dl.K, prev.gamma, x["parent"],
+                x["accepted"], dl.Q, dl.K, dl.V, dl.alpha, dl.beta, x["parent"], cur.O, cur.U,
+                cur.gamma, status=status)
+            if ev is not None:
+                ev[1][j].record()
+            dlog.flip()
+        x["flip"] ^= 1
+        return nb
 
     def two_call_step(x, ev=None, snapshot=False):
         # verify for every layer, then commit for every layer
-        for j, (dl, out, extra) in enumerate(x["layers"]):
+        for j, (dl, out, extra, _) in enumerate(x["layers"]):
             if ev is not None:
                 ev[0][j].record()
             if snapshot:
@@ -215,7 +252,7 @@ def run(args, mode, wl):
                                       out.O, out.U, out.gamma, status=status)
             if ev is not None:
                 ev[1][j].record()
-        for j, (dl, out, extra) in enumerate(x["layers"]):
+        for j, (dl, out, extra, _) in enumerate(x["layers"]):
             if ev is not None:
                 ev[2][j].record()
             if snapshot:
@@ -225,10 +262,13 @@ def run(args, mode, wl):
                                       status)
             if ev is not None:
                 ev[3][j].record()
+        return x["bytes"]["snapshot" if snapshot else "separate"]["total"]
 
     def step_fn(m):
         if m == "fused":
             return fused_step
+        if m == "deferred":
+            return deferred_step
         return lambda x, ev=None: two_call_step(x, ev, snapshot=(m == "snapshot"))
 
     K = args.steps
@@ -241,21 +281,22 @@ def run(args, mode, wl):
         def run(i, ev=None):
             if graphs is not None and ev is None:
                 graphs[i].replay()
-            else:
-                fn(pool[i], ev)
+                return pool[i]["bytes"][m]["total"]
+            return fn(pool[i], ev)
 
         for s in range(args.warmup):
             run(s % n_inst)
         torch.cuda.synchronize()
         assert int(status.item()) == 0, f"device status {int(status.item())}"
         torch.cuda.synchronize()
+        timed_bytes = 0
         t_start = time.perf_counter()
         for s in range(K):
-            run((args.warmup + s) % n_inst)
+            timed_bytes += run((args.warmup + s) % n_inst)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         assert int(status.item()) == 0, f"device status {int(status.item())}"
-        nev = 2 if m == "fused" else 4
+        nev = 2 if m in ("fused", "deferred") else 4
         events = [[[torch.cuda.Event(enable_timing=True) for _ in range(nl)] for _ in range(nev)]
                   for _ in range(K)]
         torch.cuda.synchronize()
@@ -263,17 +304,21 @@ def run(args, mode, wl):
             run((args.warmup + s) % n_inst, events[s])
         torch.cuda.synchronize()
         names = (["treewy_commit_verify"] if m == "fused" else
+                 ["treewy_commit_verify_deferred"] if m == "deferred" else
                  ["treewy_verify_snapshot", "treewy_commit_snapshot"] if m == "snapshot" else
                  ["treewy_verify", "treewy_commit"])
-        keys = ["fused"] if m == "fused" else ["verify", "commit"]
+        keys = ["fused"] if m in ("fused", "deferred") else ["verify", "commit"]
         used = [(args.warmup + s) % n_inst for s in range(K)]
+        step_bytes = timed_bytes / K
         kern = {}
         for k, (name, key) in enumerate(zip(names, keys)):
             ms = np.array([[events[s][2 * k][j].elapsed_time(events[s][2 * k + 1][j])
                             for j in range(nl)] for s in range(K)])
-            nbytes = np.mean([pool[i]["bytes"][m][key] for i in used]) / nl   # per launch
+            if m == "deferred":
+                nbytes = step_bytes / nl                                     # per launch
+            else:
+                nbytes = np.mean([pool[i]["bytes"][m][key] for i in used]) / nl
             kern[name] = (nbytes, ms.mean())
-        step_bytes = np.mean([pool[i]["bytes"][m]["total"] for i in used])
         return wall, kern, step_bytes
 
     graphs = None
@@ -330,6 +375,7 @@ def run(args, mode, wl):
         cpu = cpu_baseline(first, args.cpu_seconds)
 
     desc = {"fused": "; steady state: previous step's commit fused into this step's verify",
+            "deferred": f"; steady state: commit deferred into a log of {args.deferred} terms",
             "separate": "; verify then commit, two launches per layer",
             "snapshot": "; store-all snapshot path"}[mode]
     line = {

@@ -51,14 +51,15 @@
 extern "C" {
 #endif
 
-#define TREEWY_VERSION 2
+#define TREEWY_VERSION 3
 
 enum {
     TREEWY_OK = 0,
     TREEWY_EINVAL = 1,
     TREEWY_EHIP = 2,
     TREEWY_ETREE = 3,
-    TREEWY_EACCEPT = 4
+    TREEWY_EACCEPT = 4,
+    TREEWY_ELOG = 5
 };
 
 enum { TREEWY_F32 = 0, TREEWY_BF16 = 1 };
@@ -126,6 +127,51 @@ int treewy_commit_verify(float* S, const float* U_prev, const void* K_prev,
                          int B, int H, int N, int in_dtype,
                          float* O, float* U, float* gamma,
                          uint64_t* anc_out, int32_t* depth_out, int32_t* status, void* stream);
+
+/*
+ * The commit deferred into a log (the deferred state writes the paper's Conclusion names as
+ * a next step; §3 "Reconstruct on commit", Eq. 3, for what a commit adds).  Between writes,
+ * each (sequence b, head h) keeps its committed state as
+ *     S_committed = scale[b][h] * (S[b][h] + sum over j < len[b] of logU[b][h][j] logK[b][h][j]^T),
+ * with at most Lmax (1..16) rank-one terms.  One call does the work of
+ * treewy_commit_verify: it folds the previous step's commit into that representation and
+ * verifies this step's tree against the committed state.  When the log can take the accepted
+ * path's terms (len + depth(a) <= Lmax, and depth(a) small enough to stage: 4 for N <= 4, else
+ * 8), they are appended (u~ = (g_a/g_i) U_prev[i] / new scale) and S is not written.  Otherwise
+ * the committed state is written to S and the log is emptied.
+ *   S                       [B, H, 128, 128] float32, in place (written only when emptying)
+ *   logU                    [B, H, Lmax, 128] float32 (rows past len are ignored)
+ *   logK                    [B, H, Lmax, 128] bfloat16
+ *   scale_in, scale_out     [B, H] float32 } the log header before and after this step.  They
+ *   len_in, len_out         [B] int32      } must not overlap; alternate them between steps.
+ *                           A fresh log is len 0, scale 1 (S is then the committed state).
+ *   the rest                as treewy_commit_verify.
+ * Only bf16 inputs with N <= 16 are supported (TREEWY_EINVAL otherwise).  A header length
+ * outside [0, Lmax] is reported as TREEWY_ELOG on `status` and clamped.
+ */
+int treewy_commit_verify_deferred(float* S, float* logU, void* logK,
+                                  const float* scale_in, float* scale_out,
+                                  const int32_t* len_in, int32_t* len_out, int Lmax,
+                                  const float* U_prev, const void* K_prev,
+                                  const float* gamma_prev, const int32_t* parent_prev,
+                                  const int32_t* accepted_prev, int N_prev,
+                                  const void* Q, const void* K, const void* V,
+                                  const float* alpha, const float* beta, const int32_t* parent,
+                                  int B, int H, int N, int in_dtype,
+                                  float* O, float* U, float* gamma,
+                                  uint64_t* anc_out, int32_t* depth_out, int32_t* status,
+                                  void* stream);
+
+/*
+ * Writes the committed state a deferred-commit log stands for into S (S <- scale (S + sum of
+ * the logged terms)) and empties the log into the output header (scale 1, length 0).  Used
+ * before the state is read by anything else (another kernel, a checkpoint).  Arguments as in
+ * treewy_commit_verify_deferred; in_dtype must be TREEWY_BF16.
+ */
+int treewy_deferred_flush(float* S, const float* logU, const void* logK,
+                          const float* scale_in, float* scale_out,
+                          const int32_t* len_in, int32_t* len_out, int Lmax,
+                          int B, int H, int in_dtype, int32_t* status, void* stream);
 
 /*
  * Full-state snapshotting, the comparison scheme of the paper's §2 ("full-state

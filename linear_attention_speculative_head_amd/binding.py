@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtreewy.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "treewy.h")
 
-TREEWY_OK, TREEWY_EINVAL, TREEWY_EHIP, TREEWY_ETREE, TREEWY_EACCEPT = 0, 1, 2, 3, 4
+TREEWY_OK, TREEWY_EINVAL, TREEWY_EHIP, TREEWY_ETREE, TREEWY_EACCEPT, TREEWY_ELOG = 0, 1, 2, 3, 4, 5
 TREEWY_F32, TREEWY_BF16 = 0, 1
 D = 128
 
@@ -48,11 +48,15 @@ def lib():
         L.treewy_commit_snapshot.argtypes = [P, P, P, I, I, I, P, P]
         L.treewy_commit_verify.argtypes = ([P, P, P, P, P, P, I] + [P] * 6 + [I] * 4 +
                                            [P] * 7)
+        L.treewy_commit_verify_deferred.argtypes = ([P] * 7 + [I] + [P] * 5 + [I] + [P] * 6 +
+                                                    [I] * 4 + [P] * 7)
+        L.treewy_deferred_flush.argtypes = [P] * 7 + [I] * 4 + [P, P]
         L.treewy_strerror.argtypes = [I]
         L.treewy_strerror.restype = ctypes.c_char_p
         L.treewy_version.argtypes = []
         for f in ("treewy_verify", "treewy_commit", "treewy_verify_snapshot",
-                  "treewy_commit_snapshot", "treewy_commit_verify", "treewy_version"):
+                  "treewy_commit_snapshot", "treewy_commit_verify",
+                  "treewy_commit_verify_deferred", "treewy_deferred_flush", "treewy_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -180,6 +184,70 @@ def treewy_commit_verify(S, U_prev, K_prev, gamma_prev, parent_prev, accepted_pr
         _ptr(parent), B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma), _ptr(anc_out),
         _ptr(depth_out), _ptr(status), _stream(stream))
     _rc(rc, "treewy_commit_verify")
+
+
+def _check_log(logU, logK, scale_in, scale_out, len_in, len_out, B, H, dev):
+    import torch
+    Lmax = logU.shape[2]
+    _check(logU, "logU", (B, H, Lmax, D), (torch.float32,), dev)
+    _check(logK, "logK", (B, H, Lmax, D), (torch.bfloat16,), dev)
+    for n, t in (("scale_in", scale_in), ("scale_out", scale_out)):
+        _check(t, n, (B, H), (torch.float32,), dev)
+    for n, t in (("len_in", len_in), ("len_out", len_out)):
+        _check(t, n, (B,), (torch.int32,), dev)
+    return Lmax
+
+
+def treewy_commit_verify_deferred(S, logU, logK, scale_in, scale_out, len_in, len_out,
+                                  U_prev, K_prev, gamma_prev, parent_prev, accepted_prev,
+                                  Q, K, V, alpha, beta, parent, O, U, gamma,
+                                  anc_out=None, depth_out=None, status=None, stream=None):
+    """Enqueue one step with the commit deferred into the log (logU, logK, header in/out)."""
+    import torch
+    B, N, H, _ = Q.shape
+    Np = K_prev.shape[1]
+    dev = S.device
+    dt, qdt = _qkv_dtype(Q)
+    f32 = (torch.float32,)
+    _check(S, "S", (B, H, D, D), f32, dev)
+    Lmax = _check_log(logU, logK, scale_in, scale_out, len_in, len_out, B, H, dev)
+    _check(U_prev, "U_prev", (B, Np, H, D), f32, dev)
+    _check(K_prev, "K_prev", (B, Np, H, D), qdt, dev)
+    _check(gamma_prev, "gamma_prev", (B, Np, H), f32, dev)
+    _check(parent_prev, "parent_prev", (B, Np), (torch.int32,), dev)
+    _check(accepted_prev, "accepted_prev", (B,), (torch.int32,), dev)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check(t, n, (B, N, H, D), qdt, dev)
+    for n, t in (("alpha", alpha), ("beta", beta), ("gamma", gamma)):
+        _check(t, n, (B, N, H), f32, dev)
+    _check(parent, "parent", (B, N), (torch.int32,), dev)
+    _check(O, "O", (B, N, H, D), f32, dev)
+    _check(U, "U", (B, N, H, D), f32, dev)
+    _check(anc_out, "anc_out", (B, N), (torch.int64, torch.uint64), dev)
+    _check(depth_out, "depth_out", (B, N), (torch.int32,), dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    rc = lib().treewy_commit_verify_deferred(
+        _ptr(S), _ptr(logU), _ptr(logK), _ptr(scale_in), _ptr(scale_out), _ptr(len_in),
+        _ptr(len_out), Lmax, _ptr(U_prev), _ptr(K_prev), _ptr(gamma_prev), _ptr(parent_prev),
+        _ptr(accepted_prev), Np, _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha), _ptr(beta),
+        _ptr(parent), B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma), _ptr(anc_out),
+        _ptr(depth_out), _ptr(status), _stream(stream))
+    _rc(rc, "treewy_commit_verify_deferred")
+
+
+def treewy_deferred_flush(S, logU, logK, scale_in, scale_out, len_in, len_out, status=None,
+                          stream=None):
+    """Enqueue the write-back of the state a deferred-commit log stands for, emptying it."""
+    import torch
+    B, H = S.shape[:2]
+    dev = S.device
+    _check(S, "S", (B, H, D, D), (torch.float32,), dev)
+    Lmax = _check_log(logU, logK, scale_in, scale_out, len_in, len_out, B, H, dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    rc = lib().treewy_deferred_flush(_ptr(S), _ptr(logU), _ptr(logK), _ptr(scale_in),
+                                     _ptr(scale_out), _ptr(len_in), _ptr(len_out), Lmax, B, H,
+                                     TREEWY_BF16, _ptr(status), _stream(stream))
+    _rc(rc, "treewy_deferred_flush")
 
 
 def treewy_verify_snapshot(S0, Q, K, V, alpha, beta, parent, O, Snap, status=None, stream=None):

@@ -90,6 +90,63 @@ int treewy_commit_verify(float* S, const float* U_prev, const void* K_prev,
     return map_hip(treewy::launch_commit_verify(c, a, static_cast<hipStream_t>(stream)));
 }
 
+int treewy_commit_verify_deferred(float* S, float* logU, void* logK, const float* scale_in,
+                                  float* scale_out, const int32_t* len_in, int32_t* len_out,
+                                  int Lmax, const float* U_prev, const void* K_prev,
+                                  const float* gamma_prev, const int32_t* parent_prev,
+                                  const int32_t* accepted_prev, int N_prev, const void* Q,
+                                  const void* K, const void* V, const float* alpha,
+                                  const float* beta, const int32_t* parent, int B, int H, int N,
+                                  int in_dtype, float* O, float* U, float* gamma,
+                                  uint64_t* anc_out, int32_t* depth_out, int32_t* status,
+                                  void* stream)
+{
+    if (!S || !logU || !logK || !scale_in || !scale_out || !len_in || !len_out || !U_prev ||
+        !K_prev || !gamma_prev || !parent_prev || !accepted_prev || !Q || !K || !V || !alpha ||
+        !beta || !parent || !O || !U || !gamma)
+        return TREEWY_EINVAL;
+    if (!sizes_ok(B, H, N) || !sizes_ok(B, H, N_prev) || in_dtype != TREEWY_BF16 || N > 16 ||
+        Lmax < 1 || Lmax > 16)
+        return TREEWY_EINVAL;
+    const size_t rows = static_cast<size_t>(B) * H * D_ROW;
+    const size_t heads = static_cast<size_t>(B) * H;
+    // this step's outputs must not overwrite the previous step's factors while they are read,
+    // and the header is read from one buffer and written to another
+    const Span outs[5] = {{O, rows * N * 4}, {U, rows * N * 4},
+                          {gamma, static_cast<size_t>(B) * N * H * 4},
+                          {scale_out, heads * 4}, {len_out, static_cast<size_t>(B) * 4}};
+    const Span ins[5] = {{U_prev, rows * N_prev * 4}, {K_prev, rows * N_prev * 2},
+                         {gamma_prev, static_cast<size_t>(B) * N_prev * H * 4},
+                         {scale_in, heads * 4}, {len_in, static_cast<size_t>(B) * 4}};
+    for (const Span& o : outs)
+        for (const Span& i : ins)
+            if (overlap(o, i)) return TREEWY_EINVAL;
+    treewy::CommitArgs c{S, U_prev, K_prev, gamma_prev, parent_prev, accepted_prev, B, H, N_prev,
+                         in_dtype, status};
+    treewy::VerifyArgs a{S, Q, K, V, alpha, beta, parent, B, H, N, in_dtype,
+                         O, U, gamma, anc_out, depth_out, status};
+    treewy::DeferArgs d{logU, logK, scale_in, scale_out, len_in, len_out, Lmax};
+    return map_hip(treewy::launch_commit_verify_deferred(c, a, d, static_cast<hipStream_t>(stream)));
+}
+
+int treewy_deferred_flush(float* S, const float* logU, const void* logK, const float* scale_in,
+                          float* scale_out, const int32_t* len_in, int32_t* len_out, int Lmax,
+                          int B, int H, int in_dtype, int32_t* status, void* stream)
+{
+    if (!S || !logU || !logK || !scale_in || !scale_out || !len_in || !len_out) return TREEWY_EINVAL;
+    if (!sizes_ok(B, H, 1) || in_dtype != TREEWY_BF16 || Lmax < 1 || Lmax > 16) return TREEWY_EINVAL;
+    const size_t heads = static_cast<size_t>(B) * H;
+    if (overlap({scale_out, heads * 4}, {scale_in, heads * 4}) ||
+        overlap({len_out, static_cast<size_t>(B) * 4}, {len_in, static_cast<size_t>(B) * 4}) ||
+        overlap({scale_out, heads * 4}, {len_in, static_cast<size_t>(B) * 4}) ||
+        overlap({len_out, static_cast<size_t>(B) * 4}, {scale_in, heads * 4}))
+        return TREEWY_EINVAL;
+    treewy::DeferArgs d{const_cast<float*>(logU), const_cast<void*>(logK), scale_in, scale_out,
+                        len_in, len_out, Lmax};
+    return map_hip(treewy::launch_deferred_flush(S, d, B, H, in_dtype, status,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int treewy_verify_snapshot(const float* S0, const void* Q, const void* K, const void* V,
                            const float* alpha, const float* beta, const int32_t* parent,
                            int B, int H, int N, int in_dtype, float* O, float* Snap,
@@ -119,6 +176,7 @@ const char* treewy_strerror(int code)
         case TREEWY_EHIP: return "HIP launch or runtime error";
         case TREEWY_ETREE: return "malformed draft tree (parent outside [-1, t-1])";
         case TREEWY_EACCEPT: return "accepted node outside [-1, N-1]";
+        case TREEWY_ELOG: return "deferred-commit log length outside [0, Lmax]";
         default: return "unknown error code";
     }
 }

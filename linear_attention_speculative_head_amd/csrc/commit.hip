@@ -110,7 +110,81 @@ void commit_kernel(
     for (int j = 0; j < kVec; ++j) Sh[j * kThreads + tid] = s[j];
 }
 
+// The state a deferred-commit log stands for, written back: S <- scale (S + sum_j u~_j k_j^T)
+// for the first len[b] terms, and the log emptied (scale 1, length 0 into the output
+// header).  Same work split as commit_kernel; an empty log leaves S untouched.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
+void flush_kernel(
+    float* __restrict__ S, const float* __restrict__ logU, const uint16_t* __restrict__ logK,
+    const float* __restrict__ scale_in, float* __restrict__ scale_out,
+    const int32_t* __restrict__ len_in, int32_t* __restrict__ len_out, int H, int Lmax,
+    int32_t* __restrict__ status)
+{
+    __shared__ float s_u[kChunk][D / kParts];   // this half's rows of u~
+    __shared__ float s_k[kChunk][D];
+
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / kParts;
+    const int part = blockIdx.x - bh * kParts;
+    const int b = bh / H;
+    const int h = bh - b * H;
+
+    const int raw = len_in[b];
+    const int len = raw < 0 ? 0 : (raw > Lmax ? Lmax : raw);
+    if (tid == 0 && part == 0) {
+        if (raw != len && h == 0) report(status, TREEWY_ELOG);
+        scale_out[bh] = 1.0f;
+        if (h == 0) len_out[b] = 0;
+    }
+    if (len == 0) return;                     // an empty log: S is the state already
+    const float sc = scale_in[bh];
+
+    constexpr int kRowsPart = D / kParts;
+    float4* Sh = reinterpret_cast<float4*>(S + (static_cast<size_t>(bh) * D + part * kRowsPart) * D);
+    float4 s[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) s[j] = Sh[j * kThreads + tid];
+
+    const size_t row0 = static_cast<size_t>(bh) * Lmax;
+    const int c4 = tid & 31;
+    for (int c0 = 0; c0 < len; c0 += kChunk) {
+        const int nj = min(kChunk, len - c0);
+        __syncthreads();
+        for (int p = tid; p < nj * D; p += kThreads) {
+            const int jj = p >> 7;
+            const int x = p & (D - 1);
+            if (x < kRowsPart) s_u[jj][x] = logU[(row0 + c0 + jj) * D + part * kRowsPart + x];
+            s_k[jj][x] = Elem<uint16_t>::load1(logK + (row0 + c0 + jj) * D + x);
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int jj = 0; jj < nj; ++jj) {
+            const float4 kv = *reinterpret_cast<const float4*>(&s_k[jj][4 * c4]);
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const int r = (j * kThreads + tid) >> 5;
+                const float cu = s_u[jj][r];
+                s[j].x += cu * kv.x; s[j].y += cu * kv.y; s[j].z += cu * kv.z; s[j].w += cu * kv.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        s[j].x *= sc; s[j].y *= sc; s[j].z *= sc; s[j].w *= sc;
+        Sh[j * kThreads + tid] = s[j];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_deferred_flush(float* S, const DeferArgs& d, int B, int H, int in_dtype,
+                                 int32_t* status, hipStream_t stream) {
+    (void)in_dtype;                           // the log's keys are bf16
+    hipLaunchKernelGGL(flush_kernel, dim3(B * H * kParts), dim3(kThreads), 0, stream, S, d.logU,
+                       static_cast<const uint16_t*>(d.logK), d.scale_in, d.scale_out, d.len_in,
+                       d.len_out, H, d.Lmax, status);
+    return hipGetLastError();
+}
 
 template <typename T>
 static hipError_t launch_commit_t(const CommitArgs& a, hipStream_t stream) {

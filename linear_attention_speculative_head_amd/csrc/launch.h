@@ -56,6 +56,17 @@ struct SnapshotCommitArgs {
     int32_t* status;
 };
 
+// the log of the deferred commit (treewy_commit_verify_deferred)
+struct DeferArgs {
+    float* logU;
+    void* logK;
+    const float* scale_in;
+    float* scale_out;
+    const int32_t* len_in;
+    int32_t* len_out;
+    int Lmax;
+};
+
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
 hipError_t launch_verify_snapshot(const SnapshotVerifyArgs& a, hipStream_t stream);
@@ -63,5 +74,11 @@ hipError_t launch_commit_snapshot(const SnapshotCommitArgs& a, hipStream_t strea
 // the commit described by `c` (its S, U, K, gamma, parent, accepted and node count N of the
 // previous step), then the verify described by `a` on the committed state (a.S0 == c.S)
 hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStream_t stream);
+// the same with the commit deferred into the log `d` (bf16 inputs, N <= 16)
+hipError_t launch_commit_verify_deferred(const CommitArgs& c, const VerifyArgs& a,
+                                         const DeferArgs& d, hipStream_t stream);
+// the state the log stands for, written into S; the log is emptied into d's output header
+hipError_t launch_deferred_flush(float* S, const DeferArgs& d, int B, int H, int in_dtype,
+                                 int32_t* status, hipStream_t stream);
 
 }  // namespace treewy

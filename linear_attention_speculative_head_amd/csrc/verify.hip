@@ -255,15 +255,18 @@ constexpr int kSmallParts = D / kSmallRows; // items per head
 // right after them (bf16 rows of 256 B); the item's half of the values (rows of 128 B);
 // parents, alphas, betas (words 0-15, 16-31, 32-47) and one more word (48); the Gram matrix
 // [16][16 NCT] fp32.  With the fused commit: `path` U_prev half-rows (256 B) and K_prev rows
-// (256 B), the path's gammas [64] and the previous tree's parents [64].  16-byte chunk c of a
-// row r of S0 or of the key/query area is stored at chunk c ^ (r % 16), which keeps the MFMA
-// operand reads free of bank conflicts.
+// (256 B), the path's gammas [64] and the previous tree's parents [64].  With the deferred
+// commit also: the sequence's log length (one word, repeated), the head's log scale (one
+// word, repeated), and the log's Lmax u-half-rows (256 B) and key rows (256 B).  16-byte
+// chunk c of a row r of S0 or of the key/query area is stored at chunk c ^ (r % 16), which
+// keeps the MFMA operand reads free of bank conflicts.
 struct SmallLds {
-    uint32_t kq, v, sm, g, pu, pk, pg, idx, bytes;
+    uint32_t kq, v, sm, g, pu, pk, pg, idx, il, lg, lu, lk, bytes;
     int path;                                   // path rows staged per chunk (fused)
 };
 
-__host__ __device__ inline SmallLds small_lds(int N, int nct, bool fused) {
+// mode: 0 plain verify, 1 fused commit, 2 deferred commit (log of lmax terms)
+__host__ __device__ inline SmallLds small_lds(int N, int nct, int mode, int lmax = 0) {
     SmallLds L;
     L.kq = kSmallRows * D * 4;
     L.v = L.kq + 2048u * static_cast<uint32_t>((N + 3) / 4);
@@ -275,15 +278,22 @@ __host__ __device__ inline SmallLds small_lds(int N, int nct, bool fused) {
     L.pk = L.pu + 256u * L.path;
     L.pg = L.pk + 256u * L.path;
     L.idx = L.pg + 256u;
-    L.bytes = fused ? L.idx + 256u : end;
+    L.il = L.idx + 256u;
+    L.lg = L.il + 256u;
+    // the log rows arrive four to a transfer: room for a multiple of four
+    const uint32_t lrows = 4u * static_cast<uint32_t>((lmax + 3) / 4);
+    L.lu = L.lg + 256u;
+    L.lk = L.lu + 256u * lrows;
+    L.bytes = mode == 0 ? end : mode == 1 ? L.idx + 256u : L.lk + 256u * lrows;
     return L;
 }
 
 // Waves per SIMD the registers are budgeted for (= resident workgroups per CU): four for the
 // plain kernel on trees of up to 8 nodes; three where LDS allows no more (16 nodes) or the
-// fused commit needs the registers.
-template <int NCT, bool FUSED>
-constexpr int kSmallWavesPerSimd = (NCT == 2 || FUSED) ? 3 : 4;
+// fused commit needs the registers; two for the deferred commit on 16-node trees, whose LDS
+// (with a log of 16 terms) leaves room for two.
+template <int NCT, int MODE>
+constexpr int kSmallWavesPerSimd = (NCT == 2 && MODE == 2) ? 2 : (NCT == 2 || MODE != 0) ? 3 : 4;
 
 // resident workgroups per CU: the register budget, within the 160 KB of LDS
 inline int small_wgs(uint32_t bytes, int regs_wgs) {
@@ -506,6 +516,19 @@ struct CommitIn {
     int Np;                                 // its node count
 };
 
+// The deferred commit's log of one step (see the kernel below): per (sequence, head) up to
+// Lmax rank-one terms u~_j k_j^T and a scale, such that the committed state is
+// scale * (S + sum_j u~_j k_j^T).  Header words are read from *_in and written to *_out.
+struct DeferLog {
+    float* U;                               // [B][H][Lmax][128] fp32 terms u~
+    uint16_t* K;                            // [B][H][Lmax][128] bf16 keys
+    const float* scale_in;                  // [B][H]
+    float* scale_out;
+    const int32_t* len_in;                  // [B] terms in use (every head of a sequence alike)
+    int32_t* len_out;
+    int Lmax;
+};
+
 // One item's commit: the path of the accepted node as a mask, its length, and in lane q the
 // q-th path node in increasing order (root first).
 struct PathInfo {
@@ -602,24 +625,66 @@ __device__ __forceinline__ void fused_issue_path(const CommitIn& c, const PathIn
     }
 }
 
-// ---------------------------------------------------------------------------------------
-// The small-tree verify kernel; with FUSED the previous step's commit is applied to S on the
-// way in (see above), otherwise S0 is read as it is.
+// A log length read from memory, kept inside [0, lmax] (the header of a caller who broke the
+// contract; TREEWY_ELOG is reported where the length is used).
+__device__ __forceinline__ int log_len(int v, int lmax) {
+    return v < 0 ? 0 : (v > lmax ? lmax : v);
+}
 
-template <int NCT, bool FUSED>
+// The first `len` log terms of an item -> LDS (its half of each u~ row, every key row, four
+// rows per transfer), and the head's log scale (one word, repeated over 64 words).
+__device__ __forceinline__ void defer_issue_log(const DeferLog& dl, int len, int bh, int part,
+                                                int wave, int lane, uint32_t lds,
+                                                const SmallLds& L) {
+    const int nj = (len + 3) >> 2;
+    const int jobs = 2 * nj + 1;
+    const size_t row0 = static_cast<size_t>(bh) * dl.Lmax;
+    const uint32_t col16 = 16u * (static_cast<uint32_t>(lane) & 15u);
+    for (int j = wave; j < jobs; j += 4) {
+        if (j < 2 * nj) {
+            const bool is_k = j >= nj;
+            const int jj = is_k ? j - nj : j;
+            const int q = 4 * jj + (lane >> 4);
+            const uint32_t r = static_cast<uint32_t>(q < len ? q : 0);
+            if (is_k)
+                dma_x4(dl.K + row0 * D, r * (D * 2u) + col16, lds + L.lk + 1024u * jj);
+            else
+                dma_x4(dl.U + row0 * D + part * kSmallRows, r * (D * 4u) + col16,
+                       lds + L.lu + 1024u * jj);
+        } else {
+            dma_x1(dl.scale_in + bh, 0u, lds + L.lg);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// The small-tree verify kernel.  MODE 0 reads S0 as it is.  MODE 1 applies the previous
+// step's commit to S on the way in and writes the committed rows back (see above).  MODE 2
+// defers that write (a step of the log-structured commit, the deferred state writes the
+// paper's Conclusion names as a next step): the committed state is kept as
+// scale * (S + sum of logged rank-one terms).  Each item reads S, its log and the previous
+// step's path; it forms the committed rows in LDS as in MODE 1 and verifies against them.
+// When the log has room it appends the path's terms (divided by the new scale) instead of
+// writing S. Otherwise (or when the path is longer than one LDS chunk) it writes the
+// committed rows to S and empties the log.  Header words go to separate output buffers, so
+// no item can see another item's update of the same sequence within one launch.
+
+template <int NCT, int MODE>
 __global__ __launch_bounds__(kSmallThreads)
-__attribute__((amdgpu_waves_per_eu(kSmallWavesPerSimd<NCT, FUSED>)))
+__attribute__((amdgpu_waves_per_eu(kSmallWavesPerSimd<NCT, MODE>)))
 void verify_small_kernel(
     const float* S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ alpha,
     const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
     float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
-    int32_t* __restrict__ status, CommitIn cin)
+    int32_t* __restrict__ status, CommitIn cin, DeferLog dlog)
 {
+    constexpr bool FUSED = MODE != 0;
+    constexpr bool DEFER = MODE == 2;
     constexpr int kGP = 16 * NCT;                   // G row pitch
     extern __shared__ __align__(16) float lds[];
-    const SmallLds L = small_lds(N, NCT, FUSED);
+    const SmallLds L = small_lds(N, NCT, MODE, DEFER ? dlog.Lmax : 0);
     const char* ldsb = reinterpret_cast<const char*>(lds);
     float* G = lds + L.g / 4;                       // G[m][n] = k_m . (k|q)_n
     const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
@@ -641,27 +706,39 @@ void verify_small_kernel(
     if (bh >= BH) return;
 
     PathInfo cur{0ull, 0, 0};                       // this item's commit (FUSED)
+    int cur_len = 0;                                // this item's log length (DEFER)
     if constexpr (FUSED) {
-        // item 0's previous tree and accepted node go out first, then its S rows; the path
-        // is derived while the rows stream in, then its own rows and item 0's other inputs
-        // (with item 1's accepted node and tree) follow
+        // item 0's previous tree and accepted node (and log length) go out first, then its S
+        // rows; the path is derived while the rows stream in, then its own rows (and log) and
+        // item 0's other inputs (with item 1's accepted node and tree) follow
         int bh1, part1;
         small_item(1, slot, grid, bh1, part1);
         if (wave == 0) {
             fused_issue_index(cin, bh / H, lane, lds_addr + L.idx);
             dma_gather_x1(cin.accepted + bh / H, lds_addr + L.sm);
+            if constexpr (DEFER) dma_x1(dlog.len_in + bh / H, 0u, lds_addr + L.il);
         }
         small_issue_s0(S0, lds, bh, part, wave, lane);
-        __builtin_amdgcn_s_waitcnt(kWaitAllButEight);   // the two gathers (the eight row loads go on)
+        __builtin_amdgcn_s_waitcnt(kWaitAllButEight);   // the gathers (the eight row loads go on)
         lds_barrier();
         cur = fused_path(lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L.idx)[lane] : -1,
                          reinterpret_cast<const int*>(ldsb + L.sm)[48], cin.Np, lane,
                          wave == 0 && bh % H == 0 && part == 0, status);
+        if constexpr (DEFER) {
+            const int raw = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(ldsb + L.il)[0]);
+            cur_len = log_len(raw, dlog.Lmax);
+            if (raw != cur_len && wave == 0 && lane == 0 && bh % H == 0 && part == 0)
+                report(status, TREEWY_ELOG);
+        }
         lds_barrier();                              // index read by every wave: refill
         if (cur.depth > 0) fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr, L);
+        if constexpr (DEFER) defer_issue_log(dlog, cur_len, bh, part, wave, lane, lds_addr, L);
         small_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, L,
                            bh1 < BH ? cin.accepted + bh1 / H : nullptr);
-        if (bh1 < BH && wave == 3) fused_issue_index(cin, bh1 / H, lane, lds_addr + L.idx);
+        if (bh1 < BH && wave == 3) {
+            fused_issue_index(cin, bh1 / H, lane, lds_addr + L.idx);
+            if constexpr (DEFER) dma_x1(dlog.len_in + bh1 / H, 0u, lds_addr + L.il);
+        }
     } else {
         small_issue_s0(S0, lds, bh, part, wave, lane);
         small_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, L,
@@ -686,33 +763,64 @@ void verify_small_kernel(
         const bool more = bh_n < BH;
 
         if constexpr (FUSED) {
-            if (cur.depth > 0) {
-                // S_a = g_a S + sum over the path of (g_a / g_i) U_prev[i] k_i^T, applied to this
-                // wave's 16 rows where they sit in LDS, in the layout they arrived in (lane l:
-                // row 16w + 2i + l / 32, 16-byte chunk l % 32, for i = 0..7), and written back
-                // to HBM from there: every store is two whole 512-byte rows.  The path's gammas
-                // are in LDS in path order (a is last).
-                const float* PG = reinterpret_cast<const float*>(ldsb + L.pg);
+            int len = 0;
+            float gin = 1.0f;
+            if constexpr (DEFER) {
+                len = cur_len;
+                gin = reinterpret_cast<const float*>(ldsb + L.lg)[0];
+            }
+            const bool any = cur.depth > 0 || len > 0;
+            // MODE 1 always writes S; MODE 2 only when the log cannot take the path's terms
+            bool flush = true;
+            if constexpr (DEFER) flush = len + cur.depth > dlog.Lmax || cur.depth > L.path;
+            const float* PG = reinterpret_cast<const float*>(ldsb + L.pg);
+            const float ga = cur.depth > 0 ? PG[cur.depth - 1] : 1.0f;
+            const float gs = gin * ga;              // the scale of S (and of the logged terms)
+            if (any) {
+                // S_a = gs (S + sum_j u~_j k_j^T) + sum over the path of (g_a / g_i) U_prev[i]
+                // k_i^T (MODE 1: no log, gs = g_a), applied to this wave's 16 rows where they
+                // sit in LDS, in the layout they arrived in (lane l: row 16w + 2i + l / 32,
+                // 16-byte chunk l % 32, for i = 0..7), and written back to HBM from there when
+                // flushing: every store is two whole 512-byte rows.  The path's gammas are in
+                // LDS in path order (a is last).
                 const float* PU = reinterpret_cast<const float*>(ldsb + L.pu);
                 const char* PK = ldsb + L.pk;
-                const float ga = PG[cur.depth - 1];
                 const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
                 const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
-                for (int q0 = 0; q0 < cur.depth; q0 += L.path) {
-                    if (q0 > 0) {
+                const int nchunk = cur.depth > 0 ? (cur.depth + L.path - 1) / L.path : 1;
+                for (int ci = 0; ci < nchunk; ++ci) {
+                    const int q0 = ci * L.path;
+                    if (ci > 0) {
                         // a path longer than one chunk: the next chunk, with a blocking wait
                         lds_barrier();
-                        fused_issue_path(cin, cur, q0 / L.path, bh, part, H, wave, lane, lds_addr, L);
+                        fused_issue_path(cin, cur, ci, bh, part, H, wave, lane, lds_addr, L);
                         __builtin_amdgcn_s_waitcnt(0);
                         lds_barrier();
                     }
-                    const int cnt = cur.depth - q0 < L.path ? cur.depth - q0 : L.path;
+                    const int rem = cur.depth - q0;
+                    const int cnt = rem < L.path ? rem : L.path;
                     f32x4_t x[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const uint32_t r = 16u * wave + 2u * i + hl;
                         x[i] = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
-                        if (q0 == 0) x[i] *= ga;
+                        if (ci == 0) x[i] *= gs;
+                    }
+                    if constexpr (DEFER) {
+                        if (ci == 0) {
+                            const float* LU = reinterpret_cast<const float*>(ldsb + L.lu);
+                            const char* LK = ldsb + L.lk;
+                            for (int q = 0; q < len; ++q) {
+                                const uint2 kw = *reinterpret_cast<const uint2*>(LK + q * 256 + 8 * ch);
+                                const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
+                                                    __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
+#pragma unroll
+                                for (int i = 0; i < 8; ++i) {
+                                    const float cu = gs * LU[q * kSmallRows + 16 * wave + 2 * i + hl];
+                                    x[i] += cu * kv;
+                                }
+                            }
+                        }
                     }
                     for (int q = 0; q < cnt; ++q) {
                         const float cq = ga / PG[q0 + q];
@@ -725,15 +833,41 @@ void verify_small_kernel(
                             x[i] += cu * kv;
                         }
                     }
-                    const bool last = q0 + L.path >= cur.depth;
+                    const bool last = ci + 1 == nchunk;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const uint32_t r = 16u * wave + 2u * i + hl;
                         *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
-                        if (last)
+                        if (last && flush)
                             *reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D +
                                                                  part * kSmallRows + r) * D + 4 * ch) = x[i];
                     }
+                }
+                if constexpr (DEFER) {
+                    if (!flush && cur.depth > 0 && wave == 0) {
+                        // the path's terms join the log at rows len ..: this half of each
+                        // u~ = (g_a / g_i) U_prev[i] / gs, and this half of each key row
+                        const size_t row0 = static_cast<size_t>(bh) * dlog.Lmax + len;
+                        for (int q = lane >> 4; q < cur.depth; q += 4) {
+                            const int c4 = lane & 15;
+                            const float cq = (ga / PG[q]) / gs;
+                            const f32x4_t u = *reinterpret_cast<const f32x4_t*>(PU + q * kSmallRows + 4 * c4);
+                            *reinterpret_cast<f32x4_t*>(dlog.U + (row0 + q) * D + part * kSmallRows + 4 * c4) = cq * u;
+                        }
+                        for (int q = lane >> 3; q < cur.depth; q += 8) {
+                            const int c8 = lane & 7;
+                            const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(PK + q * 256 + 128 * part + 16 * c8);
+                            *reinterpret_cast<u32x4_t*>(dlog.K + (row0 + q) * D + part * kSmallRows + 8 * c8) = kv;
+                        }
+                    }
+                }
+            }
+            if constexpr (DEFER) {
+                // the header after this step: an emptied log has scale 1 and length 0
+                if (wave == 0 && lane == 0 && part == 0) {
+                    const bool emptied = any && flush;
+                    dlog.scale_out[bh] = emptied ? 1.0f : gs;
+                    if (h == 0) dlog.len_out[b] = emptied ? 0 : len + cur.depth;
                 }
             }
         }
@@ -758,11 +892,20 @@ void verify_small_kernel(
             }
         }
         PathInfo nxt{0ull, 0, 0};
+        int nxt_len = 0;
         if constexpr (FUSED) {
-            if (more)
+            if (more) {
                 nxt = fused_path(lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L.idx)[lane] : -1,
                                  reinterpret_cast<const int*>(ldsb + L.sm)[48], cin.Np, lane,
                                  wave == 0 && bh_n % H == 0 && part_n == 0, status);
+                if constexpr (DEFER) {
+                    const int raw = __builtin_amdgcn_readfirstlane(
+                        reinterpret_cast<const int*>(ldsb + L.il)[0]);
+                    nxt_len = log_len(raw, dlog.Lmax);
+                    if (raw != nxt_len && wave == 0 && lane == 0 && bh_n % H == 0 && part_n == 0)
+                        report(status, TREEWY_ELOG);
+                }
+            }
         }
 
         // ---- tree walk, in every 16-lane group (lane = node t): pointer jumping as in
@@ -840,7 +983,12 @@ void verify_small_kernel(
                                    lds_addr, L, bh_2 < BH ? cin.accepted + bh_2 / H : nullptr);
                 if (nxt.depth > 0)
                     fused_issue_path(cin, nxt, 0, bh_n, part_n, H, wave, lane, lds_addr, L);
-                if (bh_2 < BH && wave == 3) fused_issue_index(cin, bh_2 / H, lane, lds_addr + L.idx);
+                if constexpr (DEFER)
+                    defer_issue_log(dlog, nxt_len, bh_n, part_n, wave, lane, lds_addr, L);
+                if (bh_2 < BH && wave == 3) {
+                    fused_issue_index(cin, bh_2 / H, lane, lds_addr + L.idx);
+                    if constexpr (DEFER) dma_x1(dlog.len_in + bh_2 / H, 0u, lds_addr + L.il);
+                }
             } else {
                 small_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
                                    lds_addr, L, nullptr);
@@ -928,7 +1076,10 @@ void verify_small_kernel(
         if (!more) break;
         bh = bh_n;
         part = part_n;
-        if constexpr (FUSED) cur = nxt;
+        if constexpr (FUSED) {
+            cur = nxt;
+            cur_len = nxt_len;
+        }
     }
 }
 
@@ -1373,12 +1524,18 @@ int device_cu_count() {
     return cus;
 }
 
-template <int NCT, bool FUSED>
-static hipError_t launch_small(const VerifyArgs& a, const CommitIn& cin, hipStream_t stream) {
-    const SmallLds L = small_lds(a.N, NCT, FUSED);
+template <int NCT, int MODE>
+static hipError_t launch_small(const VerifyArgs& a, const CommitIn& cin, const DeferLog& dl,
+                               hipStream_t stream) {
+    const SmallLds L = small_lds(a.N, NCT, MODE, MODE == 2 ? dl.Lmax : 0);
     const int bytes = static_cast<int>(L.bytes);
-    const int wgs = small_wgs(L.bytes, kSmallWavesPerSimd<NCT, FUSED>);
-    auto kern = verify_small_kernel<NCT, FUSED>;
+    const int wgs = small_wgs(L.bytes, kSmallWavesPerSimd<NCT, MODE>);
+    auto kern = verify_small_kernel<NCT, MODE>;
+    if (L.bytes > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) return e;
+    }
     const int BH = a.B * a.H;
     const int items = BH * kSmallParts;
     const int slots = wgs * device_cu_count();   // resident workgroups
@@ -1386,7 +1543,7 @@ static hipError_t launch_small(const VerifyArgs& a, const CommitIn& cin, hipStre
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), bytes, stream, a.S0,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
-                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status, cin);
+                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status, cin, dl);
     return hipGetLastError();
 }
 
@@ -1437,8 +1594,9 @@ static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream) {
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     if (a.in_dtype != TREEWY_BF16) return launch_verify_t<float>(a, stream);
     const CommitIn none{};
-    if (a.N <= 8) return launch_small<1, false>(a, none, stream);
-    if (a.N <= 16) return launch_small<2, false>(a, none, stream);
+    const DeferLog nolog{};
+    if (a.N <= 8) return launch_small<1, 0>(a, none, nolog, stream);
+    if (a.N <= 16) return launch_small<2, 0>(a, none, nolog, stream);
     // trees of up to 32 nodes stage their inputs through LDS (two workgroups per CU); at 64
     // nodes the staged inputs would leave room for one workgroup per CU, which measured
     // slower than two that read key and query fragments from L2
@@ -1453,12 +1611,24 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
     if (a.in_dtype == TREEWY_BF16 && a.N <= 16) {
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
                            c.accepted, c.N};
-        return a.N <= 8 ? launch_small<1, true>(a, cin, stream)
-                        : launch_small<2, true>(a, cin, stream);
+        const DeferLog nolog{};
+        return a.N <= 8 ? launch_small<1, 1>(a, cin, nolog, stream)
+                        : launch_small<2, 1>(a, cin, nolog, stream);
     }
     hipError_t e = launch_commit(c, stream);
     if (e != hipSuccess) return e;
     return launch_verify(a, stream);
+}
+
+// The deferred commit (bf16 inputs, N <= 16 only: the caller checks).
+hipError_t launch_commit_verify_deferred(const CommitArgs& c, const VerifyArgs& a,
+                                         const DeferArgs& d, hipStream_t stream) {
+    const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
+                       c.accepted, c.N};
+    const DeferLog dl{d.logU, static_cast<uint16_t*>(d.logK), d.scale_in, d.scale_out,
+                      d.len_in, d.len_out, d.Lmax};
+    return a.N <= 8 ? launch_small<1, 2>(a, cin, dl, stream)
+                    : launch_small<2, 2>(a, cin, dl, stream);
 }
 
 }  // namespace treewy

@@ -20,16 +20,17 @@ def lib():
 def test_exports_every_header_symbol(lib):
     names = binding.header_symbols()
     assert set(names) == {"treewy_verify", "treewy_commit", "treewy_verify_snapshot",
-                          "treewy_commit_snapshot", "treewy_commit_verify", "treewy_strerror",
-                          "treewy_version"}
+                          "treewy_commit_snapshot", "treewy_commit_verify",
+                          "treewy_commit_verify_deferred", "treewy_deferred_flush",
+                          "treewy_strerror", "treewy_version"}
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_strerror(lib):
-    assert lib.treewy_version() == 2
-    for code in range(5):
+    assert lib.treewy_version() == 3
+    for code in range(6):
         assert lib.treewy_strerror(code)
     assert lib.treewy_strerror(99) == b"unknown error code"
 
@@ -102,3 +103,38 @@ def test_commit_verify_rejects_outputs_over_previous_factors(lib, which):
         == binding.TREEWY_EINVAL
     assert lib.treewy_commit_verify(*fused_args(**{which: ctypes.c_void_p(0x40000000)})) \
         == binding.TREEWY_EINVAL
+
+
+def deferred_args(**kw):
+    f = lambda x: ctypes.c_void_p(x)
+    a = dict(S=f(0x10000000), logU=f(0x11000000), logK=f(0x12000000), scale_in=f(0x13000000),
+             scale_out=f(0x14000000), len_in=f(0x15000000), len_out=f(0x16000000), Lmax=8,
+             U_prev=f(0x20000000), K_prev=f(0x30000000), gamma_prev=f(0x40000000),
+             parent_prev=f(0x50000000), accepted_prev=f(0x60000000), Np=4, Q=f(0x70000000),
+             K=f(0x80000000), V=f(0x90000000), alpha=f(0xa0000000), beta=f(0xb0000000),
+             parent=f(0xc0000000), B=2, H=2, N=4, dt=binding.TREEWY_BF16, O=f(0xd0000000),
+             U=f(0xe0000000), gamma=f(0xf0000000), anc=None, depth=None, status=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(logU=None), dict(logK=None), dict(scale_in=None),
+                                 dict(len_out=None), dict(U_prev=None), dict(Q=None),
+                                 dict(Lmax=0), dict(Lmax=17), dict(N=17), dict(Np=65),
+                                 dict(dt=binding.TREEWY_F32),
+                                 dict(scale_out=ctypes.c_void_p(0x13000000)),   # = scale_in
+                                 dict(len_out=ctypes.c_void_p(0x15000000)),     # = len_in
+                                 dict(U=ctypes.c_void_p(0x20000000))])           # = U_prev
+def test_commit_verify_deferred_rejects(lib, bad):
+    assert lib.treewy_commit_verify_deferred(*deferred_args(**bad)) == binding.TREEWY_EINVAL
+
+
+def test_deferred_flush_rejects(lib):
+    f = lambda x: ctypes.c_void_p(x)
+    ok = [f(0x10000000), f(0x11000000), f(0x12000000), f(0x13000000), f(0x14000000),
+          f(0x15000000), f(0x16000000), 8, 2, 2, binding.TREEWY_BF16, None, None]
+    for i, v in ((0, None), (1, None), (7, 0), (7, 17), (10, binding.TREEWY_F32),
+                 (4, f(0x13000000)), (6, f(0x15000000))):
+        args = list(ok)
+        args[i] = v
+        assert lib.treewy_deferred_flush(*args) == binding.TREEWY_EINVAL

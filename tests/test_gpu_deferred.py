@@ -1,0 +1,235 @@
+"""GPU parity of the deferred commit (treewy_commit_verify_deferred, treewy_deferred_flush):
+several decoding steps in a row with the committed state kept as scale * (S + logged rank-one
+terms), against the oracle stepping the same way (replay up to each step's accepted node,
+then a fresh verify of the next step's tree from there).
+
+Checked at every step: this step's O, U and gamma (max|x - oracle| / max|oracle| <= 1e-3 per
+head); the log header (length and emptying) against the rule it follows; and, after a flush,
+the written-back state against the oracle's committed state.
+"""
+
+import numpy as np
+import pytest
+
+from linear_attention_speculative_head_amd import inputs
+from parity import TOL, gather_heads, headwise_rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_attention_speculative_head_amd import binding
+    binding.lib()
+
+
+def run_steps(steps, Lmax, flush_at=()):
+    """GPU: a plain verify of step 0, then one deferred step per later step; flushes after
+    the steps listed.  Returns per-step host outputs, headers and the flushed states."""
+    import torch
+    from linear_attention_speculative_head_amd import binding, device
+    B, H = steps[0].B, steps[0].H
+    dls = [device.upload_layer(P.layers[0], P.dtype) for P in steps]
+    trees = [device.upload_tree(P) for P in steps]
+    outs = [device.alloc_outputs(B, H, P.N, fill=float("nan")) for P in steps]
+    log = device.alloc_log(B, H, Lmax)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S = dls[0].S0.clone()
+    d0 = dls[0]
+    binding.treewy_verify(S, d0.Q, d0.K, d0.V, d0.alpha, d0.beta, trees[0][0],
+                          outs[0].O, outs[0].U, outs[0].gamma, status=status)
+    res = [dict(O=outs[0].O.cpu().numpy(), U=outs[0].U.cpu().numpy())]
+    flushed = {}
+    for s in range(1, len(steps)):
+        prev, cur = outs[s - 1], outs[s]
+        dp, dc = dls[s - 1], dls[s]
+        si, so, li, lo = log.headers()
+        binding.treewy_commit_verify_deferred(S, log.U, log.K, si, so, li, lo, prev.U, dp.K,
+                                              prev.gamma, trees[s - 1][0], trees[s - 1][1],
+                                              dc.Q, dc.K, dc.V, dc.alpha, dc.beta, trees[s][0],
+                                              cur.O, cur.U, cur.gamma, status=status)
+        log.flip()
+        torch.cuda.synchronize()
+        r = dict(O=cur.O.cpu().numpy(), U=cur.U.cpu().numpy(), gamma=cur.gamma.cpu().numpy(),
+                 len=log.headers()[2].cpu().numpy().copy(), scale=log.headers()[0].cpu().numpy().copy(),
+                 S_raw=S.cpu().numpy().copy())
+        res.append(r)
+        if s in flush_at:
+            si, so, li, lo = log.headers()
+            binding.treewy_deferred_flush(S, log.U, log.K, si, so, li, lo, status=status)
+            log.flip()
+            torch.cuda.synchronize()
+            flushed[s] = S.cpu().numpy().copy()
+            assert (log.headers()[2].cpu().numpy() == 0).all()
+            assert (log.headers()[0].cpu().numpy() == 1).all()
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
+    return res, flushed
+
+
+def oracle_steps(steps):
+    """Per step: the oracle's outputs from the state committed up to the previous step, and
+    the state committed after each step."""
+    import oracle
+    B, H = steps[0].B, steps[0].H
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    S_ref = steps[0].layers[0].S0.copy()
+    outs, states = [], []
+    for P in steps:
+        L = P.layers[0]
+        layer = inputs.Layer(S0=S_ref, q=L.q, k=L.k, v=L.v, alpha=L.alpha, beta=L.beta)
+        r = oracle.batch(layer, P.parent, P.accepted, heads=heads, commit=True)
+        outs.append(r)
+        S_ref = r["S_new"].reshape(B, H, 128, 128).astype(np.float32)
+        states.append(r["S_new"].reshape(B, H, 128, 128))
+    return heads, outs, states
+
+
+def expected_lengths(steps, Lmax):
+    """The header rule: the accepted path's terms join the log when they fit (and the path
+    is short enough to stage with the next step: 4 nodes for N <= 4, else 8); otherwise the
+    log is emptied into S.  No accepted node leaves the log as it is."""
+    B = steps[0].B
+    lens = np.zeros(B, dtype=np.int64)
+    out = [None]
+    for s in range(1, len(steps)):
+        P_prev, P = steps[s - 1], steps[s]
+        stage = 4 if P.N <= 4 else 8
+        for b in range(B):
+            a = int(P_prev.accepted[b])
+            if a < 0:
+                continue
+            d = int(inputs.tree_depths(P_prev.parent[b])[a])
+            lens[b] = 0 if (lens[b] + d > Lmax or d > stage) else lens[b] + d
+        out.append(lens.copy())
+    return out
+
+
+@pytest.mark.parametrize("N,tree,Lmax,nsteps,seed", [
+    (4, "chain", 16, 6, 61),     # the configuration-1 chain: the log only grows
+    (4, "chain", 4, 7, 62),      # small log: appends and write-backs interleave
+    (6, (3, 2), 5, 7, 63),
+    (16, (5, 4), 8, 6, 64),      # 16-node trees
+    (3, (2, 2), 1, 6, 65),       # a one-term log
+])
+def test_deferred_steps(N, tree, Lmax, nsteps, seed):
+    say(f"[deferred] N={N} tree={tree} Lmax={Lmax} steps={nsteps}")
+    B, H = 5, 4
+    steps = [inputs.make_custom(seed * 10 + s, B=B, H=H, N=N, tree=tree) for s in range(nsteps)]
+    flush_at = (nsteps - 1,)
+    gpu, flushed = run_steps(steps, Lmax, flush_at=flush_at)
+    heads, ref, states = oracle_steps(steps)
+    want_len = expected_lengths(steps, Lmax)
+    worst = 0.0
+    for s in range(nsteps):
+        for key in ("O", "U"):
+            g = gather_heads(gpu[s][key], heads, "node").astype(np.float64)
+            e = headwise_rel(g, ref[s][key])
+            assert e.max() <= TOL, f"step {s} {key}: worst {e.max():.3e}"
+            worst = max(worst, float(e.max()))
+        if s > 0:
+            assert np.array_equal(gpu[s]["len"], want_len[s]), (s, gpu[s]["len"], want_len[s])
+    # after the last step's call the state stands for the commits of steps 0 .. nsteps - 2
+    S = flushed[nsteps - 1].reshape(B * H, -1).astype(np.float64)
+    e = headwise_rel(S, states[nsteps - 2].reshape(B * H, -1))
+    assert e.max() <= TOL, f"flushed state: worst {e.max():.3e}"
+    say(f"  worst O/U head-wise rel err {worst:.2e}, flushed state {e.max():.2e}")
+
+
+def test_deferred_matches_fused_path():
+    """The same steps through treewy_commit_verify (state written every step) and through
+    the deferred commit give the same outputs to the tolerance, and the same state after a
+    flush."""
+    import torch
+    from linear_attention_speculative_head_amd import binding, device
+    B, H, N = 4, 3, 4
+    steps = [inputs.make_custom(70 + s, B=B, H=H, N=N, tree="chain") for s in range(5)]
+    gpu, flushed = run_steps(steps, 16, flush_at=(4,))
+    dls = [device.upload_layer(P.layers[0], P.dtype) for P in steps]
+    trees = [device.upload_tree(P) for P in steps]
+    outs = [device.alloc_outputs(B, H, N) for _ in steps]
+    S = dls[0].S0.clone()
+    binding.treewy_verify(S, dls[0].Q, dls[0].K, dls[0].V, dls[0].alpha, dls[0].beta,
+                          trees[0][0], outs[0].O, outs[0].U, outs[0].gamma)
+    for s in range(1, 5):
+        binding.treewy_commit_verify(S, outs[s - 1].U, dls[s - 1].K, outs[s - 1].gamma,
+                                     trees[s - 1][0], trees[s - 1][1], dls[s].Q, dls[s].K,
+                                     dls[s].V, dls[s].alpha, dls[s].beta, trees[s][0],
+                                     outs[s].O, outs[s].U, outs[s].gamma)
+    torch.cuda.synchronize()
+    n = B * H
+    for s in range(1, 5):
+        f = outs[s].O.cpu().numpy().transpose(0, 2, 1, 3).reshape(n, -1).astype(np.float64)
+        d = gpu[s]["O"].transpose(0, 2, 1, 3).reshape(n, -1).astype(np.float64)
+        assert headwise_rel(d, f).max() <= TOL
+    e = headwise_rel(flushed[4].reshape(n, -1).astype(np.float64),
+                     S.cpu().numpy().reshape(n, -1).astype(np.float64))
+    assert e.max() <= TOL
+
+
+def test_deferred_rejects_unsupported_shapes():
+    import torch
+    from linear_attention_speculative_head_amd import binding, device
+    P = inputs.make_custom(80, B=2, H=2, N=20, tree=(5, 4))
+    d = device.upload_layer(P.layers[0], P.dtype)
+    par, acc = device.upload_tree(P)
+    o = device.alloc_outputs(2, 2, 20)
+    o2 = device.alloc_outputs(2, 2, 20)
+    log = device.alloc_log(2, 2, 8)
+    si, so, li, lo = log.headers()
+    with pytest.raises(binding.TreeWYError):
+        binding.treewy_commit_verify_deferred(d.S0, log.U, log.K, si, so, li, lo, o.U, d.K,
+                                              o.gamma, par, acc, d.Q, d.K, d.V, d.alpha,
+                                              d.beta, par, o2.O, o2.U, o2.gamma)
+
+
+def test_deferred_reports_bad_header():
+    """A log length outside [0, Lmax] is reported (and clamped, so nothing leaves the log)."""
+    import torch
+    from linear_attention_speculative_head_amd import binding, device
+    B, H, N = 3, 2, 4
+    P1 = inputs.make_custom(90, B=B, H=H, N=N, tree="chain")
+    P2 = inputs.make_custom(91, B=B, H=H, N=N, tree="chain")
+    d1, d2 = device.upload_layer(P1.layers[0], "bf16"), device.upload_layer(P2.layers[0], "bf16")
+    par1, acc1 = device.upload_tree(P1)
+    par2, _ = device.upload_tree(P2)
+    o1, o2 = device.alloc_outputs(B, H, N), device.alloc_outputs(B, H, N)
+    binding.treewy_verify(d1.S0, d1.Q, d1.K, d1.V, d1.alpha, d1.beta, par1, o1.O, o1.U, o1.gamma)
+    log = device.alloc_log(B, H, 4)
+    log.length[0].fill_(99)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    si, so, li, lo = log.headers()
+    binding.treewy_commit_verify_deferred(d1.S0, log.U, log.K, si, so, li, lo, o1.U, d1.K,
+                                          o1.gamma, par1, acc1, d2.Q, d2.K, d2.V, d2.alpha,
+                                          d2.beta, par2, o2.O, o2.U, o2.gamma, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == binding.TREEWY_ELOG
+
+
+def test_deferred_mixed_sizes_and_deep_paths():
+    """Node counts that change between steps: an 8-node chain accepted to its end cannot be
+    staged by a 3-node step (4 rows), so that step writes the state back."""
+    say("[deferred] mixed node counts, deep accepted paths")
+    B, H = 4, 3
+    sizes = (8, 3, 8, 3, 8, 4)
+    steps = []
+    for s, n in enumerate(sizes):
+        acc = np.full(B, n - 1, dtype=np.int32)
+        acc[1] = -1
+        acc[2] = min(1, n - 1)
+        steps.append(inputs.make_custom(100 + s, B=B, H=H, N=n, tree="chain", accepted=acc))
+    gpu, flushed = run_steps(steps, 16, flush_at=(len(sizes) - 1,))
+    heads, ref, states = oracle_steps(steps)
+    want_len = expected_lengths(steps, 16)
+    for s in range(len(sizes)):
+        for key in ("O", "U"):
+            g = gather_heads(gpu[s][key], heads, "node").astype(np.float64)
+            e = headwise_rel(g, ref[s][key])
+            assert e.max() <= TOL, f"step {s} {key}: worst {e.max():.3e}"
+        if s > 0:
+            assert np.array_equal(gpu[s]["len"], want_len[s]), (s, gpu[s]["len"], want_len[s])
+    S = flushed[len(sizes) - 1].reshape(B * H, -1).astype(np.float64)
+    e = headwise_rel(S, states[len(sizes) - 2].reshape(B * H, -1))
+    assert e.max() <= TOL
