@@ -247,6 +247,72 @@ def make_tree_shape(widths: Sequence[int], instance: int = 0, B: int = 32, H: in
     return P
 
 
+# ----------------------------------------------------------------------------- softmax layers
+
+# Softmax-attention layers of the modelled hybrids: head dimension 256, 2 key/value heads
+# (paper §2).  The pages do not give the query-head count; 8 query heads per key/value head
+# is this package's reading (grouped-query attention, query head hq reads key/value head
+# hq // G).
+ATTN_D = 256
+ATTN_HKV = 2
+ATTN_G = 8
+
+
+@dataclass
+class AttnProblem:
+    """One tree-verify pass of a softmax-attention layer: the committed cache, the draft
+    tokens' queries/keys/values and the tree.  Cache rows at or past a sequence's committed
+    length hold a large constant, so that reading them would show."""
+    B: int
+    Hkv: int
+    G: int
+    N: int
+    d: int
+    T_max: int
+    Kc: np.ndarray        # [B, Hkv, T_max, d] float32 (bf16-exact)
+    Vc: np.ndarray
+    ctx: np.ndarray       # [B] int32 committed length
+    Qd: np.ndarray        # [B, N, Hq, d]
+    Kd: np.ndarray        # [B, N, Hkv, d]
+    Vd: np.ndarray
+    parent: np.ndarray    # [B, N] int32
+    accepted: np.ndarray  # [B] int32
+
+    @property
+    def Hq(self) -> int:
+        return self.Hkv * self.G
+
+
+def make_attention_problem(seed: int, B: int, Hkv: int = ATTN_HKV, G: int = ATTN_G, N: int = 4,
+                           T_max: int = 256, ctx=None, tree="chain", d: int = ATTN_D,
+                           parent: Optional[np.ndarray] = None,
+                           accepted: Optional[np.ndarray] = None) -> AttnProblem:
+    """Entries ~ N(0, 1) rounded to bf16 (scores q.k / sqrt(d) then have unit spread)."""
+    rng = np.random.default_rng(np.random.SeedSequence([88, seed]))
+    if parent is None:
+        if tree == "chain":
+            parent = np.stack([chain_tree(N)] * B)
+        else:
+            parent = np.stack([random_tree(rng, N, tree[0], tree[1]) for _ in range(B)])
+    parent = np.ascontiguousarray(parent, dtype=np.int32).reshape(B, N)
+    if ctx is None:
+        ctx = rng.integers(0, T_max - N + 1, size=B)
+    ctx = np.ascontiguousarray(ctx, dtype=np.int32).reshape(B)
+    assert (ctx >= 0).all() and (ctx + N <= T_max).all()
+    if accepted is None:
+        accepted = rng.integers(-1, N, size=B)
+    accepted = np.ascontiguousarray(accepted, dtype=np.int32).reshape(B)
+    Hq = Hkv * G
+    f = lambda *s: round_bf16(rng.standard_normal(s, dtype=np.float32))
+    Kc, Vc = f(B, Hkv, T_max, d), f(B, Hkv, T_max, d)
+    for b in range(B):                   # rows past the committed prefix: a loud constant
+        Kc[b, :, ctx[b]:] = 64.0
+        Vc[b, :, ctx[b]:] = 4096.0
+    return AttnProblem(B=B, Hkv=Hkv, G=G, N=N, d=d, T_max=T_max, Kc=Kc, Vc=Vc, ctx=ctx,
+                       Qd=f(B, N, Hq, d), Kd=f(B, N, Hkv, d), Vd=f(B, N, Hkv, d),
+                       parent=parent, accepted=accepted)
+
+
 def make_custom(seed: int, B: int, H: int, N: int, dtype: str = "bf16",
                 parent: Optional[np.ndarray] = None, tree=(6, 4),
                 accepted: Optional[np.ndarray] = None, dk: int = D, dv: int = D) -> Problem:
