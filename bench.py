@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--deferred", type=int, default=0, metavar="LMAX",
                     help="steady state of the deferred commit with a log of LMAX terms "
                          "(treewy_commit_verify_deferred); 0 = off")
+    ap.add_argument("--attention", type=int, default=0, metavar="CTX",
+                    help="time the tree-aware softmax-attention verify instead (B=32, 2 KV heads "
+                         "x 8 query heads, head dim 256, the config-1 chain, CTX committed rows)")
     ap.add_argument("--separate", action="store_true",
                     help="time treewy_verify then treewy_commit (two launches per layer)")
     ap.add_argument("--snapshot", action="store_true",
@@ -121,6 +124,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.lib()
+    if args.attention:
+        print(json.dumps(run_attention(args)), flush=True)
+        return
     if args.sweep:
         rows = []
         for w in inputs.PAPER_TREE_SHAPES:
@@ -409,6 +415,81 @@ def run(args, mode, wl):
     del pool
     torch.cuda.empty_cache()
     return line
+
+
+def run_attention(args):
+    """The softmax layers' half of a tree verify pass: one treewy_tree_attention per step over
+    rotated instances of a B=32 batch (2 KV heads x 8 query heads, head dim 256, a chain of 4
+    draft tokens) with args.attention committed cache rows per sequence."""
+    import torch
+    from linear_attention_speculative_head_amd import binding, inputs
+    B, Hkv, G, N, ctxn = 32, inputs.ATTN_HKV, inputs.ATTN_G, 4, args.attention
+    T = ctxn + 64
+    per = B * Hkv * T * 256 * 2 * 2
+    n_inst = min(32, max(1, math.ceil(args.pool_gib * 2 ** 30 / per)))
+    log(f"[bench] tree attention: B={B} Hkv={Hkv} G={G} N={N} ctx={ctxn}; {n_inst} instance(s), "
+        f"{per * n_inst / 2 ** 30:.2f} GiB")
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16).contiguous()
+    pool = []
+    for i in range(n_inst):
+        rng = np.random.default_rng(np.random.SeedSequence([3000, i]))
+        # the cache drawn on the device (a plain normal fill): only its shape matters here
+        Kc = torch.randn((B, Hkv, T, 256), device="cuda").to(torch.bfloat16)
+        Vc = torch.randn((B, Hkv, T, 256), device="cuda").to(torch.bfloat16)
+        P = inputs.make_attention_problem(3000 + i, B=B, Hkv=Hkv, G=G, N=N, T_max=N + 1,
+                                          ctx=np.zeros(B), tree="chain")
+        pool.append(dict(Kc=Kc, Vc=Vc, ctx=torch.full((B,), ctxn, dtype=torch.int32, device="cuda"),
+                         Qd=bf(P.Qd), Kd=bf(P.Kd), Vd=bf(P.Vd),
+                         parent=torch.from_numpy(P.parent).cuda()))
+        del rng
+    O = torch.empty((B, N, Hkv * G, 256), device="cuda")
+    ws = torch.empty(binding.treewy_tree_attention_workspace(B, Hkv, G, N, T), dtype=torch.uint8,
+                     device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        x = pool[i]
+        binding.treewy_tree_attention(x["Kc"], x["Vc"], x["ctx"], x["Qd"], x["Kd"], x["Vd"],
+                                      x["parent"], O, ws, status)
+
+    for s in range(args.warmup):
+        step(s % n_inst)
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for s in range(K):
+        step((args.warmup + s) % n_inst)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for s in range(K):
+        ev[s][0].record()
+        step((args.warmup + s) % n_inst)
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # algorithmic bytes: the committed cache rows read once, the draft tokens' q/k/v read, O
+    # written (the split partials are the kernel's own traffic, not the method's)
+    nbytes = (B * Hkv * ctxn * 256 * 2 * 2 + B * N * (Hkv * G + 2 * Hkv) * 256 * 2
+              + B * N * Hkv * G * 256 * 4)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] tree attention: {wall * 1e6 / K:.1f} us/step, {ms * 1e3:.1f} us per call "
+        f"(events), {achieved:.0f} GB/s algorithmic")
+    return {
+        "metric": "tree attention verify draft-nodes*query-heads/sec",
+        "value": B * N * Hkv * G * K / wall, "unit": "nodes*heads/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, f32 accumulate",
+        "data": "synthetic (seeded queries/keys of the draft; normal-filled cache)",
+        "config": {"workload": f"tree attention: B={B}, {Hkv} KV heads x {G} query heads, "
+                               f"head dim 256, chain of {N}, {ctxn} committed rows",
+                   "instances_rotated": n_inst},
+        "roofline": {"bound": "hbm", "kernel": "treewy_tree_attention", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": nbytes, "launch_us": ms * 1e3},
+        "cpu_baseline": None,
+    }
 
 
 def measured_traffic(cfg: int, entry: str):

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TREEWY_VERSION 3
+#define TREEWY_VERSION 4
 
 enum {
     TREEWY_OK = 0,
@@ -59,7 +59,8 @@ enum {
     TREEWY_EHIP = 2,
     TREEWY_ETREE = 3,
     TREEWY_EACCEPT = 4,
-    TREEWY_ELOG = 5
+    TREEWY_ELOG = 5,
+    TREEWY_ECTX = 6
 };
 
 enum { TREEWY_F32 = 0, TREEWY_BF16 = 1 };
@@ -189,6 +190,48 @@ int treewy_verify_snapshot(const float* S0, const void* Q, const void* K, const 
  */
 int treewy_commit_snapshot(float* S, const float* Snap, const int32_t* accepted,
                            int B, int H, int N, int32_t* status, void* stream);
+
+/*
+ * Tree-aware softmax-attention verify: the softmax layers' half of a tree verify pass (the
+ * technical review "TreeWY: Removing the Memory Wall in Speculative Decoding for Gated
+ * DeltaNet Hybrids", §2.3 "KV cache attention", Eq. (2); tree-structured drafting, §2.2).
+ * For every sequence b, draft node t and query head hq:
+ *   O[b][t][hq] = softmax(q K^T / 16) V,  q = Qd[b][t][hq],
+ * over the keys/values of head hq / G: the committed cache rows 0 .. ctx[b]-1 followed by the
+ * draft tokens that are ancestors-or-self of t (the GDN path's ancestor sets).
+ * Head dimension 256 (the modelled softmax layers', paper §2), bf16 inputs only.
+ *   Kc, Vc   [B, Hkv, T_max, 256] bf16   committed cache (rows >= ctx[b] are never read)
+ *   ctx      [B] int32                  committed lengths, 0 <= ctx[b] <= T_max
+ *   Qd       [B, N, Hkv*G, 256] bf16    draft queries (query head hq reads KV head hq / G)
+ *   Kd, Vd   [B, N, Hkv, 256] bf16      draft keys and values
+ *   parent   [B, N] int32               the draft tree, as for treewy_verify
+ *   O        [B, N, Hkv*G, 256] float32
+ *   workspace  device scratch of at least treewy_tree_attention_workspace(B, Hkv, G, N, T_max)
+ *              bytes, owned by the caller; contents need no initialisation and are not kept.
+ * 1 <= N <= 64, B, Hkv, G >= 1.  TREEWY_EINVAL for bad sizes or a short workspace; on
+ * `status`: TREEWY_ETREE for a malformed parent, TREEWY_ECTX for ctx outside [0, T_max].
+ */
+int treewy_tree_attention(const void* Kc, const void* Vc, const int32_t* ctx, int T_max,
+                          const void* Qd, const void* Kd, const void* Vd,
+                          const int32_t* parent, int B, int Hkv, int G, int N, float* O,
+                          void* workspace, size_t workspace_bytes, int32_t* status,
+                          void* stream);
+
+/* Bytes of workspace treewy_tree_attention needs for these sizes (0 for invalid sizes). */
+size_t treewy_tree_attention_workspace(int B, int Hkv, int G, int N, int T_max);
+
+/*
+ * Cache commit of the softmax layers: the accepted node's root-to-node path (keys and values
+ * of every KV head) is appended after each sequence's committed rows, rejected branches are
+ * dropped (review page §2.3: rejected drafts are discarded, no recomputation), and
+ * ctx_out[b] = ctx_in[b] + depth(accepted[b]).  accepted[b] = -1 appends nothing.
+ * ctx_in and ctx_out must not overlap.  On `status`: TREEWY_EACCEPT, TREEWY_ETREE, and
+ * TREEWY_ECTX when the path would not fit in T_max rows (that sequence is left unchanged).
+ */
+int treewy_kv_commit(void* Kc, void* Vc, const int32_t* ctx_in, int32_t* ctx_out, int T_max,
+                     const void* Kd, const void* Vd, const int32_t* parent,
+                     const int32_t* accepted, int B, int Hkv, int N, int32_t* status,
+                     void* stream);
 
 /* Static, NUL-terminated description of an error code (never NULL). */
 const char* treewy_strerror(int code);

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libtreewy.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "treewy.h")
 
 TREEWY_OK, TREEWY_EINVAL, TREEWY_EHIP, TREEWY_ETREE, TREEWY_EACCEPT, TREEWY_ELOG = 0, 1, 2, 3, 4, 5
+TREEWY_ECTX = 6
 TREEWY_F32, TREEWY_BF16 = 0, 1
 D = 128
 
@@ -51,12 +52,18 @@ def lib():
         L.treewy_commit_verify_deferred.argtypes = ([P] * 7 + [I] + [P] * 5 + [I] + [P] * 6 +
                                                     [I] * 4 + [P] * 7)
         L.treewy_deferred_flush.argtypes = [P] * 7 + [I] * 4 + [P, P]
+        L.treewy_tree_attention.argtypes = ([P, P, P, I, P, P, P, P, I, I, I, I, P, P,
+                                             ctypes.c_size_t, P, P])
+        L.treewy_tree_attention_workspace.argtypes = [I] * 5
+        L.treewy_tree_attention_workspace.restype = ctypes.c_size_t
+        L.treewy_kv_commit.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, P, P]
         L.treewy_strerror.argtypes = [I]
         L.treewy_strerror.restype = ctypes.c_char_p
         L.treewy_version.argtypes = []
         for f in ("treewy_verify", "treewy_commit", "treewy_verify_snapshot",
                   "treewy_commit_snapshot", "treewy_commit_verify",
-                  "treewy_commit_verify_deferred", "treewy_deferred_flush", "treewy_version"):
+                  "treewy_commit_verify_deferred", "treewy_deferred_flush",
+                  "treewy_tree_attention", "treewy_kv_commit", "treewy_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -248,6 +255,61 @@ def treewy_deferred_flush(S, logU, logK, scale_in, scale_out, len_in, len_out, s
                                      _ptr(scale_out), _ptr(len_in), _ptr(len_out), Lmax, B, H,
                                      TREEWY_BF16, _ptr(status), _stream(stream))
     _rc(rc, "treewy_deferred_flush")
+
+
+def treewy_tree_attention_workspace(B: int, Hkv: int, G: int, N: int, T_max: int) -> int:
+    return int(lib().treewy_tree_attention_workspace(B, Hkv, G, N, T_max))
+
+
+def treewy_tree_attention(Kc, Vc, ctx, Qd, Kd, Vd, parent, O, workspace, status=None,
+                          stream=None):
+    """Enqueue the tree-aware softmax-attention verify (bf16 inputs, head dim 256)."""
+    import torch
+    B, Hkv, T_max, _ = Kc.shape
+    N, Hq = Qd.shape[1], Qd.shape[2]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    G = Hq // Hkv
+    dev = Kc.device
+    bf = (torch.bfloat16,)
+    _check(Kc, "Kc", (B, Hkv, T_max, 256), bf, dev)
+    _check(Vc, "Vc", (B, Hkv, T_max, 256), bf, dev)
+    _check(ctx, "ctx", (B,), (torch.int32,), dev)
+    _check(Qd, "Qd", (B, N, Hq, 256), bf, dev)
+    _check(Kd, "Kd", (B, N, Hkv, 256), bf, dev)
+    _check(Vd, "Vd", (B, N, Hkv, 256), bf, dev)
+    _check(parent, "parent", (B, N), (torch.int32,), dev)
+    _check(O, "O", (B, N, Hq, 256), (torch.float32,), dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    rc = lib().treewy_tree_attention(_ptr(Kc), _ptr(Vc), _ptr(ctx), T_max, _ptr(Qd), _ptr(Kd),
+                                     _ptr(Vd), _ptr(parent), B, Hkv, G, N, _ptr(O),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _ptr(status), _stream(stream))
+    _rc(rc, "treewy_tree_attention")
+
+
+def treewy_kv_commit(Kc, Vc, ctx_in, ctx_out, Kd, Vd, parent, accepted, status=None, stream=None):
+    """Enqueue the softmax layers' cache commit of the accepted path."""
+    import torch
+    B, Hkv, T_max, _ = Kc.shape
+    N = Kd.shape[1]
+    dev = Kc.device
+    bf = (torch.bfloat16,)
+    _check(Kc, "Kc", (B, Hkv, T_max, 256), bf, dev)
+    _check(Vc, "Vc", (B, Hkv, T_max, 256), bf, dev)
+    _check(ctx_in, "ctx_in", (B,), (torch.int32,), dev)
+    _check(ctx_out, "ctx_out", (B,), (torch.int32,), dev)
+    _check(Kd, "Kd", (B, N, Hkv, 256), bf, dev)
+    _check(Vd, "Vd", (B, N, Hkv, 256), bf, dev)
+    _check(parent, "parent", (B, N), (torch.int32,), dev)
+    _check(accepted, "accepted", (B,), (torch.int32,), dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    rc = lib().treewy_kv_commit(_ptr(Kc), _ptr(Vc), _ptr(ctx_in), _ptr(ctx_out), T_max,
+                                _ptr(Kd), _ptr(Vd), _ptr(parent), _ptr(accepted), B, Hkv, N,
+                                _ptr(status), _stream(stream))
+    _rc(rc, "treewy_kv_commit")
 
 
 def treewy_verify_snapshot(S0, Q, K, V, alpha, beta, parent, O, Snap, status=None, stream=None):

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtreewy.so")
-SOURCES = ["abi.hip", "verify.hip", "commit.hip", "snapshot.hip"]
+SOURCES = ["abi.hip", "verify.hip", "commit.hip", "snapshot.hip", "attention.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -168,6 +168,51 @@ int treewy_commit_snapshot(float* S, const float* Snap, const int32_t* accepted,
     return map_hip(treewy::launch_commit_snapshot(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t treewy_tree_attention_workspace(int B, int Hkv, int G, int N, int T_max)
+{
+    if (B < 1 || Hkv < 1 || G < 1 || N < 1 || N > 64 || T_max < 1) return 0;
+    return treewy::attention_workspace_bytes(B, Hkv, G, N, T_max);
+}
+
+namespace {
+
+bool attn_sizes_ok(int B, int Hkv, int G, int N, int T_max) {
+    if (B < 1 || Hkv < 1 || G < 1 || N < 1 || N > 64 || T_max < 1) return false;
+    const uint64_t bk = static_cast<uint64_t>(B) * Hkv;
+    const uint64_t nq = static_cast<uint64_t>(N) * G;
+    // grid limits (query blocks and B*Hkv in y/z) and 32-bit element offsets per head row
+    return bk <= 65535u && (nq + 31) / 32 <= 65535u &&
+           static_cast<uint64_t>(T_max) * 256u * 2u <= 0x7fffffffull;
+}
+
+}  // namespace
+
+int treewy_tree_attention(const void* Kc, const void* Vc, const int32_t* ctx, int T_max,
+                          const void* Qd, const void* Kd, const void* Vd, const int32_t* parent,
+                          int B, int Hkv, int G, int N, float* O, void* workspace,
+                          size_t workspace_bytes, int32_t* status, void* stream)
+{
+    if (!Kc || !Vc || !ctx || !Qd || !Kd || !Vd || !parent || !O || !workspace) return TREEWY_EINVAL;
+    if (!attn_sizes_ok(B, Hkv, G, N, T_max)) return TREEWY_EINVAL;
+    if (workspace_bytes < treewy::attention_workspace_bytes(B, Hkv, G, N, T_max)) return TREEWY_EINVAL;
+    treewy::AttentionArgs a{Kc, Vc, ctx, T_max, Qd, Kd, Vd, parent, B, Hkv, G, N, O, workspace,
+                            status};
+    return map_hip(treewy::launch_tree_attention(a, static_cast<hipStream_t>(stream)));
+}
+
+int treewy_kv_commit(void* Kc, void* Vc, const int32_t* ctx_in, int32_t* ctx_out, int T_max,
+                     const void* Kd, const void* Vd, const int32_t* parent,
+                     const int32_t* accepted, int B, int Hkv, int N, int32_t* status, void* stream)
+{
+    if (!Kc || !Vc || !ctx_in || !ctx_out || !Kd || !Vd || !parent || !accepted) return TREEWY_EINVAL;
+    if (!attn_sizes_ok(B, Hkv, 1, N, T_max)) return TREEWY_EINVAL;
+    if (overlap({ctx_in, static_cast<size_t>(B) * 4}, {ctx_out, static_cast<size_t>(B) * 4}))
+        return TREEWY_EINVAL;
+    treewy::KvCommitArgs a{Kc, Vc, ctx_in, ctx_out, T_max, Kd, Vd, parent, accepted, B, Hkv, N,
+                           status};
+    return map_hip(treewy::launch_kv_commit(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* treewy_strerror(int code)
 {
     switch (code) {
@@ -177,6 +222,7 @@ const char* treewy_strerror(int code)
         case TREEWY_ETREE: return "malformed draft tree (parent outside [-1, t-1])";
         case TREEWY_EACCEPT: return "accepted node outside [-1, N-1]";
         case TREEWY_ELOG: return "deferred-commit log length outside [0, Lmax]";
+        case TREEWY_ECTX: return "committed cache length outside [0, T_max] (or a path that does not fit)";
         default: return "unknown error code";
     }
 }

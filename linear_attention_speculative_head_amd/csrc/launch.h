@@ -67,6 +67,40 @@ struct DeferArgs {
     int Lmax;
 };
 
+// the tree-aware softmax-attention verify and its cache commit
+struct AttentionArgs {
+    const void* Kc;
+    const void* Vc;
+    const int32_t* ctx;
+    int T_max;
+    const void* Qd;
+    const void* Kd;
+    const void* Vd;
+    const int32_t* parent;
+    int B, Hkv, G, N;
+    float* O;
+    void* work;
+    int32_t* status;
+};
+
+struct KvCommitArgs {
+    void* Kc;
+    void* Vc;
+    const int32_t* ctx_in;
+    int32_t* ctx_out;
+    int T_max;
+    const void* Kd;
+    const void* Vd;
+    const int32_t* parent;
+    const int32_t* accepted;
+    int B, Hkv, N;
+    int32_t* status;
+};
+
+size_t attention_workspace_bytes(int B, int Hkv, int G, int N, int T_max);
+hipError_t launch_tree_attention(const AttentionArgs& a, hipStream_t stream);
+hipError_t launch_kv_commit(const KvCommitArgs& a, hipStream_t stream);
+
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
 hipError_t launch_verify_snapshot(const SnapshotVerifyArgs& a, hipStream_t stream);

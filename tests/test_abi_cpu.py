@@ -22,15 +22,16 @@ def test_exports_every_header_symbol(lib):
     assert set(names) == {"treewy_verify", "treewy_commit", "treewy_verify_snapshot",
                           "treewy_commit_snapshot", "treewy_commit_verify",
                           "treewy_commit_verify_deferred", "treewy_deferred_flush",
-                          "treewy_strerror", "treewy_version"}
+                          "treewy_tree_attention", "treewy_tree_attention_workspace",
+                          "treewy_kv_commit", "treewy_strerror", "treewy_version"}
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_strerror(lib):
-    assert lib.treewy_version() == 3
-    for code in range(6):
+    assert lib.treewy_version() == 4
+    for code in range(7):
         assert lib.treewy_strerror(code)
     assert lib.treewy_strerror(99) == b"unknown error code"
 
@@ -138,3 +139,37 @@ def test_deferred_flush_rejects(lib):
         args = list(ok)
         args[i] = v
         assert lib.treewy_deferred_flush(*args) == binding.TREEWY_EINVAL
+
+
+def test_attention_workspace_size(lib):
+    # 16 splits of 512 rows x 1 block of 32 queries x B*Hkv, (32*256 + 64) floats each
+    assert lib.treewy_tree_attention_workspace(2, 2, 8, 4, 8192) == 2 * 2 * 1 * 16 * (32 * 256 + 64) * 4
+    assert lib.treewy_tree_attention_workspace(1, 1, 8, 16, 100) == 1 * 1 * 4 * 1 * (32 * 256 + 64) * 4
+    assert lib.treewy_tree_attention_workspace(0, 2, 8, 4, 64) == 0
+    assert lib.treewy_tree_attention_workspace(1, 2, 8, 65, 64) == 0
+
+
+def attn_args(**kw):
+    f = lambda x: ctypes.c_void_p(x)
+    a = dict(Kc=f(0x1000000), Vc=f(0x2000000), ctx=f(0x3000000), T=64, Qd=f(0x4000000),
+             Kd=f(0x5000000), Vd=f(0x6000000), parent=f(0x7000000), B=2, Hkv=2, G=8, N=4,
+             O=f(0x8000000), ws=f(0x9000000), wsb=1 << 30, status=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(Kc=None), dict(ctx=None), dict(Qd=None), dict(O=None),
+                                 dict(ws=None), dict(wsb=16), dict(N=0), dict(N=65), dict(G=0),
+                                 dict(Hkv=0), dict(T=0), dict(B=70000)])
+def test_tree_attention_rejects(lib, bad):
+    assert lib.treewy_tree_attention(*attn_args(**bad)) == binding.TREEWY_EINVAL
+
+
+def test_kv_commit_rejects(lib):
+    f = lambda x: ctypes.c_void_p(x)
+    ok = [f(0x1000000), f(0x2000000), f(0x3000000), f(0x3100000), 64, f(0x5000000),
+          f(0x6000000), f(0x7000000), f(0x7100000), 2, 2, 4, None, None]
+    for i, v in ((0, None), (2, None), (3, f(0x3000000)), (4, 0), (11, 65), (8, None)):
+        args = list(ok)
+        args[i] = v
+        assert lib.treewy_kv_commit(*args) == binding.TREEWY_EINVAL
