@@ -5,14 +5,21 @@
 // attention", Eq. (2), and §2.2 on tree-structured drafting), with the ancestor sets the GDN
 // path uses.  Head dimension 256; query head hq reads key/value head hq / G.
 //
-// Split over the cache (the HBM stream): one wave per (sequence, key/value head, block of 32
-// queries, 512 cache rows).  It keeps the 32 queries in registers as MFMA fragments and walks
-// its rows 32 at a time: keys and values HBM -> LDS (global_load_lds_dwordx4), scores
-// S = Q K^T on the matrix cores (bf16 inputs, fp32 accumulation), an online softmax in base
-// 2, P = exp2(S - m) split into bf16 hi + lo (|P - hi - lo| <= 2^-18 P) and O += P V on the
-// matrix cores, rescaled as the running maximum moves.  Its partial (O unnormalised, the row
-// maxima m, the row sums l) goes to a workspace.  A second kernel merges the partials of each
-// query, adds the draft keys it may see (at most 64, walked from the tree), and normalises.
+// Split over the cache (the HBM stream): one workgroup per (sequence, key/value head, block of
+// 32 queries, range of cache rows), the ranges sized at launch so that about four workgroups
+// per compute unit cover the batch (few splits keep the partials' traffic small).  It keeps the 32 queries in registers as MFMA fragments and walks
+// its rows 32 at a time, keys and values HBM -> LDS (global_load_lds_dwordx4) in two stages so
+// that the next tile's keys stream in while this tile's values are used and the next tile's
+// values while the next scores are formed.  Scores are formed transposed, S^T = K Q^T (bf16
+// inputs, fp32 accumulation on the matrix cores), so that each lane holds one query's scores
+// for 8 cache rows: exactly the B operand the product O^T += V^T P^T needs, so P never leaves
+// the registers; it is split into bf16 hi + lo (|P - hi - lo| <= 2^-16 P).  V^T comes from LDS
+// with the transposing read of gfx950 (ds_read_b64_tr_b16).  The online softmax (base 2)
+// rescales lazily: the running maximum moves only when a score exceeds it by more than 8, so
+// P stays below 2^8 and the accumulators are touched only when the maximum really moves; the
+// scale cancels in the final normalisation.  The partial (O unnormalised, the row maxima m,
+// the row sums l) goes to a workspace.  A second kernel merges the partials of each query,
+// adds the draft keys it may see (at most 64, walked from the tree), and normalises.
 
 #include "device_common.h"
 #include "launch.h"
@@ -22,15 +29,26 @@ namespace treewy {
 namespace {
 
 constexpr int DA = 256;                     // head dimension
-constexpr int kQB = 32;                     // queries per block (two MFMA row tiles)
+constexpr int kQB = 32;                     // queries per block (two MFMA column tiles)
 constexpr int kTile = 32;                   // cache rows per step
-constexpr int kSplit = 512;                 // cache rows per wave
+constexpr int kTargetBlocks = 1024;         // split the cache until about this many workgroups
+constexpr int kMinSplit = 256;              // but keep at least this many rows per split
 constexpr int kPartFloats = kQB * DA + 2 * kQB;   // O [32][256], m [32], l [32]
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;               // rescale when a score passes the maximum by this
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// s_waitcnt immediates: vector-memory count at most 8 (one stage of a tile still in flight)
+// or 0; LDS/scalar and export counts left free.
+constexpr int kWaitVm8 = 8 | (7 << 4) | (15 << 8);
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+constexpr int kWaitLgkm0 = 0xC07F;
 
 // One HBM -> LDS load of 16 bytes per lane (lane l lands at lds + 16 l), from a scalar base and
 // a 32-bit lane offset.  M0 holds the LDS destination and is restored; the caller waits on
@@ -53,20 +71,41 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
         : "memory");
 }
 
+// This wave's half of 32 rows kk .. kk + 31 of one cache (wave w: rows 16 w .. 16 w + 15;
+// rows at or past k1 fetch row kk again, their scores are masked) into LDS: row r is 512
+// bytes, its 16-byte chunk c stored at position c ^ (r % 16).  Two rows per load, eight loads.
+__device__ __forceinline__ void load_half(const uint16_t* base, int kk, int k1, uint32_t lds,
+                                          int lane, int w) {
+    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;
+#pragma unroll
+    for (int i = 0; i < kTile / 4; ++i) {
+        const uint32_t r = 16u * w + 2u * i + hl;
+        const uint32_t row = kk + r < static_cast<uint32_t>(k1) ? kk + r : kk;
+        dma16(base, row * (DA * 2u) + 16u * (ch ^ (r & 15u)), lds + 8192u * w + 1024u * i);
+    }
+}
+
 __device__ __forceinline__ int clamp_ctx(int c, int T_max) { return c < 0 ? 0 : (c > T_max ? T_max : c); }
 
-// grid (splits, query blocks, B * Hkv), one wave
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+}
+
+// grid (splits, query blocks, B * Hkv), two waves sharing each tile of keys and values: wave w
+// owns queries 16 w .. 16 w + 15 of the block and loads rows 16 w .. 16 w + 15 of every tile.
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_partial_kernel(const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vc,
                          const int32_t* __restrict__ ctx, int T_max,
-                         const uint16_t* __restrict__ Qd, int Hkv, int G, int N,
+                         const uint16_t* __restrict__ Qd, int Hkv, int G, int N, int rows,
                          float* __restrict__ work)
 {
-    __shared__ __align__(16) uint16_t sK[kTile * DA];     // rows 512 B, chunk c at c ^ (r % 16)
-    __shared__ __align__(16) uint16_t sV[kTile * DA];     // rows 512 B, plain
-    __shared__ __align__(16) uint16_t sP[2][kQB * kTile]; // P hi / lo [32 q][32 rows]
+    __shared__ __align__(16) uint16_t sK[kTile * DA];
+    __shared__ __align__(16) uint16_t sV[kTile * DA];
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int split = blockIdx.x;
@@ -77,267 +116,294 @@ void attn_partial_kernel(const uint16_t* __restrict__ Kc, const uint16_t* __rest
     const int Hq = Hkv * G;
     const int Nq = N * G;
     const int c = clamp_ctx(ctx[b], T_max);
-    const int k0 = split * kSplit;
-    if (k0 >= c) return;                        // nothing of this sequence's cache here
-    const int k1 = k0 + kSplit < c ? k0 + kSplit : c;
+    const int k0 = split * rows;
+    if (k0 >= c) return;                        // nothing of this sequence's cache here (both waves)
+    const int k1 = c - k0 > rows ? k0 + rows : c;
+    const bool active = qb * kQB + 16 * w < Nq; // wave-uniform: has at least one query
 
-    // the block's queries as A fragments: lane L holds row L % 16 of tile qt, dims
+    const uint16_t* Kb = Kc + static_cast<size_t>(bk) * T_max * DA;
+    const uint16_t* Vb = Vc + static_cast<size_t>(bk) * T_max * DA;
+    const uint32_t ldsK = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sK));
+    const uint32_t ldsV = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sV));
+    load_half(Kb, k0, k1, ldsK, lane, w);
+    load_half(Vb, k0, k1, ldsV, lane, w);
+
+    // this wave's queries as B fragments: lane L holds query 16 w + L % 16 of the block, dims
     // 32 kb + 8 (L / 16) .. +7
-    bf16x8_t qf[2][8];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const int qi = qb * kQB + 16 * qt + col;
+    bf16x8_t qf[8];
+    {
+        const int qi = qb * kQB + 16 * w + col;
         const bool ok = qi < Nq;
         const int t = ok ? qi / G : 0;
         const int hq = kvh * G + (ok ? qi - t * G : 0);
         const uint16_t* qrow = Qd + (static_cast<size_t>(b * N + t) * Hq + hq) * DA;
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            u32x4_t w = {0u, 0u, 0u, 0u};
-            if (ok) w = *reinterpret_cast<const u32x4_t*>(qrow + 32 * kb + 8 * grp);
-            qf[qt][kb] = __builtin_bit_cast(bf16x8_t, w);
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (ok) v = *reinterpret_cast<const u32x4_t*>(qrow + 32 * kb + 8 * grp);
+            qf[kb] = __builtin_bit_cast(bf16x8_t, v);
         }
     }
 
-    f32x4_t acc[2][16];                         // O tiles: lane: dim 16 dt + L % 16, rows 4 grp + i
+    f32x4_t acc[16];                            // O^T tiles: lane: query 16 w + L % 16,
+                                                // dims 16 dt + 4 (L / 16) + i
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int dt = 0; dt < 16; ++dt) acc[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m[2][4], l[2][4];                     // per row 4 grp + i of tile qt (base-2 domain)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { m[qt][i] = -INFINITY; l[qt][i] = 0.f; }
-
-    const uint16_t* Kb = Kc + static_cast<size_t>(bk) * T_max * DA;
-    const uint16_t* Vb = Vc + static_cast<size_t>(bk) * T_max * DA;
-    const uint32_t ldsK = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sK));
-    const uint32_t ldsV = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sV));
+    for (int dt = 0; dt < 16; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;                        // running maximum of this lane's query
+    float l = 0.f;                              // this lane's share of its row sum
     const float sscale = kLog2e / 16.0f;        // 1 / sqrt(256), in base 2
-    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
-    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;
+
+    // transposing V read: lane (g, i) supplies row 4 g + i / 4 (+16), dims 4 (i % 4) .. +3 of
+    // the dim tile; it receives dim i of rows 4 g + j (+16), j = 0..3
+    const int vrow = 4 * grp + (col >> 2);
+    const uint32_t vsub = 8u * (col & 1);
+    const uint32_t vhalf = (col & 3) >> 1;
 
     for (int kk = k0; kk < k1; kk += kTile) {
-        // rows kk .. kk + 31 (past k1: row kk again, masked below) -> LDS, two rows per load
-        __builtin_amdgcn_s_waitcnt(0xC07F);     // every LDS read of the last step is done
-#pragma unroll
-        for (int i = 0; i < kTile / 2; ++i) {
-            const uint32_t r = 2u * i + hl;
-            const uint32_t row = kk + r < static_cast<uint32_t>(k1) ? kk + r : kk;
-            dma16(Kb, row * (DA * 2u) + 16u * (ch ^ (r & 15u)), ldsK + 1024u * i);
-            dma16(Vb, row * (DA * 2u) + 16u * ch, ldsV + 1024u * i);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
+        const bool more = kk + kTile < k1;
+        // this tile's keys: this wave's loads landed (its value loads may remain), then the
+        // other wave's
+        __builtin_amdgcn_s_waitcnt(kWaitVm8);
+        __syncthreads();
 
-        // scores: lane holds row kk + 16 kt + L % 16 for query rows 4 grp + i of tile qt
-        f32x4_t s[2][2];
+        f32x4_t st[2];                          // S^T: query 16 w + L % 16, rows kk + 16 kt + 4 (L / 16) + i
+        if (active) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            const int r = 16 * kt + col;
-            bf16x8_t kf[8];
+            for (int kt = 0; kt < 2; ++kt) {
+                const int r = 16 * kt + col;
+                bf16x8_t kf[8];
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) {
-                const int c16 = (4 * kb + grp) ^ (r & 15);
-                kf[kb] = __builtin_bit_cast(bf16x8_t,
-                                            *reinterpret_cast<const u32x4_t*>(sK + r * DA + 8 * c16));
-            }
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
+                for (int kb = 0; kb < 8; ++kb) {
+                    const int c16 = (4 * kb + grp) ^ col;
+                    kf[kb] = __builtin_bit_cast(
+                        bf16x8_t, *reinterpret_cast<const u32x4_t*>(sK + r * DA + 8 * c16));
+                }
                 f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < 8; ++kb)
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[qt][kb], kf[kb], a, 0, 0, 0);
-                const bool live = kk + r < k1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[qt][kt][i] = live ? a[i] * sscale : -INFINITY;
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qf[kb], a, 0, 0, 0);
+                st[kt] = a;
             }
         }
+        // both waves are done with the keys: the next ones stream in during this tile
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __syncthreads();
+        if (more) load_half(Kb, kk + kTile, k1, ldsK, lane, w);
 
-        // online softmax per query row: maxima and sums over the 16 lanes of a group
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float mx = fmaxf(s[qt][0][i], s[qt][1][i]);
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-                const float mn = fmaxf(m[qt][i], mx);          // finite: row kk is live
-                const float alpha = __builtin_amdgcn_exp2f(m[qt][i] - mn);
-                const float p0 = __builtin_amdgcn_exp2f(s[qt][0][i] - mn);
-                const float p1 = __builtin_amdgcn_exp2f(s[qt][1][i] - mn);
-                s[qt][0][i] = p0;
-                s[qt][1][i] = p1;
-                float sum = p0 + p1;
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o);
-                l[qt][i] = l[qt][i] * alpha + sum;
-                m[qt][i] = mn;
-#pragma unroll
-                for (int dt = 0; dt < 16; ++dt) acc[qt][dt][i] *= alpha;
-            }
-        }
-
-        // P -> LDS as bf16 hi and lo [query][row], then back as A fragments (row L % 16,
-        // rows of the cache 8 (L / 16) .. +7)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        bf16x8_t ph, pl;
+        if (active) {
+            // scores, masks and the tile maximum of each query
+            float v = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = s[qt][kt][i];
-                    const __bf16 ph = static_cast<__bf16>(p);
-                    const __bf16 pl = static_cast<__bf16>(p - static_cast<float>(ph));
-                    const int q = 16 * qt + 4 * grp + i;
-                    const int r = 16 * kt + col;
-                    sP[0][q * kTile + r] = __builtin_bit_cast(uint16_t, ph);
-                    sP[1][q * kTile + r] = __builtin_bit_cast(uint16_t, pl);
+                    const bool live = kk + 16 * kt + 4 * grp + i < k1;
+                    const float sc = live ? st[kt][i] * sscale : -INFINITY;
+                    st[kt][i] = sc;
+                    v = fmaxf(v, sc);
                 }
-        bf16x8_t pa[2][2];                      // [hi/lo][qt]
+            v = fmaxf(v, __shfl_xor(v, 16));
+            v = fmaxf(v, __shfl_xor(v, 32));    // finite: row kk is live
+            if (__any(v > m + kLazy)) {
+                const float mn = v > m + kLazy ? v : m;
+                const float alpha = __builtin_amdgcn_exp2f(m - mn);     // 0 on the first tile
+                m = mn;
+                l *= alpha;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
+                for (int dt = 0; dt < 16; ++dt) acc[dt] *= alpha;
+            }
+            // P^T as B fragments: k slots 0..3 = rows 4 g + 0..3, 4..7 = rows 16 + 4 g + 0..3
+            float p[8];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-                pa[h2][qt] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(&sP[h2][(16 * qt + col) * kTile + 8 * grp]));
-
-        // O += P V: B fragments lane L: dim 16 dt + L % 16, cache rows 8 (L / 16) .. +7
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int dt = 0; dt < 16; ++dt) {
-            const int d = 16 * dt + col;
-            uint32_t w[4];
+                for (int i = 0; i < 4; ++i) p[4 * kt + i] = __builtin_amdgcn_exp2f(st[kt][i] - m);
+            u32x4_t hw, lw;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t e0 = sV[(8 * grp + 2 * j) * DA + d];
-                const uint32_t e1 = sV[(8 * grp + 2 * j + 1) * DA + d];
-                w[j] = e0 | (e1 << 16);
+                hw[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+                const float h0 = __builtin_bit_cast(float, hw[j] << 16);
+                const float h1 = __builtin_bit_cast(float, hw[j] & 0xffff0000u);
+                lw[j] = pack_bf16(p[2 * j] - h0, p[2 * j + 1] - h1);
             }
-            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
+            float sum = 0.f;
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0][qt], vf, acc[qt][dt], 0, 0, 0);
-                acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1][qt], vf, acc[qt][dt], 0, 0, 0);
+            for (int j = 0; j < 8; ++j) sum += p[j];
+            l += sum;
+            ph = __builtin_bit_cast(bf16x8_t, hw);
+            pl = __builtin_bit_cast(bf16x8_t, lw);
+        }
+
+        // this tile's values: this wave's loads landed (the next keys may remain), then the
+        // other wave's
+        if (more) __builtin_amdgcn_s_waitcnt(kWaitVm8);
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+
+        if (active) {
+            // O^T += V^T P^T: A fragments lane (g, i): dim 16 dt + i, cache rows as the k slots
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt) {
+                const uint32_t chunk = 2u * dt + vhalf;
+                const uint32_t a0 = ldsV + vrow * 512u + 16u * (chunk ^ static_cast<uint32_t>(vrow & 15)) + vsub;
+                const uint32_t a1 = a0 + 16u * 512u;    // rows + 16: same position (row % 16)
+                const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    reinterpret_cast<lds_i16x4_t*>(static_cast<uintptr_t>(a0)));
+                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    reinterpret_cast<lds_i16x4_t*>(static_cast<uintptr_t>(a1)));
+                const u32x2_t w0 = __builtin_bit_cast(u32x2_t, t0);
+                const u32x2_t w1 = __builtin_bit_cast(u32x2_t, t1);
+                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[dt], 0, 0, 0);
             }
         }
+        // both waves are done with the values: the next ones stream in during the next scores
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __syncthreads();
+        if (more) load_half(Vb, kk + kTile, k1, ldsV, lane, w);
     }
+    if (!active) return;
 
-    // the partial: O rows (unnormalised), then m and l
-    const int nsplit = (T_max + kSplit - 1) / kSplit;
+    // the partial: O rows (unnormalised), then m and l (l summed over the four lanes that share
+    // a query)
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int nsplit = gridDim.x;
     const int nqb = (Nq + kQB - 1) / kQB;
     float* part = work + (static_cast<size_t>(bk * nqb + qb) * nsplit + split) * kPartFloats;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int dt = 0; dt < 16; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                part[(16 * qt + 4 * grp + i) * DA + 16 * dt + col] = acc[qt][dt][i];
-    if (col == 0) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                part[kQB * DA + 16 * qt + 4 * grp + i] = m[qt][i];
-                part[kQB * DA + kQB + 16 * qt + 4 * grp + i] = l[qt][i];
-            }
+    for (int dt = 0; dt < 16; ++dt)
+        *reinterpret_cast<f32x4_t*>(part + (16 * w + col) * DA + 16 * dt + 4 * grp) = acc[dt];
+    if (grp == 0) {
+        part[kQB * DA + 16 * w + col] = m;
+        part[kQB * DA + kQB + 16 * w + col] = l;
     }
 }
 
-// grid (query blocks, B * Hkv), 256 lanes: lane = (query row q = tid / 8, dims 32 (tid % 8) ..
-// +31).  Merges the cache partials of each query and the draft keys it may see.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// grid (query groups of 4, B * Hkv), 256 lanes: one wave per query, lane l holding dims
+// 4 l .. 4 l + 3.  Merges the cache partials of the query and the draft keys it may see.
 __global__ __launch_bounds__(256)
 void attn_combine_kernel(const int32_t* __restrict__ ctx, int T_max,
                          const uint16_t* __restrict__ Qd, const uint16_t* __restrict__ Kd,
                          const uint16_t* __restrict__ Vd, const int32_t* __restrict__ parent,
-                         int Hkv, int G, int N, const float* __restrict__ work,
-                         float* __restrict__ O, int32_t* __restrict__ status)
+                         int Hkv, int G, int N, int rows, int nsplit,
+                         const float* __restrict__ work, float* __restrict__ O,
+                         int32_t* __restrict__ status)
 {
-    const int tid = threadIdx.x;
-    const int qr = tid >> 3;
-    const int dc = (tid & 7) * 32;
-    const int qb = blockIdx.x;
+    const int lane = threadIdx.x & 63;
     const int bk = blockIdx.y;
     const int b = bk / Hkv;
     const int kvh = bk - b * Hkv;
     const int Hq = Hkv * G;
     const int Nq = N * G;
-    const int qi = qb * kQB + qr;
-    const bool ok = qi < Nq;                    // every lane takes part in the shuffles
-    const int t = ok ? qi / G : 0;
-    const int hq = kvh * G + (ok ? qi - t * G : 0);
     const int craw = ctx[b];
     const int c = clamp_ctx(craw, T_max);
-    if (tid == 0 && qb == 0 && kvh == 0 && craw != c) report(status, TREEWY_ECTX);
-    const int nsplit = (T_max + kSplit - 1) / kSplit;
+    if (threadIdx.x == 0 && blockIdx.x == 0 && kvh == 0 && craw != c) report(status, TREEWY_ECTX);
+    const int qi = 4 * blockIdx.x + (threadIdx.x >> 6);
+    if (qi >= Nq) return;                       // the whole wave
+    const int t = qi / G;
+    const int hq = kvh * G + (qi - t * G);
     const int nqb = (Nq + kQB - 1) / kQB;
-    const int used = (c + kSplit - 1) / kSplit;
+    const int qq = qi % kQB;
+    const int used = (c + rows - 1) / rows;
+    const float* base = work + static_cast<size_t>(bk * nqb + qi / kQB) * nsplit * kPartFloats;
+    const int d0 = 4 * lane;
 
-    // the query's slice and the draft part's scores
-    const uint16_t* qrow = Qd + (static_cast<size_t>(b * N + t) * Hq + hq) * DA + dc;
-    float q[32];
+    // the cache partials' maxima, 64 splits at a time
+    float mt = -INFINITY;
+    for (int s = lane; s < used; s += 64) mt = fmaxf(mt, base[static_cast<size_t>(s) * kPartFloats + kQB * DA + qq]);
+    mt = wave_max(mt);
+
+    // the draft part: ancestors-or-self of t, walked from the tree (a malformed parent ends
+    // the walk); first pass for the maximum
+    const uint16_t* qrow = Qd + (static_cast<size_t>(b * N + t) * Hq + hq) * DA + d0;
+    float q[4];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) q[e] = bf16_to_f32(qrow[e]);
-
-    float mx = -INFINITY;
-    const float* base = work + static_cast<size_t>(bk * nqb + qb) * nsplit * kPartFloats;
-    for (int s = 0; s < used; ++s) mx = fmaxf(mx, base[s * kPartFloats + kQB * DA + qr]);
-
-    // ancestors-or-self of t, walked from the tree (a malformed parent ends the walk)
+    for (int e = 0; e < 4; ++e) q[e] = bf16_to_f32(qrow[e]);
+    const float sscale = kLog2e / 16.0f;
     int node = t;
-    float acc[32];
+    for (int hop = 0; hop < 64 && node >= 0; ++hop) {
+        const uint16_t* krow = Kd + (static_cast<size_t>(b * N + node) * Hkv + kvh) * DA + d0;
+        float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) acc[e] = 0.f;
-    float lsum = 0.f;
-    float dmax = -INFINITY;
-    for (int hop = 0; hop < 64 && node >= 0; ++hop) {    // first pass: the draft maximum
-        const uint16_t* krow = Kd + (static_cast<size_t>(b * N + node) * Hkv + kvh) * DA + dc;
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) part += q[e] * bf16_to_f32(krow[e]);
-        part += __shfl_xor(part, 1);
-        part += __shfl_xor(part, 2);
-        part += __shfl_xor(part, 4);
-        dmax = fmaxf(dmax, part * (kLog2e / 16.0f));
+        for (int e = 0; e < 4; ++e) dot += q[e] * bf16_to_f32(krow[e]);
+        mt = fmaxf(mt, wave_sum(dot) * sscale);
         const int p = parent[b * N + node];
         node = (p >= -1 && p < node) ? p : -1;
     }
-    const float mt = fmaxf(mx, dmax);
-    for (int s = 0; s < used; ++s) {
-        const float* ps = base + s * kPartFloats;
-        const float w = __builtin_amdgcn_exp2f(ps[kQB * DA + qr] - mt);
-        lsum += w * ps[kQB * DA + kQB + qr];
+
+    // cache partials, weighted by 2^(m_s - mt); 8 rows in flight per lane
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+    for (int s0 = 0; s0 < used; s0 += 64) {
+        const int s = s0 + lane;
+        float w = 0.f;
+        if (s < used) {
+            const float* ps = base + static_cast<size_t>(s) * kPartFloats;
+            w = __builtin_amdgcn_exp2f(ps[kQB * DA + qq] - mt);
+            lsum += w * ps[kQB * DA + kQB + qq];
+        }
+        const int n = used - s0 < 64 ? used - s0 : 64;
+        int j = 0;
+        for (; j + 8 <= n; j += 8) {
+            f32x4_t x[8];
 #pragma unroll
-        for (int e = 0; e < 32; ++e) acc[e] += w * ps[qr * DA + dc + e];
+            for (int u = 0; u < 8; ++u)
+                x[u] = *reinterpret_cast<const f32x4_t*>(
+                    base + static_cast<size_t>(s0 + j + u) * kPartFloats + qq * DA + d0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wu = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+                acc += wu * x[u];
+            }
+        }
+        for (; j < n; ++j) {
+            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(
+                base + static_cast<size_t>(s0 + j) * kPartFloats + qq * DA + d0);
+            const float wu = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+            acc += wu * x;
+        }
     }
+    lsum = wave_sum(lsum);
+
+    // second pass over the draft: its terms
     node = t;
-    for (int hop = 0; hop < 64 && node >= 0; ++hop) {    // second pass: the draft terms
-        const size_t row = (static_cast<size_t>(b * N + node) * Hkv + kvh) * DA + dc;
-        float part = 0.f;
+    for (int hop = 0; hop < 64 && node >= 0; ++hop) {
+        const size_t row = (static_cast<size_t>(b * N + node) * Hkv + kvh) * DA + d0;
+        float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) part += q[e] * bf16_to_f32(Kd[row + e]);
-        part += __shfl_xor(part, 1);
-        part += __shfl_xor(part, 2);
-        part += __shfl_xor(part, 4);
-        const float w = __builtin_amdgcn_exp2f(part * (kLog2e / 16.0f) - mt);
+        for (int e = 0; e < 4; ++e) dot += q[e] * bf16_to_f32(Kd[row + e]);
+        const float w = __builtin_amdgcn_exp2f(wave_sum(dot) * sscale - mt);
         lsum += w;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) acc[e] += w * bf16_to_f32(Vd[row + e]);
+        for (int e = 0; e < 4; ++e) acc[e] += w * bf16_to_f32(Vd[row + e]);
         const int p = parent[b * N + node];
         if (p < -1 || p >= node) {
-            if (ok && (tid & 7) == 0) report(status, TREEWY_ETREE);
+            if (lane == 0) report(status, TREEWY_ETREE);
             node = -1;
         } else {
             node = p;
         }
     }
-    if (!ok) return;
     const float inv = 1.0f / lsum;
-    float* orow = O + (static_cast<size_t>(b * N + t) * Hq + hq) * DA + dc;
-#pragma unroll
-    for (int e = 0; e < 32; e += 4)
-        *reinterpret_cast<f32x4_t*>(orow + e) = f32x4_t{acc[e] * inv, acc[e + 1] * inv,
-                                                         acc[e + 2] * inv, acc[e + 3] * inv};
+    float* orow = O + (static_cast<size_t>(b * N + t) * Hq + hq) * DA + d0;
+    *reinterpret_cast<f32x4_t*>(orow) = acc * inv;
 }
 
 // grid (B * Hkv), 256 lanes: the accepted node's root-to-node path (keys and values of one
@@ -402,27 +468,42 @@ void kv_commit_kernel(uint16_t* __restrict__ Kc, uint16_t* __restrict__ Vc,
     }
 }
 
+
+// Cache rows per split for a launch: about kTargetBlocks workgroups over the (sequence, key/value
+// head, query block) triples, whole tiles, at least kMinSplit rows.
+int split_rows(int B, int Hkv, int G, int N, int T_max) {
+    const long long pairs = static_cast<long long>(B) * Hkv * ((static_cast<long long>(N) * G + kQB - 1) / kQB);
+    const long long want = (kTargetBlocks + pairs - 1) / pairs;
+    long long rows = (T_max + want - 1) / want;
+    rows = (rows + kTile - 1) / kTile * kTile;
+    return static_cast<int>(rows < kMinSplit ? kMinSplit : rows);
+}
+
+int split_count(int T_max, int rows) { return (T_max + rows - 1) / rows; }
+
 }  // namespace
 
 size_t attention_workspace_bytes(int B, int Hkv, int G, int N, int T_max) {
-    const size_t nsplit = (static_cast<size_t>(T_max) + kSplit - 1) / kSplit;
+    const size_t nsplit = split_count(T_max, split_rows(B, Hkv, G, N, T_max));
     const size_t nqb = (static_cast<size_t>(N) * G + kQB - 1) / kQB;
     return static_cast<size_t>(B) * Hkv * nqb * nsplit * kPartFloats * sizeof(float);
 }
 
 hipError_t launch_tree_attention(const AttentionArgs& a, hipStream_t stream) {
-    const int nsplit = (a.T_max + kSplit - 1) / kSplit;
+    const int rows = split_rows(a.B, a.Hkv, a.G, a.N, a.T_max);
+    const int nsplit = split_count(a.T_max, rows);
     const int nqb = (a.N * a.G + kQB - 1) / kQB;
-    hipLaunchKernelGGL(attn_partial_kernel, dim3(nsplit, nqb, a.B * a.Hkv), dim3(64), 0, stream,
+    hipLaunchKernelGGL(attn_partial_kernel, dim3(nsplit, nqb, a.B * a.Hkv), dim3(128), 0, stream,
                        static_cast<const uint16_t*>(a.Kc), static_cast<const uint16_t*>(a.Vc),
-                       a.ctx, a.T_max, static_cast<const uint16_t*>(a.Qd), a.Hkv, a.G, a.N,
+                       a.ctx, a.T_max, static_cast<const uint16_t*>(a.Qd), a.Hkv, a.G, a.N, rows,
                        static_cast<float*>(a.work));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(nqb, a.B * a.Hkv), dim3(256), 0, stream, a.ctx,
-                       a.T_max, static_cast<const uint16_t*>(a.Qd),
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((a.N * a.G + 3) / 4, a.B * a.Hkv), dim3(256), 0,
+                       stream, a.ctx, a.T_max, static_cast<const uint16_t*>(a.Qd),
                        static_cast<const uint16_t*>(a.Kd), static_cast<const uint16_t*>(a.Vd),
-                       a.parent, a.Hkv, a.G, a.N, static_cast<const float*>(a.work), a.O, a.status);
+                       a.parent, a.Hkv, a.G, a.N, rows, nsplit, static_cast<const float*>(a.work),
+                       a.O, a.status);
     return hipGetLastError();
 }
 

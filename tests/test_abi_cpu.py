@@ -142,8 +142,11 @@ def test_deferred_flush_rejects(lib):
 
 
 def test_attention_workspace_size(lib):
-    # 16 splits of 512 rows x 1 block of 32 queries x B*Hkv, (32*256 + 64) floats each
-    assert lib.treewy_tree_attention_workspace(2, 2, 8, 4, 8192) == 2 * 2 * 1 * 16 * (32 * 256 + 64) * 4
+    # (sequence, head, query block) triples x cache splits x one partial; the splits aim at about
+    # 1024 workgroups with at least 256 rows each
+    assert lib.treewy_tree_attention_workspace(2, 2, 8, 4, 8192) == 2 * 2 * 1 * 32 * (32 * 256 + 64) * 4
+    assert lib.treewy_tree_attention_workspace(32, 2, 8, 4, 8256) == 32 * 2 * 1 * 16 * (32 * 256 + 64) * 4
+    assert lib.treewy_tree_attention_workspace(512, 8, 8, 4, 8192) == 512 * 8 * 1 * 1 * (32 * 256 + 64) * 4
     assert lib.treewy_tree_attention_workspace(1, 1, 8, 16, 100) == 1 * 1 * 4 * 1 * (32 * 256 + 64) * 4
     assert lib.treewy_tree_attention_workspace(0, 2, 8, 4, 64) == 0
     assert lib.treewy_tree_attention_workspace(1, 2, 8, 65, 64) == 0
