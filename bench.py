@@ -38,7 +38,9 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 # HBM byte counts per launch taken with rocprofv3 (FETCH_SIZE, WRITE_SIZE, scaled by the same
 # counters on a plain copy of known size), per workload; used while the kernel source is the
 # one they were taken on
-TRAFFIC_FILES = {1: "profiles/traffic_chain4_b32h32.json"}
+TRAFFIC_FILES = {1: "profiles/traffic_chain4_b32h32.json",
+                 "attention-8192": "profiles/traffic_attention_b32_chain4_ctx8192.json",
+                 "attention-32768": "profiles/traffic_attention_b32_chain4_ctx32768.json"}
 
 
 def log(*a):
@@ -368,13 +370,7 @@ def run(args, mode, wl):
             f"{n} {t * 1e3:.1f} us" for n, (b, t) in k2.items()))
 
     if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib * 2 ** 20 // 4
-        src_t = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst_t = torch.empty_like(src_t)
-        torch.cuda.synchronize()
-        dst_t.copy_(src_t)
-        torch.cuda.synchronize()
-        del src_t, dst_t
+        copy_probe(args.copy_probe_mib)
 
     cpu = None
     if args.cpu_seconds > 0 and not args.sweep:
@@ -431,17 +427,17 @@ def run_attention(args):
         f"{per * n_inst / 2 ** 30:.2f} GiB")
     bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16).contiguous()
     pool = []
+    gen = torch.Generator(device="cuda")
     for i in range(n_inst):
-        rng = np.random.default_rng(np.random.SeedSequence([3000, i]))
-        # the cache drawn on the device (a plain normal fill): only its shape matters here
-        Kc = torch.randn((B, Hkv, T, 256), device="cuda").to(torch.bfloat16)
-        Vc = torch.randn((B, Hkv, T, 256), device="cuda").to(torch.bfloat16)
+        # the cache drawn on the device (a seeded normal fill): only its shape matters here
+        gen.manual_seed(3000 + i)
+        Kc = torch.randn((B, Hkv, T, 256), device="cuda", generator=gen).to(torch.bfloat16)
+        Vc = torch.randn((B, Hkv, T, 256), device="cuda", generator=gen).to(torch.bfloat16)
         P = inputs.make_attention_problem(3000 + i, B=B, Hkv=Hkv, G=G, N=N, T_max=N + 1,
                                           ctx=np.zeros(B), tree="chain")
         pool.append(dict(Kc=Kc, Vc=Vc, ctx=torch.full((B,), ctxn, dtype=torch.int32, device="cuda"),
                          Qd=bf(P.Qd), Kd=bf(P.Kd), Vd=bf(P.Vd),
-                         parent=torch.from_numpy(P.parent).cuda()))
-        del rng
+                         parent=torch.from_numpy(P.parent).cuda(), P=P))
     O = torch.empty((B, N, Hkv * G, 256), device="cuda")
     ws = torch.empty(binding.treewy_tree_attention_workspace(B, Hkv, G, N, T), dtype=torch.uint8,
                      device="cuda")
@@ -476,6 +472,14 @@ def run_attention(args):
     achieved = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] tree attention: {wall * 1e6 / K:.1f} us/step, {ms * 1e3:.1f} us per call "
         f"(events), {achieved:.0f} GB/s algorithmic")
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = attention_cpu_baseline(pool[0], ctxn, G, args.cpu_seconds)
+        log(f"[bench] cpu baseline (oracle): {cpu['value']:.3g} {cpu['unit']} on {cpu['cores']} "
+            f"thread(s), {cpu['sample']}")
+    traffic = measured_traffic(f"attention-{ctxn}", "treewy_tree_attention")
     return {
         "metric": "tree attention verify draft-nodes*query-heads/sec",
         "value": B * N * Hkv * G * K / wall, "unit": "nodes*heads/s", "n_gpus": 1, "steps": K,
@@ -487,12 +491,56 @@ def run_attention(args):
                    "instances_rotated": n_inst},
         "roofline": {"bound": "hbm", "kernel": "treewy_tree_attention", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": nbytes, "launch_us": ms * 1e3},
-        "cpu_baseline": None,
+                     "traffic": traffic, "bytes_per_launch": nbytes, "launch_us": ms * 1e3},
+        "cpu_baseline": cpu,
     }
 
 
-def measured_traffic(cfg: int, entry: str):
+def blas_threads():
+    """Threads numpy's BLAS may use (the attention oracle's products run there)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def attention_cpu_baseline(x, ctxn, G, seconds):
+    """The attention oracle, as it stands, on whole sequences of one instance (their committed
+    cache copied to the host), one after another until about ``seconds`` have been spent."""
+    from oracle import attention as oattn
+    P = x["P"]
+    B, N = P.parent.shape
+    done, elapsed, b = 0, 0.0, 0
+    while elapsed < seconds and done < 4 * B:
+        Kc = x["Kc"][b:b + 1, :, :ctxn].float().cpu().numpy().astype(np.float64)
+        Vc = x["Vc"][b:b + 1, :, :ctxn].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oattn.tree_attention(Kc, Vc, np.array([ctxn]), P.Qd[b:b + 1], P.Kd[b:b + 1],
+                             P.Vd[b:b + 1], P.parent[b:b + 1], G)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        b = (b + 1) % B
+    Hq = P.Qd.shape[2]
+    return {"value": done * N * Hq / elapsed, "unit": "nodes*heads/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} whole sequence(s) of {ctxn} cached rows, {N} nodes x {Hq} "
+                      f"query heads each (cache conversion to float64 not timed)"}
+
+
+def copy_probe(mib):
+    """One plain device copy of known size: a counter run scales its FETCH_SIZE / WRITE_SIZE
+    readings by what the counters report for this dispatch."""
+    import torch
+    src_t = torch.ones(mib * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
+    dst_t = torch.empty_like(src_t)
+    torch.cuda.synchronize()
+    dst_t.copy_(src_t)
+    torch.cuda.synchronize()
+
+
+def measured_traffic(cfg, entry: str):
     """Counted HBM bytes per launch of `entry` on workload `cfg`, or None when no count was
     taken or the kernel source changed since."""
     import hashlib
