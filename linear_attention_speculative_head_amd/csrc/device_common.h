@@ -59,7 +59,8 @@ __device__ __forceinline__ void report(int32_t* status, int code) {
 // Tree bookkeeping for one draft tree, run by all 64 lanes of one wave (lane t = node t).
 // Pointer jumping: after round r every lane holds the set of its ancestors at distance
 // < 2^r (itself included) and the product of their gates, plus a pointer to the ancestor
-// at distance 2^r; six rounds cover the deepest tree of 64 nodes.  A parent outside
+// at distance 2^r.  Parents precede their children, so a node's depth is at most N and
+// ceil(log2 N) rounds cover every ancestor (six for 64 nodes).  A parent outside
 // [-1, t-1] is reported and treated as -1 so that every later index stays in range.
 struct NodeInfo {
     uint64_t anc;   // inclusive ancestor mask
@@ -79,8 +80,7 @@ __device__ __forceinline__ NodeInfo tree_walk(const int32_t* parent_b, int N, fl
     uint64_t a = lane < N ? (1ull << lane) : 0ull;
     float g = lane < N ? alpha_t : 1.0f;
     int j = p;
-#pragma unroll
-    for (int r = 0; r < 6; ++r) {
+    for (int r = 0; (1 << r) < N; ++r) {
         const int src = j < 0 ? lane : j;
         const uint64_t aj = shfl_u64(a, src);
         const float gj = __shfl(g, src);

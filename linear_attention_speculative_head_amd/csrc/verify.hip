@@ -244,6 +244,7 @@ constexpr int kSmallThreads = 256;
 // left at their maxima (no wait on them)
 constexpr int kWaitAllButTwoStores = 2 | (7 << 4) | (15 << 8);
 constexpr int kWaitAllButEight = 8 | (7 << 4) | (15 << 8);
+constexpr int kWaitLdsOnly = 0xC07F;            // LDS/scalar count 0, the rest left free
 // dword 3 of a raw (unstrided, range-checked) buffer descriptor on gfx9-family parts
 constexpr int kRawBufferFlags = 0x00020000;
 constexpr int kSmallRows = 64;              // value rows per item
@@ -262,18 +263,43 @@ constexpr int kSmallParts = D / kSmallRows; // items per head
 // keeps the MFMA operand reads free of bank conflicts.
 struct SmallLds {
     uint32_t kq, v, sm, g, pu, pk, pg, idx, il, lg, lu, lk, bytes;
+    uint32_t set;                               // second input set at +set (0: one set)
     int path;                                   // path rows staged per chunk (fused)
 };
+
+// The fused kernel on trees of up to 8 nodes keeps two sets of per-item inputs (key/query and
+// value rows, parents/gates, path rows, previous tree): the next item's set is requested at
+// the top of this item, and the next item's S rows as soon as each wave has taken its own
+// rows into registers, so both stream in during this item's solve.
+__host__ __device__ constexpr bool small_two_sets(int nct, int mode) { return nct == 1 && mode == 1; }
 
 // mode: 0 plain verify, 1 fused commit, 2 deferred commit (log of lmax terms)
 __host__ __device__ inline SmallLds small_lds(int N, int nct, int mode, int lmax = 0) {
     SmallLds L;
+    L.path = N <= 4 ? 4 : 8;
+    if (small_two_sets(nct, mode)) {
+        // S rows, the Gram matrix, then two sets of [key/query rows, values, parents/gates,
+        // path rows, path gammas, previous tree]
+        L.g = kSmallRows * D * 4;
+        const uint32_t s0 = L.g + 1024u * static_cast<uint32_t>(nct);
+        L.kq = s0;
+        L.v = L.kq + 2048u * static_cast<uint32_t>((N + 3) / 4);
+        L.sm = L.v + 1024u * static_cast<uint32_t>((N + 7) / 8);
+        L.pu = L.sm + 256u;
+        L.pk = L.pu + 256u * L.path;
+        L.pg = L.pk + 256u * L.path;
+        L.idx = L.pg + 256u;
+        L.il = L.lg = L.lu = L.lk = L.idx + 256u;   // no log
+        L.set = L.idx + 256u - s0;
+        L.bytes = L.idx + 256u + L.set;
+        return L;
+    }
+    L.set = 0;
     L.kq = kSmallRows * D * 4;
     L.v = L.kq + 2048u * static_cast<uint32_t>((N + 3) / 4);
     L.sm = L.v + 1024u * static_cast<uint32_t>((N + 7) / 8);
     L.g = L.sm + 256u;
     const uint32_t end = L.g + 1024u * static_cast<uint32_t>(nct);
-    L.path = N <= 4 ? 4 : 8;
     L.pu = end;
     L.pk = L.pu + 256u * L.path;
     L.pg = L.pk + 256u * L.path;
@@ -556,8 +582,8 @@ __device__ __forceinline__ PathInfo fused_path(int p_raw, int a, int Np, int lan
     int j = bad ? -1 : p_raw;
     uint64_t am = lane < Np ? (1ull << lane) : 0ull;
     int badp = bad ? 1 : 0;
-#pragma unroll
-    for (int r = 0; r < 6; ++r) {
+    // a node's depth is at most Np (parents precede their children): ceil(log2 Np) rounds
+    for (int r = 0; (1 << r) < Np; ++r) {
         const int src = j < 0 ? lane : j;
         const uint64_t aj = shfl_u64(am, src);
         const int bj = __shfl(badp, src);
@@ -682,6 +708,7 @@ void verify_small_kernel(
 {
     constexpr bool FUSED = MODE != 0;
     constexpr bool DEFER = MODE == 2;
+    constexpr bool TWO = small_two_sets(NCT, MODE); // two input sets, early refills
     constexpr int kGP = 16 * NCT;                   // G row pitch
     extern __shared__ __align__(16) float lds[];
     const SmallLds L = small_lds(N, NCT, MODE, DEFER ? dlog.Lmax : 0);
@@ -746,6 +773,7 @@ void verify_small_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0);                  // the first item: nothing else in flight
 
+    uint32_t sb = 0;                                // this item's input set (TWO: 0 or L.set)
     for (int round = 0;; ) {
         const int b = bh / H;
         const int h = bh - b * H;
@@ -762,18 +790,39 @@ void verify_small_kernel(
         small_item(round + 1, slot, grid, bh_n, part_n);
         const bool more = bh_n < BH;
 
+        PathInfo nxt{0ull, 0, 0};
+        int nxt_len = 0;
+        if constexpr (TWO) {
+            // the next item's path (its previous tree and accepted node came with this item's
+            // transfers), then its inputs and path rows into the other set, with the previous
+            // tree and accepted node of the item after it
+            if (more) {
+                const uint32_t sbn = sb ? 0u : L.set;
+                nxt = fused_path(lane < cin.Np ? reinterpret_cast<const int*>(ldsb + sb + L.idx)[lane] : -1,
+                                 reinterpret_cast<const int*>(ldsb + sb + L.sm)[48], cin.Np, lane,
+                                 wave == 0 && bh_n % H == 0 && part_n == 0, status);
+                int bh_2, part_2;
+                small_item(round + 2, slot, grid, bh_2, part_2);
+                small_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
+                                   lds_addr + sbn, L, bh_2 < BH ? cin.accepted + bh_2 / H : nullptr);
+                if (nxt.depth > 0)
+                    fused_issue_path(cin, nxt, 0, bh_n, part_n, H, wave, lane, lds_addr + sbn, L);
+                if (bh_2 < BH && wave == 3) fused_issue_index(cin, bh_2 / H, lane, lds_addr + sbn + L.idx);
+            }
+        }
+
         if constexpr (FUSED) {
             int len = 0;
             float gin = 1.0f;
             if constexpr (DEFER) {
                 len = cur_len;
-                gin = reinterpret_cast<const float*>(ldsb + L.lg)[0];
+                gin = reinterpret_cast<const float*>(ldsb + sb + L.lg)[0];
             }
             const bool any = cur.depth > 0 || len > 0;
             // MODE 1 always writes S; MODE 2 only when the log cannot take the path's terms
             bool flush = true;
             if constexpr (DEFER) flush = len + cur.depth > dlog.Lmax || cur.depth > L.path;
-            const float* PG = reinterpret_cast<const float*>(ldsb + L.pg);
+            const float* PG = reinterpret_cast<const float*>(ldsb + sb + L.pg);
             const float ga = cur.depth > 0 ? PG[cur.depth - 1] : 1.0f;
             const float gs = gin * ga;              // the scale of S (and of the logged terms)
             if (any) {
@@ -783,8 +832,8 @@ void verify_small_kernel(
                 // 16-byte chunk l % 32, for i = 0..7), and written back to HBM from there when
                 // flushing: every store is two whole 512-byte rows.  The path's gammas are in
                 // LDS in path order (a is last).
-                const float* PU = reinterpret_cast<const float*>(ldsb + L.pu);
-                const char* PK = ldsb + L.pk;
+                const float* PU = reinterpret_cast<const float*>(ldsb + sb + L.pu);
+                const char* PK = ldsb + sb + L.pk;
                 const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
                 const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
                 const int nchunk = cur.depth > 0 ? (cur.depth + L.path - 1) / L.path : 1;
@@ -793,7 +842,7 @@ void verify_small_kernel(
                     if (ci > 0) {
                         // a path longer than one chunk: the next chunk, with a blocking wait
                         lds_barrier();
-                        fused_issue_path(cin, cur, ci, bh, part, H, wave, lane, lds_addr, L);
+                        fused_issue_path(cin, cur, ci, bh, part, H, wave, lane, lds_addr + sb, L);
                         __builtin_amdgcn_s_waitcnt(0);
                         lds_barrier();
                     }
@@ -808,8 +857,8 @@ void verify_small_kernel(
                     }
                     if constexpr (DEFER) {
                         if (ci == 0) {
-                            const float* LU = reinterpret_cast<const float*>(ldsb + L.lu);
-                            const char* LK = ldsb + L.lk;
+                            const float* LU = reinterpret_cast<const float*>(ldsb + sb + L.lu);
+                            const char* LK = ldsb + sb + L.lk;
                             for (int q = 0; q < len; ++q) {
                                 const uint2 kw = *reinterpret_cast<const uint2*>(LK + q * 256 + 8 * ch);
                                 const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
@@ -872,18 +921,42 @@ void verify_small_kernel(
             }
         }
 
+        // ---- MFMA operands of this wave's 16 rows (committed, with FUSED), split into bf16
+        //      hi and lo: lane L takes row 16w + L % 16, values 32 ks + 8 (L / 16) .. +7.
+        //      With two input sets the rows are taken here, and the wave's rows of the next
+        //      item are requested at once.
+        bf16x8_t ahi[4], alo[4];
+        auto take_rows = [&]() {
+            const int r = 16 * wave + col;
+            const float* rowp = lds + r * D;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int c0 = 2 * grp + 8 * ks;
+                split_hi_lo(*reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15))),
+                            *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15))),
+                            ahi[ks], alo[ks]);
+            }
+        };
+        if constexpr (TWO) {
+            take_rows();
+            if (more) {
+                __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);   // this wave's reads of its rows
+                small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+            }
+        }
+
         // ---- this item's operands out of LDS
-        const int my_par = node_ok ? reinterpret_cast<const int*>(ldsb + L.sm)[t] : -1;
-        const float my_alpha = node_ok ? reinterpret_cast<const float*>(ldsb + L.sm)[16 + t] : 1.0f;
-        const float my_beta = node_ok ? reinterpret_cast<const float*>(ldsb + L.sm)[32 + t] : 0.0f;
+        const int my_par = node_ok ? reinterpret_cast<const int*>(ldsb + sb + L.sm)[t] : -1;
+        const float my_alpha = node_ok ? reinterpret_cast<const float*>(ldsb + sb + L.sm)[16 + t] : 1.0f;
+        const float my_beta = node_ok ? reinterpret_cast<const float*>(ldsb + sb + L.sm)[32 + t] : 0.0f;
         uint2 vraw = make_uint2(0u, 0u);
-        if (node_ok) vraw = *reinterpret_cast<const uint2*>(ldsb + L.v + t * 128 + 32 * wave + 8 * grp);
+        if (node_ok) vraw = *reinterpret_cast<const uint2*>(ldsb + sb + L.v + t * 128 + 32 * wave + 8 * grp);
         bf16x8_t bfr[NCT][4];
 #pragma unroll
         for (int c = 0; c < NCT; ++c) {
             const int n = 16 * c + col;
             const int r = n < N ? n : (n < 2 * N ? 4 * nq4 + n - N : -1);
-            const char* rowp = ldsb + L.kq + 256 * (r < 0 ? 0 : r);
+            const char* rowp = ldsb + sb + L.kq + 256 * (r < 0 ? 0 : r);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 u32x4_t w = {0u, 0u, 0u, 0u};
@@ -891,9 +964,7 @@ void verify_small_kernel(
                 bfr[c][ks] = __builtin_bit_cast(bf16x8_t, w);
             }
         }
-        PathInfo nxt{0ull, 0, 0};
-        int nxt_len = 0;
-        if constexpr (FUSED) {
+        if constexpr (FUSED && !TWO) {
             if (more) {
                 nxt = fused_path(lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L.idx)[lane] : -1,
                                  reinterpret_cast<const int*>(ldsb + L.sm)[48], cin.Np, lane,
@@ -909,7 +980,7 @@ void verify_small_kernel(
         }
 
         // ---- tree walk, in every 16-lane group (lane = node t): pointer jumping as in
-        //      tree_walk, four rounds for the at most 16 nodes of a small tree
+        //      tree_walk, ceil(log2 N) rounds (at most four for a small tree)
         uint32_t anc;
         float g_t, rg_t;
         {
@@ -919,8 +990,7 @@ void verify_small_kernel(
             uint32_t am = node_ok ? (1u << t) : 0u;
             float g = node_ok ? my_alpha : 1.0f;
             int j = p;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int r = 0; (1 << r) < N; ++r) {    // ceil(log2 N) rounds: depth <= N
                 const int src = base | (j < 0 ? t : j);
                 const uint32_t aj = __shfl(am, src);
                 const float gj = __shfl(g, src);
@@ -957,23 +1027,10 @@ void verify_small_kernel(
             }
         }
 
-        // ---- MFMA operands of this wave's 16 rows (committed, with FUSED), split into bf16
-        //      hi and lo: lane L takes row 16w + L % 16, values 32 ks + 8 (L / 16) .. +7
-        bf16x8_t ahi[4], alo[4];
-        {
-            const int r = 16 * wave + col;
-            const float* rowp = lds + r * D;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int c0 = 2 * grp + 8 * ks;
-                split_hi_lo(*reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15))),
-                            *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15))),
-                            ahi[ks], alo[ks]);
-            }
-        }
+        if constexpr (!TWO) take_rows();
         lds_barrier();                              // operands read and G visible: refill
         ++round;
-        if (more) {
+        if (more && !TWO) {
             small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
             if constexpr (FUSED) {
                 // item i + 1's inputs and path rows; item i + 2's accepted node and tree
@@ -1080,6 +1137,7 @@ void verify_small_kernel(
             cur = nxt;
             cur_len = nxt_len;
         }
+        if constexpr (TWO) sb = sb ? 0u : L.set;
     }
 }
 
@@ -1089,7 +1147,7 @@ void verify_small_kernel(
 //
 // Output columns: keys at 0..N-1 (tiles 0..NKT-1), queries at 16 NKT + t (tiles NKT..2NKT-1),
 // so lane L holds P[t] and Y[t] for the nodes t = 16 kt + L % 16 of every node tile kt, rows
-// 16w + 4 (L / 16) .. +3.  Each wave walks the tree with lane = node (six pointer-jump rounds)
+// 16w + 4 (L / 16) .. +3.  Each wave walks the tree with lane = node (pointer jumping)
 // and hands every lane its nodes' masks and gates by lane permutes.  The forward substitution
 // and readout are the same ancestor walk as above; U of the ancestors is exchanged through a
 // per-wave LDS scratch [64 nodes][16 rows] instead of lane permutes, because an ancestor may sit
@@ -1316,8 +1374,7 @@ void verify_large_kernel(
                 uint64_t am = lane < N ? (1ull << lane) : 0ull;
                 float g = lane < N ? my_alpha : 1.0f;
                 int j = p;
-#pragma unroll
-                for (int r = 0; r < 6; ++r) {
+                for (int r = 0; (1 << r) < N; ++r) {    // ceil(log2 N) rounds: depth <= N
                     const int src = j < 0 ? lane : j;
                     const uint64_t aj = shfl_u64(am, src);
                     const float gj = __shfl(g, src);
