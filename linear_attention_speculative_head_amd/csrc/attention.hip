@@ -323,28 +323,71 @@ void attn_combine_kernel(const int32_t* __restrict__ ctx, int T_max,
     const float* base = work + static_cast<size_t>(bk * nqb + qi / kQB) * nsplit * kPartFloats;
     const int d0 = 4 * lane;
 
-    // the cache partials' maxima, 64 splits at a time
-    float mt = -INFINITY;
-    for (int s = lane; s < used; s += 64) mt = fmaxf(mt, base[static_cast<size_t>(s) * kPartFloats + kQB * DA + qq]);
-    mt = wave_max(mt);
+    // the draft part first: the ancestors-or-self of t from the whole tree at once (lane =
+    // node, pointer jumping; a malformed parent ends the path there and is reported), so that
+    // their key and value rows can be fetched together
+    int pj = lane < N ? parent[b * N + lane] : -1;
+    const bool badl = lane < N && (pj < -1 || pj >= lane);
+    if (badl) pj = -1;
+    uint64_t am = lane < N ? (1ull << lane) : 0ull;
+    int bad = badl ? 1 : 0;
+    for (int r = 0; (1 << r) < N; ++r) {        // depth <= N: ceil(log2 N) rounds
+        const int src = pj < 0 ? lane : pj;
+        const uint32_t lo = __shfl(static_cast<uint32_t>(am), src);
+        const uint32_t hi = __shfl(static_cast<uint32_t>(am >> 32), src);
+        const int bj = __shfl(bad, src);
+        const int jj = __shfl(pj, src);
+        if (pj >= 0) { am |= (static_cast<uint64_t>(hi) << 32) | lo; bad |= bj; pj = jj; }
+    }
+    const uint32_t anc_lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(am), t));
+    const uint32_t anc_hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(am >> 32), t));
+    const uint64_t anc = (static_cast<uint64_t>(anc_hi) << 32) | anc_lo;   // no sign extension
+    if (__builtin_amdgcn_readlane(bad, t) && lane == 0) report(status, TREEWY_ETREE);
+    const int na = __popcll(anc);               // 1 .. 64
 
-    // the draft part: ancestors-or-self of t, walked from the tree (a malformed parent ends
-    // the walk); first pass for the maximum
     const uint16_t* qrow = Qd + (static_cast<size_t>(b * N + t) * Hq + hq) * DA + d0;
     float q[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) q[e] = bf16_to_f32(qrow[e]);
     const float sscale = kLog2e / 16.0f;
-    int node = t;
-    for (int hop = 0; hop < 64 && node >= 0; ++hop) {
-        const uint16_t* krow = Kd + (static_cast<size_t>(b * N + node) * Hkv + kvh) * DA + d0;
-        float dot = 0.f;
+    const uint16_t* Kh = Kd + static_cast<size_t>(kvh) * DA + d0;   // + (b N + n) Hkv DA
+    const uint16_t* Vh = Vd + static_cast<size_t>(kvh) * DA + d0;
+    const size_t nstride = static_cast<size_t>(Hkv) * DA;
+
+    // scores of the draft keys, four rows in flight; lane j keeps the j-th one
+    float sc = -INFINITY;
+    {
+        uint64_t mm = anc;
+        for (int j0 = 0; j0 < na; j0 += 4) {
+            int n4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dot += q[e] * bf16_to_f32(krow[e]);
-        mt = fmaxf(mt, wave_sum(dot) * sscale);
-        const int p = parent[b * N + node];
-        node = (p >= -1 && p < node) ? p : -1;
+            for (int u = 0; u < 4; ++u) {
+                n4[u] = mm ? __builtin_ctzll(mm) : n4[0];
+                if (mm) mm &= mm - 1ull;
+            }
+            uint2 kw[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                kw[u] = *reinterpret_cast<const uint2*>(Kh + (static_cast<size_t>(b) * N + n4[u]) * nstride);
+            float dot[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                dot[u] = q[0] * __uint_as_float(kw[u].x << 16) + q[1] * __uint_as_float(kw[u].x & 0xffff0000u) +
+                         q[2] * __uint_as_float(kw[u].y << 16) + q[3] * __uint_as_float(kw[u].y & 0xffff0000u);
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dot[u] += __shfl_xor(dot[u], o);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (lane == j0 + u && j0 + u < na) sc = dot[u] * sscale;
+        }
     }
+
+    // the cache partials' maxima, 64 splits at a time, and the overall maximum
+    float mt = sc;
+    for (int s = lane; s < used; s += 64) mt = fmaxf(mt, base[static_cast<size_t>(s) * kPartFloats + kQB * DA + qq]);
+    mt = wave_max(mt);
 
     // cache partials, weighted by 2^(m_s - mt); 8 rows in flight per lane
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -380,25 +423,33 @@ void attn_combine_kernel(const int32_t* __restrict__ ctx, int T_max,
             acc += wu * x;
         }
     }
-    lsum = wave_sum(lsum);
 
-    // second pass over the draft: its terms
-    node = t;
-    for (int hop = 0; hop < 64 && node >= 0; ++hop) {
-        const size_t row = (static_cast<size_t>(b * N + node) * Hkv + kvh) * DA + d0;
-        float dot = 0.f;
+    // the draft terms: weights 2^(score - mt) held by lane j, value rows four in flight
+    const float wd = lane < na ? __builtin_amdgcn_exp2f(sc - mt) : 0.f;
+    lsum += wd;
+    lsum = wave_sum(lsum);
+    {
+        uint64_t mm = anc;
+        for (int j0 = 0; j0 < na; j0 += 4) {
+            int n4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dot += q[e] * bf16_to_f32(Kd[row + e]);
-        const float w = __builtin_amdgcn_exp2f(wave_sum(dot) * sscale - mt);
-        lsum += w;
+            for (int u = 0; u < 4; ++u) {
+                n4[u] = mm ? __builtin_ctzll(mm) : n4[0];
+                if (mm) mm &= mm - 1ull;
+            }
+            uint2 vw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += w * bf16_to_f32(Vd[row + e]);
-        const int p = parent[b * N + node];
-        if (p < -1 || p >= node) {
-            if (lane == 0) report(status, TREEWY_ETREE);
-            node = -1;
-        } else {
-            node = p;
+            for (int u = 0; u < 4; ++u)
+                vw[u] = *reinterpret_cast<const uint2*>(Vh + (static_cast<size_t>(b) * N + n4[u]) * nstride);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float w = j0 + u < na ? __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wd), j0 + u)) : 0.f;
+                acc[0] += w * __uint_as_float(vw[u].x << 16);
+                acc[1] += w * __uint_as_float(vw[u].x & 0xffff0000u);
+                acc[2] += w * __uint_as_float(vw[u].y << 16);
+                acc[3] += w * __uint_as_float(vw[u].y & 0xffff0000u);
+            }
         }
     }
     const float inv = 1.0f / lsum;
