@@ -3,9 +3,9 @@ oracle (float64 numpy, oracle/attention.py), through the C ABI.
 
 Gate: per (sequence, query head), max|O - O_oracle| / max|O_oracle| over the head's draft
 nodes <= 1e-3; the commit's cache rows and lengths bit-exact.  Cases: chains and trees up to
-64 nodes, empty and ragged committed prefixes (several 512-row splits and a ragged last 32-row
-step), query blocks of 32 with a ragged tail, and cache rows past the prefix that must not
-be read (they hold a loud constant).
+64 nodes, empty and ragged committed prefixes (several cache ranges and a ragged last 32-row
+step), query blocks of 32 with a ragged tail, malformed trees, and cache rows past the prefix
+that must not be read (they hold a loud constant).
 """
 
 import numpy as np
@@ -86,14 +86,21 @@ def test_configuration_one_shape():
     check(P, O, "B32 chain-4")
 
 
-def test_malformed_tree_is_reported():
+@pytest.mark.parametrize("N,node,bad", [(5, 3, 4), (40, 35, 39), (40, 2, -5)])
+def test_malformed_tree_is_reported(N, node, bad):
+    """A parent outside [-1, t-1] is reported; the node then counts as a root of the draft
+    (its ancestors are not seen), and every other output is unaffected."""
+    import dataclasses
     from linear_attention_speculative_head_amd import binding
-    P = inputs.make_attention_problem(12, B=2, G=2, N=5, T_max=64, ctx=np.array([10, 20]))
+    say(f"[attention] malformed parent: N={N}, parent[{node}] = {bad}")
+    P = inputs.make_attention_problem(12, B=2, G=2, N=N, T_max=N + 64, ctx=np.array([10, 20]))
     par = P.parent.copy()
-    par[1, 3] = 4
-    P.parent = par
-    _, st = run_attention(P, status_check=False)
+    par[1, node] = bad
+    O, st = run_attention(dataclasses.replace(P, parent=par), status_check=False)
     assert st == binding.TREEWY_ETREE
+    fixed = par.copy()
+    fixed[1, node] = -1
+    check(dataclasses.replace(P, parent=fixed), O, "malformed parent read as a root")
 
 
 def test_kv_commit_appends_the_accepted_path():
