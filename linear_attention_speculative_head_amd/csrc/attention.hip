@@ -323,10 +323,21 @@ void attn_combine_kernel(const int32_t* __restrict__ ctx, int T_max,
     const float* base = work + static_cast<size_t>(bk * nqb + qi / kQB) * nsplit * kPartFloats;
     const int d0 = 4 * lane;
 
-    // the draft part first: the ancestors-or-self of t from the whole tree at once (lane =
-    // node, pointer jumping; a malformed parent ends the path there and is reported), so that
-    // their key and value rows can be fetched together
+    // Everything that does not depend on the tree is requested first: the query slice, the
+    // tree, and the cache partials' maxima and sums (lane s: split s, first 64 splits).
+    const uint16_t* qrow = Qd + (static_cast<size_t>(b * N + t) * Hq + hq) * DA + d0;
+    float q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = bf16_to_f32(qrow[e]);
     int pj = lane < N ? parent[b * N + lane] : -1;
+    float ms = -INFINITY, ls = 0.f;
+    if (lane < used) {
+        ms = base[static_cast<size_t>(lane) * kPartFloats + kQB * DA + qq];
+        ls = base[static_cast<size_t>(lane) * kPartFloats + kQB * DA + kQB + qq];
+    }
+
+    // the ancestors-or-self of t from the whole tree at once (lane = node, pointer jumping; a
+    // malformed parent ends the path there and is reported)
     const bool badl = lane < N && (pj < -1 || pj >= lane);
     if (badl) pj = -1;
     uint64_t am = lane < N ? (1ull << lane) : 0ull;
@@ -345,51 +356,33 @@ void attn_combine_kernel(const int32_t* __restrict__ ctx, int T_max,
     if (__builtin_amdgcn_readlane(bad, t) && lane == 0) report(status, TREEWY_ETREE);
     const int na = __popcll(anc);               // 1 .. 64
 
-    const uint16_t* qrow = Qd + (static_cast<size_t>(b * N + t) * Hq + hq) * DA + d0;
-    float q[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) q[e] = bf16_to_f32(qrow[e]);
     const float sscale = kLog2e / 16.0f;
     const uint16_t* Kh = Kd + static_cast<size_t>(kvh) * DA + d0;   // + (b N + n) Hkv DA
     const uint16_t* Vh = Vd + static_cast<size_t>(kvh) * DA + d0;
     const size_t nstride = static_cast<size_t>(Hkv) * DA;
-
-    // scores of the draft keys, four rows in flight; lane j keeps the j-th one
-    float sc = -INFINITY;
-    {
-        uint64_t mm = anc;
-        for (int j0 = 0; j0 < na; j0 += 4) {
-            int n4[4];
+    auto next4 = [&](uint64_t& mm, int (&n4)[4]) {   // the next four ancestors (repeats past the end)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                n4[u] = mm ? __builtin_ctzll(mm) : n4[0];
-                if (mm) mm &= mm - 1ull;
-            }
-            uint2 kw[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                kw[u] = *reinterpret_cast<const uint2*>(Kh + (static_cast<size_t>(b) * N + n4[u]) * nstride);
-            float dot[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                dot[u] = q[0] * __uint_as_float(kw[u].x << 16) + q[1] * __uint_as_float(kw[u].x & 0xffff0000u) +
-                         q[2] * __uint_as_float(kw[u].y << 16) + q[3] * __uint_as_float(kw[u].y & 0xffff0000u);
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) dot[u] += __shfl_xor(dot[u], o);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (lane == j0 + u && j0 + u < na) sc = dot[u] * sscale;
+        for (int u = 0; u < 4; ++u) {
+            n4[u] = mm ? __builtin_ctzll(mm) : n4[0];
+            if (mm) mm &= mm - 1ull;
         }
+    };
+    // the first four ancestors' key and value rows go out now, with the cache partials below
+    uint64_t mk = anc, mv = anc;
+    int nk[4], nv[4];
+    next4(mk, nk);
+    uint2 kw[4], vw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        kw[u] = *reinterpret_cast<const uint2*>(Kh + (static_cast<size_t>(b) * N + nk[u]) * nstride);
+        vw[u] = *reinterpret_cast<const uint2*>(Vh + (static_cast<size_t>(b) * N + nk[u]) * nstride);
     }
 
-    // the cache partials' maxima, 64 splits at a time, and the overall maximum
-    float mt = sc;
-    for (int s = lane; s < used; s += 64) mt = fmaxf(mt, base[static_cast<size_t>(s) * kPartFloats + kQB * DA + qq]);
-    mt = wave_max(mt);
-
-    // cache partials, weighted by 2^(m_s - mt); 8 rows in flight per lane
+    // the cache part relative to its own maximum mc: O_c = sum_s 2^(m_s - mc) O_s,
+    // l_c = sum_s 2^(m_s - mc) l_s; 8 rows in flight per lane
+    float mc = ms;
+    for (int s = lane + 64; s < used; s += 64) mc = fmaxf(mc, base[static_cast<size_t>(s) * kPartFloats + kQB * DA + qq]);
+    mc = wave_max(mc);                          // -inf when nothing is cached
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
     for (int s0 = 0; s0 < used; s0 += 64) {
@@ -397,8 +390,10 @@ void attn_combine_kernel(const int32_t* __restrict__ ctx, int T_max,
         float w = 0.f;
         if (s < used) {
             const float* ps = base + static_cast<size_t>(s) * kPartFloats;
-            w = __builtin_amdgcn_exp2f(ps[kQB * DA + qq] - mt);
-            lsum += w * ps[kQB * DA + kQB + qq];
+            const float m_s = s0 == 0 ? ms : ps[kQB * DA + qq];
+            const float l_s = s0 == 0 ? ls : ps[kQB * DA + kQB + qq];
+            w = __builtin_amdgcn_exp2f(m_s - mc);
+            lsum += w * l_s;
         }
         const int n = used - s0 < 64 ? used - s0 : 64;
         int j = 0;
@@ -424,32 +419,53 @@ void attn_combine_kernel(const int32_t* __restrict__ ctx, int T_max,
         }
     }
 
-    // the draft terms: weights 2^(score - mt) held by lane j, value rows four in flight
-    const float wd = lane < na ? __builtin_amdgcn_exp2f(sc - mt) : 0.f;
-    lsum += wd;
-    lsum = wave_sum(lsum);
-    {
-        uint64_t mm = anc;
-        for (int j0 = 0; j0 < na; j0 += 4) {
-            int n4[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                n4[u] = mm ? __builtin_ctzll(mm) : n4[0];
-                if (mm) mm &= mm - 1ull;
-            }
-            uint2 vw[4];
+    // scores of the draft keys (four rows at a time); lane j keeps the j-th one
+    float sc = -INFINITY;
+    for (int j0 = 0; j0 < na; j0 += 4) {
+        if (j0 > 0) {
+            next4(mk, nk);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                vw[u] = *reinterpret_cast<const uint2*>(Vh + (static_cast<size_t>(b) * N + n4[u]) * nstride);
+                kw[u] = *reinterpret_cast<const uint2*>(Kh + (static_cast<size_t>(b) * N + nk[u]) * nstride);
+        }
+        float dot[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float w = j0 + u < na ? __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wd), j0 + u)) : 0.f;
-                acc[0] += w * __uint_as_float(vw[u].x << 16);
-                acc[1] += w * __uint_as_float(vw[u].x & 0xffff0000u);
-                acc[2] += w * __uint_as_float(vw[u].y << 16);
-                acc[3] += w * __uint_as_float(vw[u].y & 0xffff0000u);
-            }
+        for (int u = 0; u < 4; ++u)
+            dot[u] = q[0] * __uint_as_float(kw[u].x << 16) + q[1] * __uint_as_float(kw[u].x & 0xffff0000u) +
+                     q[2] * __uint_as_float(kw[u].y << 16) + q[3] * __uint_as_float(kw[u].y & 0xffff0000u);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dot[u] += __shfl_xor(dot[u], o);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (lane == j0 + u && j0 + u < na) sc = dot[u] * sscale;
+    }
+
+    // the overall maximum; the cache part rescaled to it, then the draft terms
+    const float mt = fmaxf(mc, wave_max(sc));   // finite: the node sees itself
+    const float rc = used > 0 ? __builtin_amdgcn_exp2f(mc - mt) : 0.f;
+    acc *= rc;
+    const float wd = lane < na ? __builtin_amdgcn_exp2f(sc - mt) : 0.f;
+    lsum = lsum * rc + wd;
+    lsum = wave_sum(lsum);
+    for (int j0 = 0; j0 < na; j0 += 4) {
+        if (j0 > 0) {
+            next4(mv, nv);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                vw[u] = *reinterpret_cast<const uint2*>(Vh + (static_cast<size_t>(b) * N + nv[u]) * nstride);
+        } else {
+            next4(mv, nv);                      // the first four rows are already here
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float w = j0 + u < na ? __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wd), j0 + u)) : 0.f;
+            acc[0] += w * __uint_as_float(vw[u].x << 16);
+            acc[1] += w * __uint_as_float(vw[u].x & 0xffff0000u);
+            acc[2] += w * __uint_as_float(vw[u].y << 16);
+            acc[3] += w * __uint_as_float(vw[u].y & 0xffff0000u);
         }
     }
     const float inv = 1.0f / lsum;
