@@ -444,7 +444,7 @@ def run_attention(args):
     rotated instances of a B=32 batch (2 KV heads x 8 query heads, head dim 256, a chain of 4
     draft tokens) with args.attention committed cache rows per sequence."""
     import torch
-    from linear_attention_speculative_head_amd import binding, inputs
+    from linear_attention_speculative_head_amd import accounting, binding, inputs
     B, Hkv, G, N, ctxn = 32, inputs.ATTN_HKV, inputs.ATTN_G, 4, args.attention
     T = ctxn + 64
     per = B * Hkv * T * 256 * 2 * 2
@@ -497,8 +497,7 @@ def run_attention(args):
     ms_bracketed = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     # algorithmic bytes: the committed cache rows read once, the draft tokens' q/k/v read, O
     # written (the split partials are the kernel's own traffic, not the method's)
-    nbytes = (B * Hkv * ctxn * 256 * 2 * 2 + B * N * (Hkv * G + 2 * Hkv) * 256 * 2
-              + B * N * Hkv * G * 256 * 4)
+    nbytes = accounting.attention_call_bytes(np.full(B, ctxn), N, Hkv, G)
     achieved = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] tree attention: {wall * 1e6 / K:.1f} us/step, {ms * 1e3:.1f} us per call over "
         f"the timed region ({ms_bracketed * 1e3:.1f} us with events around each call), "

@@ -129,3 +129,14 @@ def snapshot_step_bytes(parent: np.ndarray, accepted: np.ndarray, H: int, N: int
     v = layers * (B * H * snapshot_verify_bytes_per_head(N, elem) + B * 4 * N)
     c = layers * sum(4 + H * snapshot_commit_bytes_per_head(int(a)) for a in accepted)
     return dict(verify=v, commit=c, total=v + c)
+
+
+def attention_call_bytes(ctx, N: int, Hkv: int, G: int, d: int = 256, elem: int = 2) -> int:
+    """One tree-attention verify over a batch: each sequence's committed key and value rows
+    read once (every key/value head), the draft's queries (Hkv G heads), keys and values
+    (Hkv heads) read, and O (fp32, Hkv G heads) written.  The split partials are the
+    kernel's own traffic, not the method's."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    B = ctx.shape[0]
+    return int(ctx.sum() * Hkv * d * elem * 2 + B * N * (Hkv * G + 2 * Hkv) * d * elem
+               + B * N * Hkv * G * d * 4)
