@@ -1162,6 +1162,8 @@ void verify_small_kernel(
 // wait for a plain load also covers every transfer issued before it, so in that form nothing
 // may go out ahead of the fragment loads.
 
+constexpr int kLargePath = 8;                   // path rows staged per chunk (fused)
+
 template <int NKT>
 struct LargeLayout {
     static constexpr int kCols = 32 * NKT;                // G row pitch (keys | queries)
@@ -1178,19 +1180,37 @@ struct LargeLayout {
 // 0 .. 4 ceil(N/4) - 1 of a key/query area and queries right after them (256 B rows, chunk c of
 // row r at chunk c ^ (r % 16)); the item's half of the values (128 B rows); parents, alphas
 // and betas, 64 words each.
+// With the fused commit (staged kernel only) also: 8 path rows of U_prev halves and K_prev
+// (256 B each), the path's gammas (64 words), the previous tree (64 words) and the accepted
+// node (one word, repeated).
 struct LargeLds {
-    uint32_t kq, v, sm, bytes;
+    uint32_t kq, v, sm, pu, pk, pg, idx, acw, bytes;
 };
 
 template <int NKT, bool STAGE>
-__host__ __device__ inline LargeLds large_lds(int N) {
+__host__ __device__ inline LargeLds large_lds(int N, bool fused = false) {
     LargeLds L;
     const uint32_t fixed = sizeof(float) * LargeLayout<NKT>::kTotal;
     L.kq = fixed;
     L.v = L.kq + 2048u * static_cast<uint32_t>((N + 3) / 4);
     L.sm = L.v + 1024u * static_cast<uint32_t>((N + 7) / 8);
-    L.bytes = STAGE ? L.sm + 768u : fixed;
+    L.pu = L.sm + 768u;
+    L.pk = L.pu + 256u * kLargePath;
+    L.pg = L.pk + 256u * kLargePath;
+    L.idx = L.pg + 256u;
+    L.acw = L.idx + 256u;
+    L.bytes = STAGE ? (fused ? L.acw + 256u : L.sm + 768u) : fixed;
     return L;
+}
+
+// The path-row slots of the large kernel's fused commit, as the small kernel's helpers see them.
+__device__ __forceinline__ SmallLds large_path_view(const LargeLds& L) {
+    SmallLds P{};
+    P.pu = L.pu;
+    P.pk = L.pk;
+    P.pg = L.pg;
+    P.path = kLargePath;
+    return P;
 }
 
 // The staged inputs of an item -> LDS: ceil(N/4) loads of four key rows, as many of four
@@ -1273,7 +1293,68 @@ __device__ __forceinline__ void large_prefetch(LargePrefetch<NKT>& pf, const uin
     }
 }
 
-template <int NKT, bool STAGE>
+// The previous step's commit on this wave's 16 rows of an item, where they sit in LDS in the
+// layout they arrived in (lane l: row 16w + 2i + l / 32, 16-byte chunk l % 32, i = 0..7):
+// S_a = g_a S + sum over the path of a of (g_a / g_i) U_prev[i] k_i^T (paper §3 "Reconstruct
+// on commit", Eq. 3), written back to LDS for this step's contractions and to S as whole
+// 512-byte rows.  The first `P.path` path rows (and all the path's gammas) are in LDS; a
+// longer path fetches the rest chunk by chunk, with blocking waits.  Called by every wave.
+__device__ __forceinline__ void commit_rows_in_lds(float* lds, const char* ldsb, const SmallLds& P,
+                                                   const PathInfo& cur, const CommitIn& cin,
+                                                   int bh, int part, int H, int wave, int lane,
+                                                   uint32_t lds_addr) {
+    const float* PG = reinterpret_cast<const float*>(ldsb + P.pg);
+    const float* PU = reinterpret_cast<const float*>(ldsb + P.pu);
+    const char* PK = ldsb + P.pk;
+    const float ga = PG[cur.depth - 1];
+    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
+    const int nchunk = (cur.depth + P.path - 1) / P.path;
+    for (int ci = 0; ci < nchunk; ++ci) {
+        const int q0 = ci * P.path;
+        if (ci > 0) {
+            lds_barrier();
+            fused_issue_path(cin, cur, ci, bh, part, H, wave, lane, lds_addr, P);
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+        const int rem = cur.depth - q0;
+        const int cnt = rem < P.path ? rem : P.path;
+        f32x4_t x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = 16u * wave + 2u * i + hl;
+            x[i] = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
+            if (ci == 0) x[i] *= ga;
+        }
+        for (int q = 0; q < cnt; ++q) {
+            const float cq = ga / PG[q0 + q];
+            const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
+            const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
+                                __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float cu = cq * PU[q * kSmallRows + 16 * wave + 2 * i + hl];
+                x[i] += cu * kv;
+            }
+        }
+        const bool last = ci + 1 == nchunk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = 16u * wave + 2u * i + hl;
+            *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
+            if (last)
+                *reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D +
+                                                     part * kSmallRows + r) * D + 4 * ch) = x[i];
+        }
+    }
+}
+
+// FUSED (staged form only): the previous step's commit first, as in the small-tree kernel's
+// MODE 1, but with the path derived at the top of each item from the previous tree and
+// accepted node that came with the item's inputs; its rows are requested then and land while
+// the tree is walked.
+template <int NKT, bool STAGE, bool FUSED = false>
 __global__ __launch_bounds__(kSmallThreads)
 __attribute__((amdgpu_waves_per_eu(STAGE ? (NKT == 2 ? 2 : 1) : (NKT == 2 ? 3 : 2))))
 void verify_large_kernel(
@@ -1282,14 +1363,15 @@ void verify_large_kernel(
     const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
     float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
-    int32_t* __restrict__ status)
+    int32_t* __restrict__ status, CommitIn cin)
 {
+    static_assert(!FUSED || STAGE, "the fused commit runs in the staged form only");
     using Lo = LargeLayout<NKT>;
     constexpr int NCT = 2 * NKT;
     constexpr int kCols = Lo::kCols;
     extern __shared__ __align__(16) float lds[];
     float* G = lds + Lo::kS0;                       // G[m][n], n: keys 0..N-1, queries 16NKT+t
-    const LargeLds Ls = large_lds<NKT, STAGE>(N);
+    const LargeLds Ls = large_lds<NKT, STAGE>(N, FUSED);
     const char* ldsb = reinterpret_cast<const char*>(lds);
     const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     const int nq4 = (N + 3) >> 2;
@@ -1313,6 +1395,10 @@ void verify_large_kernel(
         large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, Ls);
     else
         large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh, part, wave, lane);
+    if constexpr (FUSED) {
+        if (wave == 2) fused_issue_index(cin, bh / H, lane, lds_addr + Ls.idx);
+        if (wave == 3) dma_gather_x1(cin.accepted + bh / H, lds_addr + Ls.acw);
+    }
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(pf.vraw[kt]));
@@ -1362,6 +1448,16 @@ void verify_large_kernel(
             lds_barrier();
         }
 
+        // ---- the previous step's commit: this item's path, its rows requested now
+        PathInfo cur{0ull, 0, 0};
+        if constexpr (FUSED) {
+            cur = fused_path(lane < cin.Np ? reinterpret_cast<const int*>(ldsb + Ls.idx)[lane] : -1,
+                             reinterpret_cast<const int*>(ldsb + Ls.acw)[0], cin.Np, lane,
+                             wave == 0 && bh % H == 0 && part == 0, status);
+            if (cur.depth > 0)
+                fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr, large_path_view(Ls));
+        }
+
         // ---- tree walk, lane = node (every wave)
         uint64_t anc_l;
         float g_l, rg_l;
@@ -1396,7 +1492,16 @@ void verify_large_kernel(
             }
         }
 
-        // ---- MFMA operands of this wave's 16 rows
+        if constexpr (FUSED) {
+            if (cur.depth > 0) {
+                __builtin_amdgcn_s_waitcnt(0);      // the path rows (and the last stores)
+                lds_barrier();
+                commit_rows_in_lds(lds, ldsb, large_path_view(Ls), cur, cin, bh, part, H, wave,
+                                   lane, lds_addr);
+            }
+        }
+
+        // ---- MFMA operands of this wave's 16 rows (committed, with FUSED)
         bf16x8_t ahi[4], alo[4];
         {
             const int r = 16 * wave + col;
@@ -1481,6 +1586,10 @@ void verify_large_kernel(
             if (more)
                 large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
                                    lds_addr, Ls);
+        }
+        if constexpr (FUSED) {
+            if (more && wave == 2) fused_issue_index(cin, bh_n / H, lane, lds_addr + Ls.idx);
+            if (more && wave == 3) dma_gather_x1(cin.accepted + bh_n / H, lds_addr + Ls.acw);
         }
 
         // ---- per lane: nodes t = 16 kt + col, rows v0..v0+3
@@ -1624,11 +1733,12 @@ static hipError_t launch_verify_t(const VerifyArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int NKT, bool STAGE>
-static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream) {
-    const LargeLds L = large_lds<NKT, STAGE>(a.N);
+template <int NKT, bool STAGE, bool FUSED = false>
+static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream,
+                               const CommitIn* cin = nullptr) {
+    const LargeLds L = large_lds<NKT, STAGE>(a.N, FUSED);
     const size_t dyn = L.bytes;
-    auto kern = verify_large_kernel<NKT, STAGE>;
+    auto kern = verify_large_kernel<NKT, STAGE, FUSED>;
     if (dyn > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1644,7 +1754,8 @@ static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), dyn, stream, a.S0,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
-                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status);
+                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status,
+                       cin ? *cin : CommitIn{});
     return hipGetLastError();
 }
 
@@ -1671,6 +1782,11 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
         const DeferLog nolog{};
         return a.N <= 8 ? launch_small<1, 1>(a, cin, nolog, stream)
                         : launch_small<2, 1>(a, cin, nolog, stream);
+    }
+    if (a.in_dtype == TREEWY_BF16 && a.N <= 32) {
+        const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
+                           c.accepted, c.N};
+        return launch_large<2, true, true>(a, stream, &cin);
     }
     hipError_t e = launch_commit(c, stream);
     if (e != hipSuccess) return e;

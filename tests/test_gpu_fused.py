@@ -43,6 +43,9 @@ def test_fused_config_full(cfg):
     (64, "chain", 16, "chain", 25),   # depth up to 64: eight chunks
     (40, (6, 4), 1, "chain", 26),
     (7, (3, 3), 9, (4, 3), 27),
+    (40, "chain", 24, (5, 4), 28),    # the large-tree kernel's fused commit, paths of 5 chunks
+    (64, "chain", 32, "chain", 29),   # ... at its largest tree, paths of up to 8 chunks
+    (3, (2, 2), 17, (4, 4), 30),      # ... at its smallest
 ])
 def test_fused_shapes(N1, tree1, N2, tree2, seed):
     """Ragged node counts on both steps, deep previous paths, every head compared."""
