@@ -1180,9 +1180,8 @@ struct LargeLayout {
 // 0 .. 4 ceil(N/4) - 1 of a key/query area and queries right after them (256 B rows, chunk c of
 // row r at chunk c ^ (r % 16)); the item's half of the values (128 B rows); parents, alphas
 // and betas, 64 words each.
-// With the fused commit (staged kernel only) also: 8 path rows of U_prev halves and K_prev
-// (256 B each), the path's gammas (64 words), the previous tree (64 words) and the accepted
-// node (one word, repeated).
+// With the fused commit also: 8 path rows of U_prev halves and K_prev (256 B each), the path's
+// gammas (64 words), the previous tree (64 words) and the accepted node (one word, repeated).
 struct LargeLds {
     uint32_t kq, v, sm, pu, pk, pg, idx, acw, bytes;
 };
@@ -1194,12 +1193,23 @@ __host__ __device__ inline LargeLds large_lds(int N, bool fused = false) {
     L.kq = fixed;
     L.v = L.kq + 2048u * static_cast<uint32_t>((N + 3) / 4);
     L.sm = L.v + 1024u * static_cast<uint32_t>((N + 7) / 8);
+    if (!STAGE) {
+        // unstaged, the fused commit's path rows borrow the U exchange area (the path is
+        // committed before the contractions, the exchange runs after them); the previous
+        // tree and accepted node travel in registers
+        L.pu = sizeof(float) * (LargeLayout<NKT>::kS0 + LargeLayout<NKT>::kG);
+        L.pk = L.pu + 256u * kLargePath;
+        L.pg = L.pk + 256u * kLargePath;
+        L.idx = L.acw = 0;
+        L.bytes = fixed;
+        return L;
+    }
     L.pu = L.sm + 768u;
     L.pk = L.pu + 256u * kLargePath;
     L.pg = L.pk + 256u * kLargePath;
     L.idx = L.pg + 256u;
     L.acw = L.idx + 256u;
-    L.bytes = STAGE ? (fused ? L.acw + 256u : L.sm + 768u) : fixed;
+    L.bytes = fused ? L.acw + 256u : L.sm + 768u;
     return L;
 }
 
@@ -1350,10 +1360,9 @@ __device__ __forceinline__ void commit_rows_in_lds(float* lds, const char* ldsb,
     }
 }
 
-// FUSED (staged form only): the previous step's commit first, as in the small-tree kernel's
-// MODE 1, but with the path derived at the top of each item from the previous tree and
-// accepted node that came with the item's inputs; its rows are requested then and land while
-// the tree is walked.
+// FUSED: the previous step's commit first, as in the small-tree kernel's MODE 1, but with the
+// path derived at the top of each item from the previous tree and accepted node that came
+// with the item's inputs; its rows are requested then and land while the tree is walked.
 template <int NKT, bool STAGE, bool FUSED = false>
 __global__ __launch_bounds__(kSmallThreads)
 __attribute__((amdgpu_waves_per_eu(STAGE ? (NKT == 2 ? 2 : 1) : (NKT == 2 ? 3 : 2))))
@@ -1365,7 +1374,6 @@ void verify_large_kernel(
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
     int32_t* __restrict__ status, CommitIn cin)
 {
-    static_assert(!FUSED || STAGE, "the fused commit runs in the staged form only");
     using Lo = LargeLayout<NKT>;
     constexpr int NCT = 2 * NKT;
     constexpr int kCols = Lo::kCols;
@@ -1395,9 +1403,13 @@ void verify_large_kernel(
         large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, Ls);
     else
         large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh, part, wave, lane);
-    if constexpr (FUSED) {
+    int pidx = -1, pacc = -1;                       // unstaged FUSED: previous tree, accepted
+    if constexpr (FUSED && STAGE) {
         if (wave == 2) fused_issue_index(cin, bh / H, lane, lds_addr + Ls.idx);
         if (wave == 3) dma_gather_x1(cin.accepted + bh / H, lds_addr + Ls.acw);
+    } else if constexpr (FUSED) {
+        pidx = lane < cin.Np ? cin.parent[static_cast<size_t>(bh / H) * cin.Np + lane] : -1;
+        pacc = cin.accepted[bh / H];
     }
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
@@ -1445,15 +1457,19 @@ void verify_large_kernel(
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(vraw[kt]));
             asm volatile("" ::"v"(my_par), "v"(my_alpha), "v"(my_beta));
+            if constexpr (FUSED) asm volatile("" ::"v"(pidx), "v"(pacc));
             lds_barrier();
         }
 
         // ---- the previous step's commit: this item's path, its rows requested now
         PathInfo cur{0ull, 0, 0};
         if constexpr (FUSED) {
-            cur = fused_path(lane < cin.Np ? reinterpret_cast<const int*>(ldsb + Ls.idx)[lane] : -1,
-                             reinterpret_cast<const int*>(ldsb + Ls.acw)[0], cin.Np, lane,
-                             wave == 0 && bh % H == 0 && part == 0, status);
+            if constexpr (STAGE) {
+                pidx = lane < cin.Np ? reinterpret_cast<const int*>(ldsb + Ls.idx)[lane] : -1;
+                pacc = reinterpret_cast<const int*>(ldsb + Ls.acw)[0];
+            }
+            cur = fused_path(pidx, pacc, cin.Np, lane, wave == 0 && bh % H == 0 && part == 0,
+                             status);
             if (cur.depth > 0)
                 fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr, large_path_view(Ls));
         }
@@ -1580,6 +1596,12 @@ void verify_large_kernel(
         if constexpr (!STAGE) {
             if (more)
                 large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
+            if constexpr (FUSED) {
+                if (more) {
+                    pidx = lane < cin.Np ? cin.parent[static_cast<size_t>(bh_n / H) * cin.Np + lane] : -1;
+                    pacc = cin.accepted[bh_n / H];
+                }
+            }
         }
         lds_barrier();                              // G visible to every wave; inputs read
         if constexpr (STAGE) {
@@ -1783,10 +1805,11 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
         return a.N <= 8 ? launch_small<1, 1>(a, cin, nolog, stream)
                         : launch_small<2, 1>(a, cin, nolog, stream);
     }
-    if (a.in_dtype == TREEWY_BF16 && a.N <= 32) {
+    if (a.in_dtype == TREEWY_BF16) {
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
                            c.accepted, c.N};
-        return launch_large<2, true, true>(a, stream, &cin);
+        return a.N <= 32 ? launch_large<2, true, true>(a, stream, &cin)
+                         : launch_large<4, false, true>(a, stream, &cin);
     }
     hipError_t e = launch_commit(c, stream);
     if (e != hipSuccess) return e;

@@ -46,6 +46,8 @@ def test_fused_config_full(cfg):
     (40, "chain", 24, (5, 4), 28),    # the large-tree kernel's fused commit, paths of 5 chunks
     (64, "chain", 32, "chain", 29),   # ... at its largest tree, paths of up to 8 chunks
     (3, (2, 2), 17, (4, 4), 30),      # ... at its smallest
+    (20, (5, 3), 40, (6, 4), 31),     # the unstaged large-tree kernel's fused commit
+    (64, "chain", 64, (6, 4), 32),    # ... at 64 nodes, previous paths of up to 64 rows
 ])
 def test_fused_shapes(N1, tree1, N2, tree2, seed):
     """Ragged node counts on both steps, deep previous paths, every head compared."""
@@ -67,7 +69,8 @@ def test_fused_shapes(N1, tree1, N2, tree2, seed):
 
 @pytest.mark.parametrize("N2,dtype", [(32, "bf16"), (64, "bf16"), (6, "f32")])
 def test_unfused_shapes_match(N2, dtype):
-    """Shapes the library runs as commit then verify give the same contract."""
+    """Every kernel shape under the same contract: the large-tree kernels (bf16, fused) and
+    fp32 inputs (commit then verify)."""
     say(f"[fused] two-kernel shape N={N2} {dtype}")
     P1 = inputs.make_custom(31, B=3, H=4, N=10, dtype=dtype, tree=(4, 3))
     P2 = inputs.make_custom(32, B=3, H=4, N=N2, dtype=dtype, tree=(6, 4))
