@@ -104,9 +104,9 @@ int treewy_commit(float* S, const float* U, const void* K, const float* gamma,
  *                   B, H, N_prev, in_dtype, status, stream);
  *     treewy_verify(S, Q, K, V, alpha, beta, parent, B, H, N, in_dtype,
  *                   O, U, gamma, anc_out, depth_out, status, stream);
- * but for bf16 inputs with N <= 16 it runs as one kernel that reads and writes each state
- * once: the committed rows are formed on the way into the contractions.  Other shapes run
- * the two kernels above in that order.
+ * but for bf16 inputs it runs as one kernel that reads and writes each state once: the
+ * committed rows are formed on the way into the contractions.  fp32 inputs run the two
+ * kernels above in that order.
  *   S                     [B, H, 128, 128] float32, in place: in, the state before the
  *                         previous step's commit; out, the committed state (the state this
  *                         step verified against).  Rows of sequences with
