@@ -2,7 +2,9 @@
 
 The compute path is ``libtreewy.so`` (HIP kernels for gfx950 behind the C ABI of
 ``include/treewy.h``); ``binding`` marshals torch tensors into it.  ``inputs`` draws
-seeded synthetic workloads and ``accounting`` counts the algorithmic bytes.
+seeded synthetic workloads and ``accounting`` counts the algorithmic bytes.  ``api`` has
+allocating forms of the calls (``verify``, ``commit``, ``commit_verify``, ``tree_attention``,
+``kv_commit``).
 """
 
 from .binding import (  # noqa: F401
@@ -12,3 +14,4 @@ from .binding import (  # noqa: F401
     treewy_kv_commit, treewy_strerror, treewy_tree_attention, treewy_tree_attention_workspace,
     treewy_verify, treewy_verify_snapshot, treewy_version,
 )
+from .api import commit, commit_verify, kv_commit, tree_attention, verify  # noqa: F401,E402
