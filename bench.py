@@ -418,7 +418,7 @@ def run(args, mode, wl):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; Qwen3.5-shaped GDN heads, dk=dv=128)",
-        "config": {"workload": f"{wl.name}: {wl.desc}" + desc,
+        "config": {"workload": wl.desc + desc,
                    "B": B, "H": H, "N": N, "layers": nl, "qkv_dtype": dtype,
                    "state_dtype": "f32", "instances_rotated": n_inst,
                    "launch": "hip-graph" if args.graph else "stream"},
