@@ -1267,6 +1267,29 @@ __device__ __forceinline__ void large_issue_inputs(const uint16_t* Q, const uint
     }
 }
 
+// The item's key and query rows alone -> LDS at `lds` (the staged layout: keys in rows
+// 0 .. 4 ceil(N/4) - 1, queries right after, 256 B rows, chunk c of row r at c ^ (r % 16)),
+// 2 ceil(N/4) transfers of four rows dealt to the four waves.  At most 32 KiB for N <= 64.
+__device__ __forceinline__ void large_issue_kq(const uint16_t* Q, const uint16_t* K, int H, int N,
+                                               int bh, int wave, int lane, uint32_t lds) {
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * N;
+    const uint32_t row_bytes = static_cast<uint32_t>(H) * D * 2;
+    const uint16_t* Kh = K + (node0 * H + h) * D;
+    const uint16_t* Qh = Q + (node0 * H + h) * D;
+    const uint32_t un = static_cast<uint32_t>(N);
+    const int nq4 = (N + 3) >> 2;
+    for (int j = wave; j < 2 * nq4; j += 4) {
+        const bool is_q = j >= nq4;
+        const uint32_t lr = static_cast<uint32_t>(lane) >> 4;
+        const uint32_t r = 4u * j + lr;
+        const uint32_t n = 4u * (is_q ? j - nq4 : j) + lr;
+        const uint32_t c = (static_cast<uint32_t>(lane) & 15u) ^ (r & 15u);
+        dma_x4(is_q ? Qh : Kh, (n < un ? n : 0u) * row_bytes + 16u * c, lds + 1024u * j);
+    }
+}
+
 template <int NKT>
 struct LargePrefetch {
     uint2 vraw[NKT];          // v of node 16 kt + lane % 16, rows v0..v0+3 (bf16)
@@ -1536,6 +1559,15 @@ void verify_large_kernel(
         small_item(round, slot, grid, bh_n, part_n);
         const bool more = bh_n < BH;
 
+        // unstaged: the item's key and query rows go into the S-row area, free from here until
+        // the next item's rows are requested (after the contractions)
+        const uint32_t kq_off = STAGE ? Ls.kq : 0u;
+        if constexpr (!STAGE) {
+            large_issue_kq(Q, K, H, N, bh, wave, lane, lds_addr);
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+
         // ---- contractions and Gram rows 16w..16w+15 (waves with keys there)
         const bool has_gram = wave < NKT && 16 * wave < N;
         bf16x8_t ka[4];
@@ -1544,13 +1576,9 @@ void verify_large_kernel(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 u32x4_t w = {0u, 0u, 0u, 0u};
-                if (has_gram && m < static_cast<uint32_t>(N)) {
-                    if constexpr (STAGE)
-                        w = *reinterpret_cast<const u32x4_t*>(
-                            ldsb + Ls.kq + 256 * m + 16 * ((4 * ks + grp) ^ (m & 15)));
-                    else
-                        w = *reinterpret_cast<const u32x4_t*>(Kh + (m * node_stride + kq + 32 * ks));
-                }
+                if (has_gram && m < static_cast<uint32_t>(N))
+                    w = *reinterpret_cast<const u32x4_t*>(
+                        ldsb + kq_off + 256 * m + 16 * ((4 * ks + grp) ^ (m & 15)));
                 ka[ks] = __builtin_bit_cast(bf16x8_t, w);
             }
         }
@@ -1560,19 +1588,14 @@ void verify_large_kernel(
             const uint32_t n = 16u * (c % NKT) + col;          // node of this column
             const bool is_q = c >= NKT;
             const bool live = n < static_cast<uint32_t>(N);
-            const uint16_t* src = (is_q ? Qh : Kh) + (n * node_stride + kq);
             const uint32_t r = is_q ? 4u * nq4 + n : n;            // staged row
             bf16x8_t bv[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 u32x4_t w = {0u, 0u, 0u, 0u};
-                if (live) {
-                    if constexpr (STAGE)
-                        w = *reinterpret_cast<const u32x4_t*>(
-                            ldsb + Ls.kq + 256 * r + 16 * ((4u * ks + grp) ^ (r & 15u)));
-                    else
-                        w = *reinterpret_cast<const u32x4_t*>(src + 32 * ks);
-                }
+                if (live)
+                    w = *reinterpret_cast<const u32x4_t*>(
+                        ldsb + kq_off + 256 * r + 16 * ((4u * ks + grp) ^ (r & 15u)));
                 bv[ks] = __builtin_bit_cast(bf16x8_t, w);
             }
             acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1590,10 +1613,15 @@ void verify_large_kernel(
                     G[(16 * wave + 4 * grp + e) * kCols + 16 * c + col] = gacc[e];
             }
         }
-        // the next item's rows only now: unstaged, the key and query fragments above are
-        // plain loads, and a wait for them would also wait for every transfer issued before
-        if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+        // the next item's rows only now (staged: the next inputs were requested at the top of
+        // the item; unstaged: the key and query rows sit in the S-row area until every wave
+        // is past the contractions)
+        if constexpr (STAGE) {
+            if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+        }
+        lds_barrier();                              // G visible to every wave; inputs read
         if constexpr (!STAGE) {
+            if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
             if (more)
                 large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
             if constexpr (FUSED) {
@@ -1603,7 +1631,6 @@ void verify_large_kernel(
                 }
             }
         }
-        lds_barrier();                              // G visible to every wave; inputs read
         if constexpr (STAGE) {
             if (more)
                 large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
