@@ -1667,39 +1667,73 @@ void verify_large_kernel(
             *reinterpret_cast<f32x4_t*>(Us + t * 16 + 4 * grp) =
                 f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
         }
-        // ancestor walk: step d folds in every node's depth-d ancestor (final since step d - 1)
-        for (;;) {
-            bool any = false;
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) any |= mrem[kt] != 0ull;
-            if (!__any(any)) break;
+        // ancestor walk: step d folds in every node's depth-d ancestor (final since step d - 1).
+        // The coefficients of a step (ancestor gates by lane permute, Gram entries) do not
+        // depend on U, so those of step d + 1 are requested while step d's U rows are read.
+        float cs[NKT], cw[NKT];
+        int asel[NKT];
+        auto coeffs = [&](float (&cs_)[NKT], float (&cw_)[NKT], int (&as_)[NKT]) {
             float rgsrc[NKT];
-            int asel[NKT];
             bool hasa[NKT];
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
                 hasa[kt] = mrem[kt] != 0ull;
-                asel[kt] = hasa[kt] ? __ffsll(static_cast<unsigned long long>(mrem[kt])) - 1 : tn[kt] & 63;
+                as_[kt] = hasa[kt] ? __ffsll(static_cast<unsigned long long>(mrem[kt])) - 1 : tn[kt] & 63;
                 mrem[kt] &= mrem[kt] - 1;
-                rgsrc[kt] = __shfl(rg_l, asel[kt]);
+                rgsrc[kt] = __shfl(rg_l, as_[kt]);
             }
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
-                const int a = asel[kt];
+                const int a = as_[kt];
                 const int t = tn[kt];
-                const float cs = hasa[kt] ? bgt[kt] * rgsrc[kt] * G[t * kCols + a] : 0.f;
-                const float cw = hasa[kt] ? gt[kt] * rgsrc[kt] * G[a * kCols + 16 * NKT + t] : 0.f;
-                const f32x4_t x = *reinterpret_cast<const f32x4_t*>(Us + a * 16 + 4 * grp);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    Uv[kt][e] -= cs * x[e];
-                    Ov[kt][e] += cw * x[e];
-                }
+                cs_[kt] = hasa[kt] ? bgt[kt] * rgsrc[kt] * G[t * kCols + a] : 0.f;
+                cw_[kt] = hasa[kt] ? gt[kt] * rgsrc[kt] * G[a * kCols + 16 * NKT + t] : 0.f;
             }
+        };
+        auto pending = [&]() {
+            bool any = false;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) any |= mrem[kt] != 0ull;
+            return __any(any) != 0;
+        };
+        // (not with the fused commit at 64 nodes, whose registers would spill)
+        constexpr bool kAhead = !(NKT == 4 && FUSED);
+        bool step = pending();
+        if (step) coeffs(cs, cw, asel);
+        while (step) {
+            f32x4_t x[NKT];
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
+                x[kt] = *reinterpret_cast<const f32x4_t*>(Us + asel[kt] * 16 + 4 * grp);
+            float cs_n[NKT], cw_n[NKT];
+            int as_n[NKT];
+            if constexpr (kAhead) {
+                step = pending();
+                if (step) coeffs(cs_n, cw_n, as_n);
+            }
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Uv[kt][e] -= cs[kt] * x[kt][e];
+                    Ov[kt][e] += cw[kt] * x[kt][e];
+                }
                 *reinterpret_cast<f32x4_t*>(Us + tn[kt] * 16 + 4 * grp) =
                     f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
+            }
+            if constexpr (kAhead) {
+                if (step) {
+#pragma unroll
+                    for (int kt = 0; kt < NKT; ++kt) {
+                        cs[kt] = cs_n[kt];
+                        cw[kt] = cw_n[kt];
+                        asel[kt] = as_n[kt];
+                    }
+                }
+            } else {
+                step = pending();
+                if (step) coeffs(cs, cw, asel);
+            }
         }
         const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
         const size_t row0 = (node0 * H + h) * D;
