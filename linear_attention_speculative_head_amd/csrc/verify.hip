@@ -1636,7 +1636,7 @@ void verify_large_kernel(
                 large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
                                    lds_addr, Ls);
         }
-        if constexpr (FUSED) {
+        if constexpr (FUSED && STAGE) {    // (unstaged, they travel in registers)
             if (more && wave == 2) fused_issue_index(cin, bh_n / H, lane, lds_addr + Ls.idx);
             if (more && wave == 3) dma_gather_x1(cin.accepted + bh_n / H, lds_addr + Ls.acw);
         }
