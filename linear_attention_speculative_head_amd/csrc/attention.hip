@@ -5,12 +5,13 @@
 // attention", Eq. (2), and §2.2 on tree-structured drafting), with the ancestor sets the GDN
 // path uses.  Head dimension 256; query head hq reads key/value head hq / G.
 //
-// Split over the cache (the HBM stream): one workgroup per (sequence, key/value head, block of
-// 32 queries, range of cache rows), the ranges sized at launch so that about four workgroups
-// per compute unit cover the batch (few splits keep the partials' traffic small).  It keeps the 32 queries in registers as MFMA fragments and walks
-// its rows 32 at a time, keys and values HBM -> LDS (global_load_lds_dwordx4) in two stages so
-// that the next tile's keys stream in while this tile's values are used and the next tile's
-// values while the next scores are formed.  Scores are formed transposed, S^T = K Q^T (bf16
+// Split over the cache (the HBM stream): one workgroup of two waves per (sequence, key/value
+// head, block of 32 queries, range of cache rows), the ranges sized at launch so that about
+// four workgroups per compute unit cover the batch (few ranges keep the partials' traffic
+// small).  Each wave keeps its 16 queries in registers as MFMA fragments; the two walk the
+// range's rows 32 at a time, keys and values HBM -> LDS (global_load_lds_dwordx4) in two
+// stages so that the next tile's keys stream in while this tile's values are used and the
+// next tile's values while the next scores are formed.  Scores are formed transposed, S^T = K Q^T (bf16
 // inputs, fp32 accumulation on the matrix cores), so that each lane holds one query's scores
 // for 8 cache rows: exactly the B operand the product O^T += V^T P^T needs, so P never leaves
 // the registers; it is split into bf16 hi + lo (|P - hi - lo| <= 2^-16 P).  V^T comes from LDS
@@ -19,7 +20,8 @@
 // P stays below 2^8 and the accumulators are touched only when the maximum really moves; the
 // scale cancels in the final normalisation.  The partial (O unnormalised, the row maxima m,
 // the row sums l) goes to a workspace.  A second kernel merges the partials of each query,
-// adds the draft keys it may see (at most 64, walked from the tree), and normalises.
+// adds the draft keys it may see (its ancestors-or-self, at most 64, from the whole tree by
+// pointer jumping), and normalises.
 
 #include "device_common.h"
 #include "launch.h"

@@ -1156,11 +1156,11 @@ void verify_small_kernel(
 // G = K [K;Q]^T (same column layout) is formed by waves 0..NKT-1 and staged in LDS.
 //
 // The next item's S0 rows are requested once this item's contractions are done.  With
-// STAGE, its keys, queries, values, gates and tree then follow by direct transfers into LDS,
-// and the contractions read their fragments from there.  Without it they are plain loads
-// into registers (fragments from L2 inside the contraction loop, the rest prefetched).  A
-// wait for a plain load also covers every transfer issued before it, so in that form nothing
-// may go out ahead of the fragment loads.
+// STAGE, its keys, queries, values, gates and tree then follow by direct transfers into an
+// LDS area of their own, and the contractions read their fragments from there.  Without it
+// (up to 64 nodes, where that area would leave one workgroup per CU) the item's key and
+// query rows are sent into the S-row area once the rows have been taken into registers, and
+// the contractions read them there; values, gates and tree are prefetched into registers.
 
 constexpr int kLargePath = 8;                   // path rows staged per chunk (fused)
 
@@ -1848,9 +1848,9 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     const DeferLog nolog{};
     if (a.N <= 8) return launch_small<1, 0>(a, none, nolog, stream);
     if (a.N <= 16) return launch_small<2, 0>(a, none, nolog, stream);
-    // trees of up to 32 nodes stage their inputs through LDS (two workgroups per CU); at 64
-    // nodes the staged inputs would leave room for one workgroup per CU, which measured
-    // slower than two that read key and query fragments from L2
+    // trees of up to 32 nodes stage their inputs through an LDS area of their own (two
+    // workgroups per CU); larger ones reuse the S-row area for their key and query rows, since
+    // a separate area would leave room for one workgroup per CU
     if (a.N <= 32) return launch_large<2, true>(a, stream);
     return launch_large<4, false>(a, stream);
 }
