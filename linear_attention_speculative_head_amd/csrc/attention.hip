@@ -54,7 +54,10 @@ constexpr int kWaitLgkm0 = 0xC07F;
 
 // One HBM -> LDS load of 16 bytes per lane (lane l lands at lds + 16 l), from a scalar base and
 // a 32-bit lane offset.  M0 holds the LDS destination and is restored; the caller waits on
-// vmcnt before reading the rows.
+// vmcnt before reading the rows.  With NT the load carries the non-temporal (streaming) hint:
+// for cache rows that only one workgroup of the call reads, so they do not displace other
+// data in the caches.
+template <bool NT>
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
     lds = __builtin_amdgcn_readfirstlane(lds);
     const uint64_t x = reinterpret_cast<uint64_t>(base);
@@ -62,29 +65,45 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
     const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
     const void* b = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
     uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, %3\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "s"(lds), "v"(voff), "s"(b)
-        : "memory");
+    if constexpr (NT)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %2, %3 nt\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(save)
+            : "s"(lds), "v"(voff), "s"(b)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %2, %3\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(save)
+            : "s"(lds), "v"(voff), "s"(b)
+            : "memory");
 }
 
 // This wave's half of 32 rows kk .. kk + 31 of one cache (wave w: rows 16 w .. 16 w + 15;
 // rows at or past k1 fetch row kk again, their scores are masked) into LDS: row r is 512
 // bytes, its 16-byte chunk c stored at position c ^ (r % 16).  Two rows per load, eight loads.
+// `stream`: no other query block reads these rows (one block per sequence and head).
 __device__ __forceinline__ void load_half(const uint16_t* base, int kk, int k1, uint32_t lds,
-                                          int lane, int w) {
+                                          int lane, int w, bool stream) {
     const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
     const uint32_t ch = static_cast<uint32_t>(lane) & 31u;
 #pragma unroll
     for (int i = 0; i < kTile / 4; ++i) {
         const uint32_t r = 16u * w + 2u * i + hl;
         const uint32_t row = kk + r < static_cast<uint32_t>(k1) ? kk + r : kk;
-        dma16(base, row * (DA * 2u) + 16u * (ch ^ (r & 15u)), lds + 8192u * w + 1024u * i);
+        const uint32_t off = row * (DA * 2u) + 16u * (ch ^ (r & 15u));
+        if (stream)
+            dma16<true>(base, off, lds + 8192u * w + 1024u * i);
+        else
+            dma16<false>(base, off, lds + 8192u * w + 1024u * i);
     }
 }
 
@@ -127,8 +146,9 @@ void attn_partial_kernel(const uint16_t* __restrict__ Kc, const uint16_t* __rest
     const uint16_t* Vb = Vc + static_cast<size_t>(bk) * T_max * DA;
     const uint32_t ldsK = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sK));
     const uint32_t ldsV = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sV));
-    load_half(Kb, k0, k1, ldsK, lane, w);
-    load_half(Vb, k0, k1, ldsV, lane, w);
+    const bool stream = gridDim.y == 1;         // one query block: each row is read once
+    load_half(Kb, k0, k1, ldsK, lane, w, stream);
+    load_half(Vb, k0, k1, ldsV, lane, w, stream);
 
     // this wave's queries as B fragments: lane L holds query 16 w + L % 16 of the block, dims
     // 32 kb + 8 (L / 16) .. +7
@@ -190,7 +210,7 @@ void attn_partial_kernel(const uint16_t* __restrict__ Kc, const uint16_t* __rest
         // both waves are done with the keys: the next ones stream in during this tile
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __syncthreads();
-        if (more) load_half(Kb, kk + kTile, k1, ldsK, lane, w);
+        if (more) load_half(Kb, kk + kTile, k1, ldsK, lane, w, stream);
 
         bf16x8_t ph, pl;
         if (active) {
@@ -264,7 +284,7 @@ void attn_partial_kernel(const uint16_t* __restrict__ Kc, const uint16_t* __rest
         // both waves are done with the values: the next ones stream in during the next scores
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __syncthreads();
-        if (more) load_half(Vb, kk + kTile, k1, ldsV, lane, w);
+        if (more) load_half(Vb, kk + kTile, k1, ldsV, lane, w, stream);
     }
     if (!active) return;
 

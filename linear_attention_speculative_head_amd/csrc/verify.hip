@@ -247,6 +247,7 @@ constexpr int kWaitAllButEight = 8 | (7 << 4) | (15 << 8);
 constexpr int kWaitLdsOnly = 0xC07F;            // LDS/scalar count 0, the rest left free
 // dword 3 of a raw (unstrided, range-checked) buffer descriptor on gfx9-family parts
 constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kStreamAux = 2;                   // buffer-store cache policy: non-temporal
 constexpr int kSmallRows = 64;              // value rows per item
 constexpr int kSmallParts = D / kSmallRows; // items per head
 
@@ -346,43 +347,38 @@ __device__ __forceinline__ void small_item(int round, int slot, int grid, int& b
 // so the compiler does not treat every later LDS access as a possible alias of the transfer
 // (it would wait for it right away); the caller waits on vmcnt before reading the rows.
 // M0 holds the LDS destination and is restored afterwards; only vector memory is accessed.
+// With NT the loads carry the non-temporal (streaming) hint: for state rows that are read
+// once and then overwritten, so they are not kept in the caches at the expense of other data.
+#define TREEWY_ROWS_X8(POL)                                                                    \
+    "s_mov_b32 %0, m0\n\t"                                                                   \
+    "s_mov_b32 m0, %1\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %9, %17" POL "\n\t"      \
+    "s_mov_b32 m0, %2\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %10, %17" POL "\n\t"     \
+    "s_mov_b32 m0, %3\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %11, %17" POL "\n\t"     \
+    "s_mov_b32 m0, %4\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %12, %17" POL "\n\t"     \
+    "s_mov_b32 m0, %5\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %13, %17" POL "\n\t"     \
+    "s_mov_b32 m0, %6\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %14, %17" POL "\n\t"     \
+    "s_mov_b32 m0, %7\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %15, %17" POL "\n\t"     \
+    "s_mov_b32 m0, %8\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %16, %17" POL "\n\t"     \
+    "s_mov_b32 m0, %0"
+
+template <bool NT>
 __device__ __forceinline__ void dma_rows_x8(const void* base, const uint32_t (&voff)[8],
                                             uint32_t lds0) {
     uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %9, %17\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %10, %17\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %11, %17\n\t"
-        "s_mov_b32 m0, %4\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %12, %17\n\t"
-        "s_mov_b32 m0, %5\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %13, %17\n\t"
-        "s_mov_b32 m0, %6\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %14, %17\n\t"
-        "s_mov_b32 m0, %7\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %15, %17\n\t"
-        "s_mov_b32 m0, %8\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %16, %17\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "s"(lds0), "s"(lds0 + 1024u), "s"(lds0 + 2048u), "s"(lds0 + 3072u),
-          "s"(lds0 + 4096u), "s"(lds0 + 5120u), "s"(lds0 + 6144u), "s"(lds0 + 7168u),
-          "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]),
-          "v"(voff[6]), "v"(voff[7]), "s"(base)
-        : "memory");
+#define TREEWY_ROWS_X8_OPERANDS                                                                 \
+        : "=&s"(save)                                                                           \
+        : "s"(lds0), "s"(lds0 + 1024u), "s"(lds0 + 2048u), "s"(lds0 + 3072u),                   \
+          "s"(lds0 + 4096u), "s"(lds0 + 5120u), "s"(lds0 + 6144u), "s"(lds0 + 7168u),           \
+          "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]),   \
+          "v"(voff[6]), "v"(voff[7]), "s"(base)                                                 \
+        : "memory"
+    if constexpr (NT)
+        asm volatile(TREEWY_ROWS_X8(" nt") TREEWY_ROWS_X8_OPERANDS);
+    else
+        asm volatile(TREEWY_ROWS_X8("") TREEWY_ROWS_X8_OPERANDS);
+#undef TREEWY_ROWS_X8_OPERANDS
 }
+#undef TREEWY_ROWS_X8
 
 // A pointer that is the same in every lane, kept in scalar registers (the compiler cannot
 // always prove it uniform).
@@ -446,6 +442,7 @@ __device__ __forceinline__ void dma_x1(const void* base, uint32_t voff, uint32_t
 // S0 rows of an item -> LDS: wave w takes rows 16w..16w+15, two whole rows per wave load;
 // chunk c of row r lands at slot c ^ (r % 16).  `wave` is wave-uniform (an SGPR), so the
 // LDS destinations are scalar; the source is a scalar base plus a 32-bit lane offset.
+template <bool NT>
 __device__ __forceinline__ void small_issue_s0(const float* S0, float* buf, int bh, int part,
                                                int wave, int lane) {
     const char* src = reinterpret_cast<const char*>(S0) +
@@ -459,7 +456,7 @@ __device__ __forceinline__ void small_issue_s0(const float* S0, float* buf, int 
         voff[i] = r * (D * 4u) + 16u * (slot ^ ((2u * i + hl) & 15u));
     }
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf + 16 * wave * D));
-    dma_rows_x8(src, voff, lds0);
+    dma_rows_x8<NT>(src, voff, lds0);
 }
 
 // The rest of an item's inputs -> LDS, as a list of whole-wave transfers dealt round-robin
@@ -745,7 +742,7 @@ void verify_small_kernel(
             dma_gather_x1(cin.accepted + bh / H, lds_addr + L.sm);
             if constexpr (DEFER) dma_x1(dlog.len_in + bh / H, 0u, lds_addr + L.il);
         }
-        small_issue_s0(S0, lds, bh, part, wave, lane);
+        small_issue_s0<FUSED>(S0, lds, bh, part, wave, lane);
         __builtin_amdgcn_s_waitcnt(kWaitAllButEight);   // the gathers (the eight row loads go on)
         lds_barrier();
         cur = fused_path(lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L.idx)[lane] : -1,
@@ -767,7 +764,7 @@ void verify_small_kernel(
             if constexpr (DEFER) dma_x1(dlog.len_in + bh1 / H, 0u, lds_addr + L.il);
         }
     } else {
-        small_issue_s0(S0, lds, bh, part, wave, lane);
+        small_issue_s0<FUSED>(S0, lds, bh, part, wave, lane);
         small_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, L,
                            nullptr);
     }
@@ -888,8 +885,10 @@ void verify_small_kernel(
                         const uint32_t r = 16u * wave + 2u * i + hl;
                         *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
                         if (last && flush)
-                            *reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D +
-                                                                 part * kSmallRows + r) * D + 4 * ch) = x[i];
+                            __builtin_nontemporal_store(
+                                x[i], reinterpret_cast<f32x4_t*>(
+                                          cin.S + (static_cast<size_t>(bh) * D + part * kSmallRows + r) * D +
+                                          4 * ch));
                     }
                 }
                 if constexpr (DEFER) {
@@ -941,7 +940,7 @@ void verify_small_kernel(
             take_rows();
             if (more) {
                 __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);   // this wave's reads of its rows
-                small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+                small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
             }
         }
 
@@ -1031,7 +1030,7 @@ void verify_small_kernel(
         lds_barrier();                              // operands read and G visible: refill
         ++round;
         if (more && !TWO) {
-            small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+            small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
             if constexpr (FUSED) {
                 // item i + 1's inputs and path rows; item i + 2's accepted node and tree
                 int bh_2, part_2;
@@ -1126,9 +1125,9 @@ void verify_small_kernel(
             const f32x4_t ov = {Ov[0], Ov[1], Ov[2], Ov[3]};
             const f32x4_t uv = {Uv[0], Uv[1], Uv[2], Uv[3]};
             __builtin_amdgcn_raw_buffer_store_b128(
-                ov, __builtin_amdgcn_make_buffer_rsrc(O + row0, 0, span, kRawBufferFlags), off, 0, 0);
+                ov, __builtin_amdgcn_make_buffer_rsrc(O + row0, 0, span, kRawBufferFlags), off, 0, FUSED ? kStreamAux : 0);
             __builtin_amdgcn_raw_buffer_store_b128(
-                uv, __builtin_amdgcn_make_buffer_rsrc(U + row0, 0, span, kRawBufferFlags), off, 0, 0);
+                uv, __builtin_amdgcn_make_buffer_rsrc(U + row0, 0, span, kRawBufferFlags), off, 0, FUSED ? kStreamAux : 0);
         }
         if (!more) break;
         bh = bh_n;
@@ -1421,7 +1420,7 @@ void verify_large_kernel(
     small_item(0, slot, grid, bh, part);
     if (bh >= BH) return;
     LargePrefetch<NKT> pf;
-    small_issue_s0(S0, lds, bh, part, wave, lane);
+    small_issue_s0<FUSED>(S0, lds, bh, part, wave, lane);
     if constexpr (STAGE)
         large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, Ls);
     else
@@ -1617,11 +1616,11 @@ void verify_large_kernel(
         // the item; unstaged: the key and query rows sit in the S-row area until every wave
         // is past the contractions)
         if constexpr (STAGE) {
-            if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+            if (more) small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
         }
         lds_barrier();                              // G visible to every wave; inputs read
         if constexpr (!STAGE) {
-            if (more) small_issue_s0(S0, lds, bh_n, part_n, wave, lane);
+            if (more) small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
             if (more)
                 large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
             if constexpr (FUSED) {
