@@ -22,6 +22,18 @@ constexpr int kChunk = 8;                        // path rows staged per pass
 constexpr int kParts = 2;                         // row slices per head
 constexpr int kVec = D * D / 4 / kThreads / kParts;  // float4 of S per lane (8)
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// State rows with the non-temporal (streaming) hint: the commit reads each row once and
+// overwrites it, so neither the read nor the written lines are worth keeping in the caches.
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(float4* p, float4 x) {
+    __builtin_nontemporal_store(f32x4_t{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4_t*>(p));
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void commit_kernel(
@@ -54,7 +66,7 @@ void commit_kernel(
     float4* Sh = reinterpret_cast<float4*>(S + (static_cast<size_t>(bh) * D + part * kRowsPart) * D);
     float4 s[kVec];
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) s[j] = Sh[j * kThreads + tid];
+    for (int j = 0; j < kVec; ++j) s[j] = load_stream(&Sh[j * kThreads + tid]);
 
     if (tid < N) s_par[tid] = parent[node0 + tid];
     __syncthreads();
@@ -107,7 +119,7 @@ void commit_kernel(
         }
     }
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) Sh[j * kThreads + tid] = s[j];
+    for (int j = 0; j < kVec; ++j) store_stream(&Sh[j * kThreads + tid], s[j]);
 }
 
 // The state a deferred-commit log stands for, written back: S <- scale (S + sum_j u~_j k_j^T)

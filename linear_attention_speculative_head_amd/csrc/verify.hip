@@ -1375,9 +1375,10 @@ __device__ __forceinline__ void commit_rows_in_lds(float* lds, const char* ldsb,
         for (int i = 0; i < 8; ++i) {
             const uint32_t r = 16u * wave + 2u * i + hl;
             *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
-            if (last)
-                *reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D +
-                                                     part * kSmallRows + r) * D + 4 * ch) = x[i];
+            if (last)   // streaming hint, as for the state's reads
+                __builtin_nontemporal_store(
+                    x[i], reinterpret_cast<f32x4_t*>(
+                              cin.S + (static_cast<size_t>(bh) * D + part * kSmallRows + r) * D + 4 * ch));
         }
     }
 }
