@@ -1848,10 +1848,10 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     const DeferLog nolog{};
     if (a.N <= 8) return launch_small<1, 0>(a, none, nolog, stream);
     if (a.N <= 16) return launch_small<2, 0>(a, none, nolog, stream);
-    // trees of up to 32 nodes stage their inputs through an LDS area of their own (two
-    // workgroups per CU); larger ones reuse the S-row area for their key and query rows, since
-    // a separate area would leave room for one workgroup per CU
-    if (a.N <= 32) return launch_large<2, true>(a, stream);
+    // the key and query rows go through the S-row area (no LDS area of their own), which
+    // leaves room for three workgroups per CU up to 32 nodes and two up to 64; the fused
+    // kernel below stages its inputs up to 32 nodes instead, where that measured faster
+    if (a.N <= 32) return launch_large<2, false>(a, stream);
     return launch_large<4, false>(a, stream);
 }
 
