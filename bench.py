@@ -44,6 +44,22 @@ TRAFFIC_FILES = {1: "profiles/traffic_chain4_b32h32.json",
                  "attention-32768": "profiles/traffic_attention_b32_chain4_ctx32768.json"}
 
 
+WARMUP_S = 0.25           # default warm-up: about this long ...
+WARMUP_RATE = 4.0e12      # ... estimated at this many algorithmic bytes per second
+WARMUP_MAX = 20000        # launch-bound workloads: at most this many steps
+
+
+def auto_warmup(args, step_bytes):
+    """The warm-up step count: --warmup when given, else about WARMUP_S seconds of steps of
+    `step_bytes` algorithmic bytes at WARMUP_RATE (at least 5, at most WARMUP_MAX).  On
+    MI355X kernel durations fall over the first tens of milliseconds of sustained launches
+    (a 750 us step measured 840 us as the 2nd launch and 650 us from the 60th on), so a
+    count of a few steps would time that ramp instead of the steady state."""
+    if args.warmup is not None:
+        return args.warmup
+    return min(WARMUP_MAX, max(5, math.ceil(WARMUP_S * WARMUP_RATE / max(step_bytes, 1.0))))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -52,7 +68,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: as many as take about "
+                         f"{WARMUP_S} s at {WARMUP_RATE / 1e12:.0f} TB/s of the workload's "
+                         "algorithmic bytes, at least 5: kernel durations fall over the first "
+                         "tens of milliseconds of sustained launches)")
     ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1)")
     ap.add_argument("--tree", type=str, default=None,
                     help="instead of a config: every sequence drafts the full tree W1,W2,W3 "
@@ -191,12 +211,14 @@ def run(args, mode, wl):
             "snapshot": accounting.snapshot_step_bytes(P.parent, P.accepted, H, N, elem,
                                                        layers=nl),
         }
+        if i == 0:
+            W = auto_warmup(args, nbytes["fused" if mode == "deferred" else mode]["total"])
         seq = []
         if mode == "deferred":
             # the log evolves the same way on every call of this instance: its bytes per call,
             # worked out here so that no host work sits between the timed launches
             lens = np.zeros(B, dtype=np.int64)
-            calls = math.ceil((args.warmup + 2 * args.steps) / n_inst) + 1
+            calls = math.ceil((W + 2 * args.steps) / n_inst) + 1
             for _ in range(calls):
                 nb, lens = accounting.deferred_step_bytes(P.parent, P.accepted, P.parent, H,
                                                           elem, lens, args.deferred)
@@ -297,7 +319,7 @@ def run(args, mode, wl):
                 return pool[i]["bytes"][m]["total"]
             return fn(pool[i], ev)
 
-        for s in range(args.warmup):
+        for s in range(W):
             run(s % n_inst)
         torch.cuda.synchronize()
         assert int(status.item()) == 0, f"device status {int(status.item())}"
@@ -307,7 +329,7 @@ def run(args, mode, wl):
         t_start = time.perf_counter()
         r0.record()
         for s in range(K):
-            timed_bytes += run((args.warmup + s) % n_inst)
+            timed_bytes += run((W + s) % n_inst)
         r1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
@@ -318,14 +340,14 @@ def run(args, mode, wl):
                   for _ in range(K)]
         torch.cuda.synchronize()
         for s in range(K):
-            run((args.warmup + s) % n_inst, events[s])
+            run((W + s) % n_inst, events[s])
         torch.cuda.synchronize()
         names = (["treewy_commit_verify"] if m == "fused" else
                  ["treewy_commit_verify_deferred"] if m == "deferred" else
                  ["treewy_verify_snapshot", "treewy_commit_snapshot"] if m == "snapshot" else
                  ["treewy_verify", "treewy_commit"])
         keys = ["fused"] if m in ("fused", "deferred") else ["verify", "commit"]
-        used = [(args.warmup + s) % n_inst for s in range(K)]
+        used = [(W + s) % n_inst for s in range(K)]
         step_bytes = timed_bytes / K
         kern = {}
         for k, (name, key) in enumerate(zip(names, keys)):
@@ -411,7 +433,7 @@ def run(args, mode, wl):
         "unit": "nodes*heads/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": W,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -474,7 +496,8 @@ def run_attention(args):
         binding.treewy_tree_attention(x["Kc"], x["Vc"], x["ctx"], x["Qd"], x["Kd"], x["Vd"],
                                       x["parent"], O, ws, status)
 
-    for s in range(args.warmup):
+    W = auto_warmup(args, accounting.attention_call_bytes(np.full(B, ctxn), N, Hkv, G))
+    for s in range(W):
         step(s % n_inst)
     torch.cuda.synchronize()
     K = args.steps
@@ -482,7 +505,7 @@ def run_attention(args):
     t0 = time.perf_counter()
     r0.record()
     for s in range(K):
-        step((args.warmup + s) % n_inst)
+        step((W + s) % n_inst)
     r1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -491,7 +514,7 @@ def run_attention(args):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for s in range(K):
         ev[s][0].record()
-        step((args.warmup + s) % n_inst)
+        step((W + s) % n_inst)
         ev[s][1].record()
     torch.cuda.synchronize()
     ms_bracketed = float(np.mean([a.elapsed_time(b) for a, b in ev]))
@@ -513,7 +536,7 @@ def run_attention(args):
     return {
         "metric": "tree attention verify draft-nodes*query-heads/sec",
         "value": B * N * Hkv * G * K / wall, "unit": "nodes*heads/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": wall * 1e3 / K, "higher_is_better": True,
+        "warmup": W, "ms_per_step": wall * 1e3 / K, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, f32 accumulate",
         "data": "synthetic (seeded queries/keys of the draft; normal-filled cache)",
         "config": {"workload": f"tree attention: B={B}, {Hkv} KV heads x {G} query heads, "

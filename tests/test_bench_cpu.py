@@ -79,3 +79,17 @@ def test_attention_bytes_closed_form():
     # ragged prefixes count row by row; an empty cache leaves only the draft's I/O
     assert (accounting.attention_call_bytes([3, 0], 1, 1, 1)
             == 3 * 256 * 2 * 2 + 2 * 1 * 3 * 256 * 2 + 2 * 256 * 4)
+
+
+def test_warmup_count():
+    # an explicit --warmup is taken as given; the default is about a quarter second of steps at
+    # 4 TB/s of algorithmic bytes, between 5 and 20000 steps
+    import argparse
+    sys.path.insert(0, ROOT)
+    import bench
+    given = argparse.Namespace(warmup=3)
+    auto = argparse.Namespace(warmup=None)
+    assert bench.auto_warmup(given, 131e6) == 3
+    assert bench.auto_warmup(auto, 131e6) == 7634          # ceil(0.25 * 4e12 / 131e6)
+    assert bench.auto_warmup(auto, 1e12) == 5
+    assert bench.auto_warmup(auto, 1.0) == 20000
