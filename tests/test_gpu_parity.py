@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from linear_attention_speculative_head_amd import inputs
-from parity import check_against_oracle, run_verify_commit, say
+from parity import check_against_oracle, run_verify_commit, sample_heads, say
 
 pytestmark = pytest.mark.gpu
 
@@ -22,14 +22,6 @@ def _gpu():
         pytest.skip("no GPU")
     from linear_attention_speculative_head_amd import binding
     binding.lib()
-
-
-def sample_heads(B, H, n, seed):
-    rng = np.random.default_rng(seed)
-    heads = {(0, 0), (B - 1, H - 1), (B // 2, H // 3)}
-    while len(heads) < n:
-        heads.add((int(rng.integers(B)), int(rng.integers(H))))
-    return sorted(heads)
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2])
