@@ -247,7 +247,9 @@ constexpr int kWaitAllButEight = 8 | (7 << 4) | (15 << 8);
 constexpr int kWaitLdsOnly = 0xC07F;            // LDS/scalar count 0, the rest left free
 // dword 3 of a raw (unstrided, range-checked) buffer descriptor on gfx9-family parts
 constexpr int kRawBufferFlags = 0x00020000;
-constexpr int kStreamAux = 2;                   // buffer-store cache policy: non-temporal
+// buffer-store cache policy: non-temporal (O and U of the fused kernel on 9-16 nodes; on up
+// to 8 nodes the default policy measured faster)
+constexpr int kStreamAux = 2;
 constexpr int kSmallRows = 64;              // value rows per item
 constexpr int kSmallParts = D / kSmallRows; // items per head
 
@@ -868,7 +870,10 @@ void verify_small_kernel(
                             }
                         }
                     }
-                    for (int q = 0; q < cnt; ++q) {
+                    // the path's terms; with two input sets (trees of up to 8 nodes) the loop is
+                    // unrolled over the L.path slots of the chunk, so that the reads of all of
+                    // its rows are issued together
+                    auto path_term = [&](int q) {
                         const float cq = ga / PG[q0 + q];
                         const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
                         const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
@@ -878,6 +883,15 @@ void verify_small_kernel(
                             const float cu = cq * PU[q * kSmallRows + 16 * wave + 2 * i + hl];
                             x[i] += cu * kv;
                         }
+                    };
+                    if constexpr (TWO) {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            if (q >= cnt) break;
+                            path_term(q);
+                        }
+                    } else {
+                        for (int q = 0; q < cnt; ++q) path_term(q);
                     }
                     const bool last = ci + 1 == nchunk;
 #pragma unroll
@@ -1125,9 +1139,9 @@ void verify_small_kernel(
             const f32x4_t ov = {Ov[0], Ov[1], Ov[2], Ov[3]};
             const f32x4_t uv = {Uv[0], Uv[1], Uv[2], Uv[3]};
             __builtin_amdgcn_raw_buffer_store_b128(
-                ov, __builtin_amdgcn_make_buffer_rsrc(O + row0, 0, span, kRawBufferFlags), off, 0, FUSED ? kStreamAux : 0);
+                ov, __builtin_amdgcn_make_buffer_rsrc(O + row0, 0, span, kRawBufferFlags), off, 0, (FUSED && !TWO) ? kStreamAux : 0);
             __builtin_amdgcn_raw_buffer_store_b128(
-                uv, __builtin_amdgcn_make_buffer_rsrc(U + row0, 0, span, kRawBufferFlags), off, 0, FUSED ? kStreamAux : 0);
+                uv, __builtin_amdgcn_make_buffer_rsrc(U + row0, 0, span, kRawBufferFlags), off, 0, (FUSED && !TWO) ? kStreamAux : 0);
         }
         if (!more) break;
         bh = bh_n;
