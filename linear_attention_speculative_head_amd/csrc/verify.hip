@@ -1373,7 +1373,10 @@ __device__ __forceinline__ void commit_rows_in_lds(float* lds, const char* ldsb,
             x[i] = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
             if (ci == 0) x[i] *= ga;
         }
-        for (int q = 0; q < cnt; ++q) {
+        // unrolled over the chunk's slots, so that the reads of all its rows are issued together
+#pragma unroll
+        for (int q = 0; q < kLargePath; ++q) {
+            if (q >= cnt) break;
             const float cq = ga / PG[q0 + q];
             const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
             const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
