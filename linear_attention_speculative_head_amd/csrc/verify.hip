@@ -870,9 +870,8 @@ void verify_small_kernel(
                             }
                         }
                     }
-                    // the path's terms; with two input sets (trees of up to 8 nodes) the loop is
-                    // unrolled over the L.path slots of the chunk, so that the reads of all of
-                    // its rows are issued together
+                    // the path's terms; with the fused commit the loop is unrolled over the
+                    // chunk's slots, so that the reads of all its rows are issued together
                     auto path_term = [&](int q) {
                         const float cq = ga / PG[q0 + q];
                         const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
@@ -884,7 +883,7 @@ void verify_small_kernel(
                             x[i] += cu * kv;
                         }
                     };
-                    if constexpr (TWO) {
+                    if constexpr (MODE == 1) {
 #pragma unroll
                         for (int q = 0; q < 8; ++q) {
                             if (q >= cnt) break;
