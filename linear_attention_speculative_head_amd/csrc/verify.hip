@@ -1430,6 +1430,15 @@ void verify_large_kernel(
     const int grp = lane >> 4;
     const int kq = 8 * grp;
     float* Us = lds + Lo::kS0 + Lo::kG + wave * (16 * NKT * 16);   // this wave's U scratch
+    // Unstaged at 64 nodes the S-row area and the Gram area are both 32 KiB and trade roles
+    // every item: item i's S rows sit in area X, its key and query rows go into area Y at the
+    // top of the item (Y held the previous item's Gram matrix, read by then), the Gram matrix
+    // is formed into X once the rows are taken, and item i + 1's S rows go into Y once the
+    // contractions are done.  So the key/query rows stream in together with the previous
+    // step's path rows instead of after the operand split.
+    constexpr bool ALT = !STAGE && NKT == 4;
+    static_assert(!ALT || Lo::kG == Lo::kS0, "the two areas must be the same size");
+    uint32_t xo = 0;                                // ALT: float offset of this item's S rows
     const int grid = gridDim.x;
     const int slot = blockIdx.x;
 
@@ -1512,6 +1521,8 @@ void verify_large_kernel(
             if (cur.depth > 0)
                 fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr, large_path_view(Ls));
         }
+        const uint32_t yo = ALT ? Lo::kS0 - xo : 0u;    // ALT: the other area
+        if constexpr (ALT) large_issue_kq(Q, K, H, N, bh, wave, lane, lds_addr + 4u * yo);
 
         // ---- tree walk, lane = node (every wave)
         uint64_t anc_l;
@@ -1551,8 +1562,8 @@ void verify_large_kernel(
             if (cur.depth > 0) {
                 __builtin_amdgcn_s_waitcnt(0);      // the path rows (and the last stores)
                 lds_barrier();
-                commit_rows_in_lds(lds, ldsb, large_path_view(Ls), cur, cin, bh, part, H, wave,
-                                   lane, lds_addr);
+                commit_rows_in_lds(lds + xo, ldsb, large_path_view(Ls), cur, cin, bh, part, H,
+                                   wave, lane, lds_addr);
             }
         }
 
@@ -1560,7 +1571,7 @@ void verify_large_kernel(
         bf16x8_t ahi[4], alo[4];
         {
             const int r = 16 * wave + col;
-            const float* rowp = lds + r * D;
+            const float* rowp = lds + xo + r * D;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int c0 = 2 * grp + 8 * ks;
@@ -1569,6 +1580,7 @@ void verify_large_kernel(
                             ahi[ks], alo[ks]);
             }
         }
+        if constexpr (ALT) __builtin_amdgcn_s_waitcnt(0);   // this wave's key/query rows
         lds_barrier();                              // rows read: the buffer may be refilled
         ++round;
         int bh_n, part_n;
@@ -1577,12 +1589,13 @@ void verify_large_kernel(
 
         // unstaged: the item's key and query rows go into the S-row area, free from here until
         // the next item's rows are requested (after the contractions)
-        const uint32_t kq_off = STAGE ? Ls.kq : 0u;
-        if constexpr (!STAGE) {
+        const uint32_t kq_off = STAGE ? Ls.kq : (ALT ? 4u * yo : 0u);
+        if constexpr (!STAGE && !ALT) {
             large_issue_kq(Q, K, H, N, bh, wave, lane, lds_addr);
             __builtin_amdgcn_s_waitcnt(0);
             lds_barrier();
         }
+        float* Gx = ALT ? lds + xo : G;             // this item's Gram matrix
 
         // ---- contractions and Gram rows 16w..16w+15 (waves with keys there)
         const bool has_gram = wave < NKT && 16 * wave < N;
@@ -1626,7 +1639,7 @@ void verify_large_kernel(
             if (has_gram) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    G[(16 * wave + 4 * grp + e) * kCols + 16 * c + col] = gacc[e];
+                    Gx[(16 * wave + 4 * grp + e) * kCols + 16 * c + col] = gacc[e];
             }
         }
         // the next item's rows only now (staged: the next inputs were requested at the top of
@@ -1637,7 +1650,7 @@ void verify_large_kernel(
         }
         lds_barrier();                              // G visible to every wave; inputs read
         if constexpr (!STAGE) {
-            if (more) small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
+            if (more) small_issue_s0<FUSED>(S0, lds + yo, bh_n, part_n, wave, lane);
             if (more)
                 large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
             if constexpr (FUSED) {
@@ -1702,8 +1715,8 @@ void verify_large_kernel(
             for (int kt = 0; kt < NKT; ++kt) {
                 const int a = as_[kt];
                 const int t = tn[kt];
-                cs_[kt] = hasa[kt] ? bgt[kt] * rgsrc[kt] * G[t * kCols + a] : 0.f;
-                cw_[kt] = hasa[kt] ? gt[kt] * rgsrc[kt] * G[a * kCols + 16 * NKT + t] : 0.f;
+                cs_[kt] = hasa[kt] ? bgt[kt] * rgsrc[kt] * Gx[t * kCols + a] : 0.f;
+                cw_[kt] = hasa[kt] ? gt[kt] * rgsrc[kt] * Gx[a * kCols + 16 * NKT + t] : 0.f;
             }
         };
         auto pending = [&]() {
@@ -1757,7 +1770,7 @@ void verify_large_kernel(
         for (int kt = 0; kt < NKT; ++kt) {
             const int t = tn[kt];
             const bool ok = t < N;
-            const float cw = ok ? G[t * kCols + 16 * NKT + t] : 0.f;   // the node itself
+            const float cw = ok ? Gx[t * kCols + 16 * NKT + t] : 0.f;   // the node itself
             f32x4_t ov, uv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1773,6 +1786,7 @@ void verify_large_kernel(
         if (!more) break;
         bh = bh_n;
         part = part_n;
+        if constexpr (ALT) xo = yo;
     }
 }
 
