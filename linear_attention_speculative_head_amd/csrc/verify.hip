@@ -1170,9 +1170,11 @@ void verify_small_kernel(
 // The next item's S0 rows are requested once this item's contractions are done.  With
 // STAGE, its keys, queries, values, gates and tree then follow by direct transfers into an
 // LDS area of their own, and the contractions read their fragments from there.  Without it
-// (up to 64 nodes, where that area would leave one workgroup per CU) the item's key and
-// query rows are sent into the S-row area once the rows have been taken into registers, and
-// the contractions read them there; values, gates and tree are prefetched into registers.
+// (where that area would leave one workgroup per CU) the item's key and query rows are sent
+// into the S-row area once the rows have been taken into registers, and the contractions
+// read them there; values, gates and tree are prefetched into registers.  With four node
+// tiles (33 to 64 nodes) the S-row and Gram areas alternate instead (see ALT below), so the
+// key and query rows are requested at the top of the item.
 
 constexpr int kLargePath = 8;                   // path rows staged per chunk (fused)
 
@@ -1430,8 +1432,8 @@ void verify_large_kernel(
     const int grp = lane >> 4;
     const int kq = 8 * grp;
     float* Us = lds + Lo::kS0 + Lo::kG + wave * (16 * NKT * 16);   // this wave's U scratch
-    // Unstaged at 64 nodes the S-row area and the Gram area are both 32 KiB and trade roles
-    // every item: item i's S rows sit in area X, its key and query rows go into area Y at the
+    // Unstaged with four node tiles the S-row area and the Gram area are both 32 KiB and
+    // trade roles every item: item i's S rows sit in area X, its key and query rows go into area Y at the
     // top of the item (Y held the previous item's Gram matrix, read by then), the Gram matrix
     // is formed into X once the rows are taken, and item i + 1's S rows go into Y once the
     // contractions are done.  So the key/query rows stream in together with the previous
