@@ -1433,11 +1433,11 @@ void verify_large_kernel(
     const int kq = 8 * grp;
     float* Us = lds + Lo::kS0 + Lo::kG + wave * (16 * NKT * 16);   // this wave's U scratch
     // Unstaged with four node tiles the S-row area and the Gram area are both 32 KiB and
-    // trade roles every item: item i's S rows sit in area X, its key and query rows go into area Y at the
-    // top of the item (Y held the previous item's Gram matrix, read by then), the Gram matrix
-    // is formed into X once the rows are taken, and item i + 1's S rows go into Y once the
-    // contractions are done.  So the key/query rows stream in together with the previous
-    // step's path rows instead of after the operand split.
+    // trade roles every item: item i's S rows sit in area X, its key and query rows go into
+    // area Y at the top of the item (Y held the previous item's Gram matrix, read by then),
+    // the Gram matrix is formed into X once the rows are taken, and item i + 1's S rows go
+    // into Y once the contractions are done.  So the key/query rows stream in together with
+    // the previous step's path rows instead of after the operand split.
     constexpr bool ALT = !STAGE && NKT == 4;
     static_assert(!ALT || Lo::kG == Lo::kS0, "the two areas must be the same size");
     uint32_t xo = 0;                                // ALT: float offset of this item's S rows
