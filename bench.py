@@ -40,6 +40,9 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 # counters on a plain copy of known size), per workload; used while the kernel source is the
 # one they were taken on
 TRAFFIC_FILES = {1: "profiles/traffic_chain4_b32h32.json",
+                 2: "profiles/traffic_tree16_b64h32.json",
+                 3: "profiles/traffic_tree64_b128h32_l30.json",
+                 4: "profiles/traffic_tree32_b256h64.json",
                  "attention-8192": "profiles/traffic_attention_b32_chain4_ctx8192.json",
                  "attention-32768": "profiles/traffic_attention_b32_chain4_ctx32768.json"}
 
