@@ -694,17 +694,20 @@ __device__ __forceinline__ void defer_issue_log(const DeferLog& dl, int len, int
 // committed rows to S and empties the log.  Header words go to separate output buffers, so
 // no item can see another item's update of the same sequence within one launch.
 
-template <int NCT, int MODE>
+// NFIX > 0: a form compiled for trees of exactly NFIX nodes (the fused step on up to 8 nodes),
+// whose LDS offsets, loop bounds and pointer-jumping rounds are constants; 0: N at run time.
+template <int NCT, int MODE, int NFIX = 0>
 __global__ __launch_bounds__(kSmallThreads)
 __attribute__((amdgpu_waves_per_eu(kSmallWavesPerSimd<NCT, MODE>)))
 void verify_small_kernel(
     const float* S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ alpha,
-    const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
+    const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N_rt, int BH,
     float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
     int32_t* __restrict__ status, CommitIn cin, DeferLog dlog)
 {
+    const int N = NFIX > 0 ? NFIX : N_rt;
     constexpr bool FUSED = MODE != 0;
     constexpr bool DEFER = MODE == 2;
     constexpr bool TWO = small_two_sets(NCT, MODE); // two input sets, early refills
@@ -1805,13 +1808,13 @@ int device_cu_count() {
     return cus;
 }
 
-template <int NCT, int MODE>
+template <int NCT, int MODE, int NFIX = 0>
 static hipError_t launch_small(const VerifyArgs& a, const CommitIn& cin, const DeferLog& dl,
                                hipStream_t stream) {
     const SmallLds L = small_lds(a.N, NCT, MODE, MODE == 2 ? dl.Lmax : 0);
     const int bytes = static_cast<int>(L.bytes);
     const int wgs = small_wgs(L.bytes, kSmallWavesPerSimd<NCT, MODE>);
-    auto kern = verify_small_kernel<NCT, MODE>;
+    auto kern = verify_small_kernel<NCT, MODE, NFIX>;
     if (L.bytes > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -1895,8 +1898,17 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
                            c.accepted, c.N};
         const DeferLog nolog{};
-        return a.N <= 8 ? launch_small<1, 1>(a, cin, nolog, stream)
-                        : launch_small<2, 1>(a, cin, nolog, stream);
+        switch (a.N) {   // the fused step on up to 8 nodes: one form per node count
+            case 1: return launch_small<1, 1, 1>(a, cin, nolog, stream);
+            case 2: return launch_small<1, 1, 2>(a, cin, nolog, stream);
+            case 3: return launch_small<1, 1, 3>(a, cin, nolog, stream);
+            case 4: return launch_small<1, 1, 4>(a, cin, nolog, stream);
+            case 5: return launch_small<1, 1, 5>(a, cin, nolog, stream);
+            case 6: return launch_small<1, 1, 6>(a, cin, nolog, stream);
+            case 7: return launch_small<1, 1, 7>(a, cin, nolog, stream);
+            case 8: return launch_small<1, 1, 8>(a, cin, nolog, stream);
+            default: return launch_small<2, 1>(a, cin, nolog, stream);
+        }
     }
     if (a.in_dtype == TREEWY_BF16) {
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
