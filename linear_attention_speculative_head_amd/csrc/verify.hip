@@ -694,7 +694,7 @@ __device__ __forceinline__ void defer_issue_log(const DeferLog& dl, int len, int
 // committed rows to S and empties the log.  Header words go to separate output buffers, so
 // no item can see another item's update of the same sequence within one launch.
 
-// NFIX > 0: a form compiled for trees of exactly NFIX nodes (the fused step on up to 8 nodes),
+// NFIX > 0: a form compiled for trees of exactly NFIX nodes (every mode on up to 8 nodes),
 // whose LDS offsets, loop bounds and pointer-jumping rounds are constants; 0: N at run time.
 template <int NCT, int MODE, int NFIX = 0>
 __global__ __launch_bounds__(kSmallThreads)
@@ -1832,6 +1832,22 @@ static hipError_t launch_small(const VerifyArgs& a, const CommitIn& cin, const D
 }
 
 
+// Trees of up to 8 nodes: the small-tree kernel compiled for the exact node count.
+template <int MODE>
+static hipError_t launch_small_fixed(const VerifyArgs& a, const CommitIn& cin, const DeferLog& dl,
+                                     hipStream_t stream) {
+    switch (a.N) {
+        case 1: return launch_small<1, MODE, 1>(a, cin, dl, stream);
+        case 2: return launch_small<1, MODE, 2>(a, cin, dl, stream);
+        case 3: return launch_small<1, MODE, 3>(a, cin, dl, stream);
+        case 4: return launch_small<1, MODE, 4>(a, cin, dl, stream);
+        case 5: return launch_small<1, MODE, 5>(a, cin, dl, stream);
+        case 6: return launch_small<1, MODE, 6>(a, cin, dl, stream);
+        case 7: return launch_small<1, MODE, 7>(a, cin, dl, stream);
+        default: return launch_small<1, MODE, 8>(a, cin, dl, stream);
+    }
+}
+
 }  // namespace
 
 template <typename T>
@@ -1881,7 +1897,7 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     if (a.in_dtype != TREEWY_BF16) return launch_verify_t<float>(a, stream);
     const CommitIn none{};
     const DeferLog nolog{};
-    if (a.N <= 8) return launch_small<1, 0>(a, none, nolog, stream);
+    if (a.N <= 8) return launch_small_fixed<0>(a, none, nolog, stream);
     if (a.N <= 16) return launch_small<2, 0>(a, none, nolog, stream);
     // the key and query rows go through the S-row area (no LDS area of their own), which
     // leaves room for three workgroups per CU up to 32 nodes and two up to 64; the fused
@@ -1898,17 +1914,8 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
                            c.accepted, c.N};
         const DeferLog nolog{};
-        switch (a.N) {   // the fused step on up to 8 nodes: one form per node count
-            case 1: return launch_small<1, 1, 1>(a, cin, nolog, stream);
-            case 2: return launch_small<1, 1, 2>(a, cin, nolog, stream);
-            case 3: return launch_small<1, 1, 3>(a, cin, nolog, stream);
-            case 4: return launch_small<1, 1, 4>(a, cin, nolog, stream);
-            case 5: return launch_small<1, 1, 5>(a, cin, nolog, stream);
-            case 6: return launch_small<1, 1, 6>(a, cin, nolog, stream);
-            case 7: return launch_small<1, 1, 7>(a, cin, nolog, stream);
-            case 8: return launch_small<1, 1, 8>(a, cin, nolog, stream);
-            default: return launch_small<2, 1>(a, cin, nolog, stream);
-        }
+        if (a.N <= 8) return launch_small_fixed<1>(a, cin, nolog, stream);
+        return launch_small<2, 1>(a, cin, nolog, stream);
     }
     if (a.in_dtype == TREEWY_BF16) {
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
@@ -1928,7 +1935,7 @@ hipError_t launch_commit_verify_deferred(const CommitArgs& c, const VerifyArgs& 
                        c.accepted, c.N};
     const DeferLog dl{d.logU, static_cast<uint16_t*>(d.logK), d.scale_in, d.scale_out,
                       d.len_in, d.len_out, d.Lmax};
-    return a.N <= 8 ? launch_small<1, 2>(a, cin, dl, stream)
+    return a.N <= 8 ? launch_small_fixed<2>(a, cin, dl, stream)
                     : launch_small<2, 2>(a, cin, dl, stream);
 }
 
