@@ -76,7 +76,9 @@ def parse():
                          f"{WARMUP_S} s at {WARMUP_RATE / 1e12:.0f} TB/s of the workload's "
                          "algorithmic bytes, at least 5: kernel durations fall over the first "
                          "tens of milliseconds of sustained launches)")
-    ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 0..4 (default 3: B128 x H32, 64-node trees, 30 layers, the "
+                         "largest one-GPU workload)")
     ap.add_argument("--tree", type=str, default=None,
                     help="instead of a config: every sequence drafts the full tree W1,W2,W3 "
                          "(B x H of config 1, accepted node uniform)")
@@ -97,6 +99,11 @@ def parse():
                     help="time treewy_verify then treewy_commit (two launches per layer)")
     ap.add_argument("--snapshot", action="store_true",
                     help="time the store-all comparison path instead of TreeWY")
+    ap.add_argument("--with-snapshot", type=int, default=None, choices=(0, 1),
+                    help="also time the store-all comparison path on the same inputs in the "
+                         "same run and report it under 'snapshot' (default: on for config 4)")
+    ap.add_argument("--copy-gib", type=float, default=1.0,
+                    help="size of the plain device copy timed in the same run (0 = skip)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each instance's step as a captured HIP graph (the fused step: "
                          "one graph per parity of its alternating per-step buffers)")
@@ -182,8 +189,10 @@ def run(args, mode, wl):
     elem = 2 if dtype == "bf16" else 4
 
     # ---- rotating pool of instances (each: all layers of the workload)
+    with_snap = mode == "snapshot" or (mode == "fused" and bool(
+        args.with_snapshot if args.with_snapshot is not None else getattr(args, "config", None) == 4
+        and args.tree is None))
     per_layer = (B * H * 128 * 128 * 4 + 3 * B * N * H * 128 * elem + 2 * B * N * H * 128 * 4
-                 + (B * H * N * 128 * 128 * 4 if mode == "snapshot" else 0)
                  + (2 * B * N * H * 128 * 4 if mode in ("fused", "deferred") else 0)
                  + (B * H * args.deferred * 128 * 6 if mode == "deferred" else 0))
     n_inst = max(1, math.ceil(args.pool_gib * 2 ** 30 / (per_layer * nl))) if wl.rotate else 1
@@ -201,9 +210,7 @@ def run(args, mode, wl):
             dl = device.upload_layer(L, dtype)
             out = device.alloc_outputs(B, H, N)
             extra = None
-            if mode == "snapshot":
-                extra = torch.empty((B, H, N, 128, 128), device="cuda")
-            elif mode in ("fused", "deferred"):  # second set of per-step outputs, alternated
+            if mode in ("fused", "deferred"):  # second set of per-step outputs, alternated
                 extra = device.alloc_outputs(B, H, N)
             dlog = device.alloc_log(B, H, args.deferred) if mode == "deferred" else None
             layers.append((dl, out, extra, dlog))
@@ -230,6 +237,9 @@ def run(args, mode, wl):
                          dseq=seq, calls=0))
         if i == 0:
             first = P
+    # the store-all scheme's snapshots of one layer (every node's state), shared by all layers
+    # and instances: its verify and rollback run layer by layer
+    snap = torch.empty((B, H, N, 128, 128), device="cuda") if with_snap else None
     torch.cuda.synchronize()
     log(f"[bench] inputs drawn and uploaded in {time.time() - t0:.1f} s")
 
@@ -273,43 +283,50 @@ def run(args, mode, wl):
         x["flip"] ^= 1
         return nb
 
-    def two_call_step(x, ev=None, snapshot=False):
+    def two_call_step(x, ev=None):
         # verify for every layer, then commit for every layer
         for j, (dl, out, extra, _) in enumerate(x["layers"]):
             if ev is not None:
                 ev[0][j].record()
-            if snapshot:
-                binding.treewy_verify_snapshot(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta,
-                                               x["parent"], out.O, extra, status)
-            else:
-                binding.treewy_verify(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta, x["parent"],
-                                      out.O, out.U, out.gamma, status=status)
+            binding.treewy_verify(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta, x["parent"],
+                                  out.O, out.U, out.gamma, status=status)
             if ev is not None:
                 ev[1][j].record()
         for j, (dl, out, extra, _) in enumerate(x["layers"]):
             if ev is not None:
                 ev[2][j].record()
-            if snapshot:
-                binding.treewy_commit_snapshot(dl.S0, extra, x["accepted"], status)
-            else:
-                binding.treewy_commit(dl.S0, out.U, dl.K, out.gamma, x["parent"], x["accepted"],
-                                      status)
+            binding.treewy_commit(dl.S0, out.U, dl.K, out.gamma, x["parent"], x["accepted"],
+                                  status)
             if ev is not None:
                 ev[3][j].record()
-        return x["bytes"]["snapshot" if snapshot else "separate"]["total"]
+        return x["bytes"]["separate"]["total"]
+
+    def snapshot_step(x, ev=None):
+        # per layer: every node's state written, then the accepted node's copied back
+        for j, (dl, out, _, _) in enumerate(x["layers"]):
+            if ev is not None:
+                ev[0][j].record()
+            binding.treewy_verify_snapshot(dl.S0, dl.Q, dl.K, dl.V, dl.alpha, dl.beta,
+                                           x["parent"], out.O, snap, status)
+            if ev is not None:
+                ev[1][j].record()
+                ev[2][j].record()
+            binding.treewy_commit_snapshot(dl.S0, snap, x["accepted"], status)
+            if ev is not None:
+                ev[3][j].record()
+        return x["bytes"]["snapshot"]["total"]
 
     def step_fn(m):
-        if m == "fused":
-            return fused_step
-        if m == "deferred":
-            return deferred_step
-        return lambda x, ev=None: two_call_step(x, ev, snapshot=(m == "snapshot"))
+        return {"fused": fused_step, "deferred": deferred_step, "separate": two_call_step,
+                "snapshot": snapshot_step}[m]
 
     K = args.steps
 
     def measure(m, graphs=None):
-        """Warm-up, then exactly K timed steps with nothing else on the stream, then the same
-        K steps again with HIP events around every launch (kernel durations)."""
+        """Warm-up, then exactly K timed steps with nothing else on the stream.  Where a step
+        is one launch per layer (fused, deferred), the mean launch duration is the HIP-event
+        time of that region over its launches.  Otherwise the same K steps run again with HIP
+        events around every launch, for each kernel's duration."""
         fn = step_fn(m)
 
         def run(i, ev=None):
@@ -338,28 +355,25 @@ def run(args, mode, wl):
         wall = time.perf_counter() - t_start
         region_ms = r0.elapsed_time(r1)
         assert int(status.item()) == 0, f"device status {int(status.item())}"
-        nev = 2 if m in ("fused", "deferred") else 4
-        events = [[[torch.cuda.Event(enable_timing=True) for _ in range(nl)] for _ in range(nev)]
+        used = [(W + s) % n_inst for s in range(K)]
+        step_bytes = timed_bytes / K
+        kern = {}
+        if m in ("fused", "deferred"):
+            name = "treewy_commit_verify" if m == "fused" else "treewy_commit_verify_deferred"
+            kern[name] = (step_bytes / nl, region_ms / (K * nl))
+            return wall, kern, step_bytes, region_ms
+        events = [[[torch.cuda.Event(enable_timing=True) for _ in range(nl)] for _ in range(4)]
                   for _ in range(K)]
         torch.cuda.synchronize()
         for s in range(K):
             run((W + s) % n_inst, events[s])
         torch.cuda.synchronize()
-        names = (["treewy_commit_verify"] if m == "fused" else
-                 ["treewy_commit_verify_deferred"] if m == "deferred" else
-                 ["treewy_verify_snapshot", "treewy_commit_snapshot"] if m == "snapshot" else
+        names = (["treewy_verify_snapshot", "treewy_commit_snapshot"] if m == "snapshot" else
                  ["treewy_verify", "treewy_commit"])
-        keys = ["fused"] if m in ("fused", "deferred") else ["verify", "commit"]
-        used = [(W + s) % n_inst for s in range(K)]
-        step_bytes = timed_bytes / K
-        kern = {}
-        for k, (name, key) in enumerate(zip(names, keys)):
+        for k, (name, key) in enumerate(zip(names, ["verify", "commit"])):
             ms = np.array([[events[s][2 * k][j].elapsed_time(events[s][2 * k + 1][j])
                             for j in range(nl)] for s in range(K)])
-            if m == "deferred":
-                nbytes = step_bytes / nl                                     # per launch
-            else:
-                nbytes = np.mean([pool[i]["bytes"][m][key] for i in used]) / nl
+            nbytes = np.mean([pool[i]["bytes"][m][key] for i in used]) / nl
             kern[name] = (nbytes, ms.mean())
         return wall, kern, step_bytes, region_ms
 
@@ -398,16 +412,12 @@ def run(args, mode, wl):
     nodes_heads = B * H * N * nl
     value = nodes_heads * K / wall
     dom = max(kern, key=lambda k: kern[k][1])
-    d_bytes, d_ms_bracketed = kern[dom]
-    # one launch per layer and step: its mean duration is the HIP-event time of the timed
-    # region over the launches in it (events around every launch add a few us each, so that
-    # second pass is kept only for the per-kernel breakdown)
-    d_ms = region_ms / (K * nl) if mode in ("fused", "deferred") else d_ms_bracketed
+    d_bytes, d_ms = kern[dom]
     achieved = d_bytes / (d_ms * 1e-3) / 1e9
     log(f"[bench] {mode}: {ms_step * 1e3:.1f} us/step; " + ", ".join(
-        f"{n} {t * 1e3:.1f} us ({b / (t * 1e-3) / 1e9:.0f} GB/s)" for n, (b, t) in kern.items())
-        + f"; step {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s algorithmic; {dom} "
-        f"{d_ms * 1e3:.1f} us per launch over the timed region ({achieved:.0f} GB/s)")
+        f"{n} {t * 1e3:.1f} us per launch ({b / (t * 1e-3) / 1e9:.0f} GB/s)"
+        for n, (b, t) in kern.items())
+        + f"; step {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s algorithmic")
 
     separate = None
     if mode == "fused":
@@ -419,12 +429,38 @@ def run(args, mode, wl):
         log(f"[bench] separate calls: {w2 * 1e6 / K:.1f} us/step; " + ", ".join(
             f"{n} {t * 1e3:.1f} us" for n, (b, t) in k2.items()))
 
+    snapshot = None
+    if mode == "fused" and with_snap:
+        # the store-all comparison on the same inputs, in the same run
+        w3, k3, b3, _ = measure("snapshot")
+        snapshot = {"ms_per_step": w3 * 1e3 / K, "value": nodes_heads * K / w3,
+                    "bytes_per_step": b3, "achieved_gbs": b3 / (w3 / K) / 1e9,
+                    "hbm_frac_step": b3 / (w3 / K) / 1e9 / HBM_PEAK_GBS,
+                    "time_vs_treewy": (w3 / K) / (wall / K),
+                    "bytes_vs_treewy": b3 / step_bytes,
+                    "kernels_us": {n: t * 1e3 for n, (b, t) in k3.items()},
+                    "kernels_gbs": {n: b / (t * 1e-3) / 1e9 for n, (b, t) in k3.items()}}
+        log(f"[bench] store-all snapshots: {w3 * 1e6 / K:.1f} us/step "
+            f"({snapshot['time_vs_treewy']:.1f}x TreeWY's time, "
+            f"{snapshot['bytes_vs_treewy']:.1f}x its bytes); " + ", ".join(
+                f"{n} {t * 1e3:.1f} us ({b / (t * 1e-3) / 1e9:.0f} GB/s)"
+                for n, (b, t) in k3.items()))
+    snap = None          # (the snapshot step's closure holds the buffer)
+
+    copy_gbs = copy_bandwidth(args.copy_gib) if args.copy_gib > 0 else None
+    if copy_gbs:
+        log(f"[bench] plain device copy of {args.copy_gib:g} GiB: {copy_gbs:.0f} GB/s "
+            f"(bytes read + written)")
+
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
 
     cpu = None
     if args.cpu_seconds > 0 and not args.sweep:
         cpu = cpu_baseline(first, args.cpu_seconds)
+        log(f"[bench] cpu baseline (oracle): {cpu['value']:.3g} {cpu['unit']} on "
+            f"{cpu['threads']} thread(s) of {cpu['host_cores']} host core(s) "
+            f"({cpu['cpu_model']}); {cpu['sample']}")
 
     desc = {"fused": "; steady state: previous step's commit fused into this step's verify",
             "deferred": f"; steady state: commit deferred into a log of {args.deferred} terms",
@@ -454,9 +490,14 @@ def run(args, mode, wl):
                      "traffic": (None if mode == "snapshot" or wl.traffic_key is None else
                                  measured_traffic(wl.traffic_key, dom)),
                      "bytes_per_launch": d_bytes, "launch_us": d_ms * 1e3,
-                     "launch_us_bracketed": d_ms_bracketed * 1e3},
+                     "timing": ("HIP events on the launch stream around the timed region, "
+                                "over the launches in it" if mode in ("fused", "deferred") else
+                                "HIP events around each launch, in a second pass of the "
+                                "timed steps")},
         "kernels_us": {n: t * 1e3 for n, (b, t) in kern.items()},
+        "copy_gbs": copy_gbs,
         "separate_calls": separate,
+        "snapshot": snapshot,
         "cpu_baseline": cpu,
     }
     del pool
@@ -586,6 +627,48 @@ def attention_cpu_baseline(x, ctxn, G, seconds):
                       f"query heads each (cache conversion to float64 not timed)"}
 
 
+def copy_bandwidth(gib):
+    """A plain device-to-device copy of `gib` GiB, timed with HIP events over ten copies after
+    two untimed ones: bytes read plus bytes written per second (GB/s), the achievable
+    streaming rate of this part on this machine."""
+    import torch
+    n = int(gib * 2 ** 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / t / 1e9
+
+
+def host_cpu():
+    """(cores this process may run on, CPU model name from /proc/cpuinfo)."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return cores, model
+
+
 def copy_probe(mib):
     """One plain device copy of known size: a counter run scales its FETCH_SIZE / WRITE_SIZE
     readings by what the counters report for this dispatch."""
@@ -614,33 +697,58 @@ def measured_traffic(cfg, entry: str):
     return float(k["hbm_bytes_per_launch"])
 
 
+def sample_heads(P, count, start):
+    """`count` (layer, sequence, head) triples of problem P, spread over its layers and heads:
+    the k-th one takes layer k mod L and head (start + k) * stride mod B*H, with a stride
+    coprime to B*H near the golden fraction of it, so that consecutive picks land far apart."""
+    nh = P.B * P.H
+    stride = max(1, int(round(nh * 0.6180339887)))
+    while math.gcd(stride, nh) != 1:
+        stride += 1
+    nl = len(P.layers)
+    out = []
+    for k in range(start, start + count):
+        bh = (k * stride) % nh
+        out.append((k % nl, bh // P.H, bh % P.H))
+    return out
+
+
 def cpu_baseline(P, seconds):
     """The oracle, as it stands, on a bounded sample of the same workload.
 
-    Heads of layer 0 of instance 0 are replayed (verify + commit, fp64) in batches,
-    cycling over the heads, until about ``seconds`` of wall time have been spent."""
+    Heads spread over every layer and sequence of the measured instance (sample_heads) are
+    replayed (verify + commit, fp64) in batches until about ``seconds`` of wall time have been
+    spent.  The oracle runs OpenMP over heads on up to 16 host threads (the host share of one
+    GPU on the machines this runs on)."""
     import oracle
     threads = oracle.default_threads()
-    heads = [(b, h) for b in range(P.B) for h in range(P.H)]
-    L = P.layers[0]
+    cores, model = host_cpu()
     done, elapsed, pos, chunk = 0, 0.0, 0, max(threads, 16)
+    layers_seen = set()
     while elapsed < seconds:
-        sel = [heads[(pos + i) % len(heads)] for i in range(chunk)]
+        sel = sample_heads(P, chunk, pos)
+        by_layer = {}
+        for l, b, h in sel:
+            by_layer.setdefault(l, []).append((b, h))
         t0 = time.perf_counter()
-        oracle.batch(L, P.parent, P.accepted, heads=sel, threads=threads)
+        for l, heads in by_layer.items():
+            oracle.batch(P.layers[l], P.parent, P.accepted, heads=heads, threads=threads)
         dt = time.perf_counter() - t0
         elapsed += dt
         done += len(sel)
-        pos = (pos + len(sel)) % len(heads)
+        pos += len(sel)
+        layers_seen.update(by_layer)
         # grow the batch towards about a quarter of the remaining budget
         per = dt / len(sel)
         chunk = int(min(max(chunk, 0.25 * (seconds - elapsed) / max(per, 1e-9)), 2048))
-        chunk = max(chunk, threads)
+        chunk = max(chunk, threads * len(P.layers) if len(P.layers) > 1 else threads)
     rate = done * P.N / elapsed
-    return {"value": rate, "unit": "nodes*heads/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} head replays (cycling over the {len(heads)} heads of layer 0, "
-                      f"instance 0) of the same workload, verify+commit in fp64, "
-                      f"{elapsed:.1f} s wall on {threads} threads"}
+    return {"value": rate, "unit": "nodes*heads/s", "cores": threads, "threads": threads,
+            "host_cores": cores, "cpu_model": model, "kind": "oracle",
+            "sample": f"{done} head replays of {P.N}-node trees, spread over "
+                      f"{len(layers_seen)} of {len(P.layers)} layer(s) and the {P.B * P.H} "
+                      f"heads of each, verify+commit in fp64, {elapsed:.1f} s wall on "
+                      f"{threads} thread(s)"}
 
 
 if __name__ == "__main__":

@@ -24,6 +24,7 @@ same bf16 values.
 
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence
 
@@ -221,9 +222,25 @@ def make_problem(cfg: int, instance: int = 0, layers: Optional[int] = None,
     parent, accepted = parent[:Bx].copy(), accepted[:Bx].copy()
     P = Problem(cfg=cfg, B=Bx, H=c["H"], N=c["N"], dtype=c["dtype"],
                 parent=parent, accepted=accepted)
-    for l in range(nl):
-        P.layers.append(draw_layer(np.random.default_rng(seeds[1 + l]), Bx, c["H"], c["N"], c["dtype"]))
+    draw = lambda l: draw_layer(np.random.default_rng(seeds[1 + l]), Bx, c["H"], c["N"], c["dtype"])
+    if nl > 1:
+        # every layer has a generator of its own, so drawing them on several threads (numpy
+        # releases the interpreter lock while it fills arrays) gives the same numbers
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(nl, _host_threads())) as ex:
+            P.layers.extend(ex.map(draw, range(nl)))
+    else:
+        P.layers.extend(draw(l) for l in range(nl))
     return P
+
+
+def _host_threads() -> int:
+    """Host threads for drawing: the cores this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 # the full-tree shapes of the paper's Table 2 and of Table 4 in Appendix B (w1, w2, w3 per
