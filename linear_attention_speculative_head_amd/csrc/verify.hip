@@ -1157,8 +1157,8 @@ void verify_small_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Larger trees (16 < N <= 64): the persistent streaming design of the small-tree kernel,
-// with NKT = ceil(N / 16) node tiles per lane.
+// Trees of 17 to 32 nodes: the persistent streaming design of the small-tree kernel, with
+// NKT = 2 node tiles per lane (33 to 64 nodes take the one-head-per-item kernel below).
 //
 // Output columns: keys at 0..N-1 (tiles 0..NKT-1), queries at 16 NKT + t (tiles NKT..2NKT-1),
 // so lane L holds P[t] and Y[t] for the nodes t = 16 kt + L % 16 of every node tile kt, rows
@@ -1173,11 +1173,9 @@ void verify_small_kernel(
 // The next item's S0 rows are requested once this item's contractions are done.  With
 // STAGE, its keys, queries, values, gates and tree then follow by direct transfers into an
 // LDS area of their own, and the contractions read their fragments from there.  Without it
-// (where that area would leave one workgroup per CU) the item's key and query rows are sent
-// into the S-row area once the rows have been taken into registers, and the contractions
-// read them there; values, gates and tree are prefetched into registers.  With four node
-// tiles (33 to 64 nodes) the S-row and Gram areas alternate instead (see ALT below), so the
-// key and query rows are requested at the top of the item.
+// (the plain verify, where three workgroups per CU measured faster) the item's key and query
+// rows are sent into the S-row area once the rows have been taken into registers, and the
+// contractions read them there; values, gates and tree are prefetched into registers.
 
 constexpr int kLargePath = 8;                   // path rows staged per chunk (fused)
 
@@ -1409,7 +1407,7 @@ __device__ __forceinline__ void commit_rows_in_lds(float* lds, const char* ldsb,
 // with the item's inputs; its rows are requested then and land while the tree is walked.
 template <int NKT, bool STAGE, bool FUSED = false>
 __global__ __launch_bounds__(kSmallThreads)
-__attribute__((amdgpu_waves_per_eu(STAGE ? (NKT == 2 ? 2 : 1) : (NKT == 2 ? 3 : 2))))
+__attribute__((amdgpu_waves_per_eu(STAGE ? 2 : 3)))
 void verify_large_kernel(
     const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ alpha,
@@ -1433,17 +1431,8 @@ void verify_large_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int kq = 8 * grp;
+    static_assert(NKT == 2, "33 to 64 nodes run verify_head_kernel");
     float* Us = lds + Lo::kS0 + Lo::kG + wave * (16 * NKT * 16);   // this wave's U scratch
-    // Unstaged with four node tiles the S-row area and the Gram area are both 32 KiB and
-    // trade roles every item: item i's S rows sit in area X, its key and query rows go into
-    // area Y at the top of the item (Y held the previous item's Gram matrix, read by then),
-    // the Gram matrix is formed into X once the rows are taken, and item i + 1's S rows go
-    // into Y once the contractions are done.  So the key/query rows stream in together with
-    // the previous step's path rows instead of after the operand split.
-    constexpr bool ALT = !STAGE && NKT == 4;
-    static_assert(!ALT || Lo::kG == Lo::kS0, "the two areas must be the same size");
-    uint32_t xo = 0;                                // ALT: float offset of this item's S rows
     const int grid = gridDim.x;
     const int slot = blockIdx.x;
 
@@ -1474,9 +1463,6 @@ void verify_large_kernel(
         const int h = bh - b * H;
         const size_t node0 = static_cast<size_t>(b) * N;
         const int v0 = part * kSmallRows + 16 * wave + 4 * grp;
-        const uint32_t node_stride = static_cast<uint32_t>(H) * D;
-        const uint16_t* Kh = K + (node0 * H + h) * D;
-        const uint16_t* Qh = Q + (node0 * H + h) * D;
 
         uint2 vraw[NKT];
         int my_par;
@@ -1526,8 +1512,6 @@ void verify_large_kernel(
             if (cur.depth > 0)
                 fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr, large_path_view(Ls));
         }
-        const uint32_t yo = ALT ? Lo::kS0 - xo : 0u;    // ALT: the other area
-        if constexpr (ALT) large_issue_kq(Q, K, H, N, bh, wave, lane, lds_addr + 4u * yo);
 
         // ---- tree walk, lane = node (every wave)
         uint64_t anc_l;
@@ -1567,7 +1551,7 @@ void verify_large_kernel(
             if (cur.depth > 0) {
                 __builtin_amdgcn_s_waitcnt(0);      // the path rows (and the last stores)
                 lds_barrier();
-                commit_rows_in_lds(lds + xo, ldsb, large_path_view(Ls), cur, cin, bh, part, H,
+                commit_rows_in_lds(lds, ldsb, large_path_view(Ls), cur, cin, bh, part, H,
                                    wave, lane, lds_addr);
             }
         }
@@ -1576,7 +1560,7 @@ void verify_large_kernel(
         bf16x8_t ahi[4], alo[4];
         {
             const int r = 16 * wave + col;
-            const float* rowp = lds + xo + r * D;
+            const float* rowp = lds + r * D;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int c0 = 2 * grp + 8 * ks;
@@ -1585,7 +1569,6 @@ void verify_large_kernel(
                             ahi[ks], alo[ks]);
             }
         }
-        if constexpr (ALT) __builtin_amdgcn_s_waitcnt(0);   // this wave's key/query rows
         lds_barrier();                              // rows read: the buffer may be refilled
         ++round;
         int bh_n, part_n;
@@ -1594,13 +1577,13 @@ void verify_large_kernel(
 
         // unstaged: the item's key and query rows go into the S-row area, free from here until
         // the next item's rows are requested (after the contractions)
-        const uint32_t kq_off = STAGE ? Ls.kq : (ALT ? 4u * yo : 0u);
-        if constexpr (!STAGE && !ALT) {
+        const uint32_t kq_off = STAGE ? Ls.kq : 0u;
+        if constexpr (!STAGE) {
             large_issue_kq(Q, K, H, N, bh, wave, lane, lds_addr);
             __builtin_amdgcn_s_waitcnt(0);
             lds_barrier();
         }
-        float* Gx = ALT ? lds + xo : G;             // this item's Gram matrix
+        float* Gx = G;
 
         // ---- contractions and Gram rows 16w..16w+15 (waves with keys there)
         const bool has_gram = wave < NKT && 16 * wave < N;
@@ -1655,7 +1638,7 @@ void verify_large_kernel(
         }
         lds_barrier();                              // G visible to every wave; inputs read
         if constexpr (!STAGE) {
-            if (more) small_issue_s0<FUSED>(S0, lds + yo, bh_n, part_n, wave, lane);
+            if (more) small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
             if (more)
                 large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
             if constexpr (FUSED) {
@@ -1730,8 +1713,6 @@ void verify_large_kernel(
             for (int kt = 0; kt < NKT; ++kt) any |= mrem[kt] != 0ull;
             return __any(any) != 0;
         };
-        // (not with the fused commit at 64 nodes, whose registers would spill)
-        constexpr bool kAhead = !(NKT == 4 && FUSED);
         bool step = pending();
         if (step) coeffs(cs, cw, asel);
         while (step) {
@@ -1741,10 +1722,8 @@ void verify_large_kernel(
                 x[kt] = *reinterpret_cast<const f32x4_t*>(Us + asel[kt] * 16 + 4 * grp);
             float cs_n[NKT], cw_n[NKT];
             int as_n[NKT];
-            if constexpr (kAhead) {
-                step = pending();
-                if (step) coeffs(cs_n, cw_n, as_n);
-            }
+            step = pending();
+            if (step) coeffs(cs_n, cw_n, as_n);
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
@@ -1755,18 +1734,13 @@ void verify_large_kernel(
                 *reinterpret_cast<f32x4_t*>(Us + tn[kt] * 16 + 4 * grp) =
                     f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
             }
-            if constexpr (kAhead) {
-                if (step) {
+            if (step) {
 #pragma unroll
-                    for (int kt = 0; kt < NKT; ++kt) {
-                        cs[kt] = cs_n[kt];
-                        cw[kt] = cw_n[kt];
-                        asel[kt] = as_n[kt];
-                    }
+                for (int kt = 0; kt < NKT; ++kt) {
+                    cs[kt] = cs_n[kt];
+                    cw[kt] = cw_n[kt];
+                    asel[kt] = as_n[kt];
                 }
-            } else {
-                step = pending();
-                if (step) coeffs(cs, cw, asel);
             }
         }
         const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
@@ -1791,7 +1765,680 @@ void verify_large_kernel(
         if (!more) break;
         bh = bh_n;
         part = part_n;
-        if constexpr (ALT) xo = yo;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Larger trees (16 < N <= 64), one head per item.
+//
+// A workgroup of eight waves takes whole heads (all 128 value rows; wave w owns rows
+// 16w..16w+15), one workgroup per CU, and walks a run of consecutive heads, so the heads
+// of one sequence follow one another: its tree bookkeeping (ancestor masks, the
+// pointer-jumping targets) and its previous accepted path are derived once per run, and
+// each head only forms its own gates g_t as products over the cached jump targets.
+//
+// Every input of head i + 1 is requested during head i, by direct HBM -> LDS transfers
+// into areas that head i no longer needs: its S rows as soon as head i's rows are in
+// registers (after the commit and the operand split), the previous step's path rows for its
+// commit right after, its key, query and value rows, parents and gates once head i's
+// contractions are done.  So a head finds its inputs in place, and no register carries
+// them across a head.
+//
+// The key/query rows are staged once per head for all eight waves.  The Gram entries the
+// solve uses (key . key below the diagonal, key . query above it) are formed on the matrix
+// cores by tiles: waves 0..NKT-1 take the key-key tiles of key rows 16w.., waves
+// NKT..2NKT-1 the key-query tiles, so that the two waves of each SIMD share the same
+// number.  They go, already scaled, into compact coefficient tables indexed by the
+// ancestor's depth,
+//   C[d-1][t] = b_t (g_t / g_a) (k_t . k_a)     (a the depth-d ancestor of t, strict),
+//   W[d-1][t] = (g_t / g_a) (k_a . q_t)         (a the depth-d ancestor-or-self of t),
+// which step d of the ancestor walk reads together with the ancestors' U rows: one LDS
+// round trip per step.  Ancestors deeper than the tables (kHeadSlots) get their
+// coefficients from the key and query rows in memory during the walk instead.
+
+constexpr int kHeadWaves = 8;
+constexpr int kHeadThreads = 64 * kHeadWaves;
+constexpr int kHeadSlots = 16;                 // ancestor depths with staged coefficients
+constexpr int kHeadListPer = 5;                // ancestors per packed list word (6 bits each)
+constexpr int kHeadListWords = 3;              // list words per node: depths 1..15
+static_assert(kHeadListPer * kHeadListWords < kHeadSlots, "listed depths have table slots");
+constexpr int kHeadPath = 8;                   // path rows staged per chunk (fused commit)
+
+// LDS of one head workgroup (byte offsets):
+//   S   S rows [128][128] fp32 (16-byte chunk c of row r at chunk c ^ (r % 16))
+//   KQ  key rows 0 .. 16 NKT - 1, query rows 16 NKT .. 32 NKT - 1 (256 B, the same
+//       swizzle; rows of nodes past N are never read into a result that is used)
+//   U   per wave the U exchange [16 NKT nodes][16 rows] fp32
+//   C,W coefficient tables [kHeadSlots][16 NKT] fp32
+//   V   value rows [16 NKT][128] bf16 (the same swizzle)
+//   PU, PK, PG  the previous step's path rows of one chunk (U_prev 512 B, K_prev 256 B),
+//       the path's gammas [64]
+//   SM  parents, alphas, betas of the head (64 words each)
+//   PI, PA  the previous tree (64 words) and accepted node (one word, repeated) of a later
+//       head's sequence
+template <int NKT>
+struct HeadLds {
+    static constexpr int kNodes = 16 * NKT;
+    static constexpr uint32_t kS = 0;
+    static constexpr uint32_t kKQ = kS + D * D * 4u;
+    static constexpr uint32_t kU = kKQ + 2u * kNodes * 256u;
+    static constexpr uint32_t kC = kU + kHeadWaves * kNodes * 16u * 4u;
+    static constexpr uint32_t kW = kC + kHeadSlots * kNodes * 4u;
+    static constexpr uint32_t kV = kW + kHeadSlots * kNodes * 4u;
+    static constexpr uint32_t kPU = kV + kNodes * 256u;
+    static constexpr uint32_t kPK = kPU + kHeadPath * D * 4u;
+    static constexpr uint32_t kPG = kPK + kHeadPath * D * 2u;
+    static constexpr uint32_t kSM = kPG + 256u;
+    static constexpr uint32_t kPI = kSM + 768u;
+    static constexpr uint32_t kPA = kPI + 256u;
+    static constexpr uint32_t kBytes = kPA + 256u;
+    static_assert(kBytes <= 160u * 1024u, "one workgroup per CU");
+    // s_waitcnt operand: vmcnt <= 2 NKT (the previous head's O and U stores), no other wait
+    static constexpr int kWait = (2 * NKT) | (7 << 4) | (15 << 8);
+};
+
+// A head's key, query and value rows, parents, alphas and betas -> LDS (layout above): per
+// four nodes one transfer of key rows, one of query rows and one of value rows, then three
+// gathers, dealt round-robin to the eight waves.  Lanes past the last node load node 0.
+template <int NKT>
+__device__ __forceinline__ void head_issue_inputs(const uint16_t* Q, const uint16_t* K,
+                                                  const uint16_t* V, const float* alpha,
+                                                  const float* beta, const int32_t* parent,
+                                                  int H, int N, int bh, int wave, int lane,
+                                                  uint32_t lds) {
+    using L = HeadLds<NKT>;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * N;
+    const uint32_t row_bytes = static_cast<uint32_t>(H) * D * 2;
+    const size_t hoff = (node0 * H + h) * D;
+    const uint32_t un = static_cast<uint32_t>(N);
+    const uint32_t ln = static_cast<uint32_t>(lane) < un ? static_cast<uint32_t>(lane) : 0u;
+    const int nq4 = (N + 3) >> 2;
+    const int jobs = 3 * nq4 + 3;
+    for (int j = wave; j < jobs; j += kHeadWaves) {
+        if (j < 3 * nq4) {
+            const int kind = j / nq4;                    // 0 keys, 1 queries, 2 values
+            const int jj = j - kind * nq4;
+            const uint32_t lr = static_cast<uint32_t>(lane) >> 4;
+            const uint32_t n = 4u * jj + lr;             // node
+            const uint32_t r = kind == 1 ? static_cast<uint32_t>(L::kNodes) + n : n;   // row in its area
+            const uint32_t c = (static_cast<uint32_t>(lane) & 15u) ^ (r & 15u);
+            const uint16_t* src = (kind == 0 ? K : kind == 1 ? Q : V) + hoff;
+            const uint32_t dst = kind == 2 ? L::kV + 1024u * jj
+                                           : L::kKQ + 256u * (kind * L::kNodes) + 1024u * jj;
+            dma_x4(src, (n < un ? n : 0u) * row_bytes + 16u * c, lds + dst);
+        } else if (j == 3 * nq4) {
+            dma_x1(parent + node0, 4u * ln, lds + L::kSM);
+        } else if (j == 3 * nq4 + 1) {
+            dma_x1(alpha + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds + L::kSM + 256u);
+        } else {
+            dma_x1(beta + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds + L::kSM + 512u);
+        }
+    }
+}
+
+// The previous tree and accepted node of head bh's sequence -> LDS (PI, PA), by one wave.
+template <int NKT>
+__device__ __forceinline__ void head_issue_prev_tree(const CommitIn& c, int bh, int H, int lane,
+                                                     uint32_t lds) {
+    using L = HeadLds<NKT>;
+    const int b = bh / H;
+    const uint32_t n = static_cast<uint32_t>(lane) < static_cast<uint32_t>(c.Np)
+                           ? static_cast<uint32_t>(lane) : 0u;
+    dma_x1(c.parent + static_cast<size_t>(b) * c.Np, 4u * n, lds + L::kPI);
+    dma_x1(c.accepted + b, 0u, lds + L::kPA);
+}
+
+// Path rows 8 c .. 8 c + 7 of a head -> LDS: U_prev rows (two per transfer), K_prev rows
+// (four per transfer), and with the first chunk the gammas of the whole path (one gather,
+// lane = path position).  Slots past the path repeat its first node.
+template <int NKT>
+__device__ __forceinline__ void head_issue_path(const CommitIn& c, const PathInfo& pi, int chunk,
+                                                int bh, int H, int wave, int lane, uint32_t lds) {
+    using L = HeadLds<NKT>;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * c.Np;
+    const int cnt = pi.depth - kHeadPath * chunk < kHeadPath ? pi.depth - kHeadPath * chunk : kHeadPath;
+    const int nu = (cnt + 1) >> 1;
+    const int nk = (cnt + 3) >> 2;
+    const int jobs = nu + nk + (chunk == 0 ? 1 : 0);
+    const float* Uh = c.U + (node0 * H + h) * D;
+    const uint16_t* Kh = c.K + (node0 * H + h) * D;
+    for (int j = wave; j < jobs; j += kHeadWaves) {
+        if (j < nu) {
+            const int q = 2 * j + (lane >> 5);
+            const uint32_t n = static_cast<uint32_t>(__shfl(pi.pn, kHeadPath * chunk + (q < cnt ? q : 0)));
+            dma_x4(Uh, n * static_cast<uint32_t>(H) * (D * 4u) + 16u * (static_cast<uint32_t>(lane) & 31u),
+                   lds + L::kPU + 1024u * j);
+        } else if (j < nu + nk) {
+            const int jj = j - nu;
+            const int q = 4 * jj + (lane >> 4);
+            const uint32_t n = static_cast<uint32_t>(__shfl(pi.pn, kHeadPath * chunk + (q < cnt ? q : 0)));
+            dma_x4(Kh, n * static_cast<uint32_t>(H) * (D * 2u) + 16u * (static_cast<uint32_t>(lane) & 15u),
+                   lds + L::kPK + 1024u * jj);
+        } else {
+            const int n = __shfl(pi.pn, lane < pi.depth ? lane : 0);
+            dma_gather_x1(c.gamma + (node0 + n) * H + h, lds + L::kPG);
+        }
+    }
+}
+
+// The previous step's commit on this wave's 16 rows of a head, where they sit in LDS in
+// the layout they arrived in (lane l: row 16w + 2i + l / 32, 16-byte chunk l % 32,
+// i = 0..7): S_a = g_a S + sum over the path of a of (g_a / g_i) U_prev[i] k_i^T (paper §3
+// "Reconstruct on commit", Eq. 3), written back to LDS for this step's contractions and to
+// S as whole 512-byte rows.  The first kHeadPath path rows and all the path's gammas are in
+// LDS; a longer path fetches the rest chunk by chunk, with blocking waits.  Every wave calls
+// it (the path is the same for the whole workgroup).
+template <int NKT>
+__device__ __forceinline__ void head_commit_rows(float* lds, const PathInfo& cur, const CommitIn& cin,
+                                                 int bh, int H, int wave, int lane,
+                                                 uint32_t lds_addr) {
+    using L = HeadLds<NKT>;
+    const char* ldsb = reinterpret_cast<const char*>(lds);
+    const float* PG = reinterpret_cast<const float*>(ldsb + L::kPG);
+    const float* PU = reinterpret_cast<const float*>(ldsb + L::kPU);
+    const char* PK = ldsb + L::kPK;
+    const float ga = PG[cur.depth - 1];
+    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
+    const int nchunk = (cur.depth + kHeadPath - 1) / kHeadPath;
+    f32x4_t x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = 16u * wave + 2u * i + hl;
+        x[i] = ga * *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
+    }
+    for (int ci = 0; ci < nchunk; ++ci) {
+        const int q0 = ci * kHeadPath;
+        if (ci > 0) {
+            lds_barrier();
+            head_issue_path<NKT>(cin, cur, ci, bh, H, wave, lane, lds_addr);
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+        const int rem = cur.depth - q0;
+        const int cnt = rem < kHeadPath ? rem : kHeadPath;
+#pragma unroll
+        for (int q = 0; q < kHeadPath; ++q) {
+            if (q >= cnt) break;
+            const float cq = ga * __builtin_amdgcn_rcpf(PG[q0 + q]);
+            const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
+            const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
+                                __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float cu = cq * PU[q * D + 16 * wave + 2 * i + hl];
+                x[i] += cu * kv;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = 16u * wave + 2u * i + hl;
+        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
+        // streaming hint: the state is read once and written once per step
+        __builtin_nontemporal_store(
+            x[i], reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D + r) * D + 4 * ch));
+    }
+}
+
+// Part of the dot product of two bf16 rows of 128 elements: elements 32 grp .. 32 grp + 31,
+// then summed over the four lanes col, col + 16, col + 32, col + 48.  Called by all lanes.
+__device__ __forceinline__ float head_dot_bf16(const uint16_t* x, const uint16_t* y, int grp) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 a = *reinterpret_cast<const uint4*>(x + 32 * grp + 8 * j);
+        const uint4 b = *reinterpret_cast<const uint4*>(y + 32 * grp + 8 * j);
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            s += __uint_as_float(aw[k] << 16) * __uint_as_float(bw[k] << 16);
+            s += __uint_as_float(aw[k] & 0xffff0000u) * __uint_as_float(bw[k] & 0xffff0000u);
+        }
+    }
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    return s;
+}
+
+template <int NKT, bool FUSED>
+__global__ __launch_bounds__(kHeadThreads)
+void verify_head_kernel(
+    const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
+    float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
+    uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
+    int32_t* __restrict__ status, CommitIn cin)
+{
+    using L = HeadLds<NKT>;
+    constexpr int NCT = 2 * NKT;
+    constexpr int NN = L::kNodes;
+    extern __shared__ __align__(16) float lds[];
+    char* ldsb = reinterpret_cast<char*>(lds);
+    const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+    float* Ct = reinterpret_cast<float*>(ldsb + L::kC);
+    float* Wt = reinterpret_cast<float*>(ldsb + L::kW);
+
+    const int tid = threadIdx.x;
+    const int lane0 = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // this workgroup's heads: [lo, hi), consecutive
+    const int G = gridDim.x;
+    const int s = blockIdx.x;
+    const int qh = BH / G;
+    const int rh = BH - qh * G;
+    const int lo = s * qh + (s < rh ? s : rh);
+    const int hi = lo + qh + (s < rh ? 1 : 0);
+    if (lo >= hi) return;
+
+    // ---- prologue: the first head's inputs (and, fused, its path)
+    PathInfo pnext{0ull, 0, 0};
+    if constexpr (FUSED) {
+        if (wave == 0) head_issue_prev_tree<NKT>(cin, lo, H, lane0, lds_addr);
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        const int pidx = lane0 < cin.Np ? reinterpret_cast<const int*>(ldsb + L::kPI)[lane0] : -1;
+        const int pacc = reinterpret_cast<const int*>(ldsb + L::kPA)[0];
+        pnext = fused_path(pidx, pacc, cin.Np, lane0, wave == 0 && lo % H == 0, status);
+        lds_barrier();
+        if (pnext.depth > 0) head_issue_path<NKT>(cin, pnext, 0, lo, H, wave, lane0, lds_addr);
+        if (lo + 1 < hi && wave == kHeadWaves - 1)
+            head_issue_prev_tree<NKT>(cin, lo + 1, H, lane0, lds_addr);
+    }
+    small_issue_s0<FUSED>(S0, lds, lo, 0, wave, lane0);
+    head_issue_inputs<NKT>(Q, K, V, alpha, beta, parent, H, N, lo, wave, lane0, lds_addr);
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- per-sequence state (lane = node), derived when the sequence changes
+    int seq = -1;
+    uint64_t anc_l = 0ull;
+    int jp[6] = {-1, -1, -1, -1, -1, -1};
+    int maxd = 1, grounds = 0;
+    int dtk[NKT];                             // depth of node 16 kt + col (0 past N)
+    uint32_t alist[NKT][kHeadListWords];      // its strict ancestors, packed
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+        dtk[kt] = 0;
+#pragma unroll
+        for (int wd = 0; wd < kHeadListWords; ++wd) alist[kt][wd] = 0u;
+    }
+
+    for (int bh = lo;; ) {
+        const int b = bh / H;
+        const int h = bh - b * H;
+        const size_t node0 = static_cast<size_t>(b) * N;
+        const bool more = bh + 1 < hi;
+        // the lane index made opaque here, so that the many lane-dependent LDS addresses
+        // below are formed inside each head instead of being held in registers for the
+        // whole loop
+        int lane = lane0;
+        asm volatile("" : "+v"(lane));
+        const int col = lane & 15;
+        const int grp = lane >> 4;
+        float* Us = reinterpret_cast<float*>(ldsb + L::kU) + wave * (NN * 16);
+
+        // this head's inputs: everything was requested during the previous head (or the
+        // prologue); only that head's O and U stores, issued last, may still be in flight
+        __builtin_amdgcn_s_waitcnt(L::kWait);
+        const PathInfo cur = pnext;
+        lds_barrier();
+        const int my_par = lane < N ? reinterpret_cast<const int*>(ldsb + L::kSM)[lane] : -1;
+        const float my_alpha = lane < N ? reinterpret_cast<const float*>(ldsb + L::kSM + 256)[lane] : 1.0f;
+        const float bl = lane < N ? reinterpret_cast<const float*>(ldsb + L::kSM + 512)[lane] : 0.0f;
+
+        // ---- the sequence's tree (lane = node), once per run of its heads
+        if (b != seq) {
+            seq = b;
+            int p = my_par;
+            const bool bad = lane < N && (p < -1 || p >= lane);
+            if (bad) p = -1;
+            uint64_t am = lane < N ? (1ull << lane) : 0ull;
+            int j = p;
+#pragma unroll
+            for (int r = 0; r < 6; ++r) {
+                jp[r] = j;
+                if ((1 << r) < N) {
+                    const int src = j < 0 ? lane : j;
+                    const uint64_t aj = shfl_u64(am, src);
+                    const int jj = __shfl(j, src);
+                    if (j >= 0) { am |= aj; j = jj; }
+                }
+            }
+            anc_l = am;
+            if (bad) report(status, TREEWY_ETREE);
+            int dm = __popcll(am);
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) dm = max(dm, __shfl_xor(dm, off));
+            maxd = __builtin_amdgcn_readfirstlane(dm);
+            grounds = 0;
+            while ((1 << grounds) < maxd) ++grounds;
+            // per lane and node t = 16 kt + col: its depth and its strict ancestors in depth
+            // order, packed 6 bits each (0 past the list)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const int t = 16 * kt + col;
+                const uint64_t at0 = shfl_u64(anc_l, t);
+                const uint64_t at = t < N ? at0 : 0ull;
+                dtk[kt] = __popcll(at);
+                uint64_t m = at & ~(1ull << t);
+#pragma unroll
+                for (int wd = 0; wd < kHeadListWords; ++wd) {
+                    uint32_t w = 0u;
+#pragma unroll
+                    for (int j = 0; j < kHeadListPer; ++j) {
+                        const uint32_t x = m != 0ull ? static_cast<uint32_t>(__ffsll(static_cast<unsigned long long>(m)) - 1) : 0u;
+                        m &= m - 1ull;
+                        w |= x << (6 * j);
+                    }
+                    alist[kt][wd] = w;
+                }
+            }
+        }
+
+        // ---- this head's gates: g_t = product of alpha over t's ancestors-or-self
+        float g_l = lane < N ? my_alpha : 1.0f;
+#pragma unroll
+        for (int r = 0; r < 6; ++r) {
+            if (r < grounds) {
+                const int j = jp[r];
+                const float gj = __shfl(g_l, j < 0 ? lane : j);
+                if (j >= 0) g_l *= gj;
+            }
+        }
+        if (wave == 0 && lane < N) {
+            gamma[(node0 + lane) * H + h] = g_l;
+            if (h == 0) {
+                if (anc_out) anc_out[node0 + lane] = anc_l;
+                if (depth_out) depth_out[node0 + lane] = __popcll(anc_l);
+            }
+        }
+
+        // ---- the Gram tiles, scaled, into the coefficient tables (they need the key/query
+        // rows and the gates only, so they run before the commit).  Key rows 16 rt.. have
+        // NKT + 1 tiles (key-key at or left of the diagonal, key-query at or right of it),
+        // dealt to the 8 / NKT waves of that row tile.
+        {
+            constexpr int kWavesPerRow = kHeadWaves / NKT;
+            const int rtg = wave / kWavesPerRow;
+            const int jg = wave - rtg * kWavesPerRow;
+            if (16 * rtg < N && jg <= NKT) {
+                uint64_t anc_me[4];
+                float rgm[4], bgm[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = (16 * rtg + 4 * grp + e) & 63;
+                    const uint64_t a = shfl_u64(anc_l, m);
+                    anc_me[e] = m < N ? a : 0ull;
+                    const float gme = __shfl(g_l, m);
+                    rgm[e] = __builtin_amdgcn_rcpf(gme);
+                    bgm[e] = __shfl(bl, m) * gme;
+                }
+                bf16x8_t ka[4];
+                {
+                    const uint32_t m = 16u * rtg + col;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        ka[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                            ldsb + L::kKQ + 256 * m + 16 * ((4 * ks + grp) ^ (m & 15))));
+                }
+                for (int eg = jg; eg <= NKT; eg += kWavesPerRow) {
+                    const bool is_q = eg > rtg;
+                    const int ct = is_q ? eg - 1 : eg;
+                    if (16 * ct >= N) continue;
+                    const uint32_t n = 16u * ct + col;
+                    const bool live = n < static_cast<uint32_t>(N);
+                    const uint32_t r = (is_q ? static_cast<uint32_t>(NN) : 0u) + n;
+                    bf16x8_t bv[4];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        bv[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                            ldsb + L::kKQ + 256 * r + 16 * ((4u * ks + grp) ^ (r & 15u))));
+                    const uint64_t an0 = shfl_u64(anc_l, static_cast<int>(n));
+                    const float gn = __shfl(g_l, static_cast<int>(n));
+                    const float rgn = __builtin_amdgcn_rcpf(gn);
+                    f32x4_t gacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        gacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], bv[ks], gacc, 0, 0, 0);
+                    const uint64_t an = live ? an0 : 0ull;      // node n = 16 ct + col
+                    const int dn = __popcll(an);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = 16 * rtg + 4 * grp + e;   // key row
+                        if (!is_q) {
+                            // C[depth(n) - 1][t = m], n a strict ancestor of m
+                            const bool need = live && m < N && ((anc_me[e] >> n) & 1ull) &&
+                                              static_cast<int>(n) != m;
+                            if (need && dn - 1 < kHeadSlots)
+                                Ct[(dn - 1) * NN + m] = bgm[e] * rgn * gacc[e];
+                        } else {
+                            // W[depth(m) - 1][t = n], m an ancestor-or-self of n
+                            const int dm = __popcll(anc_me[e]);
+                            const bool need = live && m < N && ((an >> m) & 1ull);
+                            if (need && dm - 1 < kHeadSlots)
+                                Wt[(dm - 1) * NN + n] = gn * rgm[e] * gacc[e];
+                        }
+                    }
+                }
+            }
+        }
+
+        // ---- the previous step's commit on this head's rows
+        if constexpr (FUSED) {
+            if (cur.depth > 0) head_commit_rows<NKT>(lds, cur, cin, bh, H, wave, lane, lds_addr);
+        }
+
+        // ---- MFMA operands of this wave's 16 rows (committed, with FUSED)
+        bf16x8_t ahi[4], alo[4];
+        {
+            const int r = 16 * wave + col;
+            const float* rowp = lds + r * D;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int c0 = 2 * grp + 8 * ks;
+                split_hi_lo(*reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15))),
+                            *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15))),
+                            ahi[ks], alo[ks]);
+            }
+        }
+        lds_barrier();                        // S rows and path rows read: both may be refilled
+
+        // ---- the next head's S rows and path rows
+        if (more) {
+            small_issue_s0<FUSED>(S0, lds, bh + 1, 0, wave, lane);
+            if constexpr (FUSED) {
+                if ((bh + 1) / H != b) {
+                    const int pidx = lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L::kPI)[lane] : -1;
+                    const int pacc = reinterpret_cast<const int*>(ldsb + L::kPA)[0];
+                    pnext = fused_path(pidx, pacc, cin.Np, lane, wave == 0 && (bh + 1) % H == 0,
+                                       status);
+                }
+                if (pnext.depth > 0)
+                    head_issue_path<NKT>(cin, pnext, 0, bh + 1, H, wave, lane, lds_addr);
+            }
+        }
+
+        // ---- contractions P = S K^T, Y = S Q^T on this wave's 16 rows (columns of nodes
+        // past N come out of whatever those rows hold and are never used)
+        f32x4_t acc[NCT];
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+            const uint32_t r = 16u * c + col;           // key rows, then query rows
+            bf16x8_t bv[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                bv[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                    ldsb + L::kKQ + 256 * r + 16 * ((4u * ks + grp) ^ (r & 15u))));
+            acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], bv[ks], acc[c], 0, 0, 0);
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bv[ks], acc[c], 0, 0, 0);
+            }
+        }
+        // this head's values: v of node 16 kt + col, rows 16 w + 4 grp .. +3
+        uint2 vraw[NKT];
+        {
+            const uint32_t ch = 2u * wave + (static_cast<uint32_t>(grp) >> 1);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const uint32_t t = 16u * kt + col;
+                vraw[kt] = *reinterpret_cast<const uint2*>(
+                    ldsb + L::kV + 256u * t + 16u * (ch ^ (t & 15u)) + 8u * (grp & 1));
+            }
+        }
+        lds_barrier();                        // coefficients visible; key/query/value rows,
+                                              // parents and gates read
+
+        // ---- the next head's key/query/value rows, parents and gates (and, fused, the
+        // previous tree of the head after it)
+        if (more) {
+            head_issue_inputs<NKT>(Q, K, V, alpha, beta, parent, H, N, bh + 1, wave, lane, lds_addr);
+            if constexpr (FUSED) {
+                if (bh + 2 < hi && wave == kHeadWaves - 1)
+                    head_issue_prev_tree<NKT>(cin, bh + 2, H, lane, lds_addr);
+            }
+        }
+
+        // ---- per lane: nodes t = 16 kt + col, rows v0..v0+3: right-hand sides and g_t Y
+        float g_kt[NKT], b_kt[NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            const int t = 16 * kt + col;
+            g_kt[kt] = __shfl(g_l, t);
+            b_kt[kt] = __shfl(bl, t);
+        }
+        const int v0 = 16 * wave + 4 * grp;
+        float Uv[NKT][4], Ov[NKT][4];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            const int t = 16 * kt + col;
+            const float vv[4] = {__uint_as_float(vraw[kt].x << 16), __uint_as_float(vraw[kt].x & 0xffff0000u),
+                                 __uint_as_float(vraw[kt].y << 16), __uint_as_float(vraw[kt].y & 0xffff0000u)};
+            const float bgt = b_kt[kt] * g_kt[kt];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Uv[kt][e] = b_kt[kt] * vv[e] - bgt * acc[kt][e];
+                Ov[kt][e] = g_kt[kt] * acc[NKT + kt][e];
+            }
+            if (dtk[kt] == 1)                  // a node of depth 1: its U is final already
+                *reinterpret_cast<f32x4_t*>(Us + t * 16 + 4 * grp) =
+                    f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
+        }
+        // ---- ancestor walk: step d folds in every node's depth-d ancestor (final since step
+        // d - 1).  Up to depth kHeadList the ancestor comes from the node's packed list and
+        // the coefficients from the tables; a node's U goes to the exchange once, when it is
+        // final.  Lanes without an ancestor at this depth read node 0 (depth 1, always
+        // written) with zero coefficients.
+        int d = 1;
+#pragma unroll
+        for (int wd = 0; wd < kHeadListWords; ++wd) {
+#pragma unroll
+            for (int j = 0; j < kHeadListPer; ++j) {
+                if (d < maxd) {
+                    float cs[NKT], cw[NKT];
+                    f32x4_t x[NKT];
+#pragma unroll
+                    for (int kt = 0; kt < NKT; ++kt) {
+                        const int t = 16 * kt + col;
+                        const int a = static_cast<int>((alist[kt][wd] >> (6 * j)) & 63u);
+                        const bool has = d < dtk[kt];
+                        x[kt] = *reinterpret_cast<const f32x4_t*>(Us + a * 16 + 4 * grp);
+                        const float c = Ct[(d - 1) * NN + t];
+                        const float w = Wt[(d - 1) * NN + t];
+                        cs[kt] = has ? c : 0.f;
+                        cw[kt] = has ? w : 0.f;
+                    }
+#pragma unroll
+                    for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            Uv[kt][e] -= cs[kt] * x[kt][e];
+                            Ov[kt][e] += cw[kt] * x[kt][e];
+                        }
+                        if (d + 1 == dtk[kt])  // that was its last ancestor: U is final
+                            *reinterpret_cast<f32x4_t*>(Us + (16 * kt + col) * 16 + 4 * grp) =
+                                f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
+                    }
+                    ++d;
+                }
+            }
+        }
+        // deeper trees: the depth-d ancestor from the mask, the coefficients from the key and
+        // query rows in memory
+        const uint16_t* Kh = K + (node0 * H + h) * D;
+        const uint16_t* Qh = Q + (node0 * H + h) * D;
+        const size_t nstride = static_cast<size_t>(H) * D;
+        for (; d < maxd; ++d) {
+            float cs[NKT], cw[NKT];
+            f32x4_t x[NKT];
+            bool fin[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const int tn = 16 * kt + col;
+                const uint64_t at = shfl_u64(anc_l, tn);
+                uint64_t m = tn < N ? (at & ~(1ull << tn)) : 0ull;
+                for (int i = 1; i < d; ++i) m &= m - 1ull;       // drop the shallower ancestors
+                const bool has = m != 0ull;
+                fin[kt] = has && (m & (m - 1ull)) == 0ull;
+                // lanes without an ancestor here read node 0's rows (nothing past N)
+                const int t = has ? tn : 0;
+                const int a = has ? __ffsll(static_cast<unsigned long long>(m)) - 1 : 0;
+                const float rga = __builtin_amdgcn_rcpf(__shfl(g_l, a));
+                const float kk = head_dot_bf16(Kh + t * nstride, Kh + a * nstride, grp);
+                const float kq = head_dot_bf16(Kh + a * nstride, Qh + t * nstride, grp);
+                cs[kt] = has ? b_kt[kt] * g_kt[kt] * rga * kk : 0.f;
+                cw[kt] = has ? g_kt[kt] * rga * kq : 0.f;
+                x[kt] = *reinterpret_cast<const f32x4_t*>(Us + a * 16 + 4 * grp);
+            }
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Uv[kt][e] -= cs[kt] * x[kt][e];
+                    Ov[kt][e] += cw[kt] * x[kt][e];
+                }
+                if (fin[kt])
+                    *reinterpret_cast<f32x4_t*>(Us + (16 * kt + col) * 16 + 4 * grp) =
+                        f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
+            }
+        }
+        // ---- the node's own term, then O and U out
+        const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
+        const size_t row0 = (node0 * H + h) * D;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            const int t = 16 * kt + col;
+            const bool ok = t < N;
+            const int dt = dtk[kt];
+            const bool in_table = ok && dt - 1 < kHeadSlots;
+            float cw = in_table ? Wt[(dt - 1) * NN + t] : 0.f;
+            if (maxd > kHeadSlots) {           // (uniform) the node's own k.q from memory
+                const int tt = ok ? t : 0;
+                const float kq = head_dot_bf16(Kh + tt * nstride, Qh + tt * nstride, grp);
+                if (ok && !in_table) cw = kq;
+            }
+            f32x4_t ov, uv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ov[e] = Ov[kt][e] + cw * Uv[kt][e];
+                uv[e] = Uv[kt][e];
+            }
+            const uint32_t off = ok ? static_cast<uint32_t>((t * H * D + v0) * sizeof(float)) : span;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                ov, __builtin_amdgcn_make_buffer_rsrc(O + row0, 0, span, kRawBufferFlags), off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                uv, __builtin_amdgcn_make_buffer_rsrc(U + row0, 0, span, kRawBufferFlags), off, 0, 0);
+        }
+        if (!more) break;
+        ++bh;
     }
 }
 
@@ -1882,10 +2529,29 @@ static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream,
     const int BH = a.B * a.H;
     const int items = BH * kSmallParts;
     // resident workgroups per CU: the register budget, within the 160 KB of LDS
-    const int regs_wgs = STAGE ? (NKT == 2 ? 2 : 1) : (NKT == 2 ? 3 : 2);
+    const int regs_wgs = STAGE ? 2 : 3;
     const int slots = small_wgs(L.bytes, regs_wgs) * device_cu_count();
     const int grid = items < slots ? items : slots;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), dyn, stream, a.S0,
+                       static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                       static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
+                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status,
+                       cin ? *cin : CommitIn{});
+    return hipGetLastError();
+}
+
+template <int NKT, bool FUSED>
+static hipError_t launch_head(const VerifyArgs& a, hipStream_t stream, const CommitIn* cin = nullptr) {
+    using L = HeadLds<NKT>;
+    auto kern = verify_head_kernel<NKT, FUSED>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(L::kBytes));
+    if (e != hipSuccess) return e;
+    const int BH = a.B * a.H;
+    const int cus = device_cu_count();          // one workgroup per CU (LDS)
+    const int grid = BH < cus ? BH : cus;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kHeadThreads), L::kBytes, stream, a.S0,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
                        BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status,
@@ -1903,7 +2569,7 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     // leaves room for three workgroups per CU up to 32 nodes and two up to 64; the fused
     // kernel below stages its inputs up to 32 nodes instead, where that measured faster
     if (a.N <= 32) return launch_large<2, false>(a, stream);
-    return launch_large<4, false>(a, stream);
+    return launch_head<4, false>(a, stream);
 }
 
 // The previous step's commit fused into this step's verify where the small-tree kernel runs
@@ -1920,8 +2586,8 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
     if (a.in_dtype == TREEWY_BF16) {
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
                            c.accepted, c.N};
-        return a.N <= 32 ? launch_large<2, true, true>(a, stream, &cin)
-                         : launch_large<4, false, true>(a, stream, &cin);
+        if (a.N <= 32) return launch_large<2, true, true>(a, stream, &cin);
+        return launch_head<4, true>(a, stream, &cin);
     }
     hipError_t e = launch_commit(c, stream);
     if (e != hipSuccess) return e;
