@@ -17,6 +17,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <atomic>
+
 namespace treewy {
 
 namespace {
@@ -2442,16 +2444,21 @@ void verify_head_kernel(
     }
 }
 
-// Compute units of the current device, cached per device.
+// Compute units of the current device, queried once per device.  The cache entries are
+// atomics: concurrent first calls from several host threads may each query the attribute,
+// and all store the same value.
 int device_cu_count() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    if (dev >= 0 && dev < 64) cache[dev] = cus;
+    if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 
