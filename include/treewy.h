@@ -11,7 +11,9 @@
  * Conventions shared by every call
  *   d = dk = dv = 128 (fixed).  1 <= N <= 64.  B, H >= 1.
  *   All pointers are DEVICE pointers owned by the caller; the library never
- *   allocates, frees or retains them, and keeps no state between calls.
+ *   allocates, frees or retains them.  Between calls it keeps only each device's
+ *   compute-unit count, queried once (and, for the one entry point that takes no
+ *   workspace, the address of its fixed device array; see below).
  *   Layouts are dense and C-contiguous:
  *     S0, S   [B, H, 128, 128] float32, row v contiguous over k (S[v][k])
  *     Q, K    [B, N, H, 128]   element type given by in_dtype
@@ -60,8 +62,12 @@ enum {
     TREEWY_ETREE = 3,
     TREEWY_EACCEPT = 4,
     TREEWY_ELOG = 5,
-    TREEWY_ECTX = 6
+    TREEWY_ECTX = 6,
+    TREEWY_ESCRATCH = 7
 };
+
+/* Size of the fixed device array behind treewy_tree_attention_noalloc (48 MiB per GPU). */
+#define TREEWY_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
 
 enum { TREEWY_F32 = 0, TREEWY_BF16 = 1 };
 
@@ -219,6 +225,24 @@ int treewy_tree_attention(const void* Kc, const void* Vc, const int32_t* ctx, in
 
 /* Bytes of workspace treewy_tree_attention needs for these sizes (0 for invalid sizes). */
 size_t treewy_tree_attention_workspace(int B, int Hkv, int G, int N, int T_max);
+
+/*
+ * treewy_tree_attention without a workspace argument, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * split partials go to a fixed device array of TREEWY_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends.  Arguments, results and `status` are
+ * those of treewy_tree_attention.  This call allocates nothing: on its first call on a device
+ * it looks up that device's array once.  Returns TREEWY_ESCRATCH (nothing enqueued) when
+ * treewy_tree_attention_workspace(B, Hkv, G, N, T_max) exceeds the array.
+ * Every call on one GPU shares that GPU's array: calls whose executions overlap on one GPU
+ * (different streams, different host threads) race on it and their outputs are undefined;
+ * serialise them (one stream, or events).  The array's contents are not kept between calls
+ * and need no initialisation.
+ */
+int treewy_tree_attention_noalloc(const void* Kc, const void* Vc, const int32_t* ctx, int T_max,
+                                  const void* Qd, const void* Kd, const void* Vd,
+                                  const int32_t* parent, int B, int Hkv, int G, int N, float* O,
+                                  int32_t* status, void* stream);
 
 /*
  * Cache commit of the softmax layers: the accepted node's root-to-node path (keys and values

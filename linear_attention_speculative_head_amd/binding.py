@@ -21,6 +21,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "treewy.h")
 
 TREEWY_OK, TREEWY_EINVAL, TREEWY_EHIP, TREEWY_ETREE, TREEWY_EACCEPT, TREEWY_ELOG = 0, 1, 2, 3, 4, 5
 TREEWY_ECTX = 6
+TREEWY_ESCRATCH = 7
 TREEWY_F32, TREEWY_BF16 = 0, 1
 D = 128
 
@@ -54,6 +55,7 @@ def lib():
         L.treewy_deferred_flush.argtypes = [P] * 7 + [I] * 4 + [P, P]
         L.treewy_tree_attention.argtypes = ([P, P, P, I, P, P, P, P, I, I, I, I, P, P,
                                              ctypes.c_size_t, P, P])
+        L.treewy_tree_attention_noalloc.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, P, P, P]
         L.treewy_tree_attention_workspace.argtypes = [I] * 5
         L.treewy_tree_attention_workspace.restype = ctypes.c_size_t
         L.treewy_kv_commit.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, P, P]
@@ -63,7 +65,8 @@ def lib():
         for f in ("treewy_verify", "treewy_commit", "treewy_verify_snapshot",
                   "treewy_commit_snapshot", "treewy_commit_verify",
                   "treewy_commit_verify_deferred", "treewy_deferred_flush",
-                  "treewy_tree_attention", "treewy_kv_commit", "treewy_version"):
+                  "treewy_tree_attention", "treewy_tree_attention_noalloc", "treewy_kv_commit",
+                  "treewy_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -288,6 +291,32 @@ def treewy_tree_attention(Kc, Vc, ctx, Qd, Kd, Vd, parent, O, workspace, status=
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _ptr(status), _stream(stream))
     _rc(rc, "treewy_tree_attention")
+
+
+def treewy_tree_attention_noalloc(Kc, Vc, ctx, Qd, Kd, Vd, parent, O, status=None, stream=None):
+    """treewy_tree_attention with its split partials in the library's fixed device array (no
+    workspace argument; calls that overlap on one GPU race on that array)."""
+    import torch
+    B, Hkv, T_max, _ = Kc.shape
+    N, Hq = Qd.shape[1], Qd.shape[2]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    G = Hq // Hkv
+    dev = Kc.device
+    bf = (torch.bfloat16,)
+    _check(Kc, "Kc", (B, Hkv, T_max, 256), bf, dev)
+    _check(Vc, "Vc", (B, Hkv, T_max, 256), bf, dev)
+    _check(ctx, "ctx", (B,), (torch.int32,), dev)
+    _check(Qd, "Qd", (B, N, Hq, 256), bf, dev)
+    _check(Kd, "Kd", (B, N, Hkv, 256), bf, dev)
+    _check(Vd, "Vd", (B, N, Hkv, 256), bf, dev)
+    _check(parent, "parent", (B, N), (torch.int32,), dev)
+    _check(O, "O", (B, N, Hq, 256), (torch.float32,), dev)
+    _check(status, "status", (1,), (torch.int32,), dev)
+    rc = lib().treewy_tree_attention_noalloc(_ptr(Kc), _ptr(Vc), _ptr(ctx), T_max, _ptr(Qd),
+                                             _ptr(Kd), _ptr(Vd), _ptr(parent), B, Hkv, G, N,
+                                             _ptr(O), _ptr(status), _stream(stream))
+    _rc(rc, "treewy_tree_attention_noalloc")
 
 
 def treewy_kv_commit(Kc, Vc, ctx_in, ctx_out, Kd, Vd, parent, accepted, status=None, stream=None):

@@ -200,6 +200,20 @@ int treewy_tree_attention(const void* Kc, const void* Vc, const int32_t* ctx, in
     return map_hip(treewy::launch_tree_attention(a, static_cast<hipStream_t>(stream)));
 }
 
+int treewy_tree_attention_noalloc(const void* Kc, const void* Vc, const int32_t* ctx, int T_max,
+                                  const void* Qd, const void* Kd, const void* Vd,
+                                  const int32_t* parent, int B, int Hkv, int G, int N, float* O,
+                                  int32_t* status, void* stream)
+{
+    if (!Kc || !Vc || !ctx || !Qd || !Kd || !Vd || !parent || !O) return TREEWY_EINVAL;
+    if (!attn_sizes_ok(B, Hkv, G, N, T_max)) return TREEWY_EINVAL;
+    if (treewy::attention_workspace_bytes(B, Hkv, G, N, T_max) > TREEWY_NOALLOC_SCRATCH_BYTES)
+        return TREEWY_ESCRATCH;
+    treewy::AttentionArgs a{Kc, Vc, ctx, T_max, Qd, Kd, Vd, parent, B, Hkv, G, N, O, nullptr,
+                            status};
+    return map_hip(treewy::launch_tree_attention_noalloc(a, static_cast<hipStream_t>(stream)));
+}
+
 int treewy_kv_commit(void* Kc, void* Vc, const int32_t* ctx_in, int32_t* ctx_out, int T_max,
                      const void* Kd, const void* Vd, const int32_t* parent,
                      const int32_t* accepted, int B, int Hkv, int N, int32_t* status, void* stream)
@@ -223,6 +237,7 @@ const char* treewy_strerror(int code)
         case TREEWY_EACCEPT: return "accepted node outside [-1, N-1]";
         case TREEWY_ELOG: return "deferred-commit log length outside [0, Lmax]";
         case TREEWY_ECTX: return "committed cache length outside [0, T_max] (or a path that does not fit)";
+        case TREEWY_ESCRATCH: return "sizes need more split partials than the fixed device array of treewy_tree_attention_noalloc holds";
         default: return "unknown error code";
     }
 }

@@ -26,6 +26,9 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace treewy {
 
 namespace {
@@ -594,6 +597,53 @@ hipError_t launch_tree_attention(const AttentionArgs& a, hipStream_t stream) {
                        a.parent, a.Hkv, a.G, a.N, rows, nsplit, static_cast<const float*>(a.work),
                        a.O, a.status);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// The fixed device array of treewy_tree_attention_noalloc: the split partials of a launch
+// go here instead of a caller's workspace.  Each GPU the library runs on holds its own copy
+// for the life of the process.  In host code `scratch` names a host-side stand-in, not a
+// device address: its address on the current device is resolved once per device with
+// hipGetSymbolAddress and only that address is passed to the kernels.
+
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+
+namespace {
+
+std::atomic<void*> g_scratch_addr[64];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up on the first call on a device, with
+// that device current).
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_tree_attention_noalloc(const AttentionArgs& a, hipStream_t stream) {
+    // the caller has checked that the partials fit (attention_workspace_bytes <= the array)
+    void* p = nullptr;
+    hipError_t e = scratch_address(&p);
+    if (e != hipSuccess) return e;
+    AttentionArgs b = a;
+    b.work = p;
+    return launch_tree_attention(b, stream);
 }
 
 hipError_t launch_kv_commit(const KvCommitArgs& a, hipStream_t stream) {

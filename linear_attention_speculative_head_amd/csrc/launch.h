@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "treewy.h"
+
 namespace treewy {
 
 struct VerifyArgs {
@@ -99,6 +101,10 @@ struct KvCommitArgs {
 
 size_t attention_workspace_bytes(int B, int Hkv, int G, int N, int T_max);
 hipError_t launch_tree_attention(const AttentionArgs& a, hipStream_t stream);
+// the same with the partials in the library's fixed device array (a.work is ignored; the
+// caller checks that attention_workspace_bytes fits kNoallocScratchBytes)
+constexpr size_t kNoallocScratchBytes = TREEWY_NOALLOC_SCRATCH_BYTES;
+hipError_t launch_tree_attention_noalloc(const AttentionArgs& a, hipStream_t stream);
 hipError_t launch_kv_commit(const KvCommitArgs& a, hipStream_t stream);
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);

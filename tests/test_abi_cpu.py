@@ -23,7 +23,8 @@ def test_exports_every_header_symbol(lib):
                           "treewy_commit_snapshot", "treewy_commit_verify",
                           "treewy_commit_verify_deferred", "treewy_deferred_flush",
                           "treewy_tree_attention", "treewy_tree_attention_workspace",
-                          "treewy_kv_commit", "treewy_strerror", "treewy_version"}
+                          "treewy_tree_attention_noalloc", "treewy_kv_commit",
+                          "treewy_strerror", "treewy_version"}
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -31,8 +32,8 @@ def test_exports_every_header_symbol(lib):
 
 def test_version_and_strerror(lib):
     assert lib.treewy_version() == 4
-    for code in range(7):
-        assert lib.treewy_strerror(code)
+    for code in range(8):
+        assert lib.treewy_strerror(code) != b"unknown error code"
     assert lib.treewy_strerror(99) == b"unknown error code"
 
 
@@ -166,6 +167,29 @@ def attn_args(**kw):
                                  dict(Hkv=0), dict(T=0), dict(B=70000)])
 def test_tree_attention_rejects(lib, bad):
     assert lib.treewy_tree_attention(*attn_args(**bad)) == binding.TREEWY_EINVAL
+
+
+def noalloc_args(**kw):
+    a = attn_args(**kw)
+    del a[13:15]                        # no workspace pointer, no workspace size
+    return a
+
+
+@pytest.mark.parametrize("bad", [dict(Kc=None), dict(ctx=None), dict(Qd=None), dict(O=None),
+                                 dict(N=0), dict(N=65), dict(G=0), dict(Hkv=0), dict(T=0),
+                                 dict(B=70000)])
+def test_tree_attention_noalloc_rejects(lib, bad):
+    assert lib.treewy_tree_attention_noalloc(*noalloc_args(**bad)) == binding.TREEWY_EINVAL
+
+
+def test_tree_attention_noalloc_rejects_sizes_past_its_array(lib):
+    # the fixed device array holds 48 MiB of split partials; 4096 sequences x 8 KV heads need
+    # one 33 KB partial each (1.08 GB), refused before anything is enqueued
+    assert lib.treewy_tree_attention_workspace(4096, 8, 8, 4, 8192) > 48 << 20
+    assert lib.treewy_tree_attention_noalloc(*noalloc_args(B=4096, Hkv=8, T=8192)) == \
+        binding.TREEWY_ESCRATCH
+    # the benchmark's shape fits: B = 32, 2 x 8 heads, 8256 cache rows
+    assert lib.treewy_tree_attention_workspace(32, 2, 8, 4, 8256) <= 48 << 20
 
 
 def test_kv_commit_rejects(lib):
