@@ -34,16 +34,6 @@ def headwise_rel(x: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return e / np.maximum(s, 1e-30)
 
 
-def sample_heads(B, H, n, seed):
-    """n distinct (sequence, head) pairs: the first, the last, one in the middle, the rest
-    drawn with the given seed."""
-    rng = np.random.default_rng(seed)
-    heads = {(0, 0), (B - 1, H - 1), (B // 2, H // 3)}
-    while len(heads) < n:
-        heads.add((int(rng.integers(B)), int(rng.integers(H))))
-    return sorted(heads)
-
-
 def gather_heads(t: np.ndarray, heads, kind: str) -> np.ndarray:
     """Pick (b, h) heads out of a device-layout array.
     kind 'node': [B,N,H,...] -> [n,N,...]; 'state': [B,H,...] -> [n,...]."""
