@@ -9,7 +9,7 @@
  * state" is its parent's (§3 "Verifying a draft").
  *
  * Conventions shared by every call
- *   d = dk = dv = 128 (fixed).  1 <= N <= 64.  B, H >= 1.
+ *   d = dk = dv = 128 (fixed).  1 <= N <= 64.  B >= 1, 1 <= H <= 65536.
  *   All pointers are DEVICE pointers owned by the caller; the library never
  *   allocates, frees or retains them.  Between calls it keeps only each device's
  *   compute-unit count, queried once (and, for the one entry point that takes no
@@ -32,7 +32,7 @@
  *
  * Errors
  *   The return value reports what the host can check: TREEWY_EINVAL for a null
- *   required pointer, N outside [1, 64], B or H < 1, an unknown in_dtype, or sizes
+ *   required pointer, N outside [1, 64], B < 1, H outside [1, 65536], an unknown in_dtype, or sizes
  *   whose element counts overflow; TREEWY_EHIP when the launch fails.  Nothing is
  *   enqueued when the return value is not TREEWY_OK.
  *   What only the device can see is written to the optional device word `status`
@@ -110,9 +110,8 @@ int treewy_commit(float* S, const float* U, const void* K, const float* gamma,
  *                   B, H, N_prev, in_dtype, status, stream);
  *     treewy_verify(S, Q, K, V, alpha, beta, parent, B, H, N, in_dtype,
  *                   O, U, gamma, anc_out, depth_out, status, stream);
- * but for bf16 inputs it runs as one kernel that reads and writes each state once: the
- * committed rows are formed on the way into the contractions.  fp32 inputs run the two
- * kernels above in that order.
+ * but it runs as one kernel that reads and writes each state once: the committed rows are
+ * formed on the way into the contractions (bf16 and fp32 inputs alike).
  *   S                     [B, H, 128, 128] float32, in place: in, the state before the
  *                         previous step's commit; out, the committed state (the state this
  *                         step verified against).  Rows of sequences with

@@ -13,7 +13,9 @@ namespace {
 // A launch covers up to 2*B*H workgroups of 256 lanes; the dispatch grid is counted in
 // lanes and must fit 32 bits.
 bool sizes_ok(int B, int H, int N) {
-    if (B < 1 || H < 1 || N < 1 || N > 64) return false;
+    // H <= 65536 keeps a node's byte offset within one sequence's rows (node x H x 512 B for
+    // fp32 rows) inside the 32-bit offsets of the kernels' transfers and range-checked stores
+    if (B < 1 || H < 1 || H > 65536 || N < 1 || N > 64) return false;
     const uint64_t groups = static_cast<uint64_t>(B) * static_cast<uint64_t>(H);
     return groups * 2u * 256u <= 0xffffffffull;
 }

@@ -4,15 +4,18 @@
 // §3 "Verifying a draft", Eq. (2), and the per-node readout o_t = S_t q_t with S_t written
 // through the unrolled form of §3 "Reconstruct on commit" (Eq. 3 evaluated at a = t).
 //
-// One workgroup of 256 lanes per (sequence, head):
-//   1. tree walk (one wave, pointer jumping): ancestor masks, depths, cumulative gates g_t;
-//      the ancestor pairs (t, i), i ancestor-or-self of t, are listed root first;
-//   2. the S0 stream: P[t] = S0 k_t and Y[t] = S0 q_t, S0 read once from HBM (lane = row v);
-//   3. R[t] = b_t (v_t - g_t P[t]);  coefficients on ancestor pairs only:
+// Every kernel here computes, per (sequence, head):
+//   1. tree bookkeeping: ancestor masks, depths, cumulative gates g_t (pointer jumping);
+//   2. P[t] = S0 k_t and Y[t] = S0 q_t, S0 read once from HBM;
+//   3. R[t] = b_t (v_t - g_t P[t]); coefficients on ancestor pairs only:
 //      C = b_t (g_t/g_i)(k_t . k_i) for strict ancestors, W = (g_t/g_i)(k_i . q_t);
-//   4. forward substitution U[t] = R[t] - sum_i C[t,i] U[i] in node order (parents first),
-//      one lane per value column v (columns are independent);
-//   5. readout O[t] = g_t Y[t] + sum_{i anc-or-self} W[t,i] U[i]; O, U, gamma written once.
+//   4. forward substitution U[t] = R[t] - sum_i C[t,i] U[i], ancestors before descendants
+//      (value rows are independent);
+//   5. readout O[t] = g_t Y[t] + sum_{i anc-or-self} W[t,i] U[i]; O, U, gamma written once;
+// and, in the fused forms, the previous step's commit (Eq. 3) on the state first.
+// Kernels: fp32 inputs (verify_f32_kernel); bf16 inputs on trees of up to 16 nodes
+// (verify_small_kernel), 17 to 32 nodes (verify_large_kernel), 33 to 64 nodes
+// (verify_head_kernel).
 
 #include "device_common.h"
 #include "launch.h"
@@ -22,165 +25,6 @@
 namespace treewy {
 
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kMaxPairs = MAXN * (MAXN + 1) / 2;  // a chain of 64 nodes
-
-struct VerifyShared {
-    uint64_t anc[MAXN];
-    float g[MAXN];
-    float beta[MAXN];
-    int depth[MAXN];
-    int base[MAXN + 1];          // first pair of node t; base[N] = number of pairs
-    uint8_t pair_t[kMaxPairs];
-    uint8_t pair_i[kMaxPairs];
-    float pair_c[kMaxPairs];     // b_t (g_t/g_i)(k_t . k_i); 0 on the diagonal pair
-    float pair_w[kMaxPairs];     // (g_t/g_i)(k_i . q_t)
-};
-
-template <typename T>
-__global__ __launch_bounds__(kThreads) void verify_kernel(
-    const float* __restrict__ S0, const T* __restrict__ Q, const T* __restrict__ K,
-    const T* __restrict__ V, const float* __restrict__ alpha, const float* __restrict__ beta,
-    const int32_t* __restrict__ parent, int H, int N, float* __restrict__ O,
-    float* __restrict__ U, float* __restrict__ gamma, uint64_t* __restrict__ anc_out,
-    int32_t* __restrict__ depth_out, int32_t* __restrict__ status)
-{
-    __shared__ VerifyShared sh;
-    extern __shared__ float dyn[];
-    float* P = dyn;                 // [N][128]: S0 k_t, then R, then U
-    float* Y = dyn + N * D;         // [N][128]: S0 q_t
-
-    const int tid = threadIdx.x;
-    const int bh = blockIdx.x;
-    const int b = bh / H;
-    const int h = bh - b * H;
-    const size_t node0 = static_cast<size_t>(b) * N;   // row (b, t=0) of [B, N, ...]
-
-    // ---- 1. tree walk (wave 0)
-    if (tid < 64) {
-        const int t = tid;
-        const size_t nh = (node0 + t) * H + h;
-        const float a_t = t < N ? alpha[nh] : 1.0f;
-        NodeInfo ni = tree_walk(parent + node0, N, a_t);
-        if (ni.bad) report(status, TREEWY_ETREE);
-        // exclusive prefix sum of depths -> first pair index of each node
-        int incl = t < N ? ni.depth : 0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off);
-            if (t >= off) incl += y;
-        }
-        if (t < N) {
-            const int start = incl - ni.depth;
-            sh.anc[t] = ni.anc;
-            sh.g[t] = ni.g;
-            sh.beta[t] = beta[nh];
-            sh.depth[t] = ni.depth;
-            sh.base[t] = start;
-            uint64_t m = ni.anc;
-            int idx = start;
-            while (m) {                       // ancestors in increasing index = root first
-                const int i = __ffsll(static_cast<unsigned long long>(m)) - 1;
-                m &= m - 1;
-                sh.pair_t[idx] = static_cast<uint8_t>(t);
-                sh.pair_i[idx] = static_cast<uint8_t>(i);
-                ++idx;
-            }
-            gamma[nh] = ni.g;
-            if (h == 0) {
-                if (anc_out) anc_out[node0 + t] = ni.anc;
-                if (depth_out) depth_out[node0 + t] = ni.depth;
-            }
-        }
-        if (t == N - 1) sh.base[N] = incl;
-    }
-
-    // ---- 2. S0 stream: lane v owns row v; the two lane halves take alternate node groups
-    {
-        const int v = tid & (D - 1);
-        const int half = tid >> 7;
-        const float* srow = S0 + (static_cast<size_t>(bh) * D + v) * D;
-        for (int t0 = half * 4; t0 < N; t0 += 8) {
-            float pk[4] = {0.f, 0.f, 0.f, 0.f};
-            float pq[4] = {0.f, 0.f, 0.f, 0.f};
-            const int nt = min(4, N - t0);
-            for (int c = 0; c < D; c += 4) {
-                const float4 s = *reinterpret_cast<const float4*>(srow + c);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (j < nt) {
-                        const size_t row = ((node0 + t0 + j) * H + h) * D + c;
-                        pk[j] += dot4(s, Elem<T>::load4(K + row));
-                        pq[j] += dot4(s, Elem<T>::load4(Q + row));
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j < nt) {
-                    P[(t0 + j) * D + v] = pk[j];
-                    Y[(t0 + j) * D + v] = pq[j];
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- 3a. right-hand side R[t] = b_t (v_t - g_t P[t]), in place
-    for (int p = tid; p < N * D; p += kThreads) {
-        const int t = p >> 7;
-        const int v = p & (D - 1);
-        const float vt = Elem<T>::load1(V + ((node0 + t) * H + h) * D + v);
-        P[p] = sh.beta[t] * (vt - sh.g[t] * P[p]);
-    }
-    // ---- 3b. coefficients on ancestor pairs
-    const int npairs = sh.base[N];
-    for (int p = tid; p < npairs; p += kThreads) {
-        const int t = sh.pair_t[p];
-        const int i = sh.pair_i[p];
-        const T* kt = K + ((node0 + t) * H + h) * D;
-        const T* ki = K + ((node0 + i) * H + h) * D;
-        const T* qt = Q + ((node0 + t) * H + h) * D;
-        float kk = 0.f, kq = 0.f;
-        for (int c = 0; c < D; c += 4) {
-            const float4 a = Elem<T>::load4(ki + c);
-            kk += dot4(a, Elem<T>::load4(kt + c));
-            kq += dot4(a, Elem<T>::load4(qt + c));
-        }
-        const float ratio = sh.g[t] / sh.g[i];
-        sh.pair_c[p] = (i == t) ? 0.f : sh.beta[t] * ratio * kk;
-        sh.pair_w[p] = ratio * kq;
-    }
-    __syncthreads();
-
-    // ---- 4. forward substitution, parents before children; lane = value column
-    if (tid < D) {
-        const int v = tid;
-        for (int t = 0; t < N; ++t) {
-            float r = P[t * D + v];
-            const int p0 = sh.base[t];
-            const int p1 = p0 + sh.depth[t] - 1;     // last pair is (t, t)
-            for (int p = p0; p < p1; ++p) r -= sh.pair_c[p] * P[sh.pair_i[p] * D + v];
-            P[t * D + v] = r;
-        }
-    }
-    __syncthreads();
-
-    // ---- 5. readout and write-out
-    for (int p = tid; p < N * D; p += kThreads) {
-        const int t = p >> 7;
-        const int v = p & (D - 1);
-        float o = sh.g[t] * Y[p];
-        const int p0 = sh.base[t];
-        const int p1 = p0 + sh.depth[t];
-        for (int q = p0; q < p1; ++q) o += sh.pair_w[q] * P[sh.pair_i[q] * D + v];
-        const size_t out = ((node0 + t) * H + h) * D + v;
-        O[out] = o;
-        U[out] = P[p];
-    }
-}
-
 
 // ---------------------------------------------------------------------------------------
 // bf16 inputs: the S0 contractions on the matrix cores.
@@ -681,6 +525,447 @@ __device__ __forceinline__ void defer_issue_log(const DeferLog& dl, int len, int
         } else {
             dma_x1(dl.scale_in + bh, 0u, lds + L.lg);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// fp32 inputs: one workgroup of 256 lanes per (sequence, head, block of 16 value rows), so
+// that a head's 128 rows run on eight workgroups side by side (rows are independent: row v
+// of the state only meets row v of S0 and column v of V, U and O).
+//
+// Every input of a workgroup reaches LDS in one batch of direct HBM -> LDS transfers issued
+// at once: its 16 S0 rows, the head's key and query rows, its 16-row slice of every value
+// row, the parents, alphas and betas, and (fused) the previous tree, accepted node and, for
+// a previous tree of up to 16 nodes, all its K_prev rows, U_prev slices and gammas.  One
+// wave walks the tree (pointer jumping); with the fused commit another derives the accepted
+// path.  A larger previous tree has only its path's rows fetched, in a second batch, 16 path
+// nodes at a time.  The products P^T = S0 K^T and Y^T = S0 Q^T of the block's rows and the
+// Gram tiles K K^T (at and below the diagonal) and K Q^T (at and above it) run on the matrix
+// cores with both operands split into bf16 hi + lo (f32_tile), one 16 x 16 tile per wave at
+// a time; rows are staged with 16-byte chunk c of row r at c ^ (r % 16), so the operand reads
+// are free of bank conflicts.  The forward substitution runs level by level (step d folds in every node's
+// depth-d ancestor, final since step d - 1), lanes over (row, node), and the readout sums
+// each node's ancestors-or-self.
+//
+// FUSED: the previous step's commit first (paper §3 "Reconstruct on commit", Eq. 3): the
+// 16 rows become g_a S + sum over the accepted path of (g_a / g_i) U_prev[i] k_i^T and are
+// written back to S before the contractions, so the fused step is one launch.  The barriers
+// order LDS only, so no phase waits for the global stores of an earlier one.
+
+constexpr int kF32Rows = 16;                    // value rows per workgroup
+constexpr int kF32Blocks = D / kF32Rows;        // workgroups per head
+constexpr int kF32Threads = 256;
+constexpr int kF32Waves = kF32Threads / 64;
+constexpr int kF32Path = 16;                    // path nodes staged per batch (fused)
+
+struct CommitInF32 {
+    float* S;
+    const float* U;                             // [B][Np][H][128]
+    const float* K;                             // [B][Np][H][128]
+    const float* gamma;                         // [B][Np][H]
+    const int32_t* parent;                      // [B][Np]
+    const int32_t* accepted;                    // [B]
+    int Np;
+};
+
+// LDS of one fp32 workgroup for N nodes (byte offsets, 16-byte aligned areas): S rows
+// [16][128]; key and query rows [N rounded up to 16][128] (whole matrix-core tiles); value
+// slices [N rounded up to 16][16]; P, Y, R-then-U [N][16]; k_t . k_i and k_i . q_t [N][N]; the ancestor of t at
+// depth j + 1 [N][64] bytes; parents, alphas, betas, previous tree, accepted (64 words each);
+// the path rows of one batch: K_prev rows [16][128], U_prev slices [16][16], gammas [64].
+struct F32Lds {
+    uint32_t s, k, q, v, p, y, u, c, w, at, sm, pk, pu, pg, bytes;
+};
+__host__ __device__ inline F32Lds f32_lds(int N) {
+    F32Lds L;
+    const uint32_t n = static_cast<uint32_t>(N);
+    const uint32_t n16 = (n + 15u) & ~15u, nn = (n * n + 3u) & ~3u;
+    L.s = 0;
+    L.k = L.s + kF32Rows * D * 4u;
+    L.q = L.k + n16 * D * 4u;
+    L.v = L.q + n16 * D * 4u;
+    L.p = L.v + n16 * kF32Rows * 4u;
+    L.y = L.p + n * kF32Rows * 4u;
+    L.u = L.y + n * kF32Rows * 4u;
+    L.c = L.u + n * kF32Rows * 4u;
+    L.w = L.c + nn * 4u;
+    L.at = L.w + nn * 4u;
+    L.sm = L.at + n * 64u;
+    L.pk = L.sm + 5u * 256u;
+    L.pu = L.pk + kF32Path * D * 4u;
+    L.pg = L.pu + kF32Path * kF32Rows * 4u;
+    L.bytes = L.pg + 256u;
+    return L;
+}
+
+// One 16 x 16 tile D[i][j] = sum_k A[i][k] B[j][k] of two sets of 16 fp32 rows of 128 in LDS
+// (chunk c of row r at c ^ (r % 16)) on the matrix cores.  Both operands are split into bf16
+// hi + lo (split_hi_lo: |x - hi - lo| <= 2^-18 |x|) and each product is taken as
+// hi.hi + hi.lo + lo.hi, dropping lo.lo (at most 2^-16 of it): three v_mfma_f32_16x16x32_bf16
+// per 32-deep k-block, fp32 accumulation.  Lane L gives row L % 16, k = 8 (L / 16) + 32 kb ..
+// +7 of both operands (the same k order, so the sums are those of the plain product) and
+// receives D[4 (L / 16) + e][L % 16], e = 0..3.
+__device__ __forceinline__ f32x4_t f32_tile(const float* A, const float* Bm, int lane) {
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int c0 = (8 * kb + 2 * g) ^ r, c1 = (8 * kb + 2 * g + 1) ^ r;
+        bf16x8_t ah, al, bh, bl;
+        split_hi_lo(*reinterpret_cast<const f32x4_t*>(A + r * D + 4 * c0),
+                    *reinterpret_cast<const f32x4_t*>(A + r * D + 4 * c1), ah, al);
+        split_hi_lo(*reinterpret_cast<const f32x4_t*>(Bm + r * D + 4 * c0),
+                    *reinterpret_cast<const f32x4_t*>(Bm + r * D + 4 * c1), bh, bl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kF32Threads)
+void verify_f32_kernel(
+    const float* __restrict__ S0, const float* __restrict__ Q, const float* __restrict__ K,
+    const float* __restrict__ V, const float* __restrict__ alpha, const float* __restrict__ beta,
+    const int32_t* __restrict__ parent, int H, int N, float* __restrict__ O,
+    float* __restrict__ U, float* __restrict__ gamma, uint64_t* __restrict__ anc_out,
+    int32_t* __restrict__ depth_out, int32_t* __restrict__ status, CommitInF32 cin)
+{
+    __shared__ uint64_t s_anc[MAXN];
+    __shared__ float s_g[MAXN], s_rg[MAXN], s_beta[MAXN];
+    __shared__ int s_dep[MAXN];
+    __shared__ int s_path[MAXN];
+    __shared__ int s_maxd, s_pdepth;
+    extern __shared__ __align__(16) float dyn[];
+    const F32Lds L = f32_lds(N);
+    char* base = reinterpret_cast<char*>(dyn);
+    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dyn));
+    float* Ss = reinterpret_cast<float*>(base + L.s);
+    float* Ks = reinterpret_cast<float*>(base + L.k);
+    float* Qs = reinterpret_cast<float*>(base + L.q);
+    float* Vs = reinterpret_cast<float*>(base + L.v);
+    float* Ps = reinterpret_cast<float*>(base + L.p);
+    float* Ys = reinterpret_cast<float*>(base + L.y);
+    float* Us = reinterpret_cast<float*>(base + L.u);
+    float* Cs = reinterpret_cast<float*>(base + L.c);
+    float* Ws = reinterpret_cast<float*>(base + L.w);
+    uint8_t* At = reinterpret_cast<uint8_t*>(base + L.at);
+    const int* SMi = reinterpret_cast<const int*>(base + L.sm);
+    const float* SMf = reinterpret_cast<const float*>(base + L.sm);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bh = blockIdx.x / kF32Blocks;
+    const int blk = blockIdx.x - bh * kF32Blocks;
+    const int r0 = blk * kF32Rows;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * N;
+    const size_t nstride = static_cast<size_t>(H) * D;   // floats between nodes of one head
+    const float* Kh = K + (node0 * H + h) * D;
+    const float* Qh = Q + (node0 * H + h) * D;
+    const float* Vh = V + (node0 * H + h) * D + r0;
+    const uint32_t un = static_cast<uint32_t>(N);
+    const uint32_t ln = static_cast<uint32_t>(lane) < un ? static_cast<uint32_t>(lane) : 0u;
+
+    // ---- every input in transfers issued at once.  Wave 0 gathers the parents, alphas and
+    // betas (fused: wave 1 the previous tree and accepted node), waits for those alone and walks
+    // its tree while the rows land; the rows are dealt round-robin to the other waves: 8
+    // transfers of S rows (two rows each), ceil(N/2) of key rows and of query rows, ceil(N/16)
+    // of value slices and (fused, previous tree of up to 16 nodes) ceil(Np/2) of K_prev rows,
+    // one of U_prev slices and one gather of gammas.  Lanes past the last node load node 0
+    // into slots nobody reads.
+    const int nr2 = (N + 1) >> 1;
+    const int nv = (N + 15) >> 4;
+    const int npk = FUSED && cin.Np <= kF32Path ? (cin.Np + 1) >> 1 : 0;
+    {
+        constexpr int kFirstRowWave = FUSED ? 2 : 1;
+        const int jobs = 8 + 2 * nr2 + nv + (npk > 0 ? npk + 2 : 0);
+        const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+        const uint32_t c32 = static_cast<uint32_t>(lane) & 31u;
+        if (wave == 0) {
+            dma_x1(parent + node0, 4u * ln, lds + L.sm);
+            dma_x1(alpha + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds + L.sm + 256u);
+            dma_x1(beta + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds + L.sm + 512u);
+        } else if (FUSED && wave == 1) {
+            const uint32_t n = static_cast<uint32_t>(lane) < static_cast<uint32_t>(cin.Np)
+                                   ? static_cast<uint32_t>(lane) : 0u;
+            dma_x1(cin.parent + static_cast<size_t>(b) * cin.Np, 4u * n, lds + L.sm + 768u);
+            dma_x1(cin.accepted + b, 0u, lds + L.sm + 1024u);
+        } else {
+            for (int j = wave - kFirstRowWave; j < jobs; j += kF32Waves - kFirstRowWave) {
+                if (j < 8) {
+                    const uint32_t r = 2u * j + hl;
+                    dma_x4(S0 + static_cast<size_t>(bh) * D * D,
+                           ((r0 + r) * D + 4u * (c32 ^ (r & 15u))) * 4u, lds + L.s + 1024u * j);
+                } else if (j < 8 + 2 * nr2) {
+                    const int jj = j - 8;
+                    const bool is_q = jj >= nr2;
+                    const uint32_t t = 2u * (is_q ? jj - nr2 : jj) + hl;
+                    dma_x4(is_q ? Qh : Kh,
+                           static_cast<uint32_t>((t < un ? t : 0u) * nstride * 4u) + 16u * (c32 ^ (t & 15u)),
+                           lds + (is_q ? L.q : L.k) + 1024u * (is_q ? jj - nr2 : jj));
+                } else if (j < 8 + 2 * nr2 + nv) {
+                    const int jj = j - 8 - 2 * nr2;
+                    const uint32_t t = 16u * jj + (static_cast<uint32_t>(lane) >> 2);
+                    dma_x4(Vh, static_cast<uint32_t>((t < un ? t : 0u) * nstride * 4u) +
+                                   16u * (static_cast<uint32_t>(lane) & 3u),
+                           lds + L.v + 1024u * jj);
+                } else {
+                    // the previous tree's rows by node: K_prev rows (two per transfer), the
+                    // block's U_prev slices (16 nodes per transfer), gammas (lane = node)
+                    const size_t p0 = static_cast<size_t>(b) * cin.Np;
+                    const uint32_t unp = static_cast<uint32_t>(cin.Np);
+                    const int gp = j - 8 - 2 * nr2 - nv;
+                    if (gp < npk) {
+                        const uint32_t n = 2u * gp + hl;
+                        dma_x4(cin.K + (p0 * H + h) * D,
+                               static_cast<uint32_t>((n < unp ? n : 0u) * nstride * 4u) + 16u * c32,
+                               lds + L.pk + 1024u * gp);
+                    } else if (gp == npk) {
+                        const uint32_t n = static_cast<uint32_t>(lane) >> 2;
+                        dma_x4(cin.U + (p0 * H + h) * D + r0,
+                               static_cast<uint32_t>((n < unp ? n : 0u) * nstride * 4u) +
+                                   16u * (static_cast<uint32_t>(lane) & 3u),
+                               lds + L.pu);
+                    } else {
+                        const uint32_t n = static_cast<uint32_t>(lane) < unp ? static_cast<uint32_t>(lane) : 0u;
+                        dma_x1(cin.gamma + p0 * H + h, 4u * n * static_cast<uint32_t>(H), lds + L.pg);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);              // this wave's own transfers
+    }
+
+    // ---- tree walk (wave 0, lane = node); with FUSED also the previous step's path (wave 1)
+    if (wave == 0) {
+        const int t = lane;
+        int p = t < N ? SMi[t] : -1;
+        const bool bad = t < N && (p < -1 || p >= t);
+        if (bad) p = -1;
+        uint64_t am = t < N ? (1ull << t) : 0ull;
+        float g = t < N ? SMf[64 + t] : 1.0f;
+        int j = p;
+        for (int r = 0; (1 << r) < N; ++r) {       // ceil(log2 N) rounds: depth <= N
+            const int src = j < 0 ? t : j;
+            const uint64_t aj = shfl_u64(am, src);
+            const float gj = __shfl(g, src);
+            const int jj = __shfl(j, src);
+            if (j >= 0) { am |= aj; g *= gj; j = jj; }
+        }
+        if (bad) report(status, TREEWY_ETREE);
+        const int depth = __popcll(am);
+        int dm = 0;                                  // the largest depth, bit by bit (ballots)
+#pragma unroll
+        for (int bit = 32; bit >= 1; bit >>= 1)
+            if (__ballot(t < N && depth >= dm + bit)) dm += bit;
+        if (t == 0) s_maxd = dm;
+        if (t < N) {
+            s_anc[t] = am;
+            s_g[t] = g;
+            s_rg[t] = 1.0f / g;
+            s_beta[t] = SMf[128 + t];
+            s_dep[t] = depth;
+            uint64_t m = am;                         // ancestors-or-self, root first
+            for (int i = 0; m != 0ull; ++i) {
+                At[t * 64 + i] = static_cast<uint8_t>(__ffsll(static_cast<unsigned long long>(m)) - 1);
+                m &= m - 1ull;
+            }
+            if (blk == 0) {
+                gamma[(node0 + t) * H + h] = g;
+                if (h == 0) {
+                    if (anc_out) anc_out[node0 + t] = am;
+                    if (depth_out) depth_out[node0 + t] = depth;
+                }
+            }
+        }
+    } else if (FUSED && wave == 1) {
+        const int p_raw = lane < cin.Np ? SMi[192 + lane] : -1;
+        const PathInfo pi = fused_path(p_raw, SMi[256], cin.Np, lane, blk == 0 && h == 0, status);
+        if (lane == 0) s_pdepth = pi.depth;
+        if (lane < pi.depth) s_path[lane] = pi.pn;
+    }
+    lds_barrier();                                   // every transfer landed; tree and path
+                                                     // visible to all waves
+
+    // ---- the previous step's commit on this block's rows (FUSED), written back to S; lane
+    // (row tid / 16, columns 8 (tid % 16) .. +7); the path rows come 16 nodes per batch
+    if constexpr (FUSED) {
+        const int pd = s_pdepth;
+        if (pd > 0) {
+            const size_t p0 = static_cast<size_t>(b) * cin.Np;
+            const int r = tid >> 4;
+            const int k0 = 8 * (tid & 15);
+            const float* PK = reinterpret_cast<const float*>(base + L.pk);
+            const float* PU = reinterpret_cast<const float*>(base + L.pu);
+            const float* PG = reinterpret_cast<const float*>(base + L.pg);
+            // rows staged by node with the inputs (previous tree of up to 16 nodes), else
+            // fetched here by path position
+            const bool by_node = cin.Np <= kF32Path;
+            float ga = 1.0f;
+            // the lane's two 16-byte chunks of row r, where the swizzle put them
+            const int p0c = (k0 >> 2) ^ r, p1c = ((k0 >> 2) + 1) ^ r;
+            float4 s0 = *reinterpret_cast<const float4*>(Ss + r * D + 4 * p0c);
+            float4 s1 = *reinterpret_cast<const float4*>(Ss + r * D + 4 * p1c);
+            for (int q0 = 0; q0 < pd; q0 += kF32Path) {
+                const int cnt = pd - q0 < kF32Path ? pd - q0 : kF32Path;
+                const int nk = (cnt + 1) >> 1;
+                const int jobs = by_node ? 0 : nk + 1 + (q0 == 0 ? 1 : 0);
+                for (int j = wave; j < jobs; j += kF32Waves) {
+                    if (j < nk) {
+                        const int q = 2 * j + (lane >> 5);
+                        const uint32_t n = static_cast<uint32_t>(s_path[q0 + (q < cnt ? q : 0)]);
+                        dma_x4(cin.K + (p0 * H + h) * D,
+                               static_cast<uint32_t>(n * nstride * 4u) + 16u * (static_cast<uint32_t>(lane) & 31u),
+                               lds + L.pk + 1024u * j);
+                    } else if (j == nk) {
+                        const int q = lane >> 2;
+                        const uint32_t n = static_cast<uint32_t>(s_path[q0 + (q < cnt ? q : 0)]);
+                        dma_x4(cin.U + (p0 * H + h) * D + r0,
+                               static_cast<uint32_t>(n * nstride * 4u) + 16u * (static_cast<uint32_t>(lane) & 3u),
+                               lds + L.pu);
+                    } else {
+                        const int n = s_path[lane < pd ? lane : 0];
+                        dma_gather_x1(cin.gamma + (p0 + n) * H + h, lds + L.pg);
+                    }
+                }
+                if (!by_node) {
+                    __builtin_amdgcn_s_waitcnt(0);
+                    lds_barrier();
+                }
+                if (q0 == 0) {
+                    ga = PG[by_node ? s_path[pd - 1] : pd - 1];
+                    s0 = make_float4(ga * s0.x, ga * s0.y, ga * s0.z, ga * s0.w);
+                    s1 = make_float4(ga * s1.x, ga * s1.y, ga * s1.z, ga * s1.w);
+                }
+#pragma unroll 4
+                for (int q = 0; q < cnt; ++q) {
+                    const int ig = by_node ? s_path[q0 + q] : q0 + q;   // gamma slot
+                    const int ir = by_node ? s_path[q0 + q] : q;        // row slot
+                    const float c = ga / PG[ig] * PU[ir * kF32Rows + r];
+                    const float4 k_lo = *reinterpret_cast<const float4*>(PK + ir * D + k0);
+                    const float4 k_hi = *reinterpret_cast<const float4*>(PK + ir * D + k0 + 4);
+                    s0 = make_float4(s0.x + c * k_lo.x, s0.y + c * k_lo.y, s0.z + c * k_lo.z, s0.w + c * k_lo.w);
+                    s1 = make_float4(s1.x + c * k_hi.x, s1.y + c * k_hi.y, s1.z + c * k_hi.z, s1.w + c * k_hi.w);
+                }
+                if (!by_node) lds_barrier();           // the batch is read: refill
+            }
+            *reinterpret_cast<float4*>(Ss + r * D + 4 * p0c) = s0;
+            *reinterpret_cast<float4*>(Ss + r * D + 4 * p1c) = s1;
+            float* dst = cin.S + (static_cast<size_t>(bh) * D + r0 + r) * D + k0;
+            *reinterpret_cast<float4*>(dst) = s0;
+            *reinterpret_cast<float4*>(dst + 4) = s1;
+            lds_barrier();
+        }
+    }
+
+    // ---- matrix-core tiles, dealt round-robin to the four waves: P^T and Y^T of this
+    // block's rows (node tiles ct), and the Gram tiles K K^T (rt >= ct) and K Q^T (rt <= ct)
+    {
+        const int nt = (N + 15) >> 4;
+        const int ntri = nt * (nt + 1) / 2;
+        const int tiles = 2 * nt + 2 * ntri;
+        const int col = lane & 15;
+        const int rq = 4 * (lane >> 4);
+        for (int tl = wave; tl < tiles; tl += kF32Waves) {
+            int kind, rt = 0, ct;
+            if (tl < 2 * nt) {
+                kind = tl < nt ? 0 : 1;                  // 0: P, 1: Y
+                ct = tl < nt ? tl : tl - nt;
+            } else {
+                const int g = tl - 2 * nt;
+                kind = g < ntri ? 2 : 3;                 // 2: k.k (rt >= ct), 3: k.q (rt <= ct)
+                int x = g < ntri ? g : g - ntri;
+                while (x > rt) { x -= rt + 1; ++rt; }    // the x-th pair of row rt, 0 <= x <= rt
+                ct = x;
+                if (kind == 3) { const int y = rt; rt = ct; ct = y; }
+            }
+            const float* Am = kind <= 1 ? Ss : Ks + 16 * rt * D;
+            const float* Bm = (kind == 1 || kind == 3 ? Qs : Ks) + 16 * ct * D;
+            const f32x4_t d = f32_tile(Am, Bm, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = rq + e;                    // row of the tile
+                const int jn = 16 * ct + col;            // node of its column
+                if (kind <= 1) {
+                    if (jn < N) (kind == 0 ? Ps : Ys)[jn * kF32Rows + i] = d[e];
+                } else if (kind == 2) {
+                    const int tn = 16 * rt + i;
+                    if (tn < N && jn < N) Cs[tn * N + jn] = d[e];     // k_t . k_i
+                } else {
+                    const int an = 16 * rt + i;
+                    if (an < N && jn < N) Ws[jn * N + an] = d[e];     // k_a . q_t
+                }
+            }
+        }
+    }
+    lds_barrier();
+
+    const int maxd = s_maxd;
+    if (N * kF32Rows <= 64) {
+        // a block's (node, row) pairs fit one wave: one pair per lane of wave 0, which takes the
+        // right-hand sides, the levels of the substitution and the readout alone.  A wave's LDS
+        // accesses take effect in issue order, so the levels need no workgroup barrier.
+        if (wave != 0) return;
+        const int x = lane;
+        const bool ok = x < N * kF32Rows;
+        const int t = ok ? x / kF32Rows : 0;
+        const int r = x - t * kF32Rows;
+        float u = ok ? s_beta[t] * (Vs[x] - s_g[t] * Ps[x]) : 0.f;
+        if (ok) Us[x] = u;
+        for (int d = 1; d < maxd; ++d) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // level d - 1 written
+            if (ok && s_dep[t] > d) {
+                const int a = At[t * 64 + d - 1];
+                u -= s_beta[t] * s_g[t] * s_rg[a] * Cs[t * N + a] * Us[a * kF32Rows + r];
+                Us[x] = u;
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (ok) {
+            float o = s_g[t] * Ys[x];
+            for (int j = 0; j < s_dep[t]; ++j) {
+                const int i = At[t * 64 + j];
+                o += s_g[t] * s_rg[i] * Ws[t * N + i] * Us[i * kF32Rows + r];
+            }
+            const size_t out = (node0 + t) * nstride + h * D + r0 + r;
+            O[out] = o;
+            U[out] = u;
+        }
+        return;
+    }
+    // ---- right-hand sides R[t][r] = b_t (v_t[r] - g_t P[t][r])
+    for (int x = tid; x < N * kF32Rows; x += kF32Threads) {
+        const int t = x / kF32Rows;
+        Us[x] = s_beta[t] * (Vs[x] - s_g[t] * Ps[x]);
+    }
+    lds_barrier();
+    // ---- forward substitution, level by level
+    for (int d = 1; d < maxd; ++d) {
+        for (int x = tid; x < N * kF32Rows; x += kF32Threads) {
+            const int t = x / kF32Rows, r = x - t * kF32Rows;
+            if (s_dep[t] > d) {
+                const int a = At[t * 64 + d - 1];
+                Us[x] -= s_beta[t] * s_g[t] * s_rg[a] * Cs[t * N + a] * Us[a * kF32Rows + r];
+            }
+        }
+        lds_barrier();
+    }
+    // ---- readout O[t] = g_t Y[t] + sum over i ancestor-or-self of t of (g_t/g_i)(k_i.q_t) U[i]
+    for (int x = tid; x < N * kF32Rows; x += kF32Threads) {
+        const int t = x / kF32Rows, r = x - t * kF32Rows;
+        float o = s_g[t] * Ys[x];
+        for (int j = 0; j < s_dep[t]; ++j) {
+            const int i = At[t * 64 + j];
+            o += s_g[t] * s_rg[i] * Ws[t * N + i] * Us[i * kF32Rows + r];
+        }
+        const size_t out = (node0 + t) * nstride + h * D + r0 + r;
+        O[out] = o;
+        U[out] = Us[x];
     }
 }
 
@@ -2504,20 +2789,21 @@ static hipError_t launch_small_fixed(const VerifyArgs& a, const CommitIn& cin, c
 
 }  // namespace
 
-template <typename T>
-static hipError_t launch_verify_t(const VerifyArgs& a, hipStream_t stream) {
-    const size_t dyn = static_cast<size_t>(2) * a.N * D * sizeof(float);
-    auto kern = verify_kernel<T>;
-    if (dyn + sizeof(VerifyShared) > 65536) {
+template <bool FUSED>
+static hipError_t launch_f32(const VerifyArgs& a, const CommitInF32& cin, hipStream_t stream) {
+    const F32Lds L = f32_lds(a.N);
+    auto kern = verify_f32_kernel<FUSED>;
+    if (L.bytes > 48u * 1024u) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(dyn));
+                                           static_cast<int>(L.bytes));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(kThreads), dyn, stream, a.S0,
-                       static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
-                       static_cast<const T*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N, a.O,
-                       a.U, a.gamma, a.anc_out, a.depth_out, a.status);
+    const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * kF32Blocks;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kF32Threads), L.bytes, stream, a.S0,
+                       static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
+                       static_cast<const float*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N, a.O,
+                       a.U, a.gamma, a.anc_out, a.depth_out, a.status, cin);
     return hipGetLastError();
 }
 
@@ -2567,7 +2853,7 @@ static hipError_t launch_head(const VerifyArgs& a, hipStream_t stream, const Com
 }
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
-    if (a.in_dtype != TREEWY_BF16) return launch_verify_t<float>(a, stream);
+    if (a.in_dtype != TREEWY_BF16) return launch_f32<false>(a, CommitInF32{}, stream);
     const CommitIn none{};
     const DeferLog nolog{};
     if (a.N <= 8) return launch_small_fixed<0>(a, none, nolog, stream);
@@ -2579,9 +2865,8 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     return launch_head<4, false>(a, stream);
 }
 
-// The previous step's commit fused into this step's verify where the small-tree kernel runs
-// (bf16 inputs, N <= 16); elsewhere the commit kernel and then the verify kernel, in order on
-// the stream, which computes the same.
+// The previous step's commit fused into this step's verify: one kernel for every tree size
+// and input type.
 hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStream_t stream) {
     if (a.in_dtype == TREEWY_BF16 && a.N <= 16) {
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
@@ -2596,9 +2881,9 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
         if (a.N <= 32) return launch_large<2, true, true>(a, stream, &cin);
         return launch_head<4, true>(a, stream, &cin);
     }
-    hipError_t e = launch_commit(c, stream);
-    if (e != hipSuccess) return e;
-    return launch_verify(a, stream);
+    const CommitInF32 cin{c.S, c.U, static_cast<const float*>(c.K), c.gamma, c.parent,
+                          c.accepted, c.N};
+    return launch_f32<true>(a, cin, stream);
 }
 
 // The deferred commit (bf16 inputs, N <= 16 only: the caller checks).

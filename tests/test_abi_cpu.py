@@ -49,7 +49,7 @@ def verify_args(**kw):
 
 
 @pytest.mark.parametrize("bad", [dict(S0=None), dict(Q=None), dict(parent=None), dict(gamma=None),
-                                 dict(N=0), dict(N=65), dict(B=0), dict(H=-1), dict(dt=7),
+                                 dict(N=0), dict(N=65), dict(B=0), dict(H=-1), dict(H=65537), dict(dt=7),
                                  dict(B=1 << 20, H=1 << 10)])
 def test_verify_rejects(lib, bad):
     assert lib.treewy_verify(*verify_args(**bad)) == binding.TREEWY_EINVAL
