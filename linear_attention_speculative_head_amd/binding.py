@@ -5,7 +5,9 @@ shape and contiguity, then their device pointers and torch's current HIP stream 
 passed to the library.  Every step of the computation runs in the HIP kernels of
 ``libtreewy.so``; there is no fallback, and a missing library raises at once.
 
-The functions carry the C names and take caller-owned output tensors, like the ABI.
+The functions carry the C names and take caller-owned output tensors, like the ABI.  With
+``prepare=True`` the launch functions check and marshal their arguments once and return a
+``PreparedCall`` that re-issues exactly that call (for launch loops).
 """
 
 from __future__ import annotations
@@ -117,8 +119,36 @@ def _rc(code: int, where: str):
         raise TreeWYError(code, where)
 
 
+class PreparedCall:
+    """A C ABI call whose arguments were checked and marshalled once: calling it re-issues
+    exactly that call (the same tensors, sizes and stream), with the arguments already in
+    ctypes form.  For launch loops whose host cost per launch should be the ctypes call
+    alone; the library still checks every argument it can on each call."""
+
+    __slots__ = ("fn", "args", "name")
+
+    def __init__(self, fn, args, name):
+        conv = []
+        for t, a in zip(fn.argtypes, args):
+            conv.append(a if a is None else t(a))
+        self.fn, self.args, self.name = fn, tuple(conv), name
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != TREEWY_OK:
+            raise TreeWYError(rc, self.name)
+
+
+def _issue(name: str, args, prepare: bool):
+    fn = getattr(lib(), name)
+    if prepare:
+        return PreparedCall(fn, args, name)
+    _rc(fn(*args), name)
+    return None
+
+
 def treewy_verify(S0, Q, K, V, alpha, beta, parent, O, U, gamma,
-                  anc_out=None, depth_out=None, status=None, stream=None):
+                  anc_out=None, depth_out=None, status=None, stream=None, prepare=False):
     """Enqueue tree verification: fills O, U, gamma (and anc_out, depth_out if given)."""
     import torch
     B, N, H, _ = Q.shape
@@ -136,13 +166,13 @@ def treewy_verify(S0, Q, K, V, alpha, beta, parent, O, U, gamma,
     _check(anc_out, "anc_out", (B, N), (torch.int64, torch.uint64), dev)
     _check(depth_out, "depth_out", (B, N), (torch.int32,), dev)
     _check(status, "status", (1,), (torch.int32,), dev)
-    rc = lib().treewy_verify(_ptr(S0), _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha), _ptr(beta),
-                             _ptr(parent), B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma),
-                             _ptr(anc_out), _ptr(depth_out), _ptr(status), _stream(stream))
-    _rc(rc, "treewy_verify")
+    args = (_ptr(S0), _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha), _ptr(beta), _ptr(parent),
+            B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma), _ptr(anc_out), _ptr(depth_out),
+            _ptr(status), _stream(stream))
+    return _issue("treewy_verify", args, prepare)
 
 
-def treewy_commit(S, U, K, gamma, parent, accepted, status=None, stream=None):
+def treewy_commit(S, U, K, gamma, parent, accepted, status=None, stream=None, prepare=False):
     """Enqueue the in-place commit of the accepted node's state into S."""
     import torch
     B, N, H, _ = K.shape
@@ -156,14 +186,14 @@ def treewy_commit(S, U, K, gamma, parent, accepted, status=None, stream=None):
     _check(parent, "parent", (B, N), (torch.int32,), dev)
     _check(accepted, "accepted", (B,), (torch.int32,), dev)
     _check(status, "status", (1,), (torch.int32,), dev)
-    rc = lib().treewy_commit(_ptr(S), _ptr(U), _ptr(K), _ptr(gamma), _ptr(parent),
-                             _ptr(accepted), B, H, N, dt, _ptr(status), _stream(stream))
-    _rc(rc, "treewy_commit")
+    args = (_ptr(S), _ptr(U), _ptr(K), _ptr(gamma), _ptr(parent), _ptr(accepted), B, H, N,
+            dt, _ptr(status), _stream(stream))
+    return _issue("treewy_commit", args, prepare)
 
 
 def treewy_commit_verify(S, U_prev, K_prev, gamma_prev, parent_prev, accepted_prev,
                          Q, K, V, alpha, beta, parent, O, U, gamma,
-                         anc_out=None, depth_out=None, status=None, stream=None):
+                         anc_out=None, depth_out=None, status=None, stream=None, prepare=False):
     """Enqueue the previous step's commit into S followed by this step's verify against the
     committed S (one kernel where the library fuses them)."""
     import torch
@@ -188,12 +218,11 @@ def treewy_commit_verify(S, U_prev, K_prev, gamma_prev, parent_prev, accepted_pr
     _check(anc_out, "anc_out", (B, N), (torch.int64, torch.uint64), dev)
     _check(depth_out, "depth_out", (B, N), (torch.int32,), dev)
     _check(status, "status", (1,), (torch.int32,), dev)
-    rc = lib().treewy_commit_verify(
-        _ptr(S), _ptr(U_prev), _ptr(K_prev), _ptr(gamma_prev), _ptr(parent_prev),
-        _ptr(accepted_prev), Np, _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha), _ptr(beta),
-        _ptr(parent), B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma), _ptr(anc_out),
-        _ptr(depth_out), _ptr(status), _stream(stream))
-    _rc(rc, "treewy_commit_verify")
+    args = (_ptr(S), _ptr(U_prev), _ptr(K_prev), _ptr(gamma_prev), _ptr(parent_prev),
+            _ptr(accepted_prev), Np, _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha), _ptr(beta),
+            _ptr(parent), B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma), _ptr(anc_out),
+            _ptr(depth_out), _ptr(status), _stream(stream))
+    return _issue("treewy_commit_verify", args, prepare)
 
 
 def _check_log(logU, logK, scale_in, scale_out, len_in, len_out, B, H, dev):
@@ -211,7 +240,8 @@ def _check_log(logU, logK, scale_in, scale_out, len_in, len_out, B, H, dev):
 def treewy_commit_verify_deferred(S, logU, logK, scale_in, scale_out, len_in, len_out,
                                   U_prev, K_prev, gamma_prev, parent_prev, accepted_prev,
                                   Q, K, V, alpha, beta, parent, O, U, gamma,
-                                  anc_out=None, depth_out=None, status=None, stream=None):
+                                  anc_out=None, depth_out=None, status=None, stream=None,
+                                  prepare=False):
     """Enqueue one step with the commit deferred into the log (logU, logK, header in/out)."""
     import torch
     B, N, H, _ = Q.shape
@@ -236,13 +266,12 @@ def treewy_commit_verify_deferred(S, logU, logK, scale_in, scale_out, len_in, le
     _check(anc_out, "anc_out", (B, N), (torch.int64, torch.uint64), dev)
     _check(depth_out, "depth_out", (B, N), (torch.int32,), dev)
     _check(status, "status", (1,), (torch.int32,), dev)
-    rc = lib().treewy_commit_verify_deferred(
-        _ptr(S), _ptr(logU), _ptr(logK), _ptr(scale_in), _ptr(scale_out), _ptr(len_in),
-        _ptr(len_out), Lmax, _ptr(U_prev), _ptr(K_prev), _ptr(gamma_prev), _ptr(parent_prev),
-        _ptr(accepted_prev), Np, _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha), _ptr(beta),
-        _ptr(parent), B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma), _ptr(anc_out),
-        _ptr(depth_out), _ptr(status), _stream(stream))
-    _rc(rc, "treewy_commit_verify_deferred")
+    args = (_ptr(S), _ptr(logU), _ptr(logK), _ptr(scale_in), _ptr(scale_out), _ptr(len_in),
+            _ptr(len_out), Lmax, _ptr(U_prev), _ptr(K_prev), _ptr(gamma_prev),
+            _ptr(parent_prev), _ptr(accepted_prev), Np, _ptr(Q), _ptr(K), _ptr(V),
+            _ptr(alpha), _ptr(beta), _ptr(parent), B, H, N, dt, _ptr(O), _ptr(U), _ptr(gamma),
+            _ptr(anc_out), _ptr(depth_out), _ptr(status), _stream(stream))
+    return _issue("treewy_commit_verify_deferred", args, prepare)
 
 
 def treewy_deferred_flush(S, logU, logK, scale_in, scale_out, len_in, len_out, status=None,
@@ -341,7 +370,8 @@ def treewy_kv_commit(Kc, Vc, ctx_in, ctx_out, Kd, Vd, parent, accepted, status=N
     _rc(rc, "treewy_kv_commit")
 
 
-def treewy_verify_snapshot(S0, Q, K, V, alpha, beta, parent, O, Snap, status=None, stream=None):
+def treewy_verify_snapshot(S0, Q, K, V, alpha, beta, parent, O, Snap, status=None, stream=None,
+                           prepare=False):
     """Enqueue store-all verification: every node's state into Snap, outputs into O."""
     import torch
     B, N, H, _ = Q.shape
@@ -357,13 +387,12 @@ def treewy_verify_snapshot(S0, Q, K, V, alpha, beta, parent, O, Snap, status=Non
     _check(O, "O", (B, N, H, D), f32, dev)
     _check(Snap, "Snap", (B, H, N, D, D), f32, dev)
     _check(status, "status", (1,), (torch.int32,), dev)
-    rc = lib().treewy_verify_snapshot(_ptr(S0), _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha),
-                                      _ptr(beta), _ptr(parent), B, H, N, dt, _ptr(O),
-                                      _ptr(Snap), _ptr(status), _stream(stream))
-    _rc(rc, "treewy_verify_snapshot")
+    args = (_ptr(S0), _ptr(Q), _ptr(K), _ptr(V), _ptr(alpha), _ptr(beta), _ptr(parent),
+            B, H, N, dt, _ptr(O), _ptr(Snap), _ptr(status), _stream(stream))
+    return _issue("treewy_verify_snapshot", args, prepare)
 
 
-def treewy_commit_snapshot(S, Snap, accepted, status=None, stream=None):
+def treewy_commit_snapshot(S, Snap, accepted, status=None, stream=None, prepare=False):
     """Enqueue store-all rollback: S <- Snap[accepted] per sequence."""
     import torch
     B, H, N = Snap.shape[:3]
@@ -373,9 +402,8 @@ def treewy_commit_snapshot(S, Snap, accepted, status=None, stream=None):
     _check(Snap, "Snap", (B, H, N, D, D), f32, dev)
     _check(accepted, "accepted", (B,), (torch.int32,), dev)
     _check(status, "status", (1,), (torch.int32,), dev)
-    rc = lib().treewy_commit_snapshot(_ptr(S), _ptr(Snap), _ptr(accepted), B, H, N,
-                                      _ptr(status), _stream(stream))
-    _rc(rc, "treewy_commit_snapshot")
+    args = (_ptr(S), _ptr(Snap), _ptr(accepted), B, H, N, _ptr(status), _stream(stream))
+    return _issue("treewy_commit_snapshot", args, prepare)
 
 
 def treewy_strerror(code: int) -> str:
