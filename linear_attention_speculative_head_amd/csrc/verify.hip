@@ -2073,10 +2073,10 @@ void verify_large_kernel(
 //
 // The key/query rows are staged once per head for all eight waves.  The Gram entries the
 // solve uses (key . key below the diagonal, key . query above it) are formed on the matrix
-// cores by tiles: waves 0..NKT-1 take the key-key tiles of key rows 16w.., waves
-// NKT..2NKT-1 the key-query tiles, so that the two waves of each SIMD share the same
-// number.  They go, already scaled, into compact coefficient tables indexed by the
-// ancestor's depth,
+// cores by 16 x 16 tiles: key rows 16 rt.. have NKT + 1 tiles, dealt to the 8 / NKT waves
+// of that row tile.  This runs after the next head's S rows are requested (it needs only
+// the key/query rows and the gates), so that transfer overlaps it.  The entries go, already
+// scaled, into compact coefficient tables indexed by the ancestor's depth,
 //   C[d-1][t] = b_t (g_t / g_a) (k_t . k_a)     (a the depth-d ancestor of t, strict),
 //   W[d-1][t] = (g_t / g_a) (k_a . q_t)         (a the depth-d ancestor-or-self of t),
 // which step d of the ancestor walk reads together with the ancestors' U rows: one LDS
@@ -2447,10 +2447,46 @@ void verify_head_kernel(
             }
         }
 
-        // ---- the Gram tiles, scaled, into the coefficient tables (they need the key/query
-        // rows and the gates only, so they run before the commit).  Key rows 16 rt.. have
-        // NKT + 1 tiles (key-key at or left of the diagonal, key-query at or right of it),
-        // dealt to the 8 / NKT waves of that row tile.
+        // ---- the previous step's commit on this head's rows
+        if constexpr (FUSED) {
+            if (cur.depth > 0) head_commit_rows<NKT>(lds, cur, cin, bh, H, wave, lane, lds_addr);
+        }
+
+        // ---- MFMA operands of this wave's 16 rows (committed, with FUSED)
+        bf16x8_t ahi[4], alo[4];
+        {
+            const int r = 16 * wave + col;
+            const float* rowp = lds + r * D;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int c0 = 2 * grp + 8 * ks;
+                split_hi_lo(*reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15))),
+                            *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15))),
+                            ahi[ks], alo[ks]);
+            }
+        }
+        lds_barrier();                        // S rows and path rows read: both may be refilled
+
+        // ---- the next head's S rows and path rows
+        if (more) {
+            small_issue_s0<FUSED>(S0, lds, bh + 1, 0, wave, lane);
+            if constexpr (FUSED) {
+                if ((bh + 1) / H != b) {
+                    const int pidx = lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L::kPI)[lane] : -1;
+                    const int pacc = reinterpret_cast<const int*>(ldsb + L::kPA)[0];
+                    pnext = fused_path(pidx, pacc, cin.Np, lane, wave == 0 && (bh + 1) % H == 0,
+                                       status);
+                }
+                if (pnext.depth > 0)
+                    head_issue_path<NKT>(cin, pnext, 0, bh + 1, H, wave, lane, lds_addr);
+            }
+        }
+
+        // ---- the Gram tiles, scaled, into the coefficient tables.  They need the key/query
+        // rows and the gates only, so they run after the next head's state rows are
+        // requested: the transfer then has the whole rest of this head to arrive.  Key rows
+        // 16 rt.. have NKT + 1 tiles (key-key at or left of the diagonal, key-query at or
+        // right of it), dealt to the 8 / NKT waves of that row tile.
         {
             constexpr int kWavesPerRow = kHeadWaves / NKT;
             const int rtg = wave / kWavesPerRow;
@@ -2514,41 +2550,6 @@ void verify_head_kernel(
                         }
                     }
                 }
-            }
-        }
-
-        // ---- the previous step's commit on this head's rows
-        if constexpr (FUSED) {
-            if (cur.depth > 0) head_commit_rows<NKT>(lds, cur, cin, bh, H, wave, lane, lds_addr);
-        }
-
-        // ---- MFMA operands of this wave's 16 rows (committed, with FUSED)
-        bf16x8_t ahi[4], alo[4];
-        {
-            const int r = 16 * wave + col;
-            const float* rowp = lds + r * D;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int c0 = 2 * grp + 8 * ks;
-                split_hi_lo(*reinterpret_cast<const f32x4_t*>(rowp + 4 * (c0 ^ (r & 15))),
-                            *reinterpret_cast<const f32x4_t*>(rowp + 4 * ((c0 + 1) ^ (r & 15))),
-                            ahi[ks], alo[ks]);
-            }
-        }
-        lds_barrier();                        // S rows and path rows read: both may be refilled
-
-        // ---- the next head's S rows and path rows
-        if (more) {
-            small_issue_s0<FUSED>(S0, lds, bh + 1, 0, wave, lane);
-            if constexpr (FUSED) {
-                if ((bh + 1) / H != b) {
-                    const int pidx = lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L::kPI)[lane] : -1;
-                    const int pacc = reinterpret_cast<const int*>(ldsb + L::kPA)[0];
-                    pnext = fused_path(pidx, pacc, cin.Np, lane, wave == 0 && (bh + 1) % H == 0,
-                                       status);
-                }
-                if (pnext.depth > 0)
-                    head_issue_path<NKT>(cin, pnext, 0, bh + 1, H, wave, lane, lds_addr);
             }
         }
 
