@@ -2095,7 +2095,8 @@ constexpr int kHeadPath = 8;                   // path rows staged per chunk (fu
 //   S   S rows [128][128] fp32 (16-byte chunk c of row r at chunk c ^ (r % 16))
 //   KQ  key rows 0 .. 16 NKT - 1, query rows 16 NKT .. 32 NKT - 1 (256 B, the same
 //       swizzle; rows of nodes past N are never read into a result that is used)
-//   U   per wave the U exchange [16 NKT nodes][16 rows] fp32
+//   U   per wave the U exchange [16 NKT nodes][16 rows] fp32; after the walk it assembles
+//       whole U rows, then whole O rows, for the stores
 //   C,W coefficient tables [kHeadSlots][16 NKT] fp32
 //   V   value rows [16 NKT][128] bf16 (the same swizzle)
 //   PU, PK, PG  the previous step's path rows of one chunk (U_prev 512 B, K_prev 256 B),
@@ -2120,8 +2121,9 @@ struct HeadLds {
     static constexpr uint32_t kPA = kPI + 256u;
     static constexpr uint32_t kBytes = kPA + 256u;
     static_assert(kBytes <= 160u * 1024u, "one workgroup per CU");
-    // s_waitcnt operand: vmcnt <= 2 NKT (the previous head's O and U stores), no other wait
-    static constexpr int kWait = (2 * NKT) | (7 << 4) | (15 << 8);
+    // s_waitcnt operand: vmcnt <= 8 (the previous head's four O and four U row stores per
+    // wave), no other wait
+    static constexpr int kWait = 8 | (7 << 4) | (15 << 8);
 };
 
 // A head's key, query and value rows, parents, alphas and betas -> LDS (layout above): per
@@ -2269,6 +2271,30 @@ __device__ __forceinline__ void head_commit_rows(float* lds, const PathInfo& cur
         // streaming hint: the state is read once and written once per step
         __builtin_nontemporal_store(
             x[i], reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D + r) * D + 4 * ch));
+    }
+}
+
+// Whole node rows of one head out of the U exchange (per wave w: [node][16 values of rows
+// 16w..16w+15]) to a [nodes][H][D] fp32 array at dst (the head's node-0 row): wave w writes
+// nodes 8w..8w+7, two 512-byte rows per store, lane l taking values 4 (l % 32)..+3 of node
+// 8w + 2i + l / 32 from wave (l % 32) / 4's area.  Nodes past N fall outside the buffer
+// range and are dropped.  Four stores per wave, with the streaming hint.
+template <int NKT>
+__device__ __forceinline__ void head_store_rows(float* dst, const char* ldsb, int H, int N,
+                                                int wave, int lane) {
+    using L = HeadLds<NKT>;
+    static_assert(L::kNodes == 8 * kHeadWaves, "eight nodes per wave");
+    const float* Ub = reinterpret_cast<const float*>(ldsb + L::kU);
+    const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
+    const int c = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 8 * wave + 2 * i + (lane >> 5);
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(
+            Ub + (c >> 2) * (L::kNodes * 16) + t * 16 + 4 * (c & 3));
+        const uint32_t off = t < N ? static_cast<uint32_t>((t * H * D + 4 * c) * sizeof(float)) : span;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            x, __builtin_amdgcn_make_buffer_rsrc(dst, 0, span, kRawBufferFlags), off, 0, kStreamAux);
     }
 }
 
@@ -2603,7 +2629,6 @@ void verify_head_kernel(
             g_kt[kt] = __shfl(g_l, t);
             b_kt[kt] = __shfl(bl, t);
         }
-        const int v0 = 16 * wave + 4 * grp;
         float Uv[NKT][4], Ov[NKT][4];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
@@ -2698,9 +2723,10 @@ void verify_head_kernel(
                         f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
             }
         }
-        // ---- the node's own term, then O and U out
-        const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
-        const size_t row0 = (node0 * H + h) * D;
+        // ---- the node's own term; then O and U out as whole rows.  A wave holds 16 values
+        // of each node, so its own stores would cover only 64 of a row's 512 bytes; the rows
+        // are assembled in the U exchange instead and each wave writes eight whole rows,
+        // with the streaming hint (written once, not read again by this launch)
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
             const int t = 16 * kt + col;
@@ -2713,18 +2739,19 @@ void verify_head_kernel(
                 const float kq = head_dot_bf16(Kh + tt * nstride, Qh + tt * nstride, grp);
                 if (ok && !in_table) cw = kq;
             }
-            f32x4_t ov, uv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ov[e] = Ov[kt][e] + cw * Uv[kt][e];
-                uv[e] = Uv[kt][e];
-            }
-            const uint32_t off = ok ? static_cast<uint32_t>((t * H * D + v0) * sizeof(float)) : span;
-            __builtin_amdgcn_raw_buffer_store_b128(
-                ov, __builtin_amdgcn_make_buffer_rsrc(O + row0, 0, span, kRawBufferFlags), off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(
-                uv, __builtin_amdgcn_make_buffer_rsrc(U + row0, 0, span, kRawBufferFlags), off, 0, 0);
+            for (int e = 0; e < 4; ++e) Ov[kt][e] += cw * Uv[kt][e];
         }
+        const size_t row0 = (node0 * H + h) * D;
+        lds_barrier();                        // every wave's U rows are in its exchange area
+        head_store_rows<NKT>(U + row0, ldsb, H, N, wave, lane);
+        lds_barrier();                        // ... and have been read
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+            *reinterpret_cast<f32x4_t*>(Us + (16 * kt + col) * 16 + 4 * grp) =
+                f32x4_t{Ov[kt][0], Ov[kt][1], Ov[kt][2], Ov[kt][3]};
+        lds_barrier();                        // O rows in the exchange
+        head_store_rows<NKT>(O + row0, ldsb, H, N, wave, lane);
         if (!more) break;
         ++bh;
     }
