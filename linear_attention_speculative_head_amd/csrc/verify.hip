@@ -1692,6 +1692,29 @@ __device__ __forceinline__ void commit_rows_in_lds(float* lds, const char* ldsb,
 // FUSED: the previous step's commit first, as in the small-tree kernel's MODE 1, but with the
 // path derived at the top of each item from the previous tree and accepted node that came
 // with the item's inputs; its rows are requested then and land while the tree is walked.
+// Whole half-rows of one item out of the U exchange (per wave w: [16 NKT nodes][16 values
+// of rows 16w..16w+15 of the item's 64]) to a [nodes][H][D] fp32 array at dst (the head's
+// node-0 row): wave w writes nodes 4 NKT w .. 4 NKT w + 4 NKT - 1, four 256-byte half-rows
+// per store, lane l taking values 4 (l % 16)..+3 of the item's half from wave (l % 16) / 4's
+// area.  Nodes past N get an offset past the buffer range and are dropped.  NKT stores per
+// wave, with the streaming hint.
+template <int NKT>
+__device__ __forceinline__ void large_store_rows(float* dst, const float* Ub, int H, int N,
+                                                 int part, int wave, int lane) {
+    const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
+    const int c = lane & 15;
+#pragma unroll
+    for (int i = 0; i < NKT; ++i) {
+        const int t = 4 * NKT * wave + 4 * i + (lane >> 4);
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(
+            Ub + (c >> 2) * (16 * NKT * 16) + t * 16 + 4 * (c & 3));
+        const uint32_t off = t < N ? static_cast<uint32_t>((t * H * D + part * kSmallRows + 4 * c) * sizeof(float))
+                                   : span;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            x, __builtin_amdgcn_make_buffer_rsrc(dst, 0, span, kRawBufferFlags), off, 0, kStreamAux);
+    }
+}
+
 template <int NKT, bool STAGE, bool FUSED = false>
 __global__ __launch_bounds__(kSmallThreads)
 __attribute__((amdgpu_waves_per_eu(STAGE ? 2 : 3)))
@@ -1749,7 +1772,6 @@ void verify_large_kernel(
         const int b = bh / H;
         const int h = bh - b * H;
         const size_t node0 = static_cast<size_t>(b) * N;
-        const int v0 = part * kSmallRows + 16 * wave + 4 * grp;
 
         uint2 vraw[NKT];
         int my_par;
@@ -2030,25 +2052,27 @@ void verify_large_kernel(
                 }
             }
         }
-        const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
-        const size_t row0 = (node0 * H + h) * D;
+        // the node's own term; then O and U out as whole half-rows (the item's 64 values of
+        // a node, 256 bytes), assembled in the U exchange: a wave's own stores would cover
+        // only 64 bytes of each
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
             const int t = tn[kt];
-            const bool ok = t < N;
-            const float cw = ok ? Gx[t * kCols + 16 * NKT + t] : 0.f;   // the node itself
-            f32x4_t ov, uv;
+            const float cw = t < N ? Gx[t * kCols + 16 * NKT + t] : 0.f;   // the node itself
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ov[e] = Ov[kt][e] + cw * Uv[kt][e];
-                uv[e] = Uv[kt][e];
-            }
-            const uint32_t off = ok ? static_cast<uint32_t>((t * H * D + v0) * sizeof(float)) : span;
-            __builtin_amdgcn_raw_buffer_store_b128(
-                ov, __builtin_amdgcn_make_buffer_rsrc(O + row0, 0, span, kRawBufferFlags), off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(
-                uv, __builtin_amdgcn_make_buffer_rsrc(U + row0, 0, span, kRawBufferFlags), off, 0, 0);
+            for (int e = 0; e < 4; ++e) Ov[kt][e] += cw * Uv[kt][e];
         }
+        const size_t row0 = (node0 * H + h) * D;
+        const float* Ub = lds + Lo::kS0 + Lo::kG;
+        lds_barrier();                              // every wave's U rows in its exchange area
+        large_store_rows<NKT>(U + row0, Ub, H, N, part, wave, lane);
+        lds_barrier();                              // ... and read
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+            *reinterpret_cast<f32x4_t*>(Us + tn[kt] * 16 + 4 * grp) =
+                f32x4_t{Ov[kt][0], Ov[kt][1], Ov[kt][2], Ov[kt][3]};
+        lds_barrier();                              // O rows in the exchange
+        large_store_rows<NKT>(O + row0, Ub, H, N, part, wave, lane);
         if (!more) break;
         bh = bh_n;
         part = part_n;
