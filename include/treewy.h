@@ -142,9 +142,12 @@ int treewy_commit_verify(float* S, const float* U_prev, const void* K_prev,
  * with at most Lmax (1..16) rank-one terms.  One call does the work of
  * treewy_commit_verify: it folds the previous step's commit into that representation and
  * verifies this step's tree against the committed state.  When the log can take the accepted
- * path's terms (len + depth(a) <= Lmax, and depth(a) small enough to stage: 4 for N <= 4, else
- * 8), they are appended (u~ = (g_a/g_i) U_prev[i] / new scale) and S is not written.  Otherwise
- * the committed state is written to S and the log is emptied.
+ * path's terms they are appended (u~ = (g_a/g_i) U_prev[i] / new scale) and S is not written;
+ * otherwise the committed state is written to S and the log is emptied.  The log can take them
+ * when, for N <= 16, len + depth(a) <= Lmax and depth(a) is small enough to stage (4 for
+ * N <= 4, else 8); for 16 < N <= 64, when len + depth(a) <= min(Lmax, 8) (the log's and the
+ * path's rows share one staged chunk of 8 terms; a longer list, on a step that writes S, is
+ * fetched chunk by chunk).
  *   S                       [B, H, 128, 128] float32, in place (written only when emptying)
  *   logU                    [B, H, Lmax, 128] float32 (rows past len are ignored)
  *   logK                    [B, H, Lmax, 128] bfloat16
@@ -152,7 +155,7 @@ int treewy_commit_verify(float* S, const float* U_prev, const void* K_prev,
  *   len_in, len_out         [B] int32      } must not overlap; alternate them between steps.
  *                           A fresh log is len 0, scale 1 (S is then the committed state).
  *   the rest                as treewy_commit_verify.
- * Only bf16 inputs with N <= 16 are supported (TREEWY_EINVAL otherwise).  A header length
+ * Only bf16 inputs are supported (TREEWY_EINVAL otherwise), N up to 64.  A header length
  * outside [0, Lmax] is reported as TREEWY_ELOG on `status` and clamped.
  */
 int treewy_commit_verify_deferred(float* S, float* logU, void* logK,

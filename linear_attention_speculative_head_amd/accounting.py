@@ -94,27 +94,30 @@ def deferred_step_bytes(parent_prev: np.ndarray, accepted_prev: np.ndarray, pare
                         H: int, elem: int, lens: np.ndarray, Lmax: int) -> tuple:
     """One step of the deferred commit over one layer, from the log lengths before it.
 
-    Per head: the state read; the logged terms read (a u~ row in fp32 and a key row each);
-    the accepted path's rows (U, key, gamma); this step's per-node I/O; then either the
-    path's terms appended to the log or, when they do not fit (or the path is longer than
-    one staged chunk: 4 rows for N <= 4, else 8), the committed state written back.  Per
-    sequence both trees, the accepted node and the log length.  Returns (bytes, lengths
-    after the step)."""
+    Per head: the state read (once, inside the verify's count); the logged terms read (a u~
+    row in fp32 and a key row each); the accepted path's rows (U, key, gamma); this step's
+    per-node I/O; then either the
+    path's terms appended to the log or, when they do not fit, the committed state written
+    back.  They fit when len + depth <= Lmax and, up to 16 nodes, the path is no longer than
+    one staged chunk (4 rows for N <= 4, else 8); above 16 nodes the log's and the path's
+    terms must fit one chunk of 8 together.  Per sequence both trees, the accepted node and
+    the log length.  Returns (bytes, lengths after the step)."""
     B, Np = parent_prev.shape
     N = parent.shape[1]
     stage = 4 if N <= 4 else 8
+    keep = Lmax if N <= 16 else min(Lmax, 8)
     row = 4 * D + elem * D
     t = B * H * verify_bytes_per_head(N, elem) + B * 4 * (N + Np + 2) + B * H * 8
     after = np.array(lens, dtype=np.int64)
     for b in range(B):
         ln = int(lens[b])
-        t += H * (4 * D * D + ln * row)
+        t += H * ln * row
         a = int(accepted_prev[b])
         if a < 0:
             continue
         da = int(tree_depths(parent_prev[b])[a])
         t += H * da * (row + 4)
-        if ln + da > Lmax or da > stage:
+        if ln + da > keep or (N <= 16 and da > stage):
             t += H * 4 * D * D
             after[b] = 0
         else:

@@ -107,7 +107,7 @@ int treewy_commit_verify_deferred(float* S, float* logU, void* logK, const float
         !K_prev || !gamma_prev || !parent_prev || !accepted_prev || !Q || !K || !V || !alpha ||
         !beta || !parent || !O || !U || !gamma)
         return TREEWY_EINVAL;
-    if (!sizes_ok(B, H, N) || !sizes_ok(B, H, N_prev) || in_dtype != TREEWY_BF16 || N > 16 ||
+    if (!sizes_ok(B, H, N) || !sizes_ok(B, H, N_prev) || in_dtype != TREEWY_BF16 ||
         Lmax < 1 || Lmax > 16)
         return TREEWY_EINVAL;
     const size_t rows = static_cast<size_t>(B) * H * D_ROW;

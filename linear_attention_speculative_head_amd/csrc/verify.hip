@@ -270,6 +270,22 @@ __device__ __forceinline__ void dma_gather_x1(const void* addr, uint32_t lds) {
         : "memory");
 }
 
+// One HBM -> LDS gather of 16 bytes per lane: lane l's bytes at its own address land at LDS
+// byte lds + 16 l.
+__device__ __forceinline__ void dma_gather_x4(const void* addr, uint32_t lds) {
+    lds = __builtin_amdgcn_readfirstlane(lds);      // wave-uniform by construction
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(addr)
+        : "memory");
+}
+
 // One HBM -> LDS load of 4 bytes per lane: lane l's word at base + voff lands at LDS byte
 // lds + 4 l.
 __device__ __forceinline__ void dma_x1(const void* base, uint32_t voff, uint32_t lds) {
@@ -1483,13 +1499,15 @@ struct LargeLayout {
 // row r at chunk c ^ (r % 16)); the item's half of the values (128 B rows); parents, alphas
 // and betas, 64 words each.
 // With the fused commit also: 8 path rows of U_prev halves and K_prev (256 B each), the path's
-// gammas (64 words), the previous tree (64 words) and the accepted node (one word, repeated).
+// gammas (64 words), the previous tree (64 words) and the accepted node (one word, repeated);
+// with the deferred commit the same 8 slots take the log's terms and then the path's, and
+// the log length and scale follow (one word each, repeated).
 struct LargeLds {
-    uint32_t kq, v, sm, pu, pk, pg, idx, acw, bytes;
+    uint32_t kq, v, sm, pu, pk, pg, idx, acw, il, lg, bytes;
 };
 
 template <int NKT, bool STAGE>
-__host__ __device__ inline LargeLds large_lds(int N, bool fused = false) {
+__host__ __device__ inline LargeLds large_lds(int N, bool fused = false, bool defer = false) {
     LargeLds L;
     const uint32_t fixed = sizeof(float) * LargeLayout<NKT>::kTotal;
     L.kq = fixed;
@@ -1502,7 +1520,7 @@ __host__ __device__ inline LargeLds large_lds(int N, bool fused = false) {
         L.pu = sizeof(float) * (LargeLayout<NKT>::kS0 + LargeLayout<NKT>::kG);
         L.pk = L.pu + 256u * kLargePath;
         L.pg = L.pk + 256u * kLargePath;
-        L.idx = L.acw = 0;
+        L.idx = L.acw = L.il = L.lg = 0;
         L.bytes = fixed;
         return L;
     }
@@ -1511,7 +1529,9 @@ __host__ __device__ inline LargeLds large_lds(int N, bool fused = false) {
     L.pg = L.pk + 256u * kLargePath;
     L.idx = L.pg + 256u;
     L.acw = L.idx + 256u;
-    L.bytes = fused ? L.acw + 256u : L.sm + 768u;
+    L.il = L.acw + 256u;                    // deferred: the log length (one word, repeated)
+    L.lg = L.il + 256u;                     // deferred: the item's log scale (the same)
+    L.bytes = fused ? (defer ? L.lg + 256u : L.acw + 256u) : L.sm + 768u;
     return L;
 }
 
@@ -1521,6 +1541,7 @@ __device__ __forceinline__ SmallLds large_path_view(const LargeLds& L) {
     P.pu = L.pu;
     P.pk = L.pk;
     P.pg = L.pg;
+    P.lg = L.lg;
     P.path = kLargePath;
     return P;
 }
@@ -1628,6 +1649,144 @@ __device__ __forceinline__ void large_prefetch(LargePrefetch<NKT>& pf, const uin
     }
 }
 
+// The deferred commit's rank-one terms of an item (half a head), chunk c (slots P c ..
+// P c + P - 1, P = P.path) -> LDS: slot s < len is log term s, slot s >= len path node
+// s - len; the item's half of each u~ / U_prev row and the whole key row, four slots per
+// transfer, by per-lane gathers (the log and the previous step's factors are separate
+// arrays).  With the first chunk also the path's gammas and the head's log scale.  Slots
+// past the terms repeat slot 0.
+__device__ __forceinline__ void defer_issue_terms(const CommitIn& c, const DeferLog& dl,
+                                                  const PathInfo& pi, int len, int chunk, int bh,
+                                                  int part, int H, int wave, int lane,
+                                                  uint32_t lds, const SmallLds& P) {
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * c.Np;
+    const int rem = len + pi.depth - P.path * chunk;
+    const int cnt = rem < P.path ? rem : P.path;
+    const int nj = cnt > 0 ? (cnt + 3) >> 2 : 0;
+    const int jobs = 2 * nj + (chunk == 0 ? 2 : 0);
+    const size_t lrow0 = static_cast<size_t>(bh) * dl.Lmax;
+    for (int j = wave; j < jobs; j += 4) {
+        if (j < 2 * nj) {
+            const bool is_k = j >= nj;
+            const int jj = is_k ? j - nj : j;
+            const int q = 4 * jj + (lane >> 4);
+            const int sl = P.path * chunk + (q < cnt ? q : 0);
+            const int pq = sl - len;
+            const int n = __shfl(pi.pn, pq >= 0 ? pq : 0);
+            if (is_k) {
+                const uint16_t* src = sl < len ? dl.K + (lrow0 + sl) * D
+                                               : c.K + ((node0 + n) * H + h) * D;
+                dma_gather_x4(src + 8 * (lane & 15), lds + P.pk + 1024u * jj);
+            } else {
+                const float* src = (sl < len ? dl.U + (lrow0 + sl) * D
+                                             : c.U + ((node0 + n) * H + h) * D) + part * kSmallRows;
+                dma_gather_x4(src + 4 * (lane & 15), lds + P.pu + 1024u * jj);
+            }
+        } else if (j == 2 * nj) {
+            const int n = __shfl(pi.pn, lane < pi.depth ? lane : 0);
+            dma_gather_x1(c.gamma + (node0 + n) * H + h, lds + P.pg);
+        } else {
+            dma_x1(dl.scale_in + bh, 0u, lds + P.lg);
+        }
+    }
+}
+
+// The deferred commit on this wave's 16 rows of an item (half a head; layout as in
+// commit_rows_in_lds): S_a = gs (S + sum_j u~_j k_j^T) + sum over the path of a of
+// (g_a / g_i) U_prev[i] k_i^T, gs = s g_a (paper §3 "Reconstruct on commit", Eq. 3, on the
+// logged state), formed in LDS for this step's contractions.  When the path's terms fit in
+// the log and in one chunk of slots (len + depth <= min(Lmax, P.path)) the item's half of
+// each u~ = (g_a / g_i) U_prev[i] / gs and of each key row is appended to the log and S is
+// not written; otherwise S_a goes to S and the log is emptied.  Part 0 writes the header:
+// scale 1 and length 0 when emptied, else gs and len + depth.  Called by every wave, with
+// len + depth > 0.
+__device__ __forceinline__ void commit_defer_in_lds(float* lds, const char* ldsb, const SmallLds& P,
+                                                    const PathInfo& cur, int len,
+                                                    const CommitIn& cin, const DeferLog& dl,
+                                                    int bh, int part, int H, int wave, int lane,
+                                                    uint32_t lds_addr) {
+    const float* PG = reinterpret_cast<const float*>(ldsb + P.pg);
+    const float* PU = reinterpret_cast<const float*>(ldsb + P.pu);
+    const char* PK = ldsb + P.pk;
+    const float gin = reinterpret_cast<const float*>(ldsb + P.lg)[0];
+    const float ga = cur.depth > 0 ? PG[cur.depth - 1] : 1.0f;
+    const float gs = gin * ga;
+    const int total = len + cur.depth;
+    const int keep = dl.Lmax < P.path ? dl.Lmax : P.path;
+    const bool flush = total > keep;
+    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
+    const int nchunk = (total + P.path - 1) / P.path;
+    f32x4_t x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = 16u * wave + 2u * i + hl;
+        x[i] = gs * *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
+    }
+    for (int ci = 0; ci < nchunk; ++ci) {
+        const int q0 = ci * P.path;
+        if (ci > 0) {
+            lds_barrier();
+            defer_issue_terms(cin, dl, cur, len, ci, bh, part, H, wave, lane, lds_addr, P);
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+        const int rem = total - q0;
+        const int cnt = rem < P.path ? rem : P.path;
+        // unrolled over the chunk's slots (P.path = kLargePath), so that the reads of all its
+        // rows are issued together
+#pragma unroll
+        for (int q = 0; q < kLargePath; ++q) {
+            if (q >= cnt) break;
+            const int sl = q0 + q;
+            const float cq = sl < len ? gs : ga / PG[sl - len >= 0 ? sl - len : 0];
+            const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
+            const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
+                                __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float cu = cq * PU[q * kSmallRows + 16 * wave + 2 * i + hl];
+                x[i] += cu * kv;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = 16u * wave + 2u * i + hl;
+        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
+        if (flush)
+            __builtin_nontemporal_store(
+                x[i], reinterpret_cast<f32x4_t*>(
+                          cin.S + (static_cast<size_t>(bh) * D + part * kSmallRows + r) * D + 4 * ch));
+    }
+    if (!flush) {
+        // every term sits in the first chunk's slots: path node q is slot len + q; wave w
+        // appends terms w, w + 4, ...: lanes 0-15 this half of u~, lanes 16-23 this half of
+        // the key row
+        const size_t lrow0 = static_cast<size_t>(bh) * dl.Lmax + len;
+        const float rgs = 1.0f / gs;
+        for (int q = wave; q < cur.depth; q += 4) {
+            const int sl = len + q;
+            if (lane < 16) {
+                const float cq = (ga / PG[q]) * rgs;
+                const f32x4_t u = *reinterpret_cast<const f32x4_t*>(PU + sl * kSmallRows + 4 * lane);
+                *reinterpret_cast<f32x4_t*>(dl.U + (lrow0 + q) * D + part * kSmallRows + 4 * lane) = cq * u;
+            } else if (lane < 24) {
+                const int c8 = lane - 16;
+                const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(PK + sl * 256 + 128 * part + 16 * c8);
+                *reinterpret_cast<u32x4_t*>(dl.K + (lrow0 + q) * D + part * kSmallRows + 8 * c8) = kv;
+            }
+        }
+    }
+    if (wave == 0 && lane == 0 && part == 0) {
+        const int b = bh / H;
+        dl.scale_out[bh] = flush ? 1.0f : gs;
+        if (bh - b * H == 0) dl.len_out[b] = flush ? 0 : total;
+    }
+}
+
 // The previous step's commit on this wave's 16 rows of an item, where they sit in LDS in the
 // layout they arrived in (lane l: row 16w + 2i + l / 32, 16-byte chunk l % 32, i = 0..7):
 // S_a = g_a S + sum over the path of a of (g_a / g_i) U_prev[i] k_i^T (paper §3 "Reconstruct
@@ -1715,7 +1874,7 @@ __device__ __forceinline__ void large_store_rows(float* dst, const float* Ub, in
     }
 }
 
-template <int NKT, bool STAGE, bool FUSED = false>
+template <int NKT, bool STAGE, bool FUSED = false, bool DEFER = false>
 __global__ __launch_bounds__(kSmallThreads)
 __attribute__((amdgpu_waves_per_eu(STAGE ? 2 : 3)))
 void verify_large_kernel(
@@ -1724,14 +1883,14 @@ void verify_large_kernel(
     const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
     float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
-    int32_t* __restrict__ status, CommitIn cin)
+    int32_t* __restrict__ status, CommitIn cin, DeferLog dlog)
 {
     using Lo = LargeLayout<NKT>;
     constexpr int NCT = 2 * NKT;
     constexpr int kCols = Lo::kCols;
     extern __shared__ __align__(16) float lds[];
     float* G = lds + Lo::kS0;                       // G[m][n], n: keys 0..N-1, queries 16NKT+t
-    const LargeLds Ls = large_lds<NKT, STAGE>(N, FUSED);
+    const LargeLds Ls = large_lds<NKT, STAGE>(N, FUSED, DEFER);
     const char* ldsb = reinterpret_cast<const char*>(lds);
     const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     const int nq4 = (N + 3) >> 2;
@@ -1759,6 +1918,9 @@ void verify_large_kernel(
     if constexpr (FUSED && STAGE) {
         if (wave == 2) fused_issue_index(cin, bh / H, lane, lds_addr + Ls.idx);
         if (wave == 3) dma_gather_x1(cin.accepted + bh / H, lds_addr + Ls.acw);
+        if constexpr (DEFER) {
+            if (wave == 1) dma_x1(dlog.len_in + bh / H, 0u, lds_addr + Ls.il);
+        }
     } else if constexpr (FUSED) {
         pidx = lane < cin.Np ? cin.parent[static_cast<size_t>(bh / H) * cin.Np + lane] : -1;
         pacc = cin.accepted[bh / H];
@@ -1811,6 +1973,7 @@ void verify_large_kernel(
 
         // ---- the previous step's commit: this item's path, its rows requested now
         PathInfo cur{0ull, 0, 0};
+        int clen = 0;                               // deferred: the log length
         if constexpr (FUSED) {
             if constexpr (STAGE) {
                 pidx = lane < cin.Np ? reinterpret_cast<const int*>(ldsb + Ls.idx)[lane] : -1;
@@ -1818,8 +1981,17 @@ void verify_large_kernel(
             }
             cur = fused_path(pidx, pacc, cin.Np, lane, wave == 0 && bh % H == 0 && part == 0,
                              status);
-            if (cur.depth > 0)
+            if constexpr (DEFER) {
+                const int raw = __builtin_amdgcn_readfirstlane(
+                    reinterpret_cast<const int*>(ldsb + Ls.il)[0]);
+                clen = log_len(raw, dlog.Lmax);
+                if (raw != clen && wave == 0 && lane == 0 && bh % H == 0 && part == 0)
+                    report(status, TREEWY_ELOG);
+                defer_issue_terms(cin, dlog, cur, clen, 0, bh, part, H, wave, lane, lds_addr,
+                                  large_path_view(Ls));
+            } else if (cur.depth > 0) {
                 fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr, large_path_view(Ls));
+            }
         }
 
         // ---- tree walk, lane = node (every wave)
@@ -1856,7 +2028,17 @@ void verify_large_kernel(
             }
         }
 
-        if constexpr (FUSED) {
+        if constexpr (FUSED && DEFER) {
+            __builtin_amdgcn_s_waitcnt(0);          // the terms and the scale (and the last stores)
+            lds_barrier();
+            if (cur.depth + clen > 0) {
+                commit_defer_in_lds(lds, ldsb, large_path_view(Ls), cur, clen, cin, dlog, bh, part,
+                                    H, wave, lane, lds_addr);
+            } else if (wave == 0 && lane == 0 && part == 0) {   // nothing logged or accepted
+                dlog.scale_out[bh] = reinterpret_cast<const float*>(ldsb + Ls.lg)[0];
+                if (h == 0) dlog.len_out[b] = 0;
+            }
+        } else if constexpr (FUSED) {
             if (cur.depth > 0) {
                 __builtin_amdgcn_s_waitcnt(0);      // the path rows (and the last stores)
                 lds_barrier();
@@ -1965,6 +2147,9 @@ void verify_large_kernel(
         if constexpr (FUSED && STAGE) {    // (unstaged, they travel in registers)
             if (more && wave == 2) fused_issue_index(cin, bh_n / H, lane, lds_addr + Ls.idx);
             if (more && wave == 3) dma_gather_x1(cin.accepted + bh_n / H, lds_addr + Ls.acw);
+            if constexpr (DEFER) {
+                if (more && wave == 1) dma_x1(dlog.len_in + bh_n / H, 0u, lds_addr + Ls.il);
+            }
         }
 
         // ---- per lane: nodes t = 16 kt + col, rows v0..v0+3
@@ -2128,6 +2313,8 @@ constexpr int kHeadPath = 8;                   // path rows staged per chunk (fu
 //   SM  parents, alphas, betas of the head (64 words each)
 //   PI, PA  the previous tree (64 words) and accepted node (one word, repeated) of a later
 //       head's sequence
+//   LN, LS  deferred commit: the log length of that sequence and the next head's log scale
+//       (one word each, repeated)
 template <int NKT>
 struct HeadLds {
     static constexpr int kNodes = 16 * NKT;
@@ -2143,7 +2330,9 @@ struct HeadLds {
     static constexpr uint32_t kSM = kPG + 256u;
     static constexpr uint32_t kPI = kSM + 768u;
     static constexpr uint32_t kPA = kPI + 256u;
-    static constexpr uint32_t kBytes = kPA + 256u;
+    static constexpr uint32_t kLN = kPA + 256u;
+    static constexpr uint32_t kLS = kLN + 256u;
+    static constexpr uint32_t kBytes = kLS + 256u;
     static_assert(kBytes <= 160u * 1024u, "one workgroup per CU");
     // s_waitcnt operand: vmcnt <= 8 (the previous head's four O and four U row stores per
     // wave), no other wait
@@ -2191,16 +2380,18 @@ __device__ __forceinline__ void head_issue_inputs(const uint16_t* Q, const uint1
     }
 }
 
-// The previous tree and accepted node of head bh's sequence -> LDS (PI, PA), by one wave.
+// The previous tree and accepted node of head bh's sequence -> LDS (PI, PA), and with the
+// deferred commit its log length (LN), by one wave.
 template <int NKT>
 __device__ __forceinline__ void head_issue_prev_tree(const CommitIn& c, int bh, int H, int lane,
-                                                     uint32_t lds) {
+                                                     uint32_t lds, const int32_t* len_in = nullptr) {
     using L = HeadLds<NKT>;
     const int b = bh / H;
     const uint32_t n = static_cast<uint32_t>(lane) < static_cast<uint32_t>(c.Np)
                            ? static_cast<uint32_t>(lane) : 0u;
     dma_x1(c.parent + static_cast<size_t>(b) * c.Np, 4u * n, lds + L::kPI);
     dma_x1(c.accepted + b, 0u, lds + L::kPA);
+    if (len_in) dma_x1(len_in + b, 0u, lds + L::kLN);
 }
 
 // Path rows 8 c .. 8 c + 7 of a head -> LDS: U_prev rows (two per transfer), K_prev rows
@@ -2235,6 +2426,155 @@ __device__ __forceinline__ void head_issue_path(const CommitIn& c, const PathInf
             const int n = __shfl(pi.pn, lane < pi.depth ? lane : 0);
             dma_gather_x1(c.gamma + (node0 + n) * H + h, lds + L::kPG);
         }
+    }
+}
+
+// The log length of the sequence whose previous tree sits in LDS (LN), clamped to
+// [0, Lmax]; a length outside is reported (TREEWY_ELOG) by the reporting lane.
+template <int NKT>
+__device__ __forceinline__ int head_log_len(const char* ldsb, int Lmax, bool reporter,
+                                            int32_t* status) {
+    const int raw = __builtin_amdgcn_readfirstlane(
+        reinterpret_cast<const int*>(ldsb + HeadLds<NKT>::kLN)[0]);
+    const int len = log_len(raw, Lmax);
+    if (raw != len && reporter) report(status, TREEWY_ELOG);
+    return len;
+}
+
+// The deferred commit's rank-one terms of a head, chunk c (slots 8 c .. 8 c + 7) -> LDS: slot
+// s < len is log term s (u~ row from the log, key row from the log), slot s >= len is path
+// node s - len (U_prev row, K_prev row), in the path slots (PU, PK; every row by a per-lane
+// gather, since the two sources are separate arrays).  With the first chunk also the
+// path's gammas (PG) and the head's log scale (LS).  Slots past the terms repeat slot 0.
+template <int NKT>
+__device__ __forceinline__ void head_issue_terms(const CommitIn& c, const DeferLog& dl,
+                                                 const PathInfo& pi, int len, int chunk, int bh,
+                                                 int H, int wave, int lane, uint32_t lds) {
+    using L = HeadLds<NKT>;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * c.Np;
+    const int rem = len + pi.depth - kHeadPath * chunk;
+    const int cnt = rem < kHeadPath ? rem : kHeadPath;
+    const int nu = cnt > 0 ? (cnt + 1) >> 1 : 0;
+    const int nk = cnt > 0 ? (cnt + 3) >> 2 : 0;
+    const int jobs = nu + nk + (chunk == 0 ? 2 : 0);
+    const size_t lrow0 = static_cast<size_t>(bh) * dl.Lmax;
+    for (int j = wave; j < jobs; j += kHeadWaves) {
+        if (j < nu + nk) {
+            const bool is_k = j >= nu;
+            const int jj = is_k ? j - nu : j;
+            const int q = is_k ? 4 * jj + (lane >> 4) : 2 * jj + (lane >> 5);
+            const int sl = kHeadPath * chunk + (q < cnt ? q : 0);
+            const int pq = sl - len;                       // path position (slot >= len)
+            const int n = __shfl(pi.pn, pq >= 0 ? pq : 0);
+            if (is_k) {
+                const uint16_t* src = sl < len ? dl.K + (lrow0 + sl) * D
+                                               : c.K + ((node0 + n) * H + h) * D;
+                dma_gather_x4(src + 8 * (lane & 15), lds + L::kPK + 1024u * jj);
+            } else {
+                const float* src = sl < len ? dl.U + (lrow0 + sl) * D
+                                            : c.U + ((node0 + n) * H + h) * D;
+                dma_gather_x4(src + 4 * (lane & 31), lds + L::kPU + 1024u * jj);
+            }
+        } else if (j == nu + nk) {
+            const int n = __shfl(pi.pn, lane < pi.depth ? lane : 0);
+            dma_gather_x1(c.gamma + (node0 + n) * H + h, lds + L::kPG);
+        } else {
+            dma_x1(dl.scale_in + bh, 0u, lds + L::kLS);
+        }
+    }
+}
+
+// The deferred commit on this wave's 16 rows of a head (layout as in head_commit_rows).  With
+// the log read as len terms u~_j k_j^T and scale s, the committed state after this step is
+//   S_a = gs (S + sum_j u~_j k_j^T) + sum over the path of a of (g_a / g_i) U_prev[i] k_i^T,
+// gs = s g_a (paper §3 "Reconstruct on commit", Eq. 3, applied to the logged state), formed
+// in LDS for this step's contractions.  When the path's terms fit in the log and in one
+// chunk of slots (len + depth <= min(Lmax, 8)) they are appended to the log as
+// u~ = (g_a / g_i) U_prev[i] / gs (one wave per term: the 512-byte u~ row and the 256-byte
+// key row) and S is not written; otherwise S_a goes to S as whole rows and the log is
+// emptied.  The header after the step: scale 1 and length 0 when emptied, else gs and
+// len + depth.  Called by every wave, with len + depth > 0.
+template <int NKT>
+__device__ __forceinline__ void head_commit_defer(float* lds, const PathInfo& cur, int len,
+                                                  const CommitIn& cin, const DeferLog& dl,
+                                                  int bh, int H, int wave, int lane,
+                                                  uint32_t lds_addr) {
+    using L = HeadLds<NKT>;
+    const char* ldsb = reinterpret_cast<const char*>(lds);
+    const float* PG = reinterpret_cast<const float*>(ldsb + L::kPG);
+    const float* PU = reinterpret_cast<const float*>(ldsb + L::kPU);
+    const char* PK = ldsb + L::kPK;
+    const float gin = reinterpret_cast<const float*>(ldsb + L::kLS)[0];
+    const float ga = cur.depth > 0 ? PG[cur.depth - 1] : 1.0f;
+    const float gs = gin * ga;
+    const int total = len + cur.depth;
+    const int keep = dl.Lmax < kHeadPath ? dl.Lmax : kHeadPath;
+    const bool flush = total > keep;
+    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
+    const int nchunk = (total + kHeadPath - 1) / kHeadPath;
+    f32x4_t x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = 16u * wave + 2u * i + hl;
+        x[i] = gs * *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
+    }
+    for (int ci = 0; ci < nchunk; ++ci) {
+        const int q0 = ci * kHeadPath;
+        if (ci > 0) {
+            lds_barrier();
+            head_issue_terms<NKT>(cin, dl, cur, len, ci, bh, H, wave, lane, lds_addr);
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+        const int rem = total - q0;
+        const int cnt = rem < kHeadPath ? rem : kHeadPath;
+        // unrolled over the chunk's slots, so that the reads of all its rows are issued together
+#pragma unroll
+        for (int q = 0; q < kHeadPath; ++q) {
+            if (q >= cnt) break;
+            const int sl = q0 + q;
+            const float cq = sl < len ? gs : ga * __builtin_amdgcn_rcpf(PG[sl - len >= 0 ? sl - len : 0]);
+            const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
+            const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
+                                __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float cu = cq * PU[q * D + 16 * wave + 2 * i + hl];
+                x[i] += cu * kv;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = 16u * wave + 2u * i + hl;
+        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
+        if (flush)
+            __builtin_nontemporal_store(
+                x[i], reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D + r) * D + 4 * ch));
+    }
+    if (!flush) {
+        // every term sits in the first chunk's slots: path node q is slot len + q
+        const size_t lrow0 = static_cast<size_t>(bh) * dl.Lmax + len;
+        const float rgs = 1.0f / gs;
+        for (int q = wave; q < cur.depth; q += kHeadWaves) {
+            const int sl = len + q;
+            if (lane < 32) {
+                const float cq = (ga / PG[q]) * rgs;
+                const f32x4_t u = *reinterpret_cast<const f32x4_t*>(PU + sl * D + 4 * lane);
+                *reinterpret_cast<f32x4_t*>(dl.U + (lrow0 + q) * D + 4 * lane) = cq * u;
+            } else if (lane < 48) {
+                const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(PK + sl * 256 + 16 * (lane - 32));
+                *reinterpret_cast<u32x4_t*>(dl.K + (lrow0 + q) * D + 8 * (lane - 32)) = kv;
+            }
+        }
+    }
+    if (wave == 0 && lane == 0) {
+        const int b = bh / H;
+        dl.scale_out[bh] = flush ? 1.0f : gs;
+        if (bh - b * H == 0) dl.len_out[b] = flush ? 0 : total;
     }
 }
 
@@ -2343,7 +2683,7 @@ __device__ __forceinline__ float head_dot_bf16(const uint16_t* x, const uint16_t
     return s;
 }
 
-template <int NKT, bool FUSED>
+template <int NKT, bool FUSED, bool DEFER = false>
 __global__ __launch_bounds__(kHeadThreads)
 void verify_head_kernel(
     const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -2351,7 +2691,7 @@ void verify_head_kernel(
     const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
     float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
-    int32_t* __restrict__ status, CommitIn cin)
+    int32_t* __restrict__ status, CommitIn cin, DeferLog dlog)
 {
     using L = HeadLds<NKT>;
     constexpr int NCT = 2 * NKT;
@@ -2377,17 +2717,24 @@ void verify_head_kernel(
 
     // ---- prologue: the first head's inputs (and, fused, its path)
     PathInfo pnext{0ull, 0, 0};
+    int plen = 0;                             // deferred: the log length of pnext's sequence
+    const int32_t* len_in = DEFER ? dlog.len_in : nullptr;
     if constexpr (FUSED) {
-        if (wave == 0) head_issue_prev_tree<NKT>(cin, lo, H, lane0, lds_addr);
+        if (wave == 0) head_issue_prev_tree<NKT>(cin, lo, H, lane0, lds_addr, len_in);
         __builtin_amdgcn_s_waitcnt(0);
         lds_barrier();
         const int pidx = lane0 < cin.Np ? reinterpret_cast<const int*>(ldsb + L::kPI)[lane0] : -1;
         const int pacc = reinterpret_cast<const int*>(ldsb + L::kPA)[0];
         pnext = fused_path(pidx, pacc, cin.Np, lane0, wave == 0 && lo % H == 0, status);
+        if constexpr (DEFER)
+            plen = head_log_len<NKT>(ldsb, dlog.Lmax, wave == 0 && lane0 == 0 && lo % H == 0, status);
         lds_barrier();
-        if (pnext.depth > 0) head_issue_path<NKT>(cin, pnext, 0, lo, H, wave, lane0, lds_addr);
+        if constexpr (DEFER)
+            head_issue_terms<NKT>(cin, dlog, pnext, plen, 0, lo, H, wave, lane0, lds_addr);
+        else if (pnext.depth > 0)
+            head_issue_path<NKT>(cin, pnext, 0, lo, H, wave, lane0, lds_addr);
         if (lo + 1 < hi && wave == kHeadWaves - 1)
-            head_issue_prev_tree<NKT>(cin, lo + 1, H, lane0, lds_addr);
+            head_issue_prev_tree<NKT>(cin, lo + 1, H, lane0, lds_addr, len_in);
     }
     small_issue_s0<FUSED>(S0, lds, lo, 0, wave, lane0);
     head_issue_inputs<NKT>(Q, K, V, alpha, beta, parent, H, N, lo, wave, lane0, lds_addr);
@@ -2425,6 +2772,7 @@ void verify_head_kernel(
         // prologue); only that head's O and U stores, issued last, may still be in flight
         __builtin_amdgcn_s_waitcnt(L::kWait);
         const PathInfo cur = pnext;
+        const int clen = plen;
         lds_barrier();
         const int my_par = lane < N ? reinterpret_cast<const int*>(ldsb + L::kSM)[lane] : -1;
         const float my_alpha = lane < N ? reinterpret_cast<const float*>(ldsb + L::kSM + 256)[lane] : 1.0f;
@@ -2498,7 +2846,14 @@ void verify_head_kernel(
         }
 
         // ---- the previous step's commit on this head's rows
-        if constexpr (FUSED) {
+        if constexpr (FUSED && DEFER) {
+            if (cur.depth + clen > 0) {
+                head_commit_defer<NKT>(lds, cur, clen, cin, dlog, bh, H, wave, lane, lds_addr);
+            } else if (wave == 0 && lane == 0) {    // nothing logged or accepted: S stays
+                dlog.scale_out[bh] = reinterpret_cast<const float*>(ldsb + L::kLS)[0];
+                if (h == 0) dlog.len_out[b] = 0;
+            }
+        } else if constexpr (FUSED) {
             if (cur.depth > 0) head_commit_rows<NKT>(lds, cur, cin, bh, H, wave, lane, lds_addr);
         }
 
@@ -2526,8 +2881,13 @@ void verify_head_kernel(
                     const int pacc = reinterpret_cast<const int*>(ldsb + L::kPA)[0];
                     pnext = fused_path(pidx, pacc, cin.Np, lane, wave == 0 && (bh + 1) % H == 0,
                                        status);
+                    if constexpr (DEFER)
+                        plen = head_log_len<NKT>(ldsb, dlog.Lmax,
+                                                 wave == 0 && lane == 0 && (bh + 1) % H == 0, status);
                 }
-                if (pnext.depth > 0)
+                if constexpr (DEFER)
+                    head_issue_terms<NKT>(cin, dlog, pnext, plen, 0, bh + 1, H, wave, lane, lds_addr);
+                else if (pnext.depth > 0)
                     head_issue_path<NKT>(cin, pnext, 0, bh + 1, H, wave, lane, lds_addr);
             }
         }
@@ -2641,7 +3001,7 @@ void verify_head_kernel(
             head_issue_inputs<NKT>(Q, K, V, alpha, beta, parent, H, N, bh + 1, wave, lane, lds_addr);
             if constexpr (FUSED) {
                 if (bh + 2 < hi && wave == kHeadWaves - 1)
-                    head_issue_prev_tree<NKT>(cin, bh + 2, H, lane, lds_addr);
+                    head_issue_prev_tree<NKT>(cin, bh + 2, H, lane, lds_addr, len_in);
             }
         }
 
@@ -2859,12 +3219,12 @@ static hipError_t launch_f32(const VerifyArgs& a, const CommitInF32& cin, hipStr
     return hipGetLastError();
 }
 
-template <int NKT, bool STAGE, bool FUSED = false>
+template <int NKT, bool STAGE, bool FUSED = false, bool DEFER = false>
 static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream,
-                               const CommitIn* cin = nullptr) {
-    const LargeLds L = large_lds<NKT, STAGE>(a.N, FUSED);
+                               const CommitIn* cin = nullptr, const DeferLog* dl = nullptr) {
+    const LargeLds L = large_lds<NKT, STAGE>(a.N, FUSED, DEFER);
     const size_t dyn = L.bytes;
-    auto kern = verify_large_kernel<NKT, STAGE, FUSED>;
+    auto kern = verify_large_kernel<NKT, STAGE, FUSED, DEFER>;
     if (dyn > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -2881,14 +3241,15 @@ static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
                        BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status,
-                       cin ? *cin : CommitIn{});
+                       cin ? *cin : CommitIn{}, dl ? *dl : DeferLog{});
     return hipGetLastError();
 }
 
-template <int NKT, bool FUSED>
-static hipError_t launch_head(const VerifyArgs& a, hipStream_t stream, const CommitIn* cin = nullptr) {
+template <int NKT, bool FUSED, bool DEFER = false>
+static hipError_t launch_head(const VerifyArgs& a, hipStream_t stream, const CommitIn* cin = nullptr,
+                              const DeferLog* dl = nullptr) {
     using L = HeadLds<NKT>;
-    auto kern = verify_head_kernel<NKT, FUSED>;
+    auto kern = verify_head_kernel<NKT, FUSED, DEFER>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(L::kBytes));
@@ -2900,7 +3261,7 @@ static hipError_t launch_head(const VerifyArgs& a, hipStream_t stream, const Com
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
                        BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status,
-                       cin ? *cin : CommitIn{});
+                       cin ? *cin : CommitIn{}, dl ? *dl : DeferLog{});
     return hipGetLastError();
 }
 
@@ -2938,15 +3299,18 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
     return launch_f32<true>(a, cin, stream);
 }
 
-// The deferred commit (bf16 inputs, N <= 16 only: the caller checks).
+// The deferred commit (bf16 inputs: the caller checks), on the kernel of the fused path for
+// the tree size.
 hipError_t launch_commit_verify_deferred(const CommitArgs& c, const VerifyArgs& a,
                                          const DeferArgs& d, hipStream_t stream) {
     const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
                        c.accepted, c.N};
     const DeferLog dl{d.logU, static_cast<uint16_t*>(d.logK), d.scale_in, d.scale_out,
                       d.len_in, d.len_out, d.Lmax};
-    return a.N <= 8 ? launch_small_fixed<2>(a, cin, dl, stream)
-                    : launch_small<2, 2>(a, cin, dl, stream);
+    if (a.N <= 8) return launch_small_fixed<2>(a, cin, dl, stream);
+    if (a.N <= 16) return launch_small<2, 2>(a, cin, dl, stream);
+    if (a.N <= 32) return launch_large<2, true, true, true>(a, stream, &cin, &dl);
+    return launch_head<4, true, true>(a, stream, &cin, &dl);
 }
 
 }  // namespace treewy

@@ -122,7 +122,7 @@ def deferred_args(**kw):
 
 @pytest.mark.parametrize("bad", [dict(logU=None), dict(logK=None), dict(scale_in=None),
                                  dict(len_out=None), dict(U_prev=None), dict(Q=None),
-                                 dict(Lmax=0), dict(Lmax=17), dict(N=17), dict(Np=65),
+                                 dict(Lmax=0), dict(Lmax=17), dict(N=65), dict(Np=65),
                                  dict(dt=binding.TREEWY_F32),
                                  dict(scale_out=ctypes.c_void_p(0x13000000)),   # = scale_in
                                  dict(len_out=ctypes.c_void_p(0x15000000)),     # = len_in

@@ -58,18 +58,24 @@ def test_step_and_fused_bytes_on_a_chain():
 
 def test_deferred_bytes_log_and_flush():
     # Lmax 4: a depth-3 path fits an empty log (appended, no state write); with 2 terms logged
-    # it does not (state written, log emptied)
+    # it does not (state written, log emptied).  The state is read once (in base).
     parent = np.array([[-1, 0, 1, 2]], dtype=np.int32)
     H, N, row = 1, 4, 4 * D + 2 * D
     base = 65536 + 1804 * N + 4 * (2 * N + 2) + 8
     t, after = accounting.deferred_step_bytes(parent, np.array([2]), parent, H, 2,
                                               np.array([0]), 4)
     assert after.tolist() == [3]
-    assert t == base + 4 * D * D + 3 * (row + 4) + 3 * row
+    assert t == base + 3 * (row + 4) + 3 * row
     t, after = accounting.deferred_step_bytes(parent, np.array([2]), parent, H, 2,
                                               np.array([2]), 4)
     assert after.tolist() == [0]
-    assert t == base + 4 * D * D + 2 * row + 3 * (row + 4) + 4 * D * D
+    assert t == base + 2 * row + 3 * (row + 4) + 4 * D * D
+    # above 16 nodes the log and the path share one chunk of 8 terms: 6 logged + 3 > 8
+    big = np.array([list(range(-1, 39))], dtype=np.int32)
+    t, after = accounting.deferred_step_bytes(big, np.array([2]), big, H, 2, np.array([6]), 16)
+    assert after.tolist() == [0]
+    t, after = accounting.deferred_step_bytes(big, np.array([2]), big, H, 2, np.array([5]), 16)
+    assert after.tolist() == [8]
 
 
 def test_attention_bytes_closed_form():

@@ -88,35 +88,46 @@ def oracle_steps(steps):
 
 
 def expected_lengths(steps, Lmax):
-    """The header rule: the accepted path's terms join the log when they fit (and the path
-    is short enough to stage with the next step: 4 nodes for N <= 4, else 8); otherwise the
-    log is emptied into S.  No accepted node leaves the log as it is."""
+    """The header rule: the accepted path's terms join the log when they fit; otherwise the
+    log is emptied into S.  Up to 16 nodes the path must also be short enough to stage with
+    the next step (4 nodes for N <= 4, else 8); above 16 nodes the log and the path together
+    must fit one chunk of 8 staged terms.  No accepted node leaves the log as it is."""
     B = steps[0].B
     lens = np.zeros(B, dtype=np.int64)
     out = [None]
     for s in range(1, len(steps)):
         P_prev, P = steps[s - 1], steps[s]
-        stage = 4 if P.N <= 4 else 8
         for b in range(B):
             a = int(P_prev.accepted[b])
             if a < 0:
                 continue
             d = int(inputs.tree_depths(P_prev.parent[b])[a])
-            lens[b] = 0 if (lens[b] + d > Lmax or d > stage) else lens[b] + d
+            if P.N <= 16:
+                stage = 4 if P.N <= 4 else 8
+                full = lens[b] + d > Lmax or d > stage
+            else:
+                full = lens[b] + d > min(Lmax, 8)
+            lens[b] = 0 if full else lens[b] + d
         out.append(lens.copy())
     return out
 
 
-@pytest.mark.parametrize("N,tree,Lmax,nsteps,seed", [
-    (4, "chain", 16, 6, 61),     # the configuration-1 chain: the log only grows
-    (4, "chain", 4, 7, 62),      # small log: appends and write-backs interleave
-    (6, (3, 2), 5, 7, 63),
-    (16, (5, 4), 8, 6, 64),      # 16-node trees
-    (3, (2, 2), 1, 6, 65),       # a one-term log
+@pytest.mark.parametrize("N,tree,Lmax,nsteps,seed,B,H", [
+    (4, "chain", 16, 6, 61, 5, 4),     # the configuration-1 chain: the log only grows
+    (4, "chain", 4, 7, 62, 5, 4),      # small log: appends and write-backs interleave
+    (6, (3, 2), 5, 7, 63, 5, 4),
+    (16, (5, 4), 8, 6, 64, 5, 4),      # 16-node trees
+    (3, (2, 2), 1, 6, 65, 5, 4),       # a one-term log
+    (32, (6, 4), 8, 6, 66, 5, 4),      # 17-32 nodes: items of half a head
+    (20, (6, 4), 3, 7, 67, 3, 8),      # a ragged tile, a three-term log
+    (64, (6, 8), 8, 6, 68, 9, 32),     # 33-64 nodes: 288 heads, some workgroups take two
+    (64, (6, 8), 16, 5, 69, 5, 4),     # a 16-term log behaves as 8 terms above 16 nodes
+    (40, (6, 8), 5, 6, 70, 5, 4),
+    (64, "chain", 8, 5, 71, 3, 4),     # deep paths: flushes over several chunks of terms
+    (24, "chain", 8, 5, 72, 3, 4),
 ])
-def test_deferred_steps(N, tree, Lmax, nsteps, seed):
-    say(f"[deferred] N={N} tree={tree} Lmax={Lmax} steps={nsteps}")
-    B, H = 5, 4
+def test_deferred_steps(N, tree, Lmax, nsteps, seed, B, H):
+    say(f"[deferred] N={N} tree={tree} Lmax={Lmax} steps={nsteps} B={B} H={H}")
     steps = [inputs.make_custom(seed * 10 + s, B=B, H=H, N=N, tree=tree) for s in range(nsteps)]
     flush_at = (nsteps - 1,)
     gpu, flushed = run_steps(steps, Lmax, flush_at=flush_at)
@@ -169,10 +180,34 @@ def test_deferred_matches_fused_path():
     assert e.max() <= TOL
 
 
+def test_deferred_mixed_tree_sizes():
+    """Consecutive steps on trees of different sizes: the log written by one kernel (up to 16
+    nodes, 17-32, 33-64) is read by another."""
+    B, H, Lmax = 4, 6, 8
+    sizes = [(5, (3, 2)), (40, (6, 8)), (20, (6, 4)), (64, (6, 8)), (12, (4, 3)), (33, (6, 8)),
+             (3, "chain")]
+    steps = [inputs.make_custom(900 + i, B=B, H=H, N=n, tree=t) for i, (n, t) in enumerate(sizes)]
+    nsteps = len(steps)
+    gpu, flushed = run_steps(steps, Lmax, flush_at=(nsteps - 1,))
+    heads, ref, states = oracle_steps(steps)
+    want_len = expected_lengths(steps, Lmax)
+    for s in range(nsteps):
+        for key in ("O", "U"):
+            g = gather_heads(gpu[s][key], heads, "node").astype(np.float64)
+            e = headwise_rel(g, ref[s][key])
+            assert e.max() <= TOL, f"step {s} (N={steps[s].N}) {key}: worst {e.max():.3e}"
+        if s > 0:
+            assert np.array_equal(gpu[s]["len"], want_len[s]), (s, gpu[s]["len"], want_len[s])
+    S = flushed[nsteps - 1].reshape(B * H, -1).astype(np.float64)
+    e = headwise_rel(S, states[nsteps - 2].reshape(B * H, -1))
+    assert e.max() <= TOL, f"flushed state: worst {e.max():.3e}"
+
+
 def test_deferred_rejects_unsupported_shapes():
+    """fp32 inputs have no deferred commit."""
     import torch
     from linear_attention_speculative_head_amd import binding, device
-    P = inputs.make_custom(80, B=2, H=2, N=20, tree=(5, 4))
+    P = inputs.make_custom(80, B=2, H=2, N=20, tree=(5, 4), dtype="f32")
     d = device.upload_layer(P.layers[0], P.dtype)
     par, acc = device.upload_tree(P)
     o = device.alloc_outputs(2, 2, 20)
@@ -185,11 +220,12 @@ def test_deferred_rejects_unsupported_shapes():
                                               d.beta, par, o2.O, o2.U, o2.gamma)
 
 
-def test_deferred_reports_bad_header():
+@pytest.mark.parametrize("N", [4, 24, 40])
+def test_deferred_reports_bad_header(N):
     """A log length outside [0, Lmax] is reported (and clamped, so nothing leaves the log)."""
     import torch
     from linear_attention_speculative_head_amd import binding, device
-    B, H, N = 3, 2, 4
+    B, H = 3, 2
     P1 = inputs.make_custom(90, B=B, H=H, N=N, tree="chain")
     P2 = inputs.make_custom(91, B=B, H=H, N=N, tree="chain")
     d1, d2 = device.upload_layer(P1.layers[0], "bf16"), device.upload_layer(P2.layers[0], "bf16")
