@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 # HBM byte counts per launch taken with rocprofv3 (FETCH_SIZE, WRITE_SIZE, scaled by the same
 # counters on a plain copy of known size), per workload; used while the kernel source is the
 # one they were taken on
-TRAFFIC_FILES = {1: "profiles/traffic_chain4_b32h32.json",
+TRAFFIC_FILES = {0: "profiles/traffic_fp32_chain4_b1h1.json",
+                 1: "profiles/traffic_chain4_b32h32.json",
                  2: "profiles/traffic_tree16_b64h32.json",
                  3: "profiles/traffic_tree64_b128h32_l30.json",
                  4: "profiles/traffic_tree32_b256h64.json",
