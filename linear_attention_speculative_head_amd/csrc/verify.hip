@@ -2334,9 +2334,9 @@ struct HeadLds {
     static constexpr uint32_t kLS = kLN + 256u;
     static constexpr uint32_t kBytes = kLS + 256u;
     static_assert(kBytes <= 160u * 1024u, "one workgroup per CU");
-    // s_waitcnt operand: vmcnt <= 8 (the previous head's four O and four U row stores per
+    // s_waitcnt operand: vmcnt <= 2 NKT (the previous head's NKT O and NKT U row stores per
     // wave), no other wait
-    static constexpr int kWait = 8 | (7 << 4) | (15 << 8);
+    static constexpr int kWait = (2 * NKT) | (7 << 4) | (15 << 8);
 };
 
 // A head's key, query and value rows, parents, alphas and betas -> LDS (layout above): per
@@ -2640,20 +2640,21 @@ __device__ __forceinline__ void head_commit_rows(float* lds, const PathInfo& cur
 
 // Whole node rows of one head out of the U exchange (per wave w: [node][16 values of rows
 // 16w..16w+15]) to a [nodes][H][D] fp32 array at dst (the head's node-0 row): wave w writes
-// nodes 8w..8w+7, two 512-byte rows per store, lane l taking values 4 (l % 32)..+3 of node
-// 8w + 2i + l / 32 from wave (l % 32) / 4's area.  Nodes past N fall outside the buffer
-// range and are dropped.  Four stores per wave, with the streaming hint.
+// nodes 2 NKT w .. 2 NKT w + 2 NKT - 1, two 512-byte rows per store, lane l taking values
+// 4 (l % 32)..+3 of node 2 NKT w + 2i + l / 32 from wave (l % 32) / 4's area.  Nodes past N
+// fall outside the buffer range and are dropped.  NKT stores per wave, with the streaming
+// hint.
 template <int NKT>
 __device__ __forceinline__ void head_store_rows(float* dst, const char* ldsb, int H, int N,
                                                 int wave, int lane) {
     using L = HeadLds<NKT>;
-    static_assert(L::kNodes == 8 * kHeadWaves, "eight nodes per wave");
+    static_assert(L::kNodes == 2 * NKT * kHeadWaves, "2 NKT nodes per wave");
     const float* Ub = reinterpret_cast<const float*>(ldsb + L::kU);
     const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
     const int c = lane & 31;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = 8 * wave + 2 * i + (lane >> 5);
+    for (int i = 0; i < NKT; ++i) {
+        const int t = 2 * NKT * wave + 2 * i + (lane >> 5);
         const f32x4_t x = *reinterpret_cast<const f32x4_t*>(
             Ub + (c >> 2) * (L::kNodes * 16) + t * 16 + 4 * (c & 3));
         const uint32_t off = t < N ? static_cast<uint32_t>((t * H * D + 4 * c) * sizeof(float)) : span;
@@ -3271,10 +3272,12 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     const DeferLog nolog{};
     if (a.N <= 8) return launch_small_fixed<0>(a, none, nolog, stream);
     if (a.N <= 16) return launch_small<2, 0>(a, none, nolog, stream);
-    // the key and query rows go through the S-row area (no LDS area of their own), which
-    // leaves room for three workgroups per CU up to 32 nodes and two up to 64; the fused
-    // kernel below stages its inputs up to 32 nodes instead, where that measured faster
+    // up to 32 nodes the key and query rows go through the S-row area (no LDS area of their
+    // own), which leaves room for three workgroups per CU; the fused kernel below stages its
+    // inputs instead, where that measured faster.  33-48 and 49-64 nodes: one head per item,
+    // three or four node tiles.
     if (a.N <= 32) return launch_large<2, false>(a, stream);
+    if (a.N <= 48) return launch_head<3, false>(a, stream);
     return launch_head<4, false>(a, stream);
 }
 
@@ -3292,6 +3295,7 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
                            c.accepted, c.N};
         if (a.N <= 32) return launch_large<2, true, true>(a, stream, &cin);
+        if (a.N <= 48) return launch_head<3, true>(a, stream, &cin);
         return launch_head<4, true>(a, stream, &cin);
     }
     const CommitInF32 cin{c.S, c.U, static_cast<const float*>(c.K), c.gamma, c.parent,
@@ -3310,6 +3314,7 @@ hipError_t launch_commit_verify_deferred(const CommitArgs& c, const VerifyArgs& 
     if (a.N <= 8) return launch_small_fixed<2>(a, cin, dl, stream);
     if (a.N <= 16) return launch_small<2, 2>(a, cin, dl, stream);
     if (a.N <= 32) return launch_large<2, true, true, true>(a, stream, &cin, &dl);
+    if (a.N <= 48) return launch_head<3, true, true>(a, stream, &cin, &dl);
     return launch_head<4, true, true>(a, stream, &cin, &dl);
 }
 

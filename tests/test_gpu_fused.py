@@ -60,6 +60,8 @@ def test_fused_config_every_head(cfg):
     (3, (2, 2), 17, (4, 4), 30),      # ... at its smallest
     (20, (5, 3), 40, (6, 4), 31),     # the unstaged large-tree kernel's fused commit
     (64, "chain", 64, (6, 4), 32),    # ... at 64 nodes, previous paths of up to 64 rows
+    (48, "chain", 48, (6, 8), 33),    # the three-tile head kernel, previous paths of 6 chunks
+    (33, (6, 4), 45, (6, 8), 34),
 ])
 def test_fused_shapes(N1, tree1, N2, tree2, seed):
     """Ragged node counts on both steps, deep previous paths, every head compared."""

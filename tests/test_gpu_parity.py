@@ -61,6 +61,8 @@ def test_config4_every_head():
     (64, (6, 8), "f32", 7),
     (64, (2, 64), "bf16", 8),      # all 64 nodes hang off S0 (a star: depth 1)
     (17, (5, 4), "bf16", 9),
+    (48, (6, 8), "bf16", 10),      # the largest tree of the three-tile head kernel
+    (49, "chain", "bf16", 11),     # the smallest of the four-tile one
 ])
 def test_edge_trees(N, tree, dtype, seed):
     """Ragged and degenerate trees, both input types, every head compared."""
