@@ -100,6 +100,10 @@ def expected_lengths(steps, Lmax):
         for b in range(B):
             a = int(P_prev.accepted[b])
             if a < 0:
+                # nothing to append; above 16 nodes a log longer than the staged chunk is
+                # written back all the same
+                if P.N > 16 and lens[b] > min(Lmax, 8):
+                    lens[b] = 0
                 continue
             d = int(inputs.tree_depths(P_prev.parent[b])[a])
             if P.N <= 16:
@@ -191,6 +195,38 @@ def test_deferred_mixed_tree_sizes():
     gpu, flushed = run_steps(steps, Lmax, flush_at=(nsteps - 1,))
     heads, ref, states = oracle_steps(steps)
     want_len = expected_lengths(steps, Lmax)
+    for s in range(nsteps):
+        for key in ("O", "U"):
+            g = gather_heads(gpu[s][key], heads, "node").astype(np.float64)
+            e = headwise_rel(g, ref[s][key])
+            assert e.max() <= TOL, f"step {s} (N={steps[s].N}) {key}: worst {e.max():.3e}"
+        if s > 0:
+            assert np.array_equal(gpu[s]["len"], want_len[s]), (s, gpu[s]["len"], want_len[s])
+    S = flushed[nsteps - 1].reshape(B * H, -1).astype(np.float64)
+    e = headwise_rel(S, states[nsteps - 2].reshape(B * H, -1))
+    assert e.max() <= TOL, f"flushed state: worst {e.max():.3e}"
+
+
+def test_deferred_long_log_meets_large_tree():
+    """A 12-term log built on 4-node chains (Lmax 16), then steps on 40- and 24-node trees:
+    the first accepts nothing in some sequences (their log is written back anyway: it does not
+    fit the large-tree kernels' 8 staged terms), the second appends again."""
+    B, H, Lmax = 4, 3, 16
+    steps = []
+    for s, (n, tree) in enumerate([(4, "chain"), (4, "chain"), (4, "chain"), (4, "chain"),
+                                   (40, (6, 8)), (24, (6, 4)), (33, (6, 8))]):
+        acc = None
+        if n == 4:
+            acc = np.full(B, 3, dtype=np.int32)          # depth 4 each step: 4, 8, 12
+        if s == 3:
+            acc = np.array([-1, -1, 3, 0], dtype=np.int32)
+        steps.append(inputs.make_custom(950 + s, B=B, H=H, N=n, tree=tree, accepted=acc))
+    nsteps = len(steps)
+    gpu, flushed = run_steps(steps, Lmax, flush_at=(nsteps - 1,))
+    heads, ref, states = oracle_steps(steps)
+    want_len = expected_lengths(steps, Lmax)
+    assert want_len[3].tolist() == [12, 12, 12, 12]
+    assert want_len[4].tolist()[:2] == [0, 0]
     for s in range(nsteps):
         for key in ("O", "U"):
             g = gather_heads(gpu[s][key], heads, "node").astype(np.float64)
