@@ -143,8 +143,8 @@ class Workload:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "every (sequence, head) is independent, so N GPUs would each run this same "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); every "
+              "(sequence, head) is independent, so N GPUs would each run this same "
               "single-GPU pass on their share.", file=sys.stderr)
         sys.exit(2)
     assert sum([bool(args.separate), bool(args.snapshot), bool(args.deferred)]) <= 1, \
