@@ -618,26 +618,34 @@ __host__ __device__ inline F32Lds f32_lds(int N) {
 // (chunk c of row r at c ^ (r % 16)) on the matrix cores.  Both operands are split into bf16
 // hi + lo (split_hi_lo: |x - hi - lo| <= 2^-18 |x|) and each product is taken as
 // hi.hi + hi.lo + lo.hi, dropping lo.lo (at most 2^-16 of it): three v_mfma_f32_16x16x32_bf16
-// per 32-deep k-block, fp32 accumulation.  Lane L gives row L % 16, k = 8 (L / 16) + 32 kb ..
-// +7 of both operands (the same k order, so the sums are those of the plain product) and
-// receives D[4 (L / 16) + e][L % 16], e = 0..3.
+// per 32-deep k-block, fp32 accumulation, one accumulator per kind of product (so the twelve
+// products form three chains of four instead of one of twelve), every operand read first.
+// Lane L gives row L % 16, k = 8 (L / 16) + 32 kb .. +7 of both operands (the same k order,
+// so the sums are those of the plain product) and receives D[4 (L / 16) + e][L % 16],
+// e = 0..3.
 __device__ __forceinline__ f32x4_t f32_tile(const float* A, const float* Bm, int lane) {
     const int r = lane & 15;
     const int g = lane >> 4;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t a0[4], a1[4], b0[4], b1[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         const int c0 = (8 * kb + 2 * g) ^ r, c1 = (8 * kb + 2 * g + 1) ^ r;
-        bf16x8_t ah, al, bh, bl;
-        split_hi_lo(*reinterpret_cast<const f32x4_t*>(A + r * D + 4 * c0),
-                    *reinterpret_cast<const f32x4_t*>(A + r * D + 4 * c1), ah, al);
-        split_hi_lo(*reinterpret_cast<const f32x4_t*>(Bm + r * D + 4 * c0),
-                    *reinterpret_cast<const f32x4_t*>(Bm + r * D + 4 * c1), bh, bl);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+        a0[kb] = *reinterpret_cast<const f32x4_t*>(A + r * D + 4 * c0);
+        a1[kb] = *reinterpret_cast<const f32x4_t*>(A + r * D + 4 * c1);
+        b0[kb] = *reinterpret_cast<const f32x4_t*>(Bm + r * D + 4 * c0);
+        b1[kb] = *reinterpret_cast<const f32x4_t*>(Bm + r * D + 4 * c1);
     }
-    return acc;
+    f32x4_t acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        bf16x8_t ah, al, bh, bl;
+        split_hi_lo(a0[kb], a1[kb], ah, al);
+        split_hi_lo(b0[kb], b1[kb], bh, bl);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[2], 0, 0, 0);
+    }
+    return acc[0] + (acc[1] + acc[2]);
 }
 
 template <bool FUSED>
@@ -931,23 +939,34 @@ void verify_f32_kernel(
         const bool ok = x < N * kF32Rows;
         const int t = ok ? x / kF32Rows : 0;
         const int r = x - t * kF32Rows;
-        float u = ok ? s_beta[t] * (Vs[x] - s_g[t] * Ps[x]) : 0.f;
+        // the node's coefficients first (N <= 4: at most 4 ancestors-or-self), so that every
+        // level of the substitution is one LDS round trip
+        const int dep = ok ? s_dep[t] : 0;
+        const float gt = s_g[t], bgt = s_beta[t] * gt;
+        int anc[4];
+        float cs[4], cw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = j < dep ? At[t * 64 + j] : t;
+            anc[j] = i * kF32Rows + r;
+            cs[j] = j < dep - 1 ? bgt * s_rg[i] * Cs[t * N + i] : 0.f;
+            cw[j] = j < dep ? gt * s_rg[i] * Ws[t * N + i] : 0.f;
+        }
+        float u = ok ? s_beta[t] * (Vs[x] - gt * Ps[x]) : 0.f;
         if (ok) Us[x] = u;
         for (int d = 1; d < maxd; ++d) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // level d - 1 written
-            if (ok && s_dep[t] > d) {
-                const int a = At[t * 64 + d - 1];
-                u -= s_beta[t] * s_g[t] * s_rg[a] * Cs[t * N + a] * Us[a * kF32Rows + r];
+            if (ok && dep > d) {
+                u -= cs[d - 1] * Us[anc[d - 1]];
                 Us[x] = u;
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (ok) {
-            float o = s_g[t] * Ys[x];
-            for (int j = 0; j < s_dep[t]; ++j) {
-                const int i = At[t * 64 + j];
-                o += s_g[t] * s_rg[i] * Ws[t * N + i] * Us[i * kF32Rows + r];
-            }
+            float o = gt * Ys[x];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < dep) o += cw[j] * Us[anc[j]];
             const size_t out = (node0 + t) * nstride + h * D + r0 + r;
             O[out] = o;
             U[out] = u;
