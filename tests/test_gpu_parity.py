@@ -130,3 +130,42 @@ def test_bad_accepted_sets_status():
     torch.cuda.synchronize()
     assert int(status.item()) == binding.TREEWY_EACCEPT
     assert np.array_equal(S[0].cpu().numpy(), L.S0[0])       # offending sequence untouched
+
+
+def max_heads_problem(seed: int, N: int, dtype: str, tree, H: int = 65536, base: int = 512):
+    """One sequence with the most heads a call takes (H = 65536), so that the last node's rows
+    sit at the largest byte offsets the kernels form (about 63 x 65536 x 512 B for O and U).
+    A base draw of `base` heads is repeated across the heads, and every head's state and
+    values get a head-dependent shift, so that a head read in place of another shows."""
+    Pb = inputs.make_custom(seed, B=1, H=base, N=N, dtype=dtype, tree=tree)
+    L = Pb.layers[0]
+    rep = H // base
+    hs = (np.arange(H) % 1009).astype(np.float32)
+    S0 = np.tile(L.S0, (1, rep, 1, 1))
+    S0 += (1e-4 * hs)[None, :, None, None]
+    v = np.tile(L.v, (1, 1, rep, 1))
+    v += (1e-3 * hs)[None, None, :, None]
+    if dtype == "bf16":
+        v = inputs.round_bf16(v)
+    layer = inputs.Layer(S0=S0, q=np.tile(L.q, (1, 1, rep, 1)), k=np.tile(L.k, (1, 1, rep, 1)),
+                         v=v, alpha=np.tile(L.alpha, (1, 1, rep)),
+                         beta=np.tile(L.beta, (1, 1, rep)))
+    P = inputs.Problem(cfg=-1, B=1, H=H, N=N, dtype=dtype, parent=Pb.parent,
+                       accepted=Pb.accepted)
+    P.layers.append(layer)
+    return P
+
+
+@pytest.mark.parametrize("N,dtype,tree,seed", [
+    (64, "bf16", (6, 8), 41),      # the one-head-per-item kernel, the last node's rows far out
+    (4, "f32", "chain", 42),       # the fp32 kernel: 8 workgroups per head, 524 288 in all
+])
+def test_max_heads(N, dtype, tree, seed):
+    """H = 65536 (the ABI's limit), one sequence: verify then commit, compared with the oracle
+    on heads spread over the whole range (the first, the last, and the middle)."""
+    say(f"[parity] H=65536 N={N} {dtype}")
+    P = max_heads_problem(seed, N, dtype, tree)
+    P.accepted[0] = int(np.argmax(inputs.tree_depths(P.parent[0])))   # the deepest node
+    gpu = run_verify_commit(P)
+    heads = [(0, h) for h in (0, 1, 511, 512, 1009, 20000, 32767, 32768, 49999, 65534, 65535)]
+    check_against_oracle(P, gpu, heads=heads, label=f"H=65536 N={N} {dtype}")
