@@ -734,10 +734,37 @@ def copy_probe(mib):
     torch.cuda.synchronize()
 
 
+def source_digest(path: str) -> str:
+    """SHA-1 of a C/C++/HIP source with its comments and whitespace removed, so that a count
+    taken on a kernel stays attached to it through edits of its comments, and no longer
+    after any change to its code."""
+    import hashlib
+    text = open(path, encoding="utf-8").read()
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":                 # a literal: copied as it is
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return hashlib.sha1("".join(out).encode("utf-8")).hexdigest()
+
+
 def measured_traffic(cfg, entry: str):
     """Counted HBM bytes per launch of `entry` on workload `cfg`, or None when no count was
-    taken or the kernel source changed since."""
-    import hashlib
+    taken or the kernel source's code changed since."""
     rel = TRAFFIC_FILES.get(cfg)
     if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
         return None
@@ -746,7 +773,7 @@ def measured_traffic(cfg, entry: str):
     if not k:
         return None
     src = os.path.join(ROOT, k["source"])
-    if not os.path.exists(src) or hashlib.sha1(open(src, "rb").read()).hexdigest() != k["source_sha1"]:
+    if not os.path.exists(src) or source_digest(src) != k.get("source_digest"):
         return None
     return float(k["hbm_bytes_per_launch"])
 

@@ -1487,7 +1487,7 @@ void verify_small_kernel(
 // 16w + 4 (L / 16) .. +3.  Each wave walks the tree with lane = node (pointer jumping)
 // and hands every lane its nodes' masks and gates by lane permutes.  The forward substitution
 // and readout are the same ancestor walk as above; U of the ancestors is exchanged through a
-// per-wave LDS scratch [64 nodes][16 rows] instead of lane permutes, because an ancestor may sit
+// per-wave LDS scratch [32 nodes][16 rows] instead of lane permutes, because an ancestor may sit
 // in another node tile.  A wave's LDS operations complete in issue order, so a value written
 // at the end of step d - 1 is what other lanes of the wave read at step d.  The Gram matrix
 // G = K [K;Q]^T (same column layout) is formed by waves 0..NKT-1 and staged in LDS.
@@ -1611,7 +1611,7 @@ __device__ __forceinline__ void large_issue_inputs(const uint16_t* Q, const uint
 
 // The item's key and query rows alone -> LDS at `lds` (the staged layout: keys in rows
 // 0 .. 4 ceil(N/4) - 1, queries right after, 256 B rows, chunk c of row r at c ^ (r % 16)),
-// 2 ceil(N/4) transfers of four rows dealt to the four waves.  At most 32 KiB for N <= 64.
+// 2 ceil(N/4) transfers of four rows dealt to the four waves.  At most 16 KiB (N <= 32).
 __device__ __forceinline__ void large_issue_kq(const uint16_t* Q, const uint16_t* K, int H, int N,
                                                int bh, int wave, int lane, uint32_t lds) {
     const int b = bh / H;
@@ -2284,7 +2284,7 @@ void verify_large_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Larger trees (16 < N <= 64), one head per item.
+// Trees of 33 to 64 nodes, one head per item (NKT = 3 node tiles up to 48 nodes, 4 above).
 //
 // A workgroup of eight waves takes whole heads (all 128 value rows; wave w owns rows
 // 16w..16w+15), one workgroup per CU, and walks a run of consecutive heads, so the heads

@@ -99,3 +99,20 @@ def test_warmup_count():
     assert bench.auto_warmup(auto, 131e6) == 7634          # ceil(0.25 * 4e12 / 131e6)
     assert bench.auto_warmup(auto, 1e12) == 5
     assert bench.auto_warmup(auto, 1.0) == 20000
+
+
+def test_source_digest_ignores_comments_only(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench
+    # a traffic count stays attached to a kernel through comment and layout edits, not code
+    # edits (string literals, with '//' inside, are code)
+    a = 'int x = 1; // one\n/* two */ const char* s = "a // b";\n'
+    b = 'int  x = 1;\n\nconst char* s = "a // b";  // another comment\n'
+    c = 'int x = 2;\nconst char* s = "a // b";\n'
+    d = 'int x = 1; const char* s = "a //  b";\n'
+    h = []
+    for i, t in enumerate((a, b, c, d)):
+        f = tmp_path / f"k{i}.hip"
+        f.write_text(t)
+        h.append(bench.source_digest(str(f)))
+    assert h[0] == h[1] and h[0] != h[2] and h[0] != h[3]
