@@ -1479,8 +1479,9 @@ void verify_small_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Trees of 17 to 32 nodes: the persistent streaming design of the small-tree kernel, with
-// NKT = 2 node tiles per lane (33 to 64 nodes take the one-head-per-item kernel below).
+// Trees of 17 to 32 nodes, the plain verify: the persistent streaming design of the
+// small-tree kernel, with NKT = 2 node tiles per lane (the fused and deferred steps on 17-64
+// nodes, and the plain verify on 33-64, take the one-head-per-item kernel below).
 //
 // Output columns: keys at 0..N-1 (tiles 0..NKT-1), queries at 16 NKT + t (tiles NKT..2NKT-1),
 // so lane L holds P[t] and Y[t] for the nodes t = 16 kt + L % 16 of every node tile kt, rows
@@ -1492,14 +1493,10 @@ void verify_small_kernel(
 // at the end of step d - 1 is what other lanes of the wave read at step d.  The Gram matrix
 // G = K [K;Q]^T (same column layout) is formed by waves 0..NKT-1 and staged in LDS.
 //
-// The next item's S0 rows are requested once this item's contractions are done.  With
-// STAGE, its keys, queries, values, gates and tree then follow by direct transfers into an
-// LDS area of their own, and the contractions read their fragments from there.  Without it
-// (the plain verify, where three workgroups per CU measured faster) the item's key and query
-// rows are sent into the S-row area once the rows have been taken into registers, and the
-// contractions read them there; values, gates and tree are prefetched into registers.
-
-constexpr int kLargePath = 8;                   // path rows staged per chunk (fused)
+// The item's key and query rows are sent into the S-row area once the rows have been taken
+// into registers, and the contractions read them there; values, gates and tree are
+// prefetched into registers.  The next item's S0 rows are requested once every wave is past
+// the contractions.  Three workgroups per CU.
 
 template <int NKT>
 struct LargeLayout {
@@ -1511,103 +1508,6 @@ struct LargeLayout {
     // s_waitcnt operand: vmcnt <= 2 NKT (the previous item's O and U stores), no other wait
     static constexpr int kWait = (2 * NKT) | (7 << 4) | (15 << 8);
 };
-
-// With STAGE, keys, queries, values and the tree/gate words reach LDS by direct transfers as in
-// the small-tree kernel, after the fixed part above (byte offsets): keys in rows
-// 0 .. 4 ceil(N/4) - 1 of a key/query area and queries right after them (256 B rows, chunk c of
-// row r at chunk c ^ (r % 16)); the item's half of the values (128 B rows); parents, alphas
-// and betas, 64 words each.
-// With the fused commit also: 8 path rows of U_prev halves and K_prev (256 B each), the path's
-// gammas (64 words), the previous tree (64 words) and the accepted node (one word, repeated);
-// with the deferred commit the same 8 slots take the log's terms and then the path's, and
-// the log length and scale follow (one word each, repeated).
-struct LargeLds {
-    uint32_t kq, v, sm, pu, pk, pg, idx, acw, il, lg, bytes;
-};
-
-template <int NKT, bool STAGE>
-__host__ __device__ inline LargeLds large_lds(int N, bool fused = false, bool defer = false) {
-    LargeLds L;
-    const uint32_t fixed = sizeof(float) * LargeLayout<NKT>::kTotal;
-    L.kq = fixed;
-    L.v = L.kq + 2048u * static_cast<uint32_t>((N + 3) / 4);
-    L.sm = L.v + 1024u * static_cast<uint32_t>((N + 7) / 8);
-    if (!STAGE) {
-        // unstaged, the fused commit's path rows borrow the U exchange area (the path is
-        // committed before the contractions, the exchange runs after them); the previous
-        // tree and accepted node travel in registers
-        L.pu = sizeof(float) * (LargeLayout<NKT>::kS0 + LargeLayout<NKT>::kG);
-        L.pk = L.pu + 256u * kLargePath;
-        L.pg = L.pk + 256u * kLargePath;
-        L.idx = L.acw = L.il = L.lg = 0;
-        L.bytes = fixed;
-        return L;
-    }
-    L.pu = L.sm + 768u;
-    L.pk = L.pu + 256u * kLargePath;
-    L.pg = L.pk + 256u * kLargePath;
-    L.idx = L.pg + 256u;
-    L.acw = L.idx + 256u;
-    L.il = L.acw + 256u;                    // deferred: the log length (one word, repeated)
-    L.lg = L.il + 256u;                     // deferred: the item's log scale (the same)
-    L.bytes = fused ? (defer ? L.lg + 256u : L.acw + 256u) : L.sm + 768u;
-    return L;
-}
-
-// The path-row slots of the large kernel's fused commit, as the small kernel's helpers see them.
-__device__ __forceinline__ SmallLds large_path_view(const LargeLds& L) {
-    SmallLds P{};
-    P.pu = L.pu;
-    P.pk = L.pk;
-    P.pg = L.pg;
-    P.lg = L.lg;
-    P.path = kLargePath;
-    return P;
-}
-
-// The staged inputs of an item -> LDS: ceil(N/4) loads of four key rows, as many of four
-// query rows, ceil(N/8) loads of eight value half-rows, and three gathers (parents, alphas,
-// betas: lane = node), dealt round-robin to the four waves.  Lanes past the last node load
-// node 0 again, into slots nobody reads.
-__device__ __forceinline__ void large_issue_inputs(const uint16_t* Q, const uint16_t* K,
-                                                   const uint16_t* V, const float* alpha,
-                                                   const float* beta, const int32_t* parent,
-                                                   int H, int N, int bh, int part, int wave,
-                                                   int lane, uint32_t lds, const LargeLds& L) {
-    const int b = bh / H;
-    const int h = bh - b * H;
-    const size_t node0 = static_cast<size_t>(b) * N;
-    const uint32_t row_bytes = static_cast<uint32_t>(H) * D * 2;
-    const uint16_t* Kh = K + (node0 * H + h) * D;
-    const uint16_t* Qh = Q + (node0 * H + h) * D;
-    const uint16_t* Vh = V + (node0 * H + h) * D + part * kSmallRows;
-    const uint32_t un = static_cast<uint32_t>(N);
-    const uint32_t ln = static_cast<uint32_t>(lane) < un ? static_cast<uint32_t>(lane) : 0u;
-    const int nq4 = (N + 3) >> 2;
-    const int nv8 = (N + 7) >> 3;
-    const int jobs = 2 * nq4 + nv8 + 3;
-    for (int j = wave; j < jobs; j += 4) {
-        if (j < 2 * nq4) {
-            const bool is_q = j >= nq4;
-            const uint32_t lr = static_cast<uint32_t>(lane) >> 4;
-            const uint32_t r = 4u * j + lr;
-            const uint32_t n = 4u * (is_q ? j - nq4 : j) + lr;
-            const uint32_t c = (static_cast<uint32_t>(lane) & 15u) ^ (r & 15u);
-            dma_x4(is_q ? Qh : Kh, (n < un ? n : 0u) * row_bytes + 16u * c, lds + L.kq + 1024u * j);
-        } else if (j < 2 * nq4 + nv8) {
-            const int jv = j - 2 * nq4;
-            const uint32_t n = 8u * jv + (static_cast<uint32_t>(lane) >> 3);
-            const uint32_t c = static_cast<uint32_t>(lane) & 7u;
-            dma_x4(Vh, (n < un ? n : 0u) * row_bytes + 16u * c, lds + L.v + 1024u * jv);
-        } else if (j == 2 * nq4 + nv8) {
-            dma_x1(parent + node0, 4u * ln, lds + L.sm);
-        } else if (j == 2 * nq4 + nv8 + 1) {
-            dma_x1(alpha + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds + L.sm + 256u);
-        } else {
-            dma_x1(beta + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds + L.sm + 512u);
-        }
-    }
-}
 
 // The item's key and query rows alone -> LDS at `lds` (the staged layout: keys in rows
 // 0 .. 4 ceil(N/4) - 1, queries right after, 256 B rows, chunk c of row r at c ^ (r % 16)),
@@ -1668,208 +1568,6 @@ __device__ __forceinline__ void large_prefetch(LargePrefetch<NKT>& pf, const uin
     }
 }
 
-// The deferred commit's rank-one terms of an item (half a head), chunk c (slots P c ..
-// P c + P - 1, P = P.path) -> LDS: slot s < len is log term s, slot s >= len path node
-// s - len; the item's half of each u~ / U_prev row and the whole key row, four slots per
-// transfer, by per-lane gathers (the log and the previous step's factors are separate
-// arrays).  With the first chunk also the path's gammas and the head's log scale.  Slots
-// past the terms repeat slot 0.
-__device__ __forceinline__ void defer_issue_terms(const CommitIn& c, const DeferLog& dl,
-                                                  const PathInfo& pi, int len, int chunk, int bh,
-                                                  int part, int H, int wave, int lane,
-                                                  uint32_t lds, const SmallLds& P) {
-    const int b = bh / H;
-    const int h = bh - b * H;
-    const size_t node0 = static_cast<size_t>(b) * c.Np;
-    const int rem = len + pi.depth - P.path * chunk;
-    const int cnt = rem < P.path ? rem : P.path;
-    const int nj = cnt > 0 ? (cnt + 3) >> 2 : 0;
-    const int jobs = 2 * nj + (chunk == 0 ? 2 : 0);
-    const size_t lrow0 = static_cast<size_t>(bh) * dl.Lmax;
-    for (int j = wave; j < jobs; j += 4) {
-        if (j < 2 * nj) {
-            const bool is_k = j >= nj;
-            const int jj = is_k ? j - nj : j;
-            const int q = 4 * jj + (lane >> 4);
-            const int sl = P.path * chunk + (q < cnt ? q : 0);
-            const int pq = sl - len;
-            const int n = __shfl(pi.pn, pq >= 0 ? pq : 0);
-            if (is_k) {
-                const uint16_t* src = sl < len ? dl.K + (lrow0 + sl) * D
-                                               : c.K + ((node0 + n) * H + h) * D;
-                dma_gather_x4(src + 8 * (lane & 15), lds + P.pk + 1024u * jj);
-            } else {
-                const float* src = (sl < len ? dl.U + (lrow0 + sl) * D
-                                             : c.U + ((node0 + n) * H + h) * D) + part * kSmallRows;
-                dma_gather_x4(src + 4 * (lane & 15), lds + P.pu + 1024u * jj);
-            }
-        } else if (j == 2 * nj) {
-            const int n = __shfl(pi.pn, lane < pi.depth ? lane : 0);
-            dma_gather_x1(c.gamma + (node0 + n) * H + h, lds + P.pg);
-        } else {
-            dma_x1(dl.scale_in + bh, 0u, lds + P.lg);
-        }
-    }
-}
-
-// The deferred commit on this wave's 16 rows of an item (half a head; layout as in
-// commit_rows_in_lds): S_a = gs (S + sum_j u~_j k_j^T) + sum over the path of a of
-// (g_a / g_i) U_prev[i] k_i^T, gs = s g_a (paper §3 "Reconstruct on commit", Eq. 3, on the
-// logged state), formed in LDS for this step's contractions.  When the path's terms fit in
-// the log and in one chunk of slots (len + depth <= min(Lmax, P.path)) the item's half of
-// each u~ = (g_a / g_i) U_prev[i] / gs and of each key row is appended to the log and S is
-// not written; otherwise S_a goes to S and the log is emptied.  Part 0 writes the header:
-// scale 1 and length 0 when emptied, else gs and len + depth.  Called by every wave, with
-// len + depth > 0.
-__device__ __forceinline__ void commit_defer_in_lds(float* lds, const char* ldsb, const SmallLds& P,
-                                                    const PathInfo& cur, int len,
-                                                    const CommitIn& cin, const DeferLog& dl,
-                                                    int bh, int part, int H, int wave, int lane,
-                                                    uint32_t lds_addr) {
-    const float* PG = reinterpret_cast<const float*>(ldsb + P.pg);
-    const float* PU = reinterpret_cast<const float*>(ldsb + P.pu);
-    const char* PK = ldsb + P.pk;
-    const float gin = reinterpret_cast<const float*>(ldsb + P.lg)[0];
-    const float ga = cur.depth > 0 ? PG[cur.depth - 1] : 1.0f;
-    const float gs = gin * ga;
-    const int total = len + cur.depth;
-    const int keep = dl.Lmax < P.path ? dl.Lmax : P.path;
-    const bool flush = total > keep;
-    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
-    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
-    const int nchunk = (total + P.path - 1) / P.path;
-    f32x4_t x[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t r = 16u * wave + 2u * i + hl;
-        x[i] = gs * *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
-    }
-    for (int ci = 0; ci < nchunk; ++ci) {
-        const int q0 = ci * P.path;
-        if (ci > 0) {
-            lds_barrier();
-            defer_issue_terms(cin, dl, cur, len, ci, bh, part, H, wave, lane, lds_addr, P);
-            __builtin_amdgcn_s_waitcnt(0);
-            lds_barrier();
-        }
-        const int rem = total - q0;
-        const int cnt = rem < P.path ? rem : P.path;
-        // unrolled over the chunk's slots (P.path = kLargePath), so that the reads of all its
-        // rows are issued together
-#pragma unroll
-        for (int q = 0; q < kLargePath; ++q) {
-            if (q >= cnt) break;
-            const int sl = q0 + q;
-            const float cq = sl < len ? gs : ga / PG[sl - len >= 0 ? sl - len : 0];
-            const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
-            const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
-                                __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float cu = cq * PU[q * kSmallRows + 16 * wave + 2 * i + hl];
-                x[i] += cu * kv;
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t r = 16u * wave + 2u * i + hl;
-        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
-        if (flush)
-            __builtin_nontemporal_store(
-                x[i], reinterpret_cast<f32x4_t*>(
-                          cin.S + (static_cast<size_t>(bh) * D + part * kSmallRows + r) * D + 4 * ch));
-    }
-    if (!flush) {
-        // every term sits in the first chunk's slots: path node q is slot len + q; wave w
-        // appends terms w, w + 4, ...: lanes 0-15 this half of u~, lanes 16-23 this half of
-        // the key row
-        const size_t lrow0 = static_cast<size_t>(bh) * dl.Lmax + len;
-        const float rgs = 1.0f / gs;
-        for (int q = wave; q < cur.depth; q += 4) {
-            const int sl = len + q;
-            if (lane < 16) {
-                const float cq = (ga / PG[q]) * rgs;
-                const f32x4_t u = *reinterpret_cast<const f32x4_t*>(PU + sl * kSmallRows + 4 * lane);
-                *reinterpret_cast<f32x4_t*>(dl.U + (lrow0 + q) * D + part * kSmallRows + 4 * lane) = cq * u;
-            } else if (lane < 24) {
-                const int c8 = lane - 16;
-                const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(PK + sl * 256 + 128 * part + 16 * c8);
-                *reinterpret_cast<u32x4_t*>(dl.K + (lrow0 + q) * D + part * kSmallRows + 8 * c8) = kv;
-            }
-        }
-    }
-    if (wave == 0 && lane == 0 && part == 0) {
-        const int b = bh / H;
-        dl.scale_out[bh] = flush ? 1.0f : gs;
-        if (bh - b * H == 0) dl.len_out[b] = flush ? 0 : total;
-    }
-}
-
-// The previous step's commit on this wave's 16 rows of an item, where they sit in LDS in the
-// layout they arrived in (lane l: row 16w + 2i + l / 32, 16-byte chunk l % 32, i = 0..7):
-// S_a = g_a S + sum over the path of a of (g_a / g_i) U_prev[i] k_i^T (paper §3 "Reconstruct
-// on commit", Eq. 3), written back to LDS for this step's contractions and to S as whole
-// 512-byte rows.  The first `P.path` path rows (and all the path's gammas) are in LDS; a
-// longer path fetches the rest chunk by chunk, with blocking waits.  Called by every wave.
-__device__ __forceinline__ void commit_rows_in_lds(float* lds, const char* ldsb, const SmallLds& P,
-                                                   const PathInfo& cur, const CommitIn& cin,
-                                                   int bh, int part, int H, int wave, int lane,
-                                                   uint32_t lds_addr) {
-    const float* PG = reinterpret_cast<const float*>(ldsb + P.pg);
-    const float* PU = reinterpret_cast<const float*>(ldsb + P.pu);
-    const char* PK = ldsb + P.pk;
-    const float ga = PG[cur.depth - 1];
-    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
-    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
-    const int nchunk = (cur.depth + P.path - 1) / P.path;
-    for (int ci = 0; ci < nchunk; ++ci) {
-        const int q0 = ci * P.path;
-        if (ci > 0) {
-            lds_barrier();
-            fused_issue_path(cin, cur, ci, bh, part, H, wave, lane, lds_addr, P);
-            __builtin_amdgcn_s_waitcnt(0);
-            lds_barrier();
-        }
-        const int rem = cur.depth - q0;
-        const int cnt = rem < P.path ? rem : P.path;
-        f32x4_t x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t r = 16u * wave + 2u * i + hl;
-            x[i] = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
-            if (ci == 0) x[i] *= ga;
-        }
-        // unrolled over the chunk's slots, so that the reads of all its rows are issued together
-#pragma unroll
-        for (int q = 0; q < kLargePath; ++q) {
-            if (q >= cnt) break;
-            const float cq = ga / PG[q0 + q];
-            const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
-            const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
-                                __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float cu = cq * PU[q * kSmallRows + 16 * wave + 2 * i + hl];
-                x[i] += cu * kv;
-            }
-        }
-        const bool last = ci + 1 == nchunk;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t r = 16u * wave + 2u * i + hl;
-            *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
-            if (last)   // streaming hint, as for the state's reads
-                __builtin_nontemporal_store(
-                    x[i], reinterpret_cast<f32x4_t*>(
-                              cin.S + (static_cast<size_t>(bh) * D + part * kSmallRows + r) * D + 4 * ch));
-        }
-    }
-}
-
-// FUSED: the previous step's commit first, as in the small-tree kernel's MODE 1, but with the
-// path derived at the top of each item from the previous tree and accepted node that came
-// with the item's inputs; its rows are requested then and land while the tree is walked.
 // Whole half-rows of one item out of the U exchange (per wave w: [16 NKT nodes][16 values
 // of rows 16w..16w+15 of the item's 64]) to a [nodes][H][D] fp32 array at dst (the head's
 // node-0 row): wave w writes nodes 4 NKT w .. 4 NKT w + 4 NKT - 1, four 256-byte half-rows
@@ -1893,23 +1591,22 @@ __device__ __forceinline__ void large_store_rows(float* dst, const float* Ub, in
     }
 }
 
-template <int NKT, bool STAGE, bool FUSED = false, bool DEFER = false>
+template <int NKT>
 __global__ __launch_bounds__(kSmallThreads)
-__attribute__((amdgpu_waves_per_eu(STAGE ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu(3)))
 void verify_large_kernel(
     const float* __restrict__ S0, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ alpha,
     const float* __restrict__ beta, const int32_t* __restrict__ parent, int H, int N, int BH,
     float* __restrict__ O, float* __restrict__ U, float* __restrict__ gamma,
     uint64_t* __restrict__ anc_out, int32_t* __restrict__ depth_out,
-    int32_t* __restrict__ status, CommitIn cin, DeferLog dlog)
+    int32_t* __restrict__ status)
 {
     using Lo = LargeLayout<NKT>;
     constexpr int NCT = 2 * NKT;
     constexpr int kCols = Lo::kCols;
     extern __shared__ __align__(16) float lds[];
     float* G = lds + Lo::kS0;                       // G[m][n], n: keys 0..N-1, queries 16NKT+t
-    const LargeLds Ls = large_lds<NKT, STAGE>(N, FUSED, DEFER);
     const char* ldsb = reinterpret_cast<const char*>(lds);
     const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     const int nq4 = (N + 3) >> 2;
@@ -1928,22 +1625,8 @@ void verify_large_kernel(
     small_item(0, slot, grid, bh, part);
     if (bh >= BH) return;
     LargePrefetch<NKT> pf;
-    small_issue_s0<FUSED>(S0, lds, bh, part, wave, lane);
-    if constexpr (STAGE)
-        large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh, part, wave, lane, lds_addr, Ls);
-    else
-        large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh, part, wave, lane);
-    int pidx = -1, pacc = -1;                       // unstaged FUSED: previous tree, accepted
-    if constexpr (FUSED && STAGE) {
-        if (wave == 2) fused_issue_index(cin, bh / H, lane, lds_addr + Ls.idx);
-        if (wave == 3) dma_gather_x1(cin.accepted + bh / H, lds_addr + Ls.acw);
-        if constexpr (DEFER) {
-            if (wave == 1) dma_x1(dlog.len_in + bh / H, 0u, lds_addr + Ls.il);
-        }
-    } else if constexpr (FUSED) {
-        pidx = lane < cin.Np ? cin.parent[static_cast<size_t>(bh / H) * cin.Np + lane] : -1;
-        pacc = cin.accepted[bh / H];
-    }
+    small_issue_s0<false>(S0, lds, bh, part, wave, lane);
+    large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh, part, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(pf.vraw[kt]));
@@ -1955,63 +1638,19 @@ void verify_large_kernel(
         const size_t node0 = static_cast<size_t>(b) * N;
 
         uint2 vraw[NKT];
-        int my_par;
-        float my_alpha, my_beta;
-        if constexpr (STAGE) {
-            // this item's transfers have landed once only the previous item's stores (2 NKT,
-            // issued last) may still be in flight
-            __builtin_amdgcn_s_waitcnt(Lo::kWait);
-            lds_barrier();
-            const bool ok = lane < N;
-            my_par = ok ? reinterpret_cast<const int*>(ldsb + Ls.sm)[lane] : -1;
-            my_alpha = ok ? reinterpret_cast<const float*>(ldsb + Ls.sm + 256)[lane] : 1.0f;
-            my_beta = ok ? reinterpret_cast<const float*>(ldsb + Ls.sm + 512)[lane] : 0.0f;
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                const int t = 16 * kt + col;
-                vraw[kt] = make_uint2(0u, 0u);
-                if (t < N)
-                    vraw[kt] = *reinterpret_cast<const uint2*>(ldsb + Ls.v + t * 128 + 32 * wave + 8 * grp);
-            }
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) vraw[kt] = pf.vraw[kt];
-            my_par = pf.par;
-            my_alpha = pf.alpha;
-            my_beta = pf.beta;
+        for (int kt = 0; kt < NKT; ++kt) vraw[kt] = pf.vraw[kt];
+        const int my_par = pf.par;
+        const float my_alpha = pf.alpha;
+        const float my_beta = pf.beta;
 
-            // this item's rows and inputs have landed once only the previous item's stores
-            // (2 NKT, issued last) may still be in flight
-            __builtin_amdgcn_s_waitcnt(Lo::kWait);
+        // this item's rows and inputs have landed once only the previous item's stores
+        // (2 NKT, issued last) may still be in flight
+        __builtin_amdgcn_s_waitcnt(Lo::kWait);
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(vraw[kt]));
-            asm volatile("" ::"v"(my_par), "v"(my_alpha), "v"(my_beta));
-            if constexpr (FUSED) asm volatile("" ::"v"(pidx), "v"(pacc));
-            lds_barrier();
-        }
-
-        // ---- the previous step's commit: this item's path, its rows requested now
-        PathInfo cur{0ull, 0, 0};
-        int clen = 0;                               // deferred: the log length
-        if constexpr (FUSED) {
-            if constexpr (STAGE) {
-                pidx = lane < cin.Np ? reinterpret_cast<const int*>(ldsb + Ls.idx)[lane] : -1;
-                pacc = reinterpret_cast<const int*>(ldsb + Ls.acw)[0];
-            }
-            cur = fused_path(pidx, pacc, cin.Np, lane, wave == 0 && bh % H == 0 && part == 0,
-                             status);
-            if constexpr (DEFER) {
-                const int raw = __builtin_amdgcn_readfirstlane(
-                    reinterpret_cast<const int*>(ldsb + Ls.il)[0]);
-                clen = log_len(raw, dlog.Lmax);
-                if (raw != clen && wave == 0 && lane == 0 && bh % H == 0 && part == 0)
-                    report(status, TREEWY_ELOG);
-                defer_issue_terms(cin, dlog, cur, clen, 0, bh, part, H, wave, lane, lds_addr,
-                                  large_path_view(Ls));
-            } else if (cur.depth > 0) {
-                fused_issue_path(cin, cur, 0, bh, part, H, wave, lane, lds_addr, large_path_view(Ls));
-            }
-        }
+        for (int kt = 0; kt < NKT; ++kt) asm volatile("" ::"v"(vraw[kt]));
+        asm volatile("" ::"v"(my_par), "v"(my_alpha), "v"(my_beta));
+        lds_barrier();
 
         // ---- tree walk, lane = node (every wave)
         uint64_t anc_l;
@@ -2047,26 +1686,7 @@ void verify_large_kernel(
             }
         }
 
-        if constexpr (FUSED && DEFER) {
-            __builtin_amdgcn_s_waitcnt(0);          // the terms and the scale (and the last stores)
-            lds_barrier();
-            if (cur.depth + clen > 0) {
-                commit_defer_in_lds(lds, ldsb, large_path_view(Ls), cur, clen, cin, dlog, bh, part,
-                                    H, wave, lane, lds_addr);
-            } else if (wave == 0 && lane == 0 && part == 0) {   // nothing logged or accepted
-                dlog.scale_out[bh] = reinterpret_cast<const float*>(ldsb + Ls.lg)[0];
-                if (h == 0) dlog.len_out[b] = 0;
-            }
-        } else if constexpr (FUSED) {
-            if (cur.depth > 0) {
-                __builtin_amdgcn_s_waitcnt(0);      // the path rows (and the last stores)
-                lds_barrier();
-                commit_rows_in_lds(lds, ldsb, large_path_view(Ls), cur, cin, bh, part, H,
-                                   wave, lane, lds_addr);
-            }
-        }
-
-        // ---- MFMA operands of this wave's 16 rows (committed, with FUSED)
+        // ---- MFMA operands of this wave's 16 rows
         bf16x8_t ahi[4], alo[4];
         {
             const int r = 16 * wave + col;
@@ -2085,14 +1705,12 @@ void verify_large_kernel(
         small_item(round, slot, grid, bh_n, part_n);
         const bool more = bh_n < BH;
 
-        // unstaged: the item's key and query rows go into the S-row area, free from here until
-        // the next item's rows are requested (after the contractions)
-        const uint32_t kq_off = STAGE ? Ls.kq : 0u;
-        if constexpr (!STAGE) {
-            large_issue_kq(Q, K, H, N, bh, wave, lane, lds_addr);
-            __builtin_amdgcn_s_waitcnt(0);
-            lds_barrier();
-        }
+        // the item's key and query rows go into the S-row area, free from here until the next
+        // item's rows are requested (after the contractions)
+        constexpr uint32_t kq_off = 0u;
+        large_issue_kq(Q, K, H, N, bh, wave, lane, lds_addr);
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
         float* Gx = G;
 
         // ---- contractions and Gram rows 16w..16w+15 (waves with keys there)
@@ -2140,35 +1758,12 @@ void verify_large_kernel(
                     Gx[(16 * wave + 4 * grp + e) * kCols + 16 * c + col] = gacc[e];
             }
         }
-        // the next item's rows only now (staged: the next inputs were requested at the top of
-        // the item; unstaged: the key and query rows sit in the S-row area until every wave
-        // is past the contractions)
-        if constexpr (STAGE) {
-            if (more) small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
-        }
+        // the next item's rows only now: the key and query rows sit in the S-row area until
+        // every wave is past the contractions
         lds_barrier();                              // G visible to every wave; inputs read
-        if constexpr (!STAGE) {
-            if (more) small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
-            if (more)
-                large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
-            if constexpr (FUSED) {
-                if (more) {
-                    pidx = lane < cin.Np ? cin.parent[static_cast<size_t>(bh_n / H) * cin.Np + lane] : -1;
-                    pacc = cin.accepted[bh_n / H];
-                }
-            }
-        }
-        if constexpr (STAGE) {
-            if (more)
-                large_issue_inputs(Q, K, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane,
-                                   lds_addr, Ls);
-        }
-        if constexpr (FUSED && STAGE) {    // (unstaged, they travel in registers)
-            if (more && wave == 2) fused_issue_index(cin, bh_n / H, lane, lds_addr + Ls.idx);
-            if (more && wave == 3) dma_gather_x1(cin.accepted + bh_n / H, lds_addr + Ls.acw);
-            if constexpr (DEFER) {
-                if (more && wave == 1) dma_x1(dlog.len_in + bh_n / H, 0u, lds_addr + Ls.il);
-            }
+        if (more) {
+            small_issue_s0<false>(S0, lds, bh_n, part_n, wave, lane);
+            large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
         }
 
         // ---- per lane: nodes t = 16 kt + col, rows v0..v0+3
@@ -3239,29 +2834,19 @@ static hipError_t launch_f32(const VerifyArgs& a, const CommitInF32& cin, hipStr
     return hipGetLastError();
 }
 
-template <int NKT, bool STAGE, bool FUSED = false, bool DEFER = false>
-static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream,
-                               const CommitIn* cin = nullptr, const DeferLog* dl = nullptr) {
-    const LargeLds L = large_lds<NKT, STAGE>(a.N, FUSED, DEFER);
-    const size_t dyn = L.bytes;
-    auto kern = verify_large_kernel<NKT, STAGE, FUSED, DEFER>;
-    if (dyn > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(dyn));
-        if (e != hipSuccess) return e;
-    }
+template <int NKT>
+static hipError_t launch_large(const VerifyArgs& a, hipStream_t stream) {
+    const size_t dyn = sizeof(float) * LargeLayout<NKT>::kTotal;
+    auto kern = verify_large_kernel<NKT>;
     const int BH = a.B * a.H;
     const int items = BH * kSmallParts;
-    // resident workgroups per CU: the register budget, within the 160 KB of LDS
-    const int regs_wgs = STAGE ? 2 : 3;
-    const int slots = small_wgs(L.bytes, regs_wgs) * device_cu_count();
+    // resident workgroups per CU: three (registers), within the 160 KB of LDS
+    const int slots = small_wgs(dyn, 3) * device_cu_count();
     const int grid = items < slots ? items : slots;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kSmallThreads), dyn, stream, a.S0,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
-                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status,
-                       cin ? *cin : CommitIn{}, dl ? *dl : DeferLog{});
+                       BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status);
     return hipGetLastError();
 }
 
@@ -3295,7 +2880,7 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     // own), which leaves room for three workgroups per CU; the fused kernel below stages its
     // inputs instead, where that measured faster.  33-48 and 49-64 nodes: one head per item,
     // three or four node tiles.
-    if (a.N <= 32) return launch_large<2, false>(a, stream);
+    if (a.N <= 32) return launch_large<2>(a, stream);
     if (a.N <= 48) return launch_head<3, false>(a, stream);
     return launch_head<4, false>(a, stream);
 }
@@ -3313,7 +2898,10 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
     if (a.in_dtype == TREEWY_BF16) {
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
                            c.accepted, c.N};
-        if (a.N <= 32) return launch_large<2, true, true>(a, stream, &cin);
+        // 17-64 nodes: one head per item (at 17-32 nodes this measured faster than items of
+        // half a head for the fused step, config 4 637 -> 613 us, while the plain verify
+        // above keeps the half-head items)
+        if (a.N <= 32) return launch_head<2, true>(a, stream, &cin);
         if (a.N <= 48) return launch_head<3, true>(a, stream, &cin);
         return launch_head<4, true>(a, stream, &cin);
     }
@@ -3332,7 +2920,7 @@ hipError_t launch_commit_verify_deferred(const CommitArgs& c, const VerifyArgs& 
                       d.len_in, d.len_out, d.Lmax};
     if (a.N <= 8) return launch_small_fixed<2>(a, cin, dl, stream);
     if (a.N <= 16) return launch_small<2, 2>(a, cin, dl, stream);
-    if (a.N <= 32) return launch_large<2, true, true, true>(a, stream, &cin, &dl);
+    if (a.N <= 32) return launch_head<2, true, true>(a, stream, &cin, &dl);
     if (a.N <= 48) return launch_head<3, true, true>(a, stream, &cin, &dl);
     return launch_head<4, true, true>(a, stream, &cin, &dl);
 }
