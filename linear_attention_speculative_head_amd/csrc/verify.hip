@@ -1913,6 +1913,8 @@ constexpr int kHeadListPer = 5;                // ancestors per packed list word
 constexpr int kHeadListWords = 3;              // list words per node: depths 1..15
 static_assert(kHeadListPer * kHeadListWords < kHeadSlots, "listed depths have table slots");
 constexpr int kHeadPath = 8;                   // path rows staged per chunk (fused commit)
+// s_waitcnt operand: vmcnt <= 8, no other wait
+constexpr int kVmcnt8 = 8 | (7 << 4) | (15 << 8);
 
 // LDS of one head workgroup (byte offsets):
 //   S   S rows [128][128] fp32 (16-byte chunk c of row r at chunk c ^ (r % 16))
@@ -1955,13 +1957,15 @@ struct HeadLds {
 
 // A head's key, query and value rows, parents, alphas and betas -> LDS (layout above): per
 // four nodes one transfer of key rows, one of query rows and one of value rows, then three
-// gathers, dealt round-robin to the eight waves.  Lanes past the last node load node 0.
+// gathers, dealt round-robin to waves w0..7.  Lanes past the last node load node 0.  With
+// `with_parents` false the parents are left out (already requested).
 template <int NKT>
 __device__ __forceinline__ void head_issue_inputs(const uint16_t* Q, const uint16_t* K,
                                                   const uint16_t* V, const float* alpha,
                                                   const float* beta, const int32_t* parent,
                                                   int H, int N, int bh, int wave, int lane,
-                                                  uint32_t lds) {
+                                                  uint32_t lds, int w0 = 0,
+                                                  bool with_parents = true) {
     using L = HeadLds<NKT>;
     const int b = bh / H;
     const int h = bh - b * H;
@@ -1972,7 +1976,8 @@ __device__ __forceinline__ void head_issue_inputs(const uint16_t* Q, const uint1
     const uint32_t ln = static_cast<uint32_t>(lane) < un ? static_cast<uint32_t>(lane) : 0u;
     const int nq4 = (N + 3) >> 2;
     const int jobs = 3 * nq4 + 3;
-    for (int j = wave; j < jobs; j += kHeadWaves) {
+    if (wave < w0) return;
+    for (int j = wave - w0; j < jobs; j += kHeadWaves - w0) {
         if (j < 3 * nq4) {
             const int kind = j / nq4;                    // 0 keys, 1 queries, 2 values
             const int jj = j - kind * nq4;
@@ -1985,7 +1990,7 @@ __device__ __forceinline__ void head_issue_inputs(const uint16_t* Q, const uint1
                                            : L::kKQ + 256u * (kind * L::kNodes) + 1024u * jj;
             dma_x4(src, (n < un ? n : 0u) * row_bytes + 16u * c, lds + dst);
         } else if (j == 3 * nq4) {
-            dma_x1(parent + node0, 4u * ln, lds + L::kSM);
+            if (with_parents) dma_x1(parent + node0, 4u * ln, lds + L::kSM);
         } else if (j == 3 * nq4 + 1) {
             dma_x1(alpha + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds + L::kSM + 256u);
         } else {
@@ -2279,6 +2284,69 @@ __device__ __forceinline__ void head_store_rows(float* dst, const char* ldsb, in
 
 // Part of the dot product of two bf16 rows of 128 elements: elements 32 grp .. 32 grp + 31,
 // then summed over the four lanes col, col + 16, col + 32, col + 48.  Called by all lanes.
+// A sequence's tree as each lane of the head kernel keeps it (lane = node): its ancestor
+// mask, its pointer-jump targets, the tree's depth and jump rounds, and for the lane's nodes
+// t = 16 kt + lane % 16 their depth and strict ancestors in depth order (packed 6 bits each,
+// 0 past the list).
+template <int NKT>
+struct HeadTree {
+    uint64_t anc_l;
+    int jp[6];
+    int maxd, grounds;
+    int dtk[NKT];
+    uint32_t alist[NKT][kHeadListWords];
+};
+
+// Derive it from the parents (lane = node; -1 past N); a malformed parent is reported and
+// taken as a root.
+template <int NKT>
+__device__ __forceinline__ void head_tree(int my_par, int N, int lane, int32_t* status,
+                                          HeadTree<NKT>& tr) {
+    const int col = lane & 15;
+    int p = my_par;
+    const bool bad = lane < N && (p < -1 || p >= lane);
+    if (bad) p = -1;
+    uint64_t am = lane < N ? (1ull << lane) : 0ull;
+    int j = p;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+        tr.jp[r] = j;
+        if ((1 << r) < N) {
+            const int src = j < 0 ? lane : j;
+            const uint64_t aj = shfl_u64(am, src);
+            const int jj = __shfl(j, src);
+            if (j >= 0) { am |= aj; j = jj; }
+        }
+    }
+    tr.anc_l = am;
+    if (bad) report(status, TREEWY_ETREE);
+    int dm = __popcll(am);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dm = max(dm, __shfl_xor(dm, off));
+    tr.maxd = __builtin_amdgcn_readfirstlane(dm);
+    tr.grounds = 0;
+    while ((1 << tr.grounds) < tr.maxd) ++tr.grounds;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+        const int t = 16 * kt + col;
+        const uint64_t at0 = shfl_u64(am, t);
+        const uint64_t at = t < N ? at0 : 0ull;
+        tr.dtk[kt] = __popcll(at);
+        uint64_t m = at & ~(1ull << t);
+#pragma unroll
+        for (int wd = 0; wd < kHeadListWords; ++wd) {
+            uint32_t w = 0u;
+#pragma unroll
+            for (int i = 0; i < kHeadListPer; ++i) {
+                const uint32_t x = m != 0ull ? static_cast<uint32_t>(__ffsll(static_cast<unsigned long long>(m)) - 1) : 0u;
+                m &= m - 1ull;
+                w |= x << (6 * i);
+            }
+            tr.alist[kt][wd] = w;
+        }
+    }
+}
+
 __device__ __forceinline__ float head_dot_bf16(const uint16_t* x, const uint16_t* y, int grp) {
     float s = 0.f;
 #pragma unroll
@@ -2330,20 +2398,35 @@ void verify_head_kernel(
     const int hi = lo + qh + (s < rh ? 1 : 0);
     if (lo >= hi) return;
 
-    // ---- prologue: the first head's inputs (and, fused, its path)
+    // ---- prologue: wave 0 requests the first head's parents (and, fused, the previous tree
+    // and accepted node of its sequence), then every wave its S rows and the other inputs
+    // (waves 1-7); the sequence's tree (and, fused, the accepted path, whose rows are
+    // requested next) is derived while those land.  Wave 0's eight S-row transfers are the
+    // only ones it issues after its first ones.
     PathInfo pnext{0ull, 0, 0};
     int plen = 0;                             // deferred: the log length of pnext's sequence
     const int32_t* len_in = DEFER ? dlog.len_in : nullptr;
+    if (wave == 0) {
+        const uint32_t ln = static_cast<uint32_t>(lane0) < static_cast<uint32_t>(N)
+                                ? static_cast<uint32_t>(lane0) : 0u;
+        dma_x1(parent + static_cast<size_t>(lo / H) * N, 4u * ln, lds_addr + L::kSM);
+        if constexpr (FUSED) head_issue_prev_tree<NKT>(cin, lo, H, lane0, lds_addr, len_in);
+    }
+    small_issue_s0<FUSED>(S0, lds, lo, 0, wave, lane0);
+    head_issue_inputs<NKT>(Q, K, V, alpha, beta, parent, H, N, lo, wave, lane0, lds_addr, 1, false);
+    if (wave == 0) __builtin_amdgcn_s_waitcnt(kVmcnt8);
+    lds_barrier();
+    int seq = lo / H;
+    HeadTree<NKT> tr;
+    head_tree<NKT>(lane0 < N ? reinterpret_cast<const int*>(ldsb + L::kSM)[lane0] : -1, N, lane0,
+                   status, tr);
     if constexpr (FUSED) {
-        if (wave == 0) head_issue_prev_tree<NKT>(cin, lo, H, lane0, lds_addr, len_in);
-        __builtin_amdgcn_s_waitcnt(0);
-        lds_barrier();
         const int pidx = lane0 < cin.Np ? reinterpret_cast<const int*>(ldsb + L::kPI)[lane0] : -1;
         const int pacc = reinterpret_cast<const int*>(ldsb + L::kPA)[0];
         pnext = fused_path(pidx, pacc, cin.Np, lane0, wave == 0 && lo % H == 0, status);
         if constexpr (DEFER)
             plen = head_log_len<NKT>(ldsb, dlog.Lmax, wave == 0 && lane0 == 0 && lo % H == 0, status);
-        lds_barrier();
+        lds_barrier();                        // the previous tree read: refill
         if constexpr (DEFER)
             head_issue_terms<NKT>(cin, dlog, pnext, plen, 0, lo, H, wave, lane0, lds_addr);
         else if (pnext.depth > 0)
@@ -2351,23 +2434,8 @@ void verify_head_kernel(
         if (lo + 1 < hi && wave == kHeadWaves - 1)
             head_issue_prev_tree<NKT>(cin, lo + 1, H, lane0, lds_addr, len_in);
     }
-    small_issue_s0<FUSED>(S0, lds, lo, 0, wave, lane0);
-    head_issue_inputs<NKT>(Q, K, V, alpha, beta, parent, H, N, lo, wave, lane0, lds_addr);
     __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- per-sequence state (lane = node), derived when the sequence changes
-    int seq = -1;
-    uint64_t anc_l = 0ull;
-    int jp[6] = {-1, -1, -1, -1, -1, -1};
-    int maxd = 1, grounds = 0;
-    int dtk[NKT];                             // depth of node 16 kt + col (0 past N)
-    uint32_t alist[NKT][kHeadListWords];      // its strict ancestors, packed
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-        dtk[kt] = 0;
-#pragma unroll
-        for (int wd = 0; wd < kHeadListWords; ++wd) alist[kt][wd] = 0u;
-    }
 
     for (int bh = lo;; ) {
         const int b = bh / H;
@@ -2393,61 +2461,19 @@ void verify_head_kernel(
         const float my_alpha = lane < N ? reinterpret_cast<const float*>(ldsb + L::kSM + 256)[lane] : 1.0f;
         const float bl = lane < N ? reinterpret_cast<const float*>(ldsb + L::kSM + 512)[lane] : 0.0f;
 
-        // ---- the sequence's tree (lane = node), once per run of its heads
+        // ---- the sequence's tree (lane = node), once per run of its heads (the first run's
+        // in the prologue)
         if (b != seq) {
             seq = b;
-            int p = my_par;
-            const bool bad = lane < N && (p < -1 || p >= lane);
-            if (bad) p = -1;
-            uint64_t am = lane < N ? (1ull << lane) : 0ull;
-            int j = p;
-#pragma unroll
-            for (int r = 0; r < 6; ++r) {
-                jp[r] = j;
-                if ((1 << r) < N) {
-                    const int src = j < 0 ? lane : j;
-                    const uint64_t aj = shfl_u64(am, src);
-                    const int jj = __shfl(j, src);
-                    if (j >= 0) { am |= aj; j = jj; }
-                }
-            }
-            anc_l = am;
-            if (bad) report(status, TREEWY_ETREE);
-            int dm = __popcll(am);
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) dm = max(dm, __shfl_xor(dm, off));
-            maxd = __builtin_amdgcn_readfirstlane(dm);
-            grounds = 0;
-            while ((1 << grounds) < maxd) ++grounds;
-            // per lane and node t = 16 kt + col: its depth and its strict ancestors in depth
-            // order, packed 6 bits each (0 past the list)
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                const int t = 16 * kt + col;
-                const uint64_t at0 = shfl_u64(anc_l, t);
-                const uint64_t at = t < N ? at0 : 0ull;
-                dtk[kt] = __popcll(at);
-                uint64_t m = at & ~(1ull << t);
-#pragma unroll
-                for (int wd = 0; wd < kHeadListWords; ++wd) {
-                    uint32_t w = 0u;
-#pragma unroll
-                    for (int j = 0; j < kHeadListPer; ++j) {
-                        const uint32_t x = m != 0ull ? static_cast<uint32_t>(__ffsll(static_cast<unsigned long long>(m)) - 1) : 0u;
-                        m &= m - 1ull;
-                        w |= x << (6 * j);
-                    }
-                    alist[kt][wd] = w;
-                }
-            }
+            head_tree<NKT>(my_par, N, lane, status, tr);
         }
 
         // ---- this head's gates: g_t = product of alpha over t's ancestors-or-self
         float g_l = lane < N ? my_alpha : 1.0f;
 #pragma unroll
         for (int r = 0; r < 6; ++r) {
-            if (r < grounds) {
-                const int j = jp[r];
+            if (r < tr.grounds) {
+                const int j = tr.jp[r];
                 const float gj = __shfl(g_l, j < 0 ? lane : j);
                 if (j >= 0) g_l *= gj;
             }
@@ -2455,8 +2481,8 @@ void verify_head_kernel(
         if (wave == 0 && lane < N) {
             gamma[(node0 + lane) * H + h] = g_l;
             if (h == 0) {
-                if (anc_out) anc_out[node0 + lane] = anc_l;
-                if (depth_out) depth_out[node0 + lane] = __popcll(anc_l);
+                if (anc_out) anc_out[node0 + lane] = tr.anc_l;
+                if (depth_out) depth_out[node0 + lane] = __popcll(tr.anc_l);
             }
         }
 
@@ -2522,7 +2548,7 @@ void verify_head_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int m = (16 * rtg + 4 * grp + e) & 63;
-                    const uint64_t a = shfl_u64(anc_l, m);
+                    const uint64_t a = shfl_u64(tr.anc_l, m);
                     anc_me[e] = m < N ? a : 0ull;
                     const float gme = __shfl(g_l, m);
                     rgm[e] = __builtin_amdgcn_rcpf(gme);
@@ -2548,7 +2574,7 @@ void verify_head_kernel(
                     for (int ks = 0; ks < 4; ++ks)
                         bv[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
                             ldsb + L::kKQ + 256 * r + 16 * ((4u * ks + grp) ^ (r & 15u))));
-                    const uint64_t an0 = shfl_u64(anc_l, static_cast<int>(n));
+                    const uint64_t an0 = shfl_u64(tr.anc_l, static_cast<int>(n));
                     const float gn = __shfl(g_l, static_cast<int>(n));
                     const float rgn = __builtin_amdgcn_rcpf(gn);
                     f32x4_t gacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -2640,7 +2666,7 @@ void verify_head_kernel(
                 Uv[kt][e] = b_kt[kt] * vv[e] - bgt * acc[kt][e];
                 Ov[kt][e] = g_kt[kt] * acc[NKT + kt][e];
             }
-            if (dtk[kt] == 1)                  // a node of depth 1: its U is final already
+            if (tr.dtk[kt] == 1)                  // a node of depth 1: its U is final already
                 *reinterpret_cast<f32x4_t*>(Us + t * 16 + 4 * grp) =
                     f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
         }
@@ -2654,14 +2680,14 @@ void verify_head_kernel(
         for (int wd = 0; wd < kHeadListWords; ++wd) {
 #pragma unroll
             for (int j = 0; j < kHeadListPer; ++j) {
-                if (d < maxd) {
+                if (d < tr.maxd) {
                     float cs[NKT], cw[NKT];
                     f32x4_t x[NKT];
 #pragma unroll
                     for (int kt = 0; kt < NKT; ++kt) {
                         const int t = 16 * kt + col;
-                        const int a = static_cast<int>((alist[kt][wd] >> (6 * j)) & 63u);
-                        const bool has = d < dtk[kt];
+                        const int a = static_cast<int>((tr.alist[kt][wd] >> (6 * j)) & 63u);
+                        const bool has = d < tr.dtk[kt];
                         x[kt] = *reinterpret_cast<const f32x4_t*>(Us + a * 16 + 4 * grp);
                         const float c = Ct[(d - 1) * NN + t];
                         const float w = Wt[(d - 1) * NN + t];
@@ -2675,7 +2701,7 @@ void verify_head_kernel(
                             Uv[kt][e] -= cs[kt] * x[kt][e];
                             Ov[kt][e] += cw[kt] * x[kt][e];
                         }
-                        if (d + 1 == dtk[kt])  // that was its last ancestor: U is final
+                        if (d + 1 == tr.dtk[kt])  // that was its last ancestor: U is final
                             *reinterpret_cast<f32x4_t*>(Us + (16 * kt + col) * 16 + 4 * grp) =
                                 f32x4_t{Uv[kt][0], Uv[kt][1], Uv[kt][2], Uv[kt][3]};
                     }
@@ -2688,14 +2714,14 @@ void verify_head_kernel(
         const uint16_t* Kh = K + (node0 * H + h) * D;
         const uint16_t* Qh = Q + (node0 * H + h) * D;
         const size_t nstride = static_cast<size_t>(H) * D;
-        for (; d < maxd; ++d) {
+        for (; d < tr.maxd; ++d) {
             float cs[NKT], cw[NKT];
             f32x4_t x[NKT];
             bool fin[NKT];
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
                 const int tn = 16 * kt + col;
-                const uint64_t at = shfl_u64(anc_l, tn);
+                const uint64_t at = shfl_u64(tr.anc_l, tn);
                 uint64_t m = tn < N ? (at & ~(1ull << tn)) : 0ull;
                 for (int i = 1; i < d; ++i) m &= m - 1ull;       // drop the shallower ancestors
                 const bool has = m != 0ull;
@@ -2730,10 +2756,10 @@ void verify_head_kernel(
         for (int kt = 0; kt < NKT; ++kt) {
             const int t = 16 * kt + col;
             const bool ok = t < N;
-            const int dt = dtk[kt];
+            const int dt = tr.dtk[kt];
             const bool in_table = ok && dt - 1 < kHeadSlots;
             float cw = in_table ? Wt[(dt - 1) * NN + t] : 0.f;
-            if (maxd > kHeadSlots) {           // (uniform) the node's own k.q from memory
+            if (tr.maxd > kHeadSlots) {           // (uniform) the node's own k.q from memory
                 const int tt = ok ? t : 0;
                 const float kq = head_dot_bf16(Kh + tt * nstride, Qh + tt * nstride, grp);
                 if (ok && !in_table) cw = kq;
