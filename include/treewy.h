@@ -145,9 +145,10 @@ int treewy_commit_verify(float* S, const float* U_prev, const void* K_prev,
  * path's terms they are appended (u~ = (g_a/g_i) U_prev[i] / new scale) and S is not written;
  * otherwise the committed state is written to S and the log is emptied.  The log can take them
  * when, for N <= 16, len + depth(a) <= Lmax and depth(a) is small enough to stage (4 for
- * N <= 4, else 8); for 16 < N <= 64, when len + depth(a) <= min(Lmax, 8) (the log's and the
- * path's rows share one staged chunk of 8 terms; a longer list, on a step that writes S, is
- * fetched chunk by chunk).
+ * N <= 4, else 8); for 16 < N <= 48, when len + depth(a) <= Lmax; for 48 < N <= 64, when
+ * len + depth(a) <= min(Lmax, 8) (the log's and the path's rows share one staged chunk of
+ * 16 terms up to 48 nodes, of 8 above; a longer list, on a step that writes S, is fetched
+ * chunk by chunk).
  *   S                       [B, H, 128, 128] float32, in place (written only when emptying)
  *   logU                    [B, H, Lmax, 128] float32 (rows past len are ignored)
  *   logK                    [B, H, Lmax, 128] bfloat16

@@ -100,12 +100,13 @@ def deferred_step_bytes(parent_prev: np.ndarray, accepted_prev: np.ndarray, pare
     path's terms appended to the log or, when they do not fit, the committed state written
     back.  They fit when len + depth <= Lmax and, up to 16 nodes, the path is no longer than
     one staged chunk (4 rows for N <= 4, else 8); above 16 nodes the log's and the path's
-    terms must fit one chunk of 8 together.  Per sequence both trees, the accepted node and
-    the log length.  Returns (bytes, lengths after the step)."""
+    terms must fit one staged chunk together (16 terms up to 48 nodes, 8 above).  Per
+    sequence both trees, the accepted node and the log length.  Returns (bytes, lengths
+    after the step)."""
     B, Np = parent_prev.shape
     N = parent.shape[1]
     stage = 4 if N <= 4 else 8
-    keep = Lmax if N <= 16 else min(Lmax, 8)
+    keep = Lmax if N <= 48 else min(Lmax, 8)
     row = 4 * D + elem * D
     t = B * H * verify_bytes_per_head(N, elem) + B * 4 * (N + Np + 2) + B * H * 8
     after = np.array(lens, dtype=np.int64)

@@ -46,6 +46,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 __device__ __forceinline__ void split_hi_lo(f32x4_t a, f32x4_t b, bf16x8_t& hi, bf16x8_t& lo) {
     const f32x8_t f = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -401,6 +405,8 @@ struct CommitIn {
     const int32_t* parent;                  // its tree [B][Np]
     const int32_t* accepted;                // its accepted node [B], -1 = none
     int Np;                                 // its node count
+    int short_path;                         // 17-64 nodes, fused commit: paths up to this
+                                            // long go on the vector ALUs (set at launch)
 };
 
 // The deferred commit's log of one step (see the kernel below): per (sequence, head) up to
@@ -1912,7 +1918,6 @@ constexpr int kHeadSlots = 16;                 // ancestor depths with staged co
 constexpr int kHeadListPer = 5;                // ancestors per packed list word (6 bits each)
 constexpr int kHeadListWords = 3;              // list words per node: depths 1..15
 static_assert(kHeadListPer * kHeadListWords < kHeadSlots, "listed depths have table slots");
-constexpr int kHeadPath = 8;                   // path rows staged per chunk (fused commit)
 // s_waitcnt operand: vmcnt <= 8, no other wait
 constexpr int kVmcnt8 = 8 | (7 << 4) | (15 << 8);
 
@@ -1924,8 +1929,9 @@ constexpr int kVmcnt8 = 8 | (7 << 4) | (15 << 8);
 //       whole U rows, then whole O rows, for the stores
 //   C,W coefficient tables [kHeadSlots][16 NKT] fp32
 //   V   value rows [16 NKT][128] bf16 (the same swizzle)
-//   PU, PK, PG  the previous step's path rows of one chunk (U_prev 512 B, K_prev 256 B),
-//       the path's gammas [64]
+//   PU, PK, PG  the previous step's commit terms of one chunk (kPath of them: U_prev or
+//       logged u~ rows 512 B, K_prev or logged key rows 256 B), the path's gammas [64].
+//       Sixteen terms per chunk up to 48 nodes, eight at 49-64 (where the LDS is full)
 //   SM  parents, alphas, betas of the head (64 words each)
 //   PI, PA  the previous tree (64 words) and accepted node (one word, repeated) of a later
 //       head's sequence
@@ -1934,6 +1940,7 @@ constexpr int kVmcnt8 = 8 | (7 << 4) | (15 << 8);
 template <int NKT>
 struct HeadLds {
     static constexpr int kNodes = 16 * NKT;
+    static constexpr int kPath = NKT <= 3 ? 16 : 8;       // commit terms staged per chunk
     static constexpr uint32_t kS = 0;
     static constexpr uint32_t kKQ = kS + D * D * 4u;
     static constexpr uint32_t kU = kKQ + 2u * kNodes * 256u;
@@ -1941,8 +1948,8 @@ struct HeadLds {
     static constexpr uint32_t kW = kC + kHeadSlots * kNodes * 4u;
     static constexpr uint32_t kV = kW + kHeadSlots * kNodes * 4u;
     static constexpr uint32_t kPU = kV + kNodes * 256u;
-    static constexpr uint32_t kPK = kPU + kHeadPath * D * 4u;
-    static constexpr uint32_t kPG = kPK + kHeadPath * D * 2u;
+    static constexpr uint32_t kPK = kPU + kPath * D * 4u;
+    static constexpr uint32_t kPG = kPK + kPath * D * 2u;
     static constexpr uint32_t kSM = kPG + 256u;
     static constexpr uint32_t kPI = kSM + 768u;
     static constexpr uint32_t kPA = kPI + 256u;
@@ -1954,6 +1961,13 @@ struct HeadLds {
     // wave), no other wait
     static constexpr int kWait = (2 * NKT) | (7 << 4) | (15 << 8);
 };
+
+// The 16-byte chunk c of staged key row q (PK) sits at chunk c ^ head_pk_swizzle(q): the
+// transposing reads of head_apply_terms take the same 32 bytes of 16 rows at once, which
+// this spreads over the LDS banks (two rows per bank group instead of sixteen).
+__device__ __forceinline__ uint32_t head_pk_swizzle(int q) {
+    return 2u * (static_cast<uint32_t>(q) & 7u);
+}
 
 // A head's key, query and value rows, parents, alphas and betas -> LDS (layout above): per
 // four nodes one transfer of key rows, one of query rows and one of value rows, then three
@@ -2013,9 +2027,9 @@ __device__ __forceinline__ void head_issue_prev_tree(const CommitIn& c, int bh, 
     if (len_in) dma_x1(len_in + b, 0u, lds + L::kLN);
 }
 
-// Path rows 8 c .. 8 c + 7 of a head -> LDS: U_prev rows (two per transfer), K_prev rows
-// (four per transfer), and with the first chunk the gammas of the whole path (one gather,
-// lane = path position).  Slots past the path repeat its first node.
+// Path rows P c .. P c + P - 1 of a head -> LDS (P = kPath): U_prev rows (two per
+// transfer), K_prev rows (four per transfer), and with the first chunk the gammas of the
+// whole path (one gather, lane = path position).  Slots past the path repeat its first node.
 template <int NKT>
 __device__ __forceinline__ void head_issue_path(const CommitIn& c, const PathInfo& pi, int chunk,
                                                 int bh, int H, int wave, int lane, uint32_t lds) {
@@ -2023,7 +2037,7 @@ __device__ __forceinline__ void head_issue_path(const CommitIn& c, const PathInf
     const int b = bh / H;
     const int h = bh - b * H;
     const size_t node0 = static_cast<size_t>(b) * c.Np;
-    const int cnt = pi.depth - kHeadPath * chunk < kHeadPath ? pi.depth - kHeadPath * chunk : kHeadPath;
+    const int cnt = pi.depth - L::kPath * chunk < L::kPath ? pi.depth - L::kPath * chunk : L::kPath;
     const int nu = (cnt + 1) >> 1;
     const int nk = (cnt + 3) >> 2;
     const int jobs = nu + nk + (chunk == 0 ? 1 : 0);
@@ -2032,14 +2046,15 @@ __device__ __forceinline__ void head_issue_path(const CommitIn& c, const PathInf
     for (int j = wave; j < jobs; j += kHeadWaves) {
         if (j < nu) {
             const int q = 2 * j + (lane >> 5);
-            const uint32_t n = static_cast<uint32_t>(__shfl(pi.pn, kHeadPath * chunk + (q < cnt ? q : 0)));
+            const uint32_t n = static_cast<uint32_t>(__shfl(pi.pn, L::kPath * chunk + (q < cnt ? q : 0)));
             dma_x4(Uh, n * static_cast<uint32_t>(H) * (D * 4u) + 16u * (static_cast<uint32_t>(lane) & 31u),
                    lds + L::kPU + 1024u * j);
         } else if (j < nu + nk) {
             const int jj = j - nu;
             const int q = 4 * jj + (lane >> 4);
-            const uint32_t n = static_cast<uint32_t>(__shfl(pi.pn, kHeadPath * chunk + (q < cnt ? q : 0)));
-            dma_x4(Kh, n * static_cast<uint32_t>(H) * (D * 2u) + 16u * (static_cast<uint32_t>(lane) & 15u),
+            const uint32_t n = static_cast<uint32_t>(__shfl(pi.pn, L::kPath * chunk + (q < cnt ? q : 0)));
+            dma_x4(Kh, n * static_cast<uint32_t>(H) * (D * 2u) +
+                           16u * ((static_cast<uint32_t>(lane) & 15u) ^ head_pk_swizzle(q)),
                    lds + L::kPK + 1024u * jj);
         } else {
             const int n = __shfl(pi.pn, lane < pi.depth ? lane : 0);
@@ -2060,11 +2075,12 @@ __device__ __forceinline__ int head_log_len(const char* ldsb, int Lmax, bool rep
     return len;
 }
 
-// The deferred commit's rank-one terms of a head, chunk c (slots 8 c .. 8 c + 7) -> LDS: slot
-// s < len is log term s (u~ row from the log, key row from the log), slot s >= len is path
-// node s - len (U_prev row, K_prev row), in the path slots (PU, PK; every row by a per-lane
-// gather, since the two sources are separate arrays).  With the first chunk also the
-// path's gammas (PG) and the head's log scale (LS).  Slots past the terms repeat slot 0.
+// The deferred commit's rank-one terms of a head, chunk c (slots P c .. P c + P - 1,
+// P = kPath) -> LDS: slot s < len is log term s (u~ row from the log, key row from the log),
+// slot s >= len is path node s - len (U_prev row, K_prev row), in the path slots (PU, PK;
+// every row by a per-lane gather, since the two sources are separate arrays).  With the
+// first chunk also the path's gammas (PG) and the head's log scale (LS).  Slots past the
+// terms repeat slot 0.
 template <int NKT>
 __device__ __forceinline__ void head_issue_terms(const CommitIn& c, const DeferLog& dl,
                                                  const PathInfo& pi, int len, int chunk, int bh,
@@ -2073,8 +2089,8 @@ __device__ __forceinline__ void head_issue_terms(const CommitIn& c, const DeferL
     const int b = bh / H;
     const int h = bh - b * H;
     const size_t node0 = static_cast<size_t>(b) * c.Np;
-    const int rem = len + pi.depth - kHeadPath * chunk;
-    const int cnt = rem < kHeadPath ? rem : kHeadPath;
+    const int rem = len + pi.depth - L::kPath * chunk;
+    const int cnt = rem < L::kPath ? rem : L::kPath;
     const int nu = cnt > 0 ? (cnt + 1) >> 1 : 0;
     const int nk = cnt > 0 ? (cnt + 3) >> 2 : 0;
     const int jobs = nu + nk + (chunk == 0 ? 2 : 0);
@@ -2084,13 +2100,14 @@ __device__ __forceinline__ void head_issue_terms(const CommitIn& c, const DeferL
             const bool is_k = j >= nu;
             const int jj = is_k ? j - nu : j;
             const int q = is_k ? 4 * jj + (lane >> 4) : 2 * jj + (lane >> 5);
-            const int sl = kHeadPath * chunk + (q < cnt ? q : 0);
+            const int sl = L::kPath * chunk + (q < cnt ? q : 0);
             const int pq = sl - len;                       // path position (slot >= len)
             const int n = __shfl(pi.pn, pq >= 0 ? pq : 0);
             if (is_k) {
                 const uint16_t* src = sl < len ? dl.K + (lrow0 + sl) * D
                                                : c.K + ((node0 + n) * H + h) * D;
-                dma_gather_x4(src + 8 * (lane & 15), lds + L::kPK + 1024u * jj);
+                dma_gather_x4(src + 8 * ((static_cast<uint32_t>(lane) & 15u) ^ head_pk_swizzle(q)),
+                              lds + L::kPK + 1024u * jj);
             } else {
                 const float* src = sl < len ? dl.U + (lrow0 + sl) * D
                                             : c.U + ((node0 + n) * H + h) * D;
@@ -2105,12 +2122,95 @@ __device__ __forceinline__ void head_issue_terms(const CommitIn& c, const DeferL
     }
 }
 
-// The deferred commit on this wave's 16 rows of a head (layout as in head_commit_rows).  With
-// the log read as len terms u~_j k_j^T and scale s, the committed state after this step is
+// One staged chunk of commit terms applied to this wave's 16 rows of S in LDS, on the matrix
+// cores: S[r] <- c0 S[r] + sum over slots k < cnt of coef_k U_k[r] key_k^T, r = 16w + n
+// (U_k the slot's 512-byte row in PU, key_k its bf16 row in PK, 16-byte chunks swizzled by
+// head_pk_swizzle).  Taken per 16-column tile jt as Delta^T = K^T (coef U) with
+// v_mfma_f32_16x16x16_bf16: lane (g = lane / 16, n = lane % 16) gives A = key[4g + t][16 jt
+// + n], t = 0..3 (one transposing LDS read of the key rows: the 16 lanes of a group address
+// a block of 4 key rows x 16 columns and each receives one column), B = coef_{4g+t}
+// U_{4g+t}[r] split into bf16 hi + lo (two products; the keys are exact in bf16,
+// |x - hi - lo| <= 2^-18 |x|), C = c0 times the lane's 16-byte chunk 4 jt + g of row r, and
+// D, the same four columns of row r after the update, goes back where C came from.  Slots
+// past cnt are zero in both operands.  `coef` holds the lane's slots 4g..4g+3.
+template <int NKT>
+__device__ __forceinline__ void head_apply_terms(float* lds, uint32_t lds_addr, int cnt,
+                                                 const float (&coef)[4], float c0, int wave,
+                                                 int lane) {
+    using L = HeadLds<NKT>;
+    const int g = lane >> 4;
+    const int n = lane & 15;
+    const int r = 16 * wave + n;
+    const float* PU = reinterpret_cast<const float*>(reinterpret_cast<const char*>(lds) + L::kPU);
+    f32x4_t u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int k = 4 * g + t;
+        u[t] = k < cnt ? coef[t] * PU[k * D + r] : 0.f;
+    }
+    // the key row this lane addresses (clamped into the staged rows; masked below) and its
+    // 8 bytes of each tile: chunk 2 jt + (n % 4) / 2 of the row, half n % 2
+    const int qrow = 4 * g + (n >> 2) < L::kPath ? 4 * g + (n >> 2) : 0;
+    const uint32_t sw = head_pk_swizzle(qrow);
+    const uint32_t arow = lds_addr + L::kPK + 256u * static_cast<uint32_t>(qrow) + 8u * static_cast<uint32_t>(n & 1);
+    const uint32_t h2 = static_cast<uint32_t>(n & 3) >> 1;
+    // every read first (the writes below may alias them as far as the compiler knows)
+    i16x4_t a[D / 16];
+    f32x4_t c[D / 16];
+#pragma unroll
+    for (int jt = 0; jt < D / 16; ++jt)
+        a[jt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(
+            static_cast<uintptr_t>(arow + 16u * ((2u * jt + h2) ^ sw))));
+#pragma unroll
+    for (int jt = 0; jt < D / 16; ++jt)
+        c[jt] = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * ((4 * jt + g) ^ (r & 15)));
+    const bf16x4_t uh = __builtin_convertvector(u, bf16x4_t);
+    const u32x2_t hw = __builtin_bit_cast(u32x2_t, uh);
+    const f32x4_t rem = {u[0] - __uint_as_float(hw[0] << 16), u[1] - __uint_as_float(hw[0] & 0xffff0000u),
+                         u[2] - __uint_as_float(hw[1] << 16), u[3] - __uint_as_float(hw[1] & 0xffff0000u)};
+    const i16x4_t bh = __builtin_bit_cast(i16x4_t, uh);
+    const i16x4_t bl = __builtin_bit_cast(i16x4_t, __builtin_convertvector(rem, bf16x4_t));
+    const uint32_t m0 = (4 * g < cnt ? 0x0000ffffu : 0u) | (4 * g + 1 < cnt ? 0xffff0000u : 0u);
+    const uint32_t m1 = (4 * g + 2 < cnt ? 0x0000ffffu : 0u) | (4 * g + 3 < cnt ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int jt = 0; jt < D / 16; ++jt) {
+        u32x2_t aw = __builtin_bit_cast(u32x2_t, a[jt]);
+        aw[0] &= m0;
+        aw[1] &= m1;
+        const i16x4_t am = __builtin_bit_cast(i16x4_t, aw);
+        c[jt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bh, c0 * c[jt], 0, 0, 0);
+        c[jt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bl, c[jt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int jt = 0; jt < D / 16; ++jt)
+        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * ((4 * jt + g) ^ (r & 15))) = c[jt];
+}
+
+// This wave's 16 rows of S, final in LDS, to S in HBM as whole 512-byte rows (lane l: row
+// 16w + 2i + l / 32, 16-byte chunk l % 32, i = 0..7), with the streaming hint (the state is
+// read once and written once per step).  The rows were written by other lanes of this wave;
+// a wave's LDS accesses complete in issue order.
+template <int NKT>
+__device__ __forceinline__ void head_store_state(const float* lds, float* S, int bh, int wave,
+                                                 int lane) {
+    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;
+    asm volatile("" ::: "memory");            // after the rows' last LDS writes
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = 16u * wave + 2u * i + hl;
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
+        __builtin_nontemporal_store(
+            x, reinterpret_cast<f32x4_t*>(S + (static_cast<size_t>(bh) * D + r) * D + 4 * ch));
+    }
+}
+
+// The deferred commit on this wave's 16 rows of a head.  With the log read as len terms
+// u~_j k_j^T and scale s, the committed state after this step is
 //   S_a = gs (S + sum_j u~_j k_j^T) + sum over the path of a of (g_a / g_i) U_prev[i] k_i^T,
 // gs = s g_a (paper §3 "Reconstruct on commit", Eq. 3, applied to the logged state), formed
-// in LDS for this step's contractions.  When the path's terms fit in the log and in one
-// chunk of slots (len + depth <= min(Lmax, 8)) they are appended to the log as
+// in LDS on the matrix cores (head_apply_terms) for this step's contractions.  When the path's terms fit in the log and in one
+// chunk of slots (len + depth <= min(Lmax, kPath)) they are appended to the log as
 // u~ = (g_a / g_i) U_prev[i] / gs (one wave per term: the 512-byte u~ row and the 256-byte
 // key row) and S is not written; otherwise S_a goes to S as whole rows and the log is
 // emptied.  The header after the step: scale 1 and length 0 when emptied, else gs and
@@ -2129,19 +2229,12 @@ __device__ __forceinline__ void head_commit_defer(float* lds, const PathInfo& cu
     const float ga = cur.depth > 0 ? PG[cur.depth - 1] : 1.0f;
     const float gs = gin * ga;
     const int total = len + cur.depth;
-    const int keep = dl.Lmax < kHeadPath ? dl.Lmax : kHeadPath;
+    const int keep = dl.Lmax < L::kPath ? dl.Lmax : L::kPath;
     const bool flush = total > keep;
-    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
-    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
-    const int nchunk = (total + kHeadPath - 1) / kHeadPath;
-    f32x4_t x[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t r = 16u * wave + 2u * i + hl;
-        x[i] = gs * *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
-    }
+    const int g = lane >> 4;
+    const int nchunk = (total + L::kPath - 1) / L::kPath;
     for (int ci = 0; ci < nchunk; ++ci) {
-        const int q0 = ci * kHeadPath;
+        const int q0 = ci * L::kPath;
         if (ci > 0) {
             lds_barrier();
             head_issue_terms<NKT>(cin, dl, cur, len, ci, bh, H, wave, lane, lds_addr);
@@ -2149,30 +2242,16 @@ __device__ __forceinline__ void head_commit_defer(float* lds, const PathInfo& cu
             lds_barrier();
         }
         const int rem = total - q0;
-        const int cnt = rem < kHeadPath ? rem : kHeadPath;
-        // unrolled over the chunk's slots, so that the reads of all its rows are issued together
+        const int cnt = rem < L::kPath ? rem : L::kPath;
+        // log terms carry the new scale; path term i carries g_a / g_i
+        float coef[4];
 #pragma unroll
-        for (int q = 0; q < kHeadPath; ++q) {
-            if (q >= cnt) break;
-            const int sl = q0 + q;
-            const float cq = sl < len ? gs : ga * __builtin_amdgcn_rcpf(PG[sl - len >= 0 ? sl - len : 0]);
-            const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
-            const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
-                                __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float cu = cq * PU[q * D + 16 * wave + 2 * i + hl];
-                x[i] += cu * kv;
-            }
+        for (int t = 0; t < 4; ++t) {
+            const int sl = q0 + 4 * g + t;
+            const int pq = sl - len;
+            coef[t] = sl < len ? gs : ga * __builtin_amdgcn_rcpf(PG[pq >= 0 && pq < 64 ? pq : 0]);
         }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t r = 16u * wave + 2u * i + hl;
-        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
-        if (flush)
-            __builtin_nontemporal_store(
-                x[i], reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D + r) * D + 4 * ch));
+        head_apply_terms<NKT>(lds, lds_addr, cnt, coef, ci == 0 ? gs : 1.0f, wave, lane);
     }
     if (!flush) {
         // every term sits in the first chunk's slots: path node q is slot len + q
@@ -2185,7 +2264,8 @@ __device__ __forceinline__ void head_commit_defer(float* lds, const PathInfo& cu
                 const f32x4_t u = *reinterpret_cast<const f32x4_t*>(PU + sl * D + 4 * lane);
                 *reinterpret_cast<f32x4_t*>(dl.U + (lrow0 + q) * D + 4 * lane) = cq * u;
             } else if (lane < 48) {
-                const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(PK + sl * 256 + 16 * (lane - 32));
+                const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(
+                    PK + sl * 256 + 16 * ((static_cast<uint32_t>(lane) - 32u) ^ head_pk_swizzle(sl)));
                 *reinterpret_cast<u32x4_t*>(dl.K + (lrow0 + q) * D + 8 * (lane - 32)) = kv;
             }
         }
@@ -2195,15 +2275,17 @@ __device__ __forceinline__ void head_commit_defer(float* lds, const PathInfo& cu
         dl.scale_out[bh] = flush ? 1.0f : gs;
         if (bh - b * H == 0) dl.len_out[b] = flush ? 0 : total;
     }
+    if (flush) head_store_state<NKT>(lds, cin.S, bh, wave, lane);
 }
 
-// The previous step's commit on this wave's 16 rows of a head, where they sit in LDS in
-// the layout they arrived in (lane l: row 16w + 2i + l / 32, 16-byte chunk l % 32,
-// i = 0..7): S_a = g_a S + sum over the path of a of (g_a / g_i) U_prev[i] k_i^T (paper §3
-// "Reconstruct on commit", Eq. 3), written back to LDS for this step's contractions and to
-// S as whole 512-byte rows.  The first kHeadPath path rows and all the path's gammas are in
-// LDS; a longer path fetches the rest chunk by chunk, with blocking waits.  Every wave calls
-// it (the path is the same for the whole workgroup).
+// The previous step's commit on this wave's 16 rows of a head, in LDS: S_a = g_a S + sum
+// over the path of a of (g_a / g_i) U_prev[i] k_i^T (paper §3 "Reconstruct on commit",
+// Eq. 3), on the matrix cores (head_apply_terms; paths of up to cin.short_path nodes on the
+// vector ALUs), written back to LDS for this step's contractions and to S as whole 512-byte
+// rows.
+// The first kPath path rows and all the path's gammas are in LDS; a longer path fetches the
+// rest chunk by chunk, with blocking waits.  Every wave calls it (the path is the same for
+// the whole workgroup).
 template <int NKT>
 __device__ __forceinline__ void head_commit_rows(float* lds, const PathInfo& cur, const CommitIn& cin,
                                                  int bh, int H, int wave, int lane,
@@ -2211,20 +2293,45 @@ __device__ __forceinline__ void head_commit_rows(float* lds, const PathInfo& cur
     using L = HeadLds<NKT>;
     const char* ldsb = reinterpret_cast<const char*>(lds);
     const float* PG = reinterpret_cast<const float*>(ldsb + L::kPG);
-    const float* PU = reinterpret_cast<const float*>(ldsb + L::kPU);
-    const char* PK = ldsb + L::kPK;
     const float ga = PG[cur.depth - 1];
-    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
-    const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
-    const int nchunk = (cur.depth + kHeadPath - 1) / kHeadPath;
-    f32x4_t x[8];
+    if (cur.depth <= cin.short_path) {
+        // a short path (cin.short_path <= 4): the terms on the vector ALUs, in the rows'
+        // arrival layout (lane l: row 16w + 2i + l / 32, 16-byte chunk l % 32, i = 0..7),
+        // which has less latency than the matrix-core form for so few terms
+        const float* PU = reinterpret_cast<const float*>(ldsb + L::kPU);
+        const char* PK = ldsb + L::kPK;
+        const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+        const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
+        f32x4_t x[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t r = 16u * wave + 2u * i + hl;
-        x[i] = ga * *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = 16u * wave + 2u * i + hl;
+            x[i] = ga * *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q >= cur.depth) break;
+            const float cq = ga * __builtin_amdgcn_rcpf(PG[q]);
+            const uint2 kw = *reinterpret_cast<const uint2*>(
+                PK + q * 256 + 16 * ((ch >> 1) ^ head_pk_swizzle(q)) + 8 * (ch & 1u));
+            const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
+                                __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] += (cq * PU[q * D + 16 * wave + 2 * i + hl]) * kv;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = 16u * wave + 2u * i + hl;
+            *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
+            __builtin_nontemporal_store(
+                x[i], reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D + r) * D + 4 * ch));
+        }
+        return;
     }
+    const int g = lane >> 4;
+    const int nchunk = (cur.depth + L::kPath - 1) / L::kPath;
     for (int ci = 0; ci < nchunk; ++ci) {
-        const int q0 = ci * kHeadPath;
+        const int q0 = ci * L::kPath;
         if (ci > 0) {
             lds_barrier();
             head_issue_path<NKT>(cin, cur, ci, bh, H, wave, lane, lds_addr);
@@ -2232,29 +2339,16 @@ __device__ __forceinline__ void head_commit_rows(float* lds, const PathInfo& cur
             lds_barrier();
         }
         const int rem = cur.depth - q0;
-        const int cnt = rem < kHeadPath ? rem : kHeadPath;
+        const int cnt = rem < L::kPath ? rem : L::kPath;
+        float coef[4];
 #pragma unroll
-        for (int q = 0; q < kHeadPath; ++q) {
-            if (q >= cnt) break;
-            const float cq = ga * __builtin_amdgcn_rcpf(PG[q0 + q]);
-            const uint2 kw = *reinterpret_cast<const uint2*>(PK + q * 256 + 8 * ch);
-            const f32x4_t kv = {__uint_as_float(kw.x << 16), __uint_as_float(kw.x & 0xffff0000u),
-                                __uint_as_float(kw.y << 16), __uint_as_float(kw.y & 0xffff0000u)};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float cu = cq * PU[q * D + 16 * wave + 2 * i + hl];
-                x[i] += cu * kv;
-            }
+        for (int t = 0; t < 4; ++t) {
+            const int q = q0 + 4 * g + t;
+            coef[t] = ga * __builtin_amdgcn_rcpf(PG[q < 64 ? q : 0]);
         }
+        head_apply_terms<NKT>(lds, lds_addr, cnt, coef, ci == 0 ? ga : 1.0f, wave, lane);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t r = 16u * wave + 2u * i + hl;
-        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u))) = x[i];
-        // streaming hint: the state is read once and written once per step
-        __builtin_nontemporal_store(
-            x[i], reinterpret_cast<f32x4_t*>(cin.S + (static_cast<size_t>(bh) * D + r) * D + 4 * ch));
-    }
+    head_store_state<NKT>(lds, cin.S, bh, wave, lane);
 }
 
 // Whole node rows of one head out of the U exchange (per wave w: [node][16 values of rows
@@ -2888,11 +2982,17 @@ static hipError_t launch_head(const VerifyArgs& a, hipStream_t stream, const Com
     const int BH = a.B * a.H;
     const int cus = device_cu_count();          // one workgroup per CU (LDS)
     const int grid = BH < cus ? BH : cus;
+    // the fused commit of a path of up to four nodes: on the vector ALUs (less latency)
+    // unless each workgroup has at least 32 heads, where the matrix-core form measured faster
+    // (B256 x H64 32-node trees 604 -> 599 us; B128 x H32 64-node trees 217 -> 219 us and
+    // B32 x H32 21-node trees 41.4 -> 43.5 us the other way)
+    CommitIn c = cin ? *cin : CommitIn{};
+    c.short_path = BH < 32 * cus ? 4 : 0;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kHeadThreads), L::kBytes, stream, a.S0,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
                        BH, a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status,
-                       cin ? *cin : CommitIn{}, dl ? *dl : DeferLog{});
+                       c, dl ? *dl : DeferLog{});
     return hipGetLastError();
 }
 

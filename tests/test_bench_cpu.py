@@ -70,8 +70,15 @@ def test_deferred_bytes_log_and_flush():
                                               np.array([2]), 4)
     assert after.tolist() == [0]
     assert t == base + 2 * row + 3 * (row + 4) + 4 * D * D
-    # above 16 nodes the log and the path share one chunk of 8 terms: 6 logged + 3 > 8
-    big = np.array([list(range(-1, 39))], dtype=np.int32)
+    # above 16 nodes the log and the path share one staged chunk: 16 terms up to 48 nodes
+    # (40-node chain: 6 logged + 3 fit, 14 + 3 do not), 8 above (64-node chain: 5 + 3 fit,
+    # 6 + 3 do not)
+    mid = np.array([list(range(-1, 39))], dtype=np.int32)
+    t, after = accounting.deferred_step_bytes(mid, np.array([2]), mid, H, 2, np.array([6]), 16)
+    assert after.tolist() == [9]
+    t, after = accounting.deferred_step_bytes(mid, np.array([2]), mid, H, 2, np.array([14]), 16)
+    assert after.tolist() == [0]
+    big = np.array([list(range(-1, 63))], dtype=np.int32)
     t, after = accounting.deferred_step_bytes(big, np.array([2]), big, H, 2, np.array([6]), 16)
     assert after.tolist() == [0]
     t, after = accounting.deferred_step_bytes(big, np.array([2]), big, H, 2, np.array([5]), 16)

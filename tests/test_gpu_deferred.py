@@ -87,11 +87,17 @@ def oracle_steps(steps):
     return heads, outs, states
 
 
+def chunk_terms(N):
+    """Commit terms the 17-64-node kernel stages per chunk."""
+    return 16 if N <= 48 else 8
+
+
 def expected_lengths(steps, Lmax):
     """The header rule: the accepted path's terms join the log when they fit; otherwise the
     log is emptied into S.  Up to 16 nodes the path must also be short enough to stage with
     the next step (4 nodes for N <= 4, else 8); above 16 nodes the log and the path together
-    must fit one chunk of 8 staged terms.  No accepted node leaves the log as it is."""
+    must fit one chunk of staged terms (16 up to 48 nodes, 8 above).  No accepted node
+    leaves the log as it is."""
     B = steps[0].B
     lens = np.zeros(B, dtype=np.int64)
     out = [None]
@@ -102,7 +108,7 @@ def expected_lengths(steps, Lmax):
             if a < 0:
                 # nothing to append; above 16 nodes a log longer than the staged chunk is
                 # written back all the same
-                if P.N > 16 and lens[b] > min(Lmax, 8):
+                if P.N > 16 and lens[b] > min(Lmax, chunk_terms(P.N)):
                     lens[b] = 0
                 continue
             d = int(inputs.tree_depths(P_prev.parent[b])[a])
@@ -110,7 +116,7 @@ def expected_lengths(steps, Lmax):
                 stage = 4 if P.N <= 4 else 8
                 full = lens[b] + d > Lmax or d > stage
             else:
-                full = lens[b] + d > min(Lmax, 8)
+                full = lens[b] + d > min(Lmax, chunk_terms(P.N))
             lens[b] = 0 if full else lens[b] + d
         out.append(lens.copy())
     return out
@@ -125,8 +131,10 @@ def expected_lengths(steps, Lmax):
     (32, (6, 4), 8, 6, 66, 5, 4),      # 17-32 nodes: items of half a head
     (20, (6, 4), 3, 7, 67, 3, 8),      # a ragged tile, a three-term log
     (64, (6, 8), 8, 6, 68, 9, 32),     # 33-64 nodes: 288 heads, some workgroups take two
-    (64, (6, 8), 16, 5, 69, 5, 4),     # a 16-term log behaves as 8 terms above 16 nodes
+    (64, (6, 8), 16, 5, 69, 5, 4),     # a 16-term log behaves as 8 terms above 48 nodes
     (40, (6, 8), 5, 6, 70, 5, 4),
+    (40, (6, 8), 16, 7, 73, 5, 4),     # 17-48 nodes: a 16-term log fills up to 16
+    (32, (6, 4), 12, 7, 74, 3, 8),
     (64, "chain", 8, 5, 71, 3, 4),     # deep paths: flushes over several chunks of terms
     (24, "chain", 8, 5, 72, 3, 4),
 ])
@@ -207,14 +215,17 @@ def test_deferred_mixed_tree_sizes():
     assert e.max() <= TOL, f"flushed state: worst {e.max():.3e}"
 
 
-def test_deferred_long_log_meets_large_tree():
-    """A 12-term log built on 4-node chains (Lmax 16), then steps on 40- and 24-node trees:
-    the first accepts nothing in some sequences (their log is written back anyway: it does not
-    fit the large-tree kernels' 8 staged terms), the second appends again."""
+@pytest.mark.parametrize("n_big,kept", [(64, False), (40, True)])
+def test_deferred_long_log_meets_large_tree(n_big, kept):
+    """A 12-term log built on 4-node chains (Lmax 16), then steps on n_big-, 24- and 33-node
+    trees.  The first accepts nothing in some sequences: at 64 nodes their log is written
+    back all the same (it does not fit the 8 terms staged there), at 40 nodes it stays (16
+    staged terms).  The later steps append again."""
+    say(f"[deferred] long log meets N={n_big}")
     B, H, Lmax = 4, 3, 16
     steps = []
     for s, (n, tree) in enumerate([(4, "chain"), (4, "chain"), (4, "chain"), (4, "chain"),
-                                   (40, (6, 8)), (24, (6, 4)), (33, (6, 8))]):
+                                   (n_big, (6, 8)), (24, (6, 4)), (33, (6, 8))]):
         acc = None
         if n == 4:
             acc = np.full(B, 3, dtype=np.int32)          # depth 4 each step: 4, 8, 12
@@ -226,7 +237,7 @@ def test_deferred_long_log_meets_large_tree():
     heads, ref, states = oracle_steps(steps)
     want_len = expected_lengths(steps, Lmax)
     assert want_len[3].tolist() == [12, 12, 12, 12]
-    assert want_len[4].tolist()[:2] == [0, 0]
+    assert want_len[4].tolist()[:2] == ([12, 12] if kept else [0, 0])
     for s in range(nsteps):
         for key in ("O", "U"):
             g = gather_heads(gpu[s][key], heads, "node").astype(np.float64)
