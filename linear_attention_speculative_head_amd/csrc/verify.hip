@@ -3002,10 +3002,10 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     const DeferLog nolog{};
     if (a.N <= 8) return launch_small_fixed<0>(a, none, nolog, stream);
     if (a.N <= 16) return launch_small<2, 0>(a, none, nolog, stream);
-    // up to 32 nodes the key and query rows go through the S-row area (no LDS area of their
-    // own), which leaves room for three workgroups per CU; the fused kernel below stages its
-    // inputs instead, where that measured faster.  33-48 and 49-64 nodes: one head per item,
-    // three or four node tiles.
+    // 17-32 nodes: items of half a head, three workgroups per CU (the key and query rows go
+    // through the S-row area, no LDS area of their own); this measured faster for the plain
+    // verify than one head per item.  33-48 and 49-64 nodes: one head per item, three or
+    // four node tiles.
     if (a.N <= 32) return launch_large<2>(a, stream);
     if (a.N <= 48) return launch_head<3, false>(a, stream);
     return launch_head<4, false>(a, stream);
@@ -3025,8 +3025,8 @@ hipError_t launch_commit_verify(const CommitArgs& c, const VerifyArgs& a, hipStr
         const CommitIn cin{c.S, c.U, static_cast<const uint16_t*>(c.K), c.gamma, c.parent,
                            c.accepted, c.N};
         // 17-64 nodes: one head per item (at 17-32 nodes this measured faster than items of
-        // half a head for the fused step, config 4 637 -> 613 us, while the plain verify
-        // above keeps the half-head items)
+        // half a head for the fused step, B256 x H64 32-node trees 637 -> 604 us, while the
+        // plain verify above keeps the half-head items)
         if (a.N <= 32) return launch_head<2, true>(a, stream, &cin);
         if (a.N <= 48) return launch_head<3, true>(a, stream, &cin);
         return launch_head<4, true>(a, stream, &cin);
