@@ -14,8 +14,9 @@
 //   5. readout O[t] = g_t Y[t] + sum_{i anc-or-self} W[t,i] U[i]; O, U, gamma written once;
 // and, in the fused forms, the previous step's commit (Eq. 3) on the state first.
 // Kernels: fp32 inputs (verify_f32_kernel); bf16 inputs on trees of up to 16 nodes
-// (verify_small_kernel), 17 to 32 nodes (verify_large_kernel), 33 to 64 nodes
-// (verify_head_kernel).
+// (verify_small_kernel), the plain verify on 17 to 32 nodes (verify_large_kernel), and one
+// head per item for the rest: the fused and deferred steps on 17 to 64 nodes, the plain
+// verify on 33 to 64 (verify_head_kernel).
 
 #include "device_common.h"
 #include "launch.h"
