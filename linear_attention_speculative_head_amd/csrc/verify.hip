@@ -1012,6 +1012,351 @@ void verify_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
+// fp32 inputs on trees of up to four nodes (and, fused, a previous tree of up to four): the
+// same eight workgroups of 16 value rows per head, with everything after the transfers in
+// registers.  Lane (r = tid / 16, c = tid % 16) owns columns 8c .. 8c + 7 of state row
+// r0 + r.  Every lane derives the (tiny) trees from the staged parents itself: ancestor
+// masks in topological order (parents precede children), gates as products.  It commits its
+// eight state values (S_a = g_a S + sum over the path of (g_a / g_i) U_prev[i][r] k_i), takes
+// its partial dot products with the keys and queries (P[t] = S_r . k_t, Y[t] = S_r . q_t,
+// k_t . k_i, k_i . q_t over its eight columns) and sums them over the row's 16 lanes with
+// DPP adds (quad permutes, half-row and row mirrors).  Each row's 16 lanes then hold the
+// whole row of P and Y and the whole Gram matrix and solve the row's nodes in order, in fp32
+// FMAs: U[t] = b_t (v_t - g_t P[t]) - sum over strict ancestors of b_t (g_t/g_i)(k_t.k_i) U[i],
+// O[t] = g_t Y[t] + sum over ancestors-or-self of (g_t/g_i)(k_i.q_t) U[i]; lane c = t writes
+// node t's O and U.  No LDS round trip or barrier follows the transfers: at one head the
+// step is a chain of latencies, and this cuts it to one.
+
+constexpr int kTinyN = 4;                       // nodes (and previous nodes) of this form
+
+// v moved across lanes by the DPP control CTRL (all rows and banks, no bound control).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// The sum of v over the 16 lanes of a row (lanes 16q .. 16q + 15), in every one of them.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xb1>(v);                      // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp_mov<0x4e>(v);                      // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp_mov<0x141>(v);                     // row_half_mirror: the other quad of eight
+    v += dpp_mov<0x140>(v);                     // row_mirror: the other half of sixteen
+    return v;
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kF32Threads)
+void verify_f32_tiny_kernel(
+    const float* __restrict__ S0, const float* __restrict__ Q, const float* __restrict__ K,
+    const float* __restrict__ V, const float* __restrict__ alpha, const float* __restrict__ beta,
+    const int32_t* __restrict__ parent, int H, int N, float* __restrict__ O,
+    float* __restrict__ U, float* __restrict__ gamma, uint64_t* __restrict__ anc_out,
+    int32_t* __restrict__ depth_out, int32_t* __restrict__ status, CommitInF32 cin)
+{
+    // staged inputs (transfer destinations: whole 1 KB wave loads, 256 B gathers)
+    __shared__ __align__(16) float Ss[kF32Rows * D];     // this block's 16 state rows
+    __shared__ __align__(16) float Ks[kTinyN * D];       // key rows
+    __shared__ __align__(16) float Qs[kTinyN * D];       // query rows
+    __shared__ __align__(16) float PKs[kTinyN * D];      // previous keys (fused)
+    __shared__ __align__(16) float Vs[256];              // value slices [node][16]
+    __shared__ __align__(16) float PUs[256];             // previous U slices [node][16] (fused)
+    __shared__ __align__(16) int32_t SMi[6 * 64];        // parent, alpha, beta, previous parent,
+                                                         // accepted, previous gamma
+    const float* SMf = reinterpret_cast<const float*>(SMi);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bh = blockIdx.x / kF32Blocks;
+    const int blk = blockIdx.x - bh * kF32Blocks;
+    const int r0 = blk * kF32Rows;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const size_t node0 = static_cast<size_t>(b) * N;
+    const size_t nstride = static_cast<size_t>(H) * D;   // floats between nodes of one head
+    const uint32_t un = static_cast<uint32_t>(N);
+    const int Np = FUSED ? cin.Np : 0;
+    const uint32_t unp = static_cast<uint32_t>(Np);
+    const size_t p0 = static_cast<size_t>(b) * Np;
+
+    // ---- every input in transfers issued at once, then each wave waits for its own
+    {
+        const uint32_t ln = static_cast<uint32_t>(lane) < un ? static_cast<uint32_t>(lane) : 0u;
+        const uint32_t lnp = static_cast<uint32_t>(lane) < unp ? static_cast<uint32_t>(lane) : 0u;
+        const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+        const uint32_t c32 = static_cast<uint32_t>(lane) & 31u;
+        const uint32_t q4 = static_cast<uint32_t>(lane) >> 2;       // slices: node of the lane
+        const uint32_t s4 = 16u * (static_cast<uint32_t>(lane) & 3u);
+        const uint32_t lds_sm = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(SMi));
+        const float* Kh = K + (node0 * H + h) * D;
+        const float* Qh = Q + (node0 * H + h) * D;
+        // 8 S rows transfers, 2 + 2 key/query, 1 value slices, 3 gathers; fused: 2 previous
+        // key rows, 1 previous U slices, 3 gathers
+        const int jobs = FUSED ? 22 : 16;
+        for (int j = wave; j < jobs; j += kF32Waves) {
+            if (j < 8) {
+                const uint32_t rr = 2u * j + hl;
+                dma_x4(S0 + static_cast<size_t>(bh) * D * D, ((r0 + rr) * D + 4u * c32) * 4u,
+                       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(Ss)) + 1024u * j);
+            } else if (j < 12) {
+                const bool is_q = j >= 10;
+                const uint32_t t = 2u * (j - (is_q ? 10 : 8)) + hl;
+                dma_x4(is_q ? Qh : Kh, static_cast<uint32_t>((t < un ? t : 0u) * nstride * 4u) + 16u * c32,
+                       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(is_q ? Qs : Ks)) +
+                           1024u * (j - (is_q ? 10 : 8)));
+            } else if (j == 12) {
+                dma_x4(V + (node0 * H + h) * D + r0,
+                       static_cast<uint32_t>((q4 < un ? q4 : 0u) * nstride * 4u) + s4,
+                       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(Vs)));
+            } else if (j == 13) {
+                dma_x1(parent + node0, 4u * ln, lds_sm);
+            } else if (j == 14) {
+                dma_x1(alpha + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds_sm + 256u);
+            } else if (j == 15) {
+                dma_x1(beta + node0 * H + h, 4u * ln * static_cast<uint32_t>(H), lds_sm + 512u);
+            } else if (j < 18) {
+                const uint32_t n = 2u * (j - 16) + hl;
+                dma_x4(cin.K + (p0 * H + h) * D,
+                       static_cast<uint32_t>((n < unp ? n : 0u) * nstride * 4u) + 16u * c32,
+                       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(PKs)) + 1024u * (j - 16));
+            } else if (j == 18) {
+                dma_x4(cin.U + (p0 * H + h) * D + r0,
+                       static_cast<uint32_t>((q4 < unp ? q4 : 0u) * nstride * 4u) + s4,
+                       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(PUs)));
+            } else if (j == 19) {
+                dma_x1(cin.parent + p0, 4u * lnp, lds_sm + 768u);
+            } else if (j == 20) {
+                dma_x1(cin.accepted + b, 0u, lds_sm + 1024u);
+            } else {
+                dma_x1(cin.gamma + p0 * H + h, 4u * lnp * static_cast<uint32_t>(H), lds_sm + 1280u);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    lds_barrier();
+
+    const int r = tid >> 4;                     // row r0 + r
+    const int c = tid & 15;                     // columns 8c .. 8c + 7
+    const bool reporter = blk == 0 && tid == 0;
+
+    // ---- the Gram entries first: they need the key and query rows only
+    // the Gram entries (the same for every row): k_i . q_t (i <= t) and k_t . k_i (i < t),
+    // 16 pairs; each row of the wave takes four (its lanes read those pairs' rows), and the
+    // sums are read back from the four rows as wave-uniform values.  Pair pp is (i, t) =
+    // (0,0) (0,1) (1,1) (0,2) (1,2) (2,2) (0,3) (1,3) (2,3) (3,3) for k_i . q_t, then (t, i) =
+    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2) for k_t . k_i: first index in nibble pp of kPairA,
+    // second in nibble pp of kPairB.
+    float G[16];
+    {
+        constexpr uint64_t kPairA = 0x3332213210210100ull;
+        constexpr uint64_t kPairB = 0x2101003333222110ull;
+        const int q = (tid >> 4) & 3;           // this lane's row within the wave
+        float part[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pp = 4 * q + j;
+            const int ia = static_cast<int>((kPairA >> (4 * pp)) & 15u);
+            const int ib = static_cast<int>((kPairB >> (4 * pp)) & 15u);
+            const float* ra = Ks + ia * D + 8 * c;
+            const float* rb = (pp < 10 ? Qs : Ks) + ib * D + 8 * c;
+            const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(ra);
+            const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(ra + 4);
+            const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(rb);
+            const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(rb + 4);
+            float x = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x += a0[e] * b0[e] + a1[e] * b1[e];
+            part[j] = row16_sum(x);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                G[4 * qq + j] = __int_as_float(
+                    __builtin_amdgcn_readlane(__float_as_int(part[j]), 16 * qq));
+    }
+    // ---- this step's tree, in every lane
+    // (every staged slot holds a real node's words: slots past N repeat node 0, so all are
+    // read at once and the ones past N are dropped)
+    int par[kTinyN];
+    float al[kTinyN], bt[kTinyN];
+#pragma unroll
+    for (int t = 0; t < kTinyN; ++t) {
+        par[t] = SMi[t];
+        al[t] = SMf[64 + t];
+        bt[t] = t < N ? SMf[128 + t] : 0.0f;
+    }
+    uint32_t anc[kTinyN];
+    float g[kTinyN];
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < kTinyN; ++t) {
+        int p = par[t];
+        if (t < N && (p < -1 || p >= t)) { bad = true; p = -1; }
+        uint32_t ap = 0u;
+        float gp = 1.0f;
+#pragma unroll
+        for (int i = 0; i < t; ++i)
+            if (p == i) { ap = anc[i]; gp = g[i]; }
+        anc[t] = t < N ? (ap | (1u << t)) : 0u;
+        g[t] = t < N ? al[t] * gp : 1.0f;
+    }
+    if (bad && reporter) report(status, TREEWY_ETREE);
+    if (blk == 0 && tid < N) {
+        gamma[(node0 + tid) * H + h] = g[tid];
+        if (h == 0) {
+            uint64_t m = 0ull;
+            int dd = 0;
+#pragma unroll
+            for (int t = 0; t < kTinyN; ++t)
+                if (t == tid) { m = anc[t]; dd = __popc(anc[t]); }
+            if (anc_out) anc_out[node0 + tid] = m;
+            if (depth_out) depth_out[node0 + tid] = dd;
+        }
+    }
+
+    // ---- this lane's eight state values, committed (fused)
+    float sv[8];
+    {
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(Ss + r * D + 8 * c);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(Ss + r * D + 8 * c + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { sv[e] = x0[e]; sv[4 + e] = x1[e]; }
+    }
+    if constexpr (FUSED) {
+        // the previous tree's ancestor masks; a bad parent spoils every path through it
+        // every operand first (slots past Np repeat node 0), the terms masked by the path
+        int ppar[kTinyN];
+        float pg[kTinyN], pu[kTinyN];
+        f32x4_t pk0[kTinyN], pk1[kTinyN];
+#pragma unroll
+        for (int n = 0; n < kTinyN; ++n) {
+            ppar[n] = SMi[192 + n];
+            pg[n] = SMf[320 + n];
+            pu[n] = PUs[n * kF32Rows + r];
+            pk0[n] = *reinterpret_cast<const f32x4_t*>(PKs + n * D + 8 * c);
+            pk1[n] = *reinterpret_cast<const f32x4_t*>(PKs + n * D + 8 * c + 4);
+        }
+        const int a = SMi[256];
+        uint32_t panc[kTinyN], pbad = 0u;
+#pragma unroll
+        for (int n = 0; n < kTinyN; ++n) {
+            int p = ppar[n];
+            const bool bn = p < -1 || p >= n;
+            if (bn) p = -1;
+            uint32_t ap = 0u;
+            bool bp = false;
+#pragma unroll
+            for (int i = 0; i < n; ++i)
+                if (p == i) { ap = panc[i]; bp = (pbad >> i) & 1u; }
+            panc[n] = n < Np ? (ap | (1u << n)) : 0u;
+            if (n < Np && (bn || bp)) pbad |= 1u << n;
+        }
+        uint32_t path = 0u;
+        if (a < -1 || a >= Np) {
+            if (reporter) report(status, TREEWY_EACCEPT);
+        } else if (a >= 0) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int n = 0; n < kTinyN; ++n)
+                if (n == a) m = panc[n];
+            if ((pbad >> a) & 1u) {
+                if (reporter) report(status, TREEWY_ETREE);
+            } else {
+                path = m;
+            }
+        }
+        if (path != 0u) {
+            float ga = 1.0f;
+#pragma unroll
+            for (int n = 0; n < kTinyN; ++n)
+                if (n == a) ga = pg[n];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[e] *= ga;
+#pragma unroll
+            for (int n = 0; n < kTinyN; ++n) {
+                const float cu = ((path >> n) & 1u) ? ga * __builtin_amdgcn_rcpf(pg[n]) * pu[n] : 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sv[e] += cu * pk0[n][e];
+                    sv[4 + e] += cu * pk1[n][e];
+                }
+            }
+            float* dst = cin.S + (static_cast<size_t>(bh) * D + r0 + r) * D + 8 * c;
+            *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{sv[0], sv[1], sv[2], sv[3]};
+            *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{sv[4], sv[5], sv[6], sv[7]};
+        }
+    }
+
+    // ---- partial dot products over the lane's eight columns, summed over the row
+    float kv[kTinyN][8], qv[kTinyN][8];
+#pragma unroll
+    for (int t = 0; t < kTinyN; ++t) {
+        const f32x4_t k0 = *reinterpret_cast<const f32x4_t*>(Ks + t * D + 8 * c);
+        const f32x4_t k1 = *reinterpret_cast<const f32x4_t*>(Ks + t * D + 8 * c + 4);
+        const f32x4_t q0 = *reinterpret_cast<const f32x4_t*>(Qs + t * D + 8 * c);
+        const f32x4_t q1 = *reinterpret_cast<const f32x4_t*>(Qs + t * D + 8 * c + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kv[t][e] = k0[e];
+            kv[t][4 + e] = k1[e];
+            qv[t][e] = q0[e];
+            qv[t][4 + e] = q1[e];
+        }
+    }
+    float P[kTinyN], Y[kTinyN];
+#pragma unroll
+    for (int t = 0; t < kTinyN; ++t) {
+        float p = 0.f, y = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p += sv[e] * kv[t][e];
+            y += sv[e] * qv[t][e];
+        }
+        P[t] = row16_sum(p);
+        Y[t] = row16_sum(y);
+    }
+    // KQ[i][t] = k_i . q_t, KK[t][i] = k_t . k_i from the pair list above
+    auto KQv = [&](int i, int t) {
+        return G[t * (t + 1) / 2 + i];
+    };
+    auto KKv = [&](int t, int i) {
+        return G[10 + (t - 1) * t / 2 + i];
+    };
+
+    // ---- the row's solve and readout, in order (ancestors precede their descendants)
+    float Uv[kTinyN], Ov[kTinyN];
+#pragma unroll
+    for (int t = 0; t < kTinyN; ++t) {
+        Uv[t] = 0.f;
+        Ov[t] = 0.f;
+        if (t < N) {
+            float u = bt[t] * (Vs[t * kF32Rows + r] - g[t] * P[t]);
+#pragma unroll
+            for (int i = 0; i < t; ++i)
+                if ((anc[t] >> i) & 1u)
+                    u -= bt[t] * g[t] * __builtin_amdgcn_rcpf(g[i]) * KKv(t, i) * Uv[i];
+            Uv[t] = u;
+            float o = g[t] * Y[t];
+#pragma unroll
+            for (int i = 0; i <= t; ++i)
+                if ((anc[t] >> i) & 1u)
+                    o += g[t] * __builtin_amdgcn_rcpf(g[i]) * KQv(i, t) * Uv[i];
+            Ov[t] = o;
+        }
+    }
+    if (c < N) {
+        float uo = 0.f, oo = 0.f;
+#pragma unroll
+        for (int t = 0; t < kTinyN; ++t)
+            if (t == c) { uo = Uv[t]; oo = Ov[t]; }
+        const size_t out = (node0 + c) * nstride + h * D + r0 + r;
+        O[out] = oo;
+        U[out] = uo;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // The small-tree verify kernel.  MODE 0 reads S0 as it is.  MODE 1 applies the previous
 // step's commit to S on the way in and writes the committed rows back (see above).  MODE 2
 // defers that write (a step of the log-structured commit, the deferred state writes the
@@ -2939,6 +3284,14 @@ static hipError_t launch_small_fixed(const VerifyArgs& a, const CommitIn& cin, c
 
 template <bool FUSED>
 static hipError_t launch_f32(const VerifyArgs& a, const CommitInF32& cin, hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * kF32Blocks;
+    if (a.N <= kTinyN && (!FUSED || cin.Np <= kTinyN)) {
+        hipLaunchKernelGGL(verify_f32_tiny_kernel<FUSED>, dim3(grid), dim3(kF32Threads), 0, stream,
+                           a.S0, static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
+                           static_cast<const float*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
+                           a.O, a.U, a.gamma, a.anc_out, a.depth_out, a.status, cin);
+        return hipGetLastError();
+    }
     const F32Lds L = f32_lds(a.N);
     auto kern = verify_f32_kernel<FUSED>;
     if (L.bytes > 48u * 1024u) {
@@ -2947,7 +3300,6 @@ static hipError_t launch_f32(const VerifyArgs& a, const CommitInF32& cin, hipStr
                                            static_cast<int>(L.bytes));
         if (e != hipSuccess) return e;
     }
-    const unsigned grid = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * kF32Blocks;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kF32Threads), L.bytes, stream, a.S0,
                        static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
                        static_cast<const float*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N, a.O,

@@ -81,6 +81,76 @@ def test_fused_shapes(N1, tree1, N2, tree2, seed):
     check_fused(P1, P2, gpu, label=f"N_prev={N1} N={N2}")
 
 
+@pytest.mark.parametrize("N1,tree1,N2,tree2,seed", [
+    (4, "chain", 4, "chain", 51),     # the configuration-0 shape: the register-resident form
+    (3, (2, 2), 2, "chain", 52),
+    (1, "chain", 4, (3, 2), 53),
+    (4, (3, 2), 1, "chain", 54),
+    (6, (3, 2), 4, "chain", 55),      # previous tree of 6 nodes: the general fp32 kernel
+    (4, "chain", 5, (3, 2), 56),      # 5 nodes: the general fp32 kernel
+])
+def test_fp32_small_trees(N1, tree1, N2, tree2, seed):
+    """fp32 inputs on trees of up to four nodes (and either side of that bound), fused, with
+    the deepest, no, and the last accepted node among the sequences; every head compared."""
+    say(f"[fused] fp32 N_prev={N1} {tree1} -> N={N2} {tree2}")
+    B, H = 5, 6
+    P1 = inputs.make_custom(seed, B=B, H=H, N=N1, tree=tree1, dtype="f32")
+    d = np.array([inputs.tree_depths(P1.parent[b]) for b in range(B)])
+    acc = P1.accepted.copy()
+    acc[0] = int(np.argmax(d[0]))
+    acc[1] = -1
+    acc[2] = N1 - 1
+    P1 = inputs.Problem(cfg=-1, B=B, H=H, N=N1, dtype=P1.dtype, parent=P1.parent,
+                        accepted=acc.astype(np.int32), layers=P1.layers)
+    P2 = inputs.make_custom(seed + 1000, B=B, H=H, N=N2, tree=tree2, dtype="f32")
+    gpu = run_fused(P1, P2)
+    check_fused(P1, P2, gpu, label=f"fp32 N_prev={N1} N={N2}")
+
+
+@pytest.mark.parametrize("case", ["accepted", "parent_prev", "parent"])
+def test_fp32_small_trees_bad_inputs(case):
+    """The register-resident fp32 form on a bad accepted node, a bad previous parent on the
+    accepted path, or a bad parent in this step's tree: the error is reported on the status
+    word, the offending sequence's state is left as it was (bad accepted node or path), and
+    the other sequences match the oracle."""
+    say(f"[fused] fp32 four-node trees, bad {case}")
+    B, H = 3, 4
+    P1 = inputs.make_custom(57, B=B, H=H, N=4, tree="chain", dtype="f32",
+                            accepted=np.array([3, 2, 3]))
+    P2 = inputs.make_custom(58, B=B, H=H, N=4, tree="chain", dtype="f32")
+    if case == "accepted":
+        acc = P1.accepted.copy()
+        acc[0] = 9
+        P1b = inputs.Problem(cfg=-1, B=B, H=H, N=4, dtype=P1.dtype, parent=P1.parent,
+                             accepted=acc, layers=P1.layers)
+        P2b, want = P2, binding_code("TREEWY_EACCEPT")
+    elif case == "parent_prev":
+        par = P1.parent.copy()
+        par[0, 2] = 3                  # a parent after its child, on node 3's path
+        P1b = inputs.Problem(cfg=-1, B=B, H=H, N=4, dtype=P1.dtype, parent=par,
+                             accepted=P1.accepted, layers=P1.layers)
+        P2b, want = P2, binding_code("TREEWY_ETREE")
+    else:
+        par = P2.parent.copy()
+        par[0, 1] = 2
+        P1b = P1
+        P2b = inputs.Problem(cfg=-1, B=B, H=H, N=4, dtype=P2.dtype, parent=par,
+                             accepted=P2.accepted, layers=P2.layers)
+        want = binding_code("TREEWY_ETREE")
+    gpu = run_fused(P1b, P2b, status_check=False)
+    assert gpu["status"] == want, (gpu["status"], want)
+    if case != "parent":
+        # the offending sequence keeps its state bit for bit
+        assert np.array_equal(gpu["S"][0], P1.layers[0].S0[0])
+    heads = [(b, h) for b in (1, 2) for h in range(H)]
+    check_fused(P1, P2, gpu, heads=heads, label=f"fp32 bad {case}: valid sequences")
+
+
+def binding_code(name):
+    from linear_attention_speculative_head_amd import binding
+    return getattr(binding, name)
+
+
 @pytest.mark.parametrize("N2,dtype", [(32, "bf16"), (64, "bf16"), (6, "f32")])
 def test_unfused_shapes_match(N2, dtype):
     """Every kernel shape under the same contract: the large-tree kernels (bf16, fused) and
