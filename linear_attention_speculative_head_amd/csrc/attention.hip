@@ -36,7 +36,7 @@ namespace {
 constexpr int DA = 256;                     // head dimension
 constexpr int kQB = 32;                     // queries per block (two MFMA column tiles)
 constexpr int kTile = 32;                   // cache rows per step
-constexpr int kTargetBlocks = 1024;         // split the cache until about this many workgroups
+constexpr int kTargetBlocks = 640;          // split the cache until about this many workgroups
 constexpr int kMinSplit = 256;              // but keep at least this many rows per split
 constexpr int kPartFloats = kQB * DA + 2 * kQB;   // O [32][256], m [32], l [32]
 constexpr float kLog2e = 1.4426950408889634f;
