@@ -25,7 +25,7 @@ def _gpu():
     binding.lib()
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2])
 def test_fused_config_full(cfg):
     """Two consecutive draws of a configuration: the fused kernel at full size, every head."""
     say(f"[fused] config {cfg}: {inputs.CONFIGS[cfg]['desc']}")
