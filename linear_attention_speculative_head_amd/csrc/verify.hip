@@ -1018,14 +1018,17 @@ void verify_f32_kernel(
 // r0 + r.  Every lane derives the (tiny) trees from the staged parents itself: ancestor
 // masks in topological order (parents precede children), gates as products.  It commits its
 // eight state values (S_a = g_a S + sum over the path of (g_a / g_i) U_prev[i][r] k_i), takes
-// its partial dot products with the keys and queries (P[t] = S_r . k_t, Y[t] = S_r . q_t,
-// k_t . k_i, k_i . q_t over its eight columns) and sums them over the row's 16 lanes with
-// DPP adds (quad permutes, half-row and row mirrors).  Each row's 16 lanes then hold the
-// whole row of P and Y and the whole Gram matrix and solve the row's nodes in order, in fp32
-// FMAs: U[t] = b_t (v_t - g_t P[t]) - sum over strict ancestors of b_t (g_t/g_i)(k_t.k_i) U[i],
+// its partial dot products with the keys and queries (P[t] = S_r . k_t, Y[t] = S_r . q_t over
+// its eight columns) and sums them over the row's 16 lanes with DPP adds (quad permutes,
+// half-row and row mirrors); the Gram entries k_t . k_i and k_i . q_t, the same for every
+// row, are split over the wave's four rows and read back as wave-uniform values.  Each row's
+// 16 lanes then hold the whole row of P and Y and the whole Gram matrix and solve the row's
+// nodes in order (paper §3, Eq. 2 and the readout), in fp32 FMAs:
+// U[t] = b_t (v_t - g_t P[t]) - sum over strict ancestors of b_t (g_t/g_i)(k_t.k_i) U[i],
 // O[t] = g_t Y[t] + sum over ancestors-or-self of (g_t/g_i)(k_i.q_t) U[i]; lane c = t writes
-// node t's O and U.  No LDS round trip or barrier follows the transfers: at one head the
-// step is a chain of latencies, and this cuts it to one.
+// node t's O and U.  After the transfers the only LDS accesses are batches of operand reads,
+// and no barrier follows: at one head the step is a chain of latencies, and this shortens it
+// to the transfers and a few dependent register phases.
 
 constexpr int kTinyN = 4;                       // nodes (and previous nodes) of this form
 
