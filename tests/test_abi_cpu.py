@@ -144,9 +144,10 @@ def test_deferred_flush_rejects(lib):
 
 def test_attention_workspace_size(lib):
     # (sequence, head, query block) triples x cache splits x one partial; the splits aim at about
-    # 1024 workgroups with at least 256 rows each
+    # 640 workgroups, whole 32-row tiles, with at least 256 rows each (8256 rows over 64
+    # triples: 10 ranges of 832 rows)
     assert lib.treewy_tree_attention_workspace(2, 2, 8, 4, 8192) == 2 * 2 * 1 * 32 * (32 * 256 + 64) * 4
-    assert lib.treewy_tree_attention_workspace(32, 2, 8, 4, 8256) == 32 * 2 * 1 * 16 * (32 * 256 + 64) * 4
+    assert lib.treewy_tree_attention_workspace(32, 2, 8, 4, 8256) == 32 * 2 * 1 * 10 * (32 * 256 + 64) * 4
     assert lib.treewy_tree_attention_workspace(512, 8, 8, 4, 8192) == 512 * 8 * 1 * 1 * (32 * 256 + 64) * 4
     assert lib.treewy_tree_attention_workspace(1, 1, 8, 16, 100) == 1 * 1 * 4 * 1 * (32 * 256 + 64) * 4
     assert lib.treewy_tree_attention_workspace(0, 2, 8, 4, 64) == 0
