@@ -407,7 +407,8 @@ struct CommitIn {
     const int32_t* accepted;                // its accepted node [B], -1 = none
     int Np;                                 // its node count
     int short_path;                         // 17-64 nodes, fused commit: paths up to this
-                                            // long go on the vector ALUs (set at launch)
+                                            // long (0 or 8) go on the vector ALUs (set at
+                                            // launch)
 };
 
 // The deferred commit's log of one step (see the kernel below): per (sequence, head) up to
@@ -2644,9 +2645,9 @@ __device__ __forceinline__ void head_commit_rows(float* lds, const PathInfo& cur
     const float* PG = reinterpret_cast<const float*>(ldsb + L::kPG);
     const float ga = PG[cur.depth - 1];
     if (cur.depth <= cin.short_path) {
-        // a short path (cin.short_path <= 4): the terms on the vector ALUs, in the rows'
-        // arrival layout (lane l: row 16w + 2i + l / 32, 16-byte chunk l % 32, i = 0..7),
-        // which has less latency than the matrix-core form for so few terms
+        // a short path (cin.short_path <= 8, one staged chunk): the terms on the vector ALUs,
+        // in the rows' arrival layout (lane l: row 16w + 2i + l / 32, 16-byte chunk l % 32,
+        // i = 0..7), which has less latency than the matrix-core form for so few terms
         const float* PU = reinterpret_cast<const float*>(ldsb + L::kPU);
         const char* PK = ldsb + L::kPK;
         const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
@@ -2658,7 +2659,7 @@ __device__ __forceinline__ void head_commit_rows(float* lds, const PathInfo& cur
             x[i] = ga * *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 8; ++q) {
             if (q >= cur.depth) break;
             const float cq = ga * __builtin_amdgcn_rcpf(PG[q]);
             const uint2 kw = *reinterpret_cast<const uint2*>(
@@ -3338,12 +3339,12 @@ static hipError_t launch_head(const VerifyArgs& a, hipStream_t stream, const Com
     const int BH = a.B * a.H;
     const int cus = device_cu_count();          // one workgroup per CU (LDS)
     const int grid = BH < cus ? BH : cus;
-    // the fused commit of a path of up to four nodes: on the vector ALUs (less latency)
+    // the fused commit of a path of up to eight nodes: on the vector ALUs (less latency)
     // unless each workgroup has at least 32 heads, where the matrix-core form measured faster
     // (B256 x H64 32-node trees 604 -> 599 us; B128 x H32 64-node trees 217 -> 219 us and
     // B32 x H32 21-node trees 41.4 -> 43.5 us the other way)
     CommitIn c = cin ? *cin : CommitIn{};
-    c.short_path = BH < 32 * cus ? 4 : 0;
+    c.short_path = BH < 32 * cus ? 8 : 0;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kHeadThreads), L::kBytes, stream, a.S0,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.alpha, a.beta, a.parent, a.H, a.N,
