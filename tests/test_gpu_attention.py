@@ -86,6 +86,27 @@ def test_configuration_one_shape():
     check(P, O, "B32 chain-4")
 
 
+def test_benchmark_shape_full_prefix():
+    """The benchmark's launch at 8192 committed rows (B=32, 2 KV heads x 8 query heads, chain
+    of 4: ten cache ranges per (sequence, KV head), the last one ragged), three sequences
+    compared with the oracle (which is run on those alone)."""
+    say("[attention] B=32 chain-4 at 8192 committed rows, sequences 0, 13, 31")
+    P = inputs.make_attention_problem(12, B=32, N=4, T_max=8200, ctx=np.full(32, 8192))
+    O, _ = run_attention(P)
+    from oracle import attention as att
+    sel = np.array([0, 13, 31])
+    ref = att.tree_attention(P.Kc[sel], P.Vc[sel], P.ctx[sel], P.Qd[sel], P.Kd[sel], P.Vd[sel],
+                             P.parent[sel], P.G)
+    assert np.all(np.isfinite(O[sel])), "non-finite outputs"
+    worst = 0.0
+    for i, b in enumerate(sel):
+        for hq in range(P.Hq):
+            e = np.abs(O[b, :, hq] - ref[i, :, hq]).max() / np.abs(ref[i, :, hq]).max()
+            worst = max(worst, e)
+            assert e <= TOL, f"b={b} hq={hq} rel err {e:.3e}"
+    say(f"  worst head-wise rel err {worst:.2e}")
+
+
 @pytest.mark.parametrize("N,node,bad", [(5, 3, 4), (40, 35, 39), (40, 2, -5)])
 def test_malformed_tree_is_reported(N, node, bad):
     """A parent outside [-1, t-1] is reported; the node then counts as a root of the draft
