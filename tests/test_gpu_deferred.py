@@ -250,6 +250,77 @@ def test_deferred_long_log_meets_large_tree(n_big, kept):
     assert e.max() <= TOL, f"flushed state: worst {e.max():.3e}"
 
 
+def test_deferred_config4_sampled():
+    """The deferred step at the benchmark's configuration-4 launch (B256 x H64, 32-node trees,
+    64 heads per workgroup, the commit on the matrix cores), four steps with Lmax 8: the log
+    lengths of every sequence against the header rule, O and U of 48 sampled heads (spread
+    over the persistent grid's rounds) against the oracle each step, and the flushed state of
+    those heads after the last step."""
+    import torch
+    import oracle
+    from linear_attention_speculative_head_amd import binding, device
+    say("[deferred] config 4 full size, 4 steps, Lmax 8, 48 sampled heads")
+    Lmax = 8
+    steps = [inputs.make_problem(4, instance=s, layers=1) for s in range(4)]
+    B, H = steps[0].B, steps[0].H
+    rng = np.random.default_rng(7)
+    hid = np.unique(np.concatenate([[0, B * H - 1], rng.choice(B * H, 46, replace=False)]))
+    heads = [(int(x) // H, int(x) % H) for x in hid]
+    hb = np.array([x[0] for x in heads])
+    hh = np.array([x[1] for x in heads])
+    # GPU: a plain verify of step 0, then deferred steps, then a flush
+    dls = [device.upload_layer(P.layers[0], P.dtype) for P in steps]
+    trees = [device.upload_tree(P) for P in steps]
+    outs = [device.alloc_outputs(B, H, P.N) for P in steps[:2]]
+    log = device.alloc_log(B, H, Lmax)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S = dls[0].S0.clone()
+    d0 = dls[0]
+    binding.treewy_verify(S, d0.Q, d0.K, d0.V, d0.alpha, d0.beta, trees[0][0],
+                          outs[0].O, outs[0].U, outs[0].gamma, status=status)
+    gpu = []
+    for s_ in range(1, len(steps)):
+        prev, cur = outs[(s_ - 1) % 2], outs[s_ % 2]
+        dp, dc = dls[s_ - 1], dls[s_]
+        si, so, li, lo = log.headers()
+        binding.treewy_commit_verify_deferred(S, log.U, log.K, si, so, li, lo, prev.U, dp.K,
+                                              prev.gamma, trees[s_ - 1][0], trees[s_ - 1][1],
+                                              dc.Q, dc.K, dc.V, dc.alpha, dc.beta, trees[s_][0],
+                                              cur.O, cur.U, cur.gamma, status=status)
+        log.flip()
+        torch.cuda.synchronize()
+        ti_b = torch.from_numpy(hb).cuda()
+        ti_h = torch.from_numpy(hh).cuda()
+        gpu.append(dict(O=cur.O[ti_b, :, ti_h].cpu().numpy(), U=cur.U[ti_b, :, ti_h].cpu().numpy(),
+                        len=log.headers()[2].cpu().numpy().copy()))
+    si, so, li, lo = log.headers()
+    binding.treewy_deferred_flush(S, log.U, log.K, si, so, li, lo, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
+    S_flushed = S[torch.from_numpy(hb).cuda(), torch.from_numpy(hh).cuda()].cpu().numpy()
+    # oracle on the sampled heads only, the committed state carried from step to step
+    want_len = expected_lengths(steps, Lmax)
+    S_ref = steps[0].layers[0].S0.copy()
+    for s_, P in enumerate(steps):
+        L = P.layers[0]
+        layer = inputs.Layer(S0=S_ref, q=L.q, k=L.k, v=L.v, alpha=L.alpha, beta=L.beta)
+        r = oracle.batch(layer, P.parent, P.accepted, heads=heads, commit=True)
+        if s_ > 0:
+            g = gpu[s_ - 1]
+            for key in ("O", "U"):
+                e = headwise_rel(g[key].astype(np.float64), r[key])
+                assert e.max() <= TOL, f"step {s_} {key}: worst {e.max():.3e}"
+            assert np.array_equal(g["len"], want_len[s_]), f"step {s_} lengths"
+        if s_ == len(steps) - 1:
+            break                       # the flush holds the state committed before this step
+        S_new = r["S_new"].reshape(len(heads), 128, 128).astype(np.float32)
+        S_ref = S_ref.copy()
+        S_ref[hb, hh] = S_new
+    e = headwise_rel(S_flushed.astype(np.float64), S_ref[hb, hh].astype(np.float64))
+    say(f"  flushed state worst head-wise rel err {e.max():.2e}")
+    assert e.max() <= TOL, f"flushed state: worst {e.max():.3e}"
+
+
 def test_deferred_rejects_unsupported_shapes():
     """fp32 inputs have no deferred commit."""
     import torch
