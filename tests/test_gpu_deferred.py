@@ -250,18 +250,20 @@ def test_deferred_long_log_meets_large_tree(n_big, kept):
     assert e.max() <= TOL, f"flushed state: worst {e.max():.3e}"
 
 
-def test_deferred_config4_sampled():
-    """The deferred step at the benchmark's configuration-4 launch (B256 x H64, 32-node trees,
-    64 heads per workgroup, the commit on the matrix cores), four steps with Lmax 8: the log
-    lengths of every sequence against the header rule, O and U of 48 sampled heads (spread
-    over the persistent grid's rounds) against the oracle each step, and the flushed state of
-    those heads after the last step."""
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_deferred_full_size_sampled(cfg):
+    """The deferred step at the benchmark's launches (configuration 3: B128 x H32, 64-node
+    trees, eight staged terms, write-backs over two chunks; configuration 4: B256 x H64,
+    32-node trees, 64 heads per workgroup), four steps with Lmax 8: the log lengths of every
+    sequence against the header rule, O and U of 48 sampled heads (spread over the persistent
+    grid's rounds) against the oracle each step, and the flushed state of those heads after
+    the last step."""
     import torch
     import oracle
     from linear_attention_speculative_head_amd import binding, device
-    say("[deferred] config 4 full size, 4 steps, Lmax 8, 48 sampled heads")
+    say(f"[deferred] config {cfg} full size, 4 steps, Lmax 8, 48 sampled heads")
     Lmax = 8
-    steps = [inputs.make_problem(4, instance=s, layers=1) for s in range(4)]
+    steps = [inputs.make_problem(cfg, instance=s, layers=1) for s in range(4)]
     B, H = steps[0].B, steps[0].H
     rng = np.random.default_rng(7)
     hid = np.unique(np.concatenate([[0, B * H - 1], rng.choice(B * H, 46, replace=False)]))
