@@ -233,6 +233,33 @@ __device__ __forceinline__ void dma_rows_x8(const void* base, const uint32_t (&v
 }
 #undef TREEWY_ROWS_X8
 
+// Two HBM -> LDS loads of 16 bytes per lane: lane l's bytes from base + voff0 land at LDS
+// byte lds0 + 16 l, those from base + voff1 at lds0 + 1024 + 16 l.  lds0 and base are
+// wave-uniform.
+template <bool NT>
+__device__ __forceinline__ void dma_rows_x2(const void* base, uint32_t voff0, uint32_t voff1,
+                                            uint32_t lds0) {
+    uint32_t save;
+    if constexpr (NT)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %3, %5 nt\n\t"
+            "s_mov_b32 m0, %2\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %4, %5 nt\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(save)
+            : "s"(lds0), "s"(lds0 + 1024u), "v"(voff0), "v"(voff1), "s"(base)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %3, %5\n\t"
+            "s_mov_b32 m0, %2\n\t" "s_nop 0\n\t" "global_load_lds_dwordx4 %4, %5\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(save)
+            : "s"(lds0), "s"(lds0 + 1024u), "v"(voff0), "v"(voff1), "s"(base)
+            : "memory");
+}
+
 // A pointer that is the same in every lane, kept in scalar registers (the compiler cannot
 // always prove it uniform).
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
@@ -326,6 +353,31 @@ __device__ __forceinline__ void small_issue_s0(const float* S0, float* buf, int 
     }
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf + 16 * wave * D));
     dma_rows_x8<NT>(src, voff, lds0);
+}
+
+// Part of an item's S rows -> LDS, in the layout of small_issue_s0: wave w's row pairs
+// i0 .. i0 + 2 n - 1 (pair i: rows 16w + 2i and 16w + 2i + 1, one whole row per half-wave),
+// two pairs per dma_rows_x2.  The kernels that request their next item's rows during the
+// current one split the request into such parts, spread over the item: issued at once, the
+// eight transfers of a wave stall its issue (the CU's queue of vector-memory requests is
+// full) while the other phases wait for it; in parts they queue behind work that does not.
+template <bool NT>
+__device__ __forceinline__ void issue_s_pairs(const float* S0, uint32_t lds_addr, int bh, int part,
+                                              int i0, int n, int wave, int lane) {
+    const void* src = uniform_ptr(reinterpret_cast<const char*>(S0) +
+                                  (static_cast<size_t>(bh) * D + part * kSmallRows) * D *
+                                      sizeof(float));
+    const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
+    const uint32_t slot = static_cast<uint32_t>(lane) & 31u;
+    for (int j = 0; j < n; ++j) {
+        const uint32_t i = static_cast<uint32_t>(i0 + 2 * j);
+        const uint32_t r0 = 16u * wave + 2u * i + hl;
+        const uint32_t voff0 = r0 * (D * 4u) + 16u * (slot ^ ((2u * i + hl) & 15u));
+        const uint32_t voff1 = (r0 + 2u) * (D * 4u) + 16u * (slot ^ ((2u * i + 2u + hl) & 15u));
+        const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+            lds_addr + 16u * static_cast<uint32_t>(wave) * D * 4u + 1024u * i);
+        dma_rows_x2<NT>(src, voff0, voff1, lds0);
+    }
 }
 
 // The rest of an item's inputs -> LDS, as a list of whole-wave transfers dealt round-robin
@@ -1724,7 +1776,7 @@ void verify_small_kernel(
         lds_barrier();                              // operands read and G visible: refill
         ++round;
         if (more && !TWO) {
-            small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
+            issue_s_pairs<FUSED>(S0, lds_addr, bh_n, part_n, 0, 2, wave, lane);   // half the rows
             if constexpr (FUSED) {
                 // item i + 1's inputs and path rows; item i + 2's accepted node and tree
                 int bh_2, part_2;
@@ -1782,6 +1834,9 @@ void verify_small_kernel(
             Uv[e] = b_t * vv[e] - bg_t * acc[0][e];  // R[t] = b_t (v_t - g_t S0 k_t)
             Ov[e] = gg_t * Yv[e];                    // g_t S0 q_t
         }
+
+        if (more && !TWO)                           // the other half of the next item's rows
+            issue_s_pairs<FUSED>(S0, lds_addr, bh_n, part_n, 4, 2, wave, lane);
 
         // One walk down the ancestors serves both the forward substitution and the readout:
         // at step d the depth-d ancestor a of t is final (its own terms ended at step d - 1),
@@ -2118,7 +2173,7 @@ void verify_large_kernel(
         // every wave is past the contractions
         lds_barrier();                              // G visible to every wave; inputs read
         if (more) {
-            small_issue_s0<false>(S0, lds, bh_n, part_n, wave, lane);
+            issue_s_pairs<false>(S0, lds_addr, bh_n, part_n, 0, 2, wave, lane);   // half the rows
             large_prefetch<NKT>(pf, V, alpha, beta, parent, H, N, bh_n, part_n, wave, lane);
         }
 
@@ -2207,6 +2262,8 @@ void verify_large_kernel(
                 }
             }
         }
+        if (more)                                   // the other half of the next item's rows
+            issue_s_pairs<false>(S0, lds_addr, bh_n, part_n, 4, 2, wave, lane);
         // the node's own term; then O and U out as whole half-rows (the item's 64 values of
         // a node, 256 bytes), assembled in the U exchange: a wave's own stores would cover
         // only 64 bytes of each
@@ -2235,7 +2292,8 @@ void verify_large_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Trees of 33 to 64 nodes, one head per item (NKT = 3 node tiles up to 48 nodes, 4 above).
+// One head per item: the fused and deferred steps on 17 to 64 nodes, the plain verify on 33
+// to 64 (NKT = 2 node tiles up to 32 nodes, 3 up to 48, 4 above).
 //
 // A workgroup of eight waves takes whole heads (all 128 value rows; wave w owns rows
 // 16w..16w+15), one workgroup per CU, and walks a run of consecutive heads, so the heads
@@ -2244,11 +2302,12 @@ void verify_large_kernel(
 // each head only forms its own gates g_t as products over the cached jump targets.
 //
 // Every input of head i + 1 is requested during head i, by direct HBM -> LDS transfers
-// into areas that head i no longer needs: its S rows as soon as head i's rows are in
-// registers (after the commit and the operand split), the previous step's path rows for its
-// commit right after, its key, query and value rows, parents and gates once head i's
-// contractions are done.  So a head finds its inputs in place, and no register carries
-// them across a head.
+// into areas that head i no longer needs: its S rows once head i's rows are in registers
+// (after the commit and the operand split), in four quarters spread over head i (after the
+// split, after the Gram tiles, after the contractions, with the other inputs; see
+// issue_s_pairs), the previous step's path rows for its commit with the first quarter, its
+// key, query and value rows, parents and gates once head i's contractions are done.  So a
+// head finds its inputs in place, and no register carries them across a head.
 //
 // The key/query rows are staged once per head for all eight waves.  The Gram entries the
 // solve uses (key . key below the diagonal, key . query above it) are formed on the matrix
@@ -2957,9 +3016,9 @@ void verify_head_kernel(
         }
         lds_barrier();                        // S rows and path rows read: both may be refilled
 
-        // ---- the next head's S rows and path rows
+        // ---- the next head's S rows (the first quarter) and path rows
         if (more) {
-            small_issue_s0<FUSED>(S0, lds, bh + 1, 0, wave, lane);
+            issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 0, 1, wave, lane);
             if constexpr (FUSED) {
                 if ((bh + 1) / H != b) {
                     const int pidx = lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L::kPI)[lane] : -1;
@@ -3048,6 +3107,8 @@ void verify_head_kernel(
             }
         }
 
+        if (more) issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 2, 1, wave, lane);
+
         // ---- contractions P = S K^T, Y = S Q^T on this wave's 16 rows (columns of nodes
         // past N come out of whatever those rows hold and are never used)
         f32x4_t acc[NCT];
@@ -3066,6 +3127,7 @@ void verify_head_kernel(
                 acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bv[ks], acc[c], 0, 0, 0);
             }
         }
+        if (more) issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 4, 1, wave, lane);
         // this head's values: v of node 16 kt + col, rows 16 w + 4 grp .. +3
         uint2 vraw[NKT];
         {
@@ -3080,9 +3142,10 @@ void verify_head_kernel(
         lds_barrier();                        // coefficients visible; key/query/value rows,
                                               // parents and gates read
 
-        // ---- the next head's key/query/value rows, parents and gates (and, fused, the
-        // previous tree of the head after it)
+        // ---- the next head's last S-row quarter, key/query/value rows, parents and gates
+        // (and, fused, the previous tree of the head after it)
         if (more) {
+            issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 6, 1, wave, lane);
             head_issue_inputs<NKT>(Q, K, V, alpha, beta, parent, H, N, bh + 1, wave, lane, lds_addr);
             if constexpr (FUSED) {
                 if (bh + 2 < hi && wave == kHeadWaves - 1)
