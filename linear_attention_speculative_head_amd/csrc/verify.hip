@@ -2346,6 +2346,8 @@ constexpr int kVmcnt8 = 8 | (7 << 4) | (15 << 8);
 //       head's sequence
 //   LN, LS  deferred commit: the log length of that sequence and the next head's log scale
 //       (one word each, repeated)
+//   O   (NKT = 2 only, where the LDS has room) an O exchange beside the U one, so that the
+//       O rows are assembled while the U rows are and both leave after one barrier
 template <int NKT>
 struct HeadLds {
     static constexpr int kNodes = 16 * NKT;
@@ -2364,7 +2366,9 @@ struct HeadLds {
     static constexpr uint32_t kPA = kPI + 256u;
     static constexpr uint32_t kLN = kPA + 256u;
     static constexpr uint32_t kLS = kLN + 256u;
-    static constexpr uint32_t kBytes = kLS + 256u;
+    static constexpr bool kOwnO = NKT == 2;
+    static constexpr uint32_t kO = kLS + 256u;
+    static constexpr uint32_t kBytes = kO + (kOwnO ? kHeadWaves * kNodes * 16u * 4u : 0u);
     static_assert(kBytes <= 160u * 1024u, "one workgroup per CU");
     // s_waitcnt operand: vmcnt <= 2 NKT (the previous head's NKT O and NKT U row stores per
     // wave), no other wait
@@ -2768,10 +2772,10 @@ __device__ __forceinline__ void head_commit_rows(float* lds, const PathInfo& cur
 // hint.
 template <int NKT>
 __device__ __forceinline__ void head_store_rows(float* dst, const char* ldsb, int H, int N,
-                                                int wave, int lane) {
+                                                int wave, int lane, uint32_t area = HeadLds<NKT>::kU) {
     using L = HeadLds<NKT>;
     static_assert(L::kNodes == 2 * NKT * kHeadWaves, "2 NKT nodes per wave");
-    const float* Ub = reinterpret_cast<const float*>(ldsb + L::kU);
+    const float* Ub = reinterpret_cast<const float*>(ldsb + area);
     const uint32_t span = static_cast<uint32_t>(((N - 1) * H + 1) * D * sizeof(float));
     const int c = lane & 31;
 #pragma unroll
@@ -3275,15 +3279,26 @@ void verify_head_kernel(
             for (int e = 0; e < 4; ++e) Ov[kt][e] += cw * Uv[kt][e];
         }
         const size_t row0 = (node0 * H + h) * D;
-        lds_barrier();                        // every wave's U rows are in its exchange area
-        head_store_rows<NKT>(U + row0, ldsb, H, N, wave, lane);
-        lds_barrier();                        // ... and have been read
+        if constexpr (L::kOwnO) {
+            float* Os = reinterpret_cast<float*>(ldsb + L::kO) + wave * (NN * 16);
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-            *reinterpret_cast<f32x4_t*>(Us + (16 * kt + col) * 16 + 4 * grp) =
-                f32x4_t{Ov[kt][0], Ov[kt][1], Ov[kt][2], Ov[kt][3]};
-        lds_barrier();                        // O rows in the exchange
-        head_store_rows<NKT>(O + row0, ldsb, H, N, wave, lane);
+            for (int kt = 0; kt < NKT; ++kt)
+                *reinterpret_cast<f32x4_t*>(Os + (16 * kt + col) * 16 + 4 * grp) =
+                    f32x4_t{Ov[kt][0], Ov[kt][1], Ov[kt][2], Ov[kt][3]};
+            lds_barrier();                    // every wave's U and O rows in their exchanges
+            head_store_rows<NKT>(U + row0, ldsb, H, N, wave, lane);
+            head_store_rows<NKT>(O + row0, ldsb, H, N, wave, lane, L::kO);
+        } else {
+            lds_barrier();                    // every wave's U rows are in its exchange area
+            head_store_rows<NKT>(U + row0, ldsb, H, N, wave, lane);
+            lds_barrier();                    // ... and have been read
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+                *reinterpret_cast<f32x4_t*>(Us + (16 * kt + col) * 16 + 4 * grp) =
+                    f32x4_t{Ov[kt][0], Ov[kt][1], Ov[kt][2], Ov[kt][3]};
+            lds_barrier();                    // O rows in the exchange
+            head_store_rows<NKT>(O + row0, ldsb, H, N, wave, lane);
+        }
         if (!more) break;
         ++bh;
     }
