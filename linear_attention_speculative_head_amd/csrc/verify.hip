@@ -1668,8 +1668,8 @@ void verify_small_kernel(
 
         // ---- MFMA operands of this wave's 16 rows (committed, with FUSED), split into bf16
         //      hi and lo: lane L takes row 16w + L % 16, values 32 ks + 8 (L / 16) .. +7.
-        //      With two input sets the rows are taken here, and the wave's rows of the next
-        //      item are requested at once.
+        //      With two input sets the rows are taken here, and half of the wave's rows of
+        //      the next item are requested at once (the other half before the walk).
         bf16x8_t ahi[4], alo[4];
         auto take_rows = [&]() {
             const int r = 16 * wave + col;
@@ -1686,7 +1686,7 @@ void verify_small_kernel(
             take_rows();
             if (more) {
                 __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);   // this wave's reads of its rows
-                small_issue_s0<FUSED>(S0, lds, bh_n, part_n, wave, lane);
+                issue_s_pairs<FUSED>(S0, lds_addr, bh_n, part_n, 0, 2, wave, lane);   // half the rows
             }
         }
 
@@ -1835,7 +1835,7 @@ void verify_small_kernel(
             Ov[e] = gg_t * Yv[e];                    // g_t S0 q_t
         }
 
-        if (more && !TWO)                           // the other half of the next item's rows
+        if (more)                                   // the other half of the next item's rows
             issue_s_pairs<FUSED>(S0, lds_addr, bh_n, part_n, 4, 2, wave, lane);
 
         // One walk down the ancestors serves both the forward substitution and the readout:
