@@ -1424,6 +1424,66 @@ void verify_f32_tiny_kernel(
 // committed rows to S and empties the log.  Header words go to separate output buffers, so
 // no item can see another item's update of the same sequence within one launch.
 
+// Up to 16 rank-one terms applied to this wave's 16 state rows of an item, on the matrix
+// cores: rows 16w .. 16w + 15 of the item's S rows in LDS (chunk c of row r at c ^ (r % 16))
+// become c0 * S + sum_k coef_k u_k k_k^T, with u_k the item's 64 values of term k (fp32 rows
+// of kSmallRows at byte u_area + 4 kSmallRows k) and k_k its key row (bf16, 256-byte rows at
+// byte k_area + 256 k, k < k_rows).  Lane (g, n) = (lane / 16, lane % 16) supplies terms
+// 4g .. 4g + 3 (coef[t] for term 4g + t) of row 16w + n; terms from cnt on count as zero.
+// Per 16-column tile one pair of v_mfma_f32_16x16x16_bf16: A = the key rows read transposed
+// out of LDS (ds_read_b64_tr_b16), B = the coefficient-scaled values split into bf16 hi and lo
+// (an fp32-grade product), C = the rows themselves.
+__device__ __forceinline__ void small_apply_terms(float* lds, uint32_t lds_addr, int cnt,
+                                                  const float (&coef)[4], float c0,
+                                                  uint32_t u_area, uint32_t k_area, int k_rows,
+                                                  int wave, int lane) {
+    const int g = lane >> 4;
+    const int n = lane & 15;
+    const int r = 16 * wave + n;
+    const float* PU = reinterpret_cast<const float*>(reinterpret_cast<const char*>(lds) + u_area);
+    f32x4_t u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int k = 4 * g + t;
+        u[t] = k < cnt ? coef[t] * PU[k * kSmallRows + r] : 0.f;
+    }
+    // the key row this lane addresses (clamped into the staged rows; masked below) and its
+    // 8 bytes of each tile: chunk 2 jt + (n % 4) / 2 of the row, half n % 2
+    const int qrow = 4 * g + (n >> 2) < k_rows ? 4 * g + (n >> 2) : 0;
+    const uint32_t arow = lds_addr + k_area + 256u * static_cast<uint32_t>(qrow) + 8u * static_cast<uint32_t>(n & 1);
+    const uint32_t h2 = static_cast<uint32_t>(n & 3) >> 1;
+    // every read first (the writes below may alias them as far as the compiler knows)
+    i16x4_t ak[D / 16];
+    f32x4_t c[D / 16];
+#pragma unroll
+    for (int jt = 0; jt < D / 16; ++jt)
+        ak[jt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(
+            static_cast<uintptr_t>(arow + 16u * (2u * jt + h2))));
+#pragma unroll
+    for (int jt = 0; jt < D / 16; ++jt)
+        c[jt] = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * ((4 * jt + g) ^ (r & 15)));
+    const bf16x4_t uh = __builtin_convertvector(u, bf16x4_t);
+    const u32x2_t hw = __builtin_bit_cast(u32x2_t, uh);
+    const f32x4_t rem = {u[0] - __uint_as_float(hw[0] << 16), u[1] - __uint_as_float(hw[0] & 0xffff0000u),
+                         u[2] - __uint_as_float(hw[1] << 16), u[3] - __uint_as_float(hw[1] & 0xffff0000u)};
+    const i16x4_t bh = __builtin_bit_cast(i16x4_t, uh);
+    const i16x4_t bl = __builtin_bit_cast(i16x4_t, __builtin_convertvector(rem, bf16x4_t));
+    const uint32_t m0 = (4 * g < cnt ? 0x0000ffffu : 0u) | (4 * g + 1 < cnt ? 0xffff0000u : 0u);
+    const uint32_t m1 = (4 * g + 2 < cnt ? 0x0000ffffu : 0u) | (4 * g + 3 < cnt ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int jt = 0; jt < D / 16; ++jt) {
+        u32x2_t aw = __builtin_bit_cast(u32x2_t, ak[jt]);
+        aw[0] &= m0;
+        aw[1] &= m1;
+        const i16x4_t am = __builtin_bit_cast(i16x4_t, aw);
+        c[jt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bh, c0 * c[jt], 0, 0, 0);
+        c[jt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bl, c[jt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int jt = 0; jt < D / 16; ++jt)
+        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * ((4 * jt + g) ^ (r & 15))) = c[jt];
+}
+
 // NFIX > 0: a form compiled for trees of exactly NFIX nodes (every mode on up to 8 nodes),
 // whose LDS offsets, loop bounds and pointer-jumping rounds are constants; 0: N at run time.
 template <int NCT, int MODE, int NFIX = 0>
@@ -1441,6 +1501,10 @@ void verify_small_kernel(
     constexpr bool FUSED = MODE != 0;
     constexpr bool DEFER = MODE == 2;
     constexpr bool TWO = small_two_sets(NCT, MODE); // two input sets, early refills
+    // the deferred commit's terms on the matrix cores (small_apply_terms) on 9-16 nodes; on up
+    // to 8 the vector-ALU form (the product's registers would spill at this kernel's budget
+    // of three waves per SIMD)
+    constexpr bool kMatrixDefer = DEFER && NCT == 2;
     constexpr int kGP = 16 * NCT;                   // G row pitch
     extern __shared__ __align__(16) float lds[];
     const SmallLds L = small_lds(N, NCT, MODE, DEFER ? dlog.Lmax : 0);
@@ -1562,14 +1626,60 @@ void verify_small_kernel(
                 // k_i^T (MODE 1: no log, gs = g_a), applied to this wave's 16 rows where they
                 // sit in LDS, in the layout they arrived in (lane l: row 16w + 2i + l / 32,
                 // 16-byte chunk l % 32, for i = 0..7), and written back to HBM from there when
-                // flushing: every store is two whole 512-byte rows.  The path's gammas are in
-                // LDS in path order (a is last).
+                // flushing: every store is two whole 512-byte rows (the deferred form on 9-16
+                // nodes applies the terms with small_apply_terms instead).  The path's gammas
+                // are in LDS in path order (a is last).
                 const float* PU = reinterpret_cast<const float*>(ldsb + sb + L.pu);
                 const char* PK = ldsb + sb + L.pk;
                 const uint32_t hl = static_cast<uint32_t>(lane) >> 5;
                 const uint32_t ch = static_cast<uint32_t>(lane) & 31u;   // values 4 ch .. 4 ch + 3
                 const int nchunk = cur.depth > 0 ? (cur.depth + L.path - 1) / L.path : 1;
-                for (int ci = 0; ci < nchunk; ++ci) {
+                if constexpr (kMatrixDefer) {
+                    // the log's terms (one product: at most 16), then the path's, per chunk,
+                    // on the matrix cores; the first product also scales S by gs
+                    const int g = lane >> 4;
+                    bool scaled = false;
+                    if (len > 0) {
+                        const float coef[4] = {gs, gs, gs, gs};
+                        small_apply_terms(lds, lds_addr, len, coef, gs, sb + L.lu, sb + L.lk,
+                                          4 * ((dlog.Lmax + 3) / 4), wave, lane);
+                        scaled = true;
+                    }
+                    for (int ci = 0; ci < (cur.depth > 0 ? nchunk : 0); ++ci) {
+                        const int q0 = ci * L.path;
+                        if (ci > 0) {
+                            // a path longer than one chunk: the next chunk, with a blocking wait
+                            lds_barrier();
+                            fused_issue_path(cin, cur, ci, bh, part, H, wave, lane, lds_addr + sb, L);
+                            __builtin_amdgcn_s_waitcnt(0);
+                            lds_barrier();
+                        }
+                        const int rem = cur.depth - q0;
+                        const int cnt = rem < L.path ? rem : L.path;
+                        float coef[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int q = q0 + 4 * g + t;
+                            coef[t] = ga * __builtin_amdgcn_rcpf(PG[q < 64 ? q : 0]);
+                        }
+                        small_apply_terms(lds, lds_addr, cnt, coef, scaled ? 1.0f : gs,
+                                          sb + L.pu, sb + L.pk, L.path, wave, lane);
+                        scaled = true;
+                    }
+                    if (flush) {
+                        // the committed rows back to HBM as whole rows (this wave's own rows,
+                        // written by its products above)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const uint32_t r = 16u * wave + 2u * i + hl;
+                            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * (ch ^ (r & 15u)));
+                            __builtin_nontemporal_store(
+                                x, reinterpret_cast<f32x4_t*>(
+                                       cin.S + (static_cast<size_t>(bh) * D + part * kSmallRows + r) * D + 4 * ch));
+                        }
+                    }
+                }
+                for (int ci = 0; ci < (kMatrixDefer ? 0 : nchunk); ++ci) {
                     const int q0 = ci * L.path;
                     if (ci > 0) {
                         // a path longer than one chunk: the next chunk, with a blocking wait
