@@ -137,6 +137,8 @@ def expected_lengths(steps, Lmax):
     (32, (6, 4), 12, 7, 74, 3, 8),
     (64, "chain", 8, 5, 71, 3, 4),     # deep paths: flushes over several chunks of terms
     (24, "chain", 8, 5, 72, 3, 4),
+    (16, "chain", 16, 6, 75, 3, 4),    # 9-16 nodes, deep paths: two staged chunks of 8
+    (12, (4, 3), 16, 7, 76, 5, 4),     # 9-16 nodes: a log of up to 16 terms in one product
 ])
 def test_deferred_steps(N, tree, Lmax, nsteps, seed, B, H):
     say(f"[deferred] N={N} tree={tree} Lmax={Lmax} steps={nsteps} B={B} H={H}")
