@@ -2415,7 +2415,7 @@ void verify_large_kernel(
 // into areas that head i no longer needs: its S rows once head i's rows are in registers
 // (after the commit and the operand split), in four quarters spread over head i (after the
 // split, after the Gram tiles, after the contractions, with the other inputs; see
-// issue_s_pairs), the previous step's path rows for its commit with the first quarter, its
+// issue_s_pairs; the plain verify in two halves), the previous step's path rows for its commit with the first quarter, its
 // key, query and value rows, parents and gates once head i's contractions are done.  So a
 // head finds its inputs in place, and no register carries them across a head.
 //
@@ -2996,6 +2996,10 @@ void verify_head_kernel(
     using L = HeadLds<NKT>;
     constexpr int NCT = 2 * NKT;
     constexpr int NN = L::kNodes;
+    // the next head's S rows go out in four parts with the commit (fused), in two halves
+    // without (after the split and after the contractions: measured 173 -> 170 us per
+    // 64-node layer, where four parts suit the fused step)
+    constexpr int kSParts = FUSED ? 4 : 2;
     extern __shared__ __align__(16) float lds[];
     char* ldsb = reinterpret_cast<char*>(lds);
     const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
@@ -3132,7 +3136,7 @@ void verify_head_kernel(
 
         // ---- the next head's S rows (the first quarter) and path rows
         if (more) {
-            issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 0, 1, wave, lane);
+            issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 0, kSParts == 4 ? 1 : 2, wave, lane);
             if constexpr (FUSED) {
                 if ((bh + 1) / H != b) {
                     const int pidx = lane < cin.Np ? reinterpret_cast<const int*>(ldsb + L::kPI)[lane] : -1;
@@ -3221,7 +3225,9 @@ void verify_head_kernel(
             }
         }
 
-        if (more) issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 2, 1, wave, lane);
+        if constexpr (kSParts == 4) {
+            if (more) issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 2, 1, wave, lane);
+        }
 
         // ---- contractions P = S K^T, Y = S Q^T on this wave's 16 rows (columns of nodes
         // past N come out of whatever those rows hold and are never used)
@@ -3241,7 +3247,7 @@ void verify_head_kernel(
                 acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bv[ks], acc[c], 0, 0, 0);
             }
         }
-        if (more) issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 4, 1, wave, lane);
+        if (more) issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 4, kSParts == 4 ? 1 : 2, wave, lane);
         // this head's values: v of node 16 kt + col, rows 16 w + 4 grp .. +3
         uint2 vraw[NKT];
         {
@@ -3259,7 +3265,7 @@ void verify_head_kernel(
         // ---- the next head's last S-row quarter, key/query/value rows, parents and gates
         // (and, fused, the previous tree of the head after it)
         if (more) {
-            issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 6, 1, wave, lane);
+            if constexpr (kSParts == 4) issue_s_pairs<FUSED>(S0, lds_addr, bh + 1, 0, 6, 1, wave, lane);
             head_issue_inputs<NKT>(Q, K, V, alpha, beta, parent, H, N, bh + 1, wave, lane, lds_addr);
             if constexpr (FUSED) {
                 if (bh + 2 < hi && wave == kHeadWaves - 1)
