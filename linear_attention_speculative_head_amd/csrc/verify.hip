@@ -1424,19 +1424,30 @@ void verify_f32_tiny_kernel(
 // committed rows to S and empties the log.  Header words go to separate output buffers, so
 // no item can see another item's update of the same sequence within one launch.
 
-// Up to 16 rank-one terms applied to this wave's 16 state rows of an item, on the matrix
-// cores: rows 16w .. 16w + 15 of the item's S rows in LDS (chunk c of row r at c ^ (r % 16))
-// become c0 * S + sum_k coef_k u_k k_k^T, with u_k the item's 64 values of term k (fp32 rows
-// of kSmallRows at byte u_area + 4 kSmallRows k) and k_k its key row (bf16, 256-byte rows at
-// byte k_area + 256 k, k < k_rows).  Lane (g, n) = (lane / 16, lane % 16) supplies terms
-// 4g .. 4g + 3 (coef[t] for term 4g + t) of row 16w + n; terms from cnt on count as zero.
-// Per 16-column tile one pair of v_mfma_f32_16x16x16_bf16: A = the key rows read transposed
-// out of LDS (ds_read_b64_tr_b16), B = the coefficient-scaled values split into bf16 hi and lo
-// (an fp32-grade product), C = the rows themselves.
-__device__ __forceinline__ void small_apply_terms(float* lds, uint32_t lds_addr, int cnt,
-                                                  const float (&coef)[4], float c0,
-                                                  uint32_t u_area, uint32_t k_area, int k_rows,
-                                                  int wave, int lane) {
+// The 16-byte chunk c of staged key row q (PK) sits at chunk c ^ head_pk_swizzle(q): the
+// transposing reads of apply_terms take the same 32 bytes of 16 rows at once, which
+// this spreads over the LDS banks (two rows per bank group instead of sixteen).
+__device__ __forceinline__ uint32_t head_pk_swizzle(int q) {
+    return 2u * (static_cast<uint32_t>(q) & 7u);
+}
+
+// Up to 16 rank-one terms applied to this wave's 16 rows of the state in LDS, on the matrix
+// cores: S[r] <- c0 S[r] + sum over slots k < cnt of coef_k U_k[r] key_k^T, r = 16w + n (rows of
+// the item in LDS, chunk c of row r at c ^ (r % 16)).  U_k is the slot's fp32 row of UStride
+// values at byte u_area + 4 UStride k (r indexes it), key_k its bf16 row of 256 bytes at byte
+// k_area + 256 k (k < k_rows staged; with Swizzled its 16-byte chunks sit at c ^
+// head_pk_swizzle(k)).  Taken per 16-column tile jt as Delta^T = K^T (coef U) with
+// v_mfma_f32_16x16x16_bf16: lane (g = lane / 16, n = lane % 16) gives A = key[4g + t][16 jt
+// + n], t = 0..3 (one transposing LDS read of the key rows: the 16 lanes of a group address
+// a block of 4 key rows x 16 columns and each receives one column), B = coef_{4g+t}
+// U_{4g+t}[r] split into bf16 hi + lo (two products; the keys are exact in bf16,
+// |x - hi - lo| <= 2^-18 |x|), C = c0 times the lane's 16-byte chunk 4 jt + g of row r, and
+// D, the same four columns of row r after the update, goes back where C came from.  Slots
+// past cnt are zero in both operands.  `coef` holds the lane's slots 4g..4g+3.
+template <int UStride, bool Swizzled>
+__device__ __forceinline__ void apply_terms(float* lds, uint32_t lds_addr, int cnt,
+                                            const float (&coef)[4], float c0, uint32_t u_area,
+                                            uint32_t k_area, int k_rows, int wave, int lane) {
     const int g = lane >> 4;
     const int n = lane & 15;
     const int r = 16 * wave + n;
@@ -1445,20 +1456,21 @@ __device__ __forceinline__ void small_apply_terms(float* lds, uint32_t lds_addr,
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int k = 4 * g + t;
-        u[t] = k < cnt ? coef[t] * PU[k * kSmallRows + r] : 0.f;
+        u[t] = k < cnt ? coef[t] * PU[k * UStride + r] : 0.f;
     }
     // the key row this lane addresses (clamped into the staged rows; masked below) and its
     // 8 bytes of each tile: chunk 2 jt + (n % 4) / 2 of the row, half n % 2
     const int qrow = 4 * g + (n >> 2) < k_rows ? 4 * g + (n >> 2) : 0;
+    const uint32_t sw = Swizzled ? head_pk_swizzle(qrow) : 0u;
     const uint32_t arow = lds_addr + k_area + 256u * static_cast<uint32_t>(qrow) + 8u * static_cast<uint32_t>(n & 1);
     const uint32_t h2 = static_cast<uint32_t>(n & 3) >> 1;
     // every read first (the writes below may alias them as far as the compiler knows)
-    i16x4_t ak[D / 16];
+    i16x4_t a[D / 16];
     f32x4_t c[D / 16];
 #pragma unroll
     for (int jt = 0; jt < D / 16; ++jt)
-        ak[jt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(
-            static_cast<uintptr_t>(arow + 16u * (2u * jt + h2))));
+        a[jt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(
+            static_cast<uintptr_t>(arow + 16u * ((2u * jt + h2) ^ sw))));
 #pragma unroll
     for (int jt = 0; jt < D / 16; ++jt)
         c[jt] = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * ((4 * jt + g) ^ (r & 15)));
@@ -1472,7 +1484,7 @@ __device__ __forceinline__ void small_apply_terms(float* lds, uint32_t lds_addr,
     const uint32_t m1 = (4 * g + 2 < cnt ? 0x0000ffffu : 0u) | (4 * g + 3 < cnt ? 0xffff0000u : 0u);
 #pragma unroll
     for (int jt = 0; jt < D / 16; ++jt) {
-        u32x2_t aw = __builtin_bit_cast(u32x2_t, ak[jt]);
+        u32x2_t aw = __builtin_bit_cast(u32x2_t, a[jt]);
         aw[0] &= m0;
         aw[1] &= m1;
         const i16x4_t am = __builtin_bit_cast(i16x4_t, aw);
@@ -1483,6 +1495,7 @@ __device__ __forceinline__ void small_apply_terms(float* lds, uint32_t lds_addr,
     for (int jt = 0; jt < D / 16; ++jt)
         *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * ((4 * jt + g) ^ (r & 15))) = c[jt];
 }
+
 
 // NFIX > 0: a form compiled for trees of exactly NFIX nodes (every mode on up to 8 nodes),
 // whose LDS offsets, loop bounds and pointer-jumping rounds are constants; 0: N at run time.
@@ -1501,7 +1514,7 @@ void verify_small_kernel(
     constexpr bool FUSED = MODE != 0;
     constexpr bool DEFER = MODE == 2;
     constexpr bool TWO = small_two_sets(NCT, MODE); // two input sets, early refills
-    // the deferred commit's terms on the matrix cores (small_apply_terms) on 9-16 nodes; on up
+    // the deferred commit's terms on the matrix cores (apply_terms) on 9-16 nodes; on up
     // to 8 the vector-ALU form (the product's registers would spill at this kernel's budget
     // of three waves per SIMD)
     constexpr bool kMatrixDefer = DEFER && NCT == 2;
@@ -1627,7 +1640,7 @@ void verify_small_kernel(
                 // sit in LDS, in the layout they arrived in (lane l: row 16w + 2i + l / 32,
                 // 16-byte chunk l % 32, for i = 0..7), and written back to HBM from there when
                 // flushing: every store is two whole 512-byte rows (the deferred form on 9-16
-                // nodes applies the terms with small_apply_terms instead).  The path's gammas
+                // nodes applies the terms with apply_terms instead).  The path's gammas
                 // are in LDS in path order (a is last).
                 const float* PU = reinterpret_cast<const float*>(ldsb + sb + L.pu);
                 const char* PK = ldsb + sb + L.pk;
@@ -1641,7 +1654,7 @@ void verify_small_kernel(
                     bool scaled = false;
                     if (len > 0) {
                         const float coef[4] = {gs, gs, gs, gs};
-                        small_apply_terms(lds, lds_addr, len, coef, gs, sb + L.lu, sb + L.lk,
+                        apply_terms<kSmallRows, false>(lds, lds_addr, len, coef, gs, sb + L.lu, sb + L.lk,
                                           4 * ((dlog.Lmax + 3) / 4), wave, lane);
                         scaled = true;
                     }
@@ -1662,7 +1675,7 @@ void verify_small_kernel(
                             const int q = q0 + 4 * g + t;
                             coef[t] = ga * __builtin_amdgcn_rcpf(PG[q < 64 ? q : 0]);
                         }
-                        small_apply_terms(lds, lds_addr, cnt, coef, scaled ? 1.0f : gs,
+                        apply_terms<kSmallRows, false>(lds, lds_addr, cnt, coef, scaled ? 1.0f : gs,
                                           sb + L.pu, sb + L.pk, L.path, wave, lane);
                         scaled = true;
                     }
@@ -2485,12 +2498,6 @@ struct HeadLds {
     static constexpr int kWait = (2 * NKT) | (7 << 4) | (15 << 8);
 };
 
-// The 16-byte chunk c of staged key row q (PK) sits at chunk c ^ head_pk_swizzle(q): the
-// transposing reads of head_apply_terms take the same 32 bytes of 16 rows at once, which
-// this spreads over the LDS banks (two rows per bank group instead of sixteen).
-__device__ __forceinline__ uint32_t head_pk_swizzle(int q) {
-    return 2u * (static_cast<uint32_t>(q) & 7u);
-}
 
 // A head's key, query and value rows, parents, alphas and betas -> LDS (layout above): per
 // four nodes one transfer of key rows, one of query rows and one of value rows, then three
@@ -2646,67 +2653,14 @@ __device__ __forceinline__ void head_issue_terms(const CommitIn& c, const DeferL
 }
 
 // One staged chunk of commit terms applied to this wave's 16 rows of S in LDS, on the matrix
-// cores: S[r] <- c0 S[r] + sum over slots k < cnt of coef_k U_k[r] key_k^T, r = 16w + n
-// (U_k the slot's 512-byte row in PU, key_k its bf16 row in PK, 16-byte chunks swizzled by
-// head_pk_swizzle).  Taken per 16-column tile jt as Delta^T = K^T (coef U) with
-// v_mfma_f32_16x16x16_bf16: lane (g = lane / 16, n = lane % 16) gives A = key[4g + t][16 jt
-// + n], t = 0..3 (one transposing LDS read of the key rows: the 16 lanes of a group address
-// a block of 4 key rows x 16 columns and each receives one column), B = coef_{4g+t}
-// U_{4g+t}[r] split into bf16 hi + lo (two products; the keys are exact in bf16,
-// |x - hi - lo| <= 2^-18 |x|), C = c0 times the lane's 16-byte chunk 4 jt + g of row r, and
-// D, the same four columns of row r after the update, goes back where C came from.  Slots
-// past cnt are zero in both operands.  `coef` holds the lane's slots 4g..4g+3.
+// cores (apply_terms): U rows of 512 bytes in PU, key rows in PK with 16-byte chunks swizzled
+// by head_pk_swizzle.
 template <int NKT>
 __device__ __forceinline__ void head_apply_terms(float* lds, uint32_t lds_addr, int cnt,
                                                  const float (&coef)[4], float c0, int wave,
                                                  int lane) {
     using L = HeadLds<NKT>;
-    const int g = lane >> 4;
-    const int n = lane & 15;
-    const int r = 16 * wave + n;
-    const float* PU = reinterpret_cast<const float*>(reinterpret_cast<const char*>(lds) + L::kPU);
-    f32x4_t u;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int k = 4 * g + t;
-        u[t] = k < cnt ? coef[t] * PU[k * D + r] : 0.f;
-    }
-    // the key row this lane addresses (clamped into the staged rows; masked below) and its
-    // 8 bytes of each tile: chunk 2 jt + (n % 4) / 2 of the row, half n % 2
-    const int qrow = 4 * g + (n >> 2) < L::kPath ? 4 * g + (n >> 2) : 0;
-    const uint32_t sw = head_pk_swizzle(qrow);
-    const uint32_t arow = lds_addr + L::kPK + 256u * static_cast<uint32_t>(qrow) + 8u * static_cast<uint32_t>(n & 1);
-    const uint32_t h2 = static_cast<uint32_t>(n & 3) >> 1;
-    // every read first (the writes below may alias them as far as the compiler knows)
-    i16x4_t a[D / 16];
-    f32x4_t c[D / 16];
-#pragma unroll
-    for (int jt = 0; jt < D / 16; ++jt)
-        a[jt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(
-            static_cast<uintptr_t>(arow + 16u * ((2u * jt + h2) ^ sw))));
-#pragma unroll
-    for (int jt = 0; jt < D / 16; ++jt)
-        c[jt] = *reinterpret_cast<const f32x4_t*>(lds + r * D + 4 * ((4 * jt + g) ^ (r & 15)));
-    const bf16x4_t uh = __builtin_convertvector(u, bf16x4_t);
-    const u32x2_t hw = __builtin_bit_cast(u32x2_t, uh);
-    const f32x4_t rem = {u[0] - __uint_as_float(hw[0] << 16), u[1] - __uint_as_float(hw[0] & 0xffff0000u),
-                         u[2] - __uint_as_float(hw[1] << 16), u[3] - __uint_as_float(hw[1] & 0xffff0000u)};
-    const i16x4_t bh = __builtin_bit_cast(i16x4_t, uh);
-    const i16x4_t bl = __builtin_bit_cast(i16x4_t, __builtin_convertvector(rem, bf16x4_t));
-    const uint32_t m0 = (4 * g < cnt ? 0x0000ffffu : 0u) | (4 * g + 1 < cnt ? 0xffff0000u : 0u);
-    const uint32_t m1 = (4 * g + 2 < cnt ? 0x0000ffffu : 0u) | (4 * g + 3 < cnt ? 0xffff0000u : 0u);
-#pragma unroll
-    for (int jt = 0; jt < D / 16; ++jt) {
-        u32x2_t aw = __builtin_bit_cast(u32x2_t, a[jt]);
-        aw[0] &= m0;
-        aw[1] &= m1;
-        const i16x4_t am = __builtin_bit_cast(i16x4_t, aw);
-        c[jt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bh, c0 * c[jt], 0, 0, 0);
-        c[jt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bl, c[jt], 0, 0, 0);
-    }
-#pragma unroll
-    for (int jt = 0; jt < D / 16; ++jt)
-        *reinterpret_cast<f32x4_t*>(lds + r * D + 4 * ((4 * jt + g) ^ (r & 15))) = c[jt];
+    apply_terms<D, true>(lds, lds_addr, cnt, coef, c0, L::kPU, L::kPK, L::kPath, wave, lane);
 }
 
 // This wave's 16 rows of S, final in LDS, to S in HBM as whole 512-byte rows (lane l: row
